@@ -1,0 +1,145 @@
+"""Oracle, part 1: the Vertical-Slash index (test infrastructure only).
+
+Follows the MTraining paper note, Algorithm 1 ("dynamic sparse training
+head"), and MTraining (arXiv 2510.18830) §4.1:
+
+* an observation window of the last ``last_q`` queries is scored against all
+  keys with a causal softmax (Algorithm 1, first step);
+* vertical scores are column sums of the window probabilities, at token
+  granularity; slash scores are the window probability mass on each
+  block-diagonal of the 64x64 block grid (§4.1 (ii): verticals per token,
+  slashes pooled over 64x64 blocks);
+* ``argtopk`` keeps the k highest scores; ties go to the lowest index;
+* ``sparseformat`` turns (vertical columns, slash block-diagonals) into the
+  attention mask: causal, and the column is selected or the block-diagonal is.
+
+Positions are global token positions inside one batch row.  A segment
+[a, e) is one packed document; its block index of position p is
+beta(p) = floor((p - a) / B).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-int(a) // int(b))
+
+
+def capacities(v_budget: int, s_budget: int, seg_len: int, n_total: int, block: int):
+    """Number of verticals and slash block-diagonals kept for one segment.
+
+    Budgets are tokens over the whole packed row; a segment of length L gets
+    ceil(k * L / N) of each, the slash share is turned into ceil(share / B)
+    block-diagonals, and both are clipped to the number of candidates (L
+    columns, ceil(L / B) block-diagonals).  With one segment this is
+    (min(k_v, N), min(ceil(k_s / B), N / B)).
+    """
+    share_v = _ceil_div(v_budget * seg_len, n_total)
+    share_s = _ceil_div(s_budget * seg_len, n_total)
+    nb = _ceil_div(seg_len, block)
+    return min(share_v, seg_len), min(_ceil_div(share_s, block), nb)
+
+
+def window_probs(q_h: np.ndarray, k_h: np.ndarray, a: int, e: int, scale: float, last_q: int):
+    """Observation-window attention probabilities A_hat (Algorithm 1, first step).
+
+    q_h: [N, d], k_h: [N, d] float64 rows of one head.  The window is the last
+    w = min(last_q, L) rows of the segment [a, e).  Each window row r is a
+    softmax over the keys a <= m <= r.  Returns (rows, A_hat [w, L], lse [w]).
+    """
+    w = min(last_q, e - a)
+    rows = np.arange(e - w, e)
+    cols = np.arange(a, e)
+    s = scale * (q_h[rows] @ k_h[a:e].T)
+    causal = cols[None, :] <= rows[:, None]
+    s = np.where(causal, s, -np.inf)
+    mx = s.max(axis=1)
+    lse = mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
+    probs = np.exp(s - lse[:, None])
+    return rows, probs, lse
+
+
+def window_scores(q_h, k_h, a, e, scale, block, last_q):
+    """Vertical scores v[m] (token columns) and slash scores sigma[g] (block-diagonals).
+
+    v[m] = sum over window rows of A_hat[r, m] (Algorithm 1, ``sum_v``).
+    sigma[g] = sum of A_hat[r, m] over window entries whose block offset
+    beta(r) - beta(m) equals g (``sum_s`` pooled on the 64x64 grid, §4.1 (ii)).
+    Returns (v [L] indexed by m - a, sigma [nb]).
+    """
+    rows, probs, _ = window_probs(q_h, k_h, a, e, scale, last_q)
+    L = e - a
+    nb = _ceil_div(L, block)
+    v = probs.sum(axis=0)
+    g = ((rows - a) // block)[:, None] - (np.arange(L) // block)[None, :]
+    keep = probs > 0
+    sigma = np.bincount(g[keep], weights=probs[keep], minlength=nb)
+    return v, sigma
+
+
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """``argtopk``: the k highest scores, ties to the lowest index, returned ascending."""
+    k = min(int(k), scores.shape[0])
+    order = np.lexsort((np.arange(scores.shape[0]), -scores))
+    return np.sort(order[:k])
+
+
+def estimate_index(q, k, cu_seqlens, v_budget, s_budget, block=64, last_q=64, scale=None,
+                   return_scores=False):
+    """Vertical-Slash index for every (Q head, segment) of one batch row.
+
+    q: [N, Hq, d], k: [N, Hkv, d] (any float dtype; computed in float64).
+    Q head h reads KV head floor(h * Hkv / Hq) (grouped-query attention).
+    v_budget / s_budget: per Q head, tokens.
+    Returns {(h, seg): (iv, is_)} with iv global token positions (ascending)
+    and is_ block-diagonal offsets g (ascending); optionally also the scores.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    out, scores = {}, {}
+    for h in range(hq):
+        g = h * hkv // hq
+        for s in range(len(cu_seqlens) - 1):
+            a, e = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+            kv, kg = capacities(v_budget[h], s_budget[h], e - a, n, block)
+            v, sigma = window_scores(q[:, h], k[:, g], a, e, scale, block, last_q)
+            out[(h, s)] = (select_topk(v, kv) + a, select_topk(sigma, kg))
+            scores[(h, s)] = (v, sigma)
+    return (out, scores) if return_scores else out
+
+
+def _segment_of(pos, cu_seqlens):
+    return np.searchsorted(np.asarray(cu_seqlens), pos, side="right") - 1
+
+
+def dense_mask(rows_pos, cols_pos, cu_seqlens, index, h, block=64):
+    """``sparseformat``: boolean mask [len(rows_pos), len(cols_pos)] for Q head h.
+
+    M[n, m] holds when n and m lie in the same segment, m <= n (causal), and
+    m is a selected vertical or beta(n) - beta(m) is a selected
+    block-diagonal.  Vertical and slash entries form a union (Algorithm 1).
+    rows_pos / cols_pos are global positions, so a striped chunk's mask is the
+    global mask restricted to its rows and columns.
+    """
+    rows_pos = np.asarray(rows_pos)
+    cols_pos = np.asarray(cols_pos)
+    sr = _segment_of(rows_pos, cu_seqlens)
+    sc = _segment_of(cols_pos, cu_seqlens)
+    M = np.zeros((rows_pos.size, cols_pos.size), dtype=bool)
+    for s in range(len(cu_seqlens) - 1):
+        a = int(cu_seqlens[s])
+        ri = np.nonzero(sr == s)[0]
+        ci = np.nonzero(sc == s)[0]
+        if ri.size == 0 or ci.size == 0:
+            continue
+        iv, is_ = index[(h, s)]
+        n = rows_pos[ri][:, None]
+        m = cols_pos[ci][None, :]
+        vert = np.isin(m, iv)
+        slash = np.isin((n - a) // block - (m - a) // block, is_)
+        M[np.ix_(ri, ci)] = (m <= n) & (vert | slash)
+    return M

@@ -1,0 +1,478 @@
+"""Pins of the CPU oracle against facts the pages and mathematics fix (no GPU).
+
+Each test names the passage or the mathematical fact that fixes the expected
+value, so that a slip in the oracle (a dropped term, a wrong sign, index or
+operand) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import rope as orope
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_index(rng, n, hq, block, cu=None, kv=None, kg=None):
+    """Random (not estimated) Vertical-Slash index for every (head, segment)."""
+    cu = cu or [0, n]
+    idx = {}
+    for h in range(hq):
+        for s in range(len(cu) - 1):
+            a, e = cu[s], cu[s + 1]
+            L = e - a
+            nb = -(-L // block)
+            nv = rng.integers(0, L + 1) if kv is None else min(kv, L)
+            ng = rng.integers(0, nb + 1) if kg is None else min(kg, nb)
+            iv = np.sort(rng.choice(L, size=nv, replace=False)) + a
+            is_ = np.sort(rng.choice(nb, size=ng, replace=False))
+            idx[(h, s)] = (iv.astype(np.int64), is_.astype(np.int64))
+    return idx
+
+
+def full_index(n, hq, block, cu=None):
+    cu = cu or [0, n]
+    return {(h, s): (np.zeros(0, np.int64), np.arange(-(-(cu[s + 1] - cu[s]) // block)))
+            for h in range(hq) for s in range(len(cu) - 1)}
+
+
+def triple_loop_causal(q, k, v, scale):
+    """Textbook causal softmax attention, scalar Python loops (one head)."""
+    n, d = q.shape
+    out = np.zeros_like(v)
+    lse = np.zeros(n)
+    for i in range(n):
+        s = [scale * sum(q[i, c] * k[j, c] for c in range(d)) for j in range(i + 1)]
+        mx = max(s)
+        z = sum(math.exp(x - mx) for x in s)
+        lse[i] = mx + math.log(z)
+        for j in range(i + 1):
+            p = math.exp(s[j] - lse[i])
+            out[i] += p * v[j]
+    return out, lse
+
+
+# ---------------------------------------------------------------- P1 brute force
+def test_p1_all_blocks_equals_dense_causal():
+    """All block-diagonals selected gives plain causal attention (Algorithm 1 mask)."""
+    rng = np.random.default_rng(1)
+    n, d, B = 48, 8, 16
+    q, k, v = (rng.standard_normal((n, 1, d)) for _ in range(3))
+    pos = np.arange(n)
+    O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], full_index(n, 1, B), B)
+    O2, L2 = triple_loop_causal(q[:, 0], k[:, 0], v[:, 0], 1 / math.sqrt(d))
+    assert np.abs(O[:, 0] - O2).max() < 1e-12
+    assert np.abs(L[0] - L2).max() < 1e-12
+    # the same with every vertical selected and no slash
+    idx = {(0, 0): (np.arange(n), np.zeros(0, np.int64))}
+    O3, L3 = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], idx, B)
+    assert np.abs(O3 - O).max() < 1e-12 and np.abs(L3 - L).max() < 1e-12
+
+
+def test_p1_gqa_fwd_bwd_equals_torch_sdpa():
+    """Full index, GQA: forward and gradients equal torch's causal SDPA in fp64 on CPU."""
+    rng = np.random.default_rng(2)
+    n, hq, hkv, d, B = 128, 4, 2, 16, 32
+    q, do = rng.standard_normal((n, hq, d)), rng.standard_normal((n, hq, d))
+    k, v = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    pos = np.arange(n)
+    idx = full_index(n, hq, B)
+    O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], idx, B)
+    D = oracle.bwd_delta(O, do)
+    assert np.abs(D - (O * do).sum(-1).T).max() < 1e-15
+    dq, dk, dv = oracle.attn_bwd_dense(q, k, v, do, L, D, pos, pos, [0, n], idx, B)
+    tq = torch.tensor(q).permute(1, 0, 2).requires_grad_()
+    tk = torch.tensor(k).permute(1, 0, 2).requires_grad_()
+    tv = torch.tensor(v).permute(1, 0, 2).requires_grad_()
+    kk = tk.repeat_interleave(hq // hkv, 0)
+    vv = tv.repeat_interleave(hq // hkv, 0)
+    to = torch.nn.functional.scaled_dot_product_attention(tq, kk, vv, is_causal=True)
+    to.backward(torch.tensor(do).permute(1, 0, 2))
+    assert np.abs(to.detach().permute(1, 0, 2).numpy() - O).max() < 1e-12
+    assert np.abs(tq.grad.permute(1, 0, 2).numpy() - dq).max() < 1e-12
+    assert np.abs(tk.grad.permute(1, 0, 2).numpy() - dk).max() < 1e-12
+    assert np.abs(tv.grad.permute(1, 0, 2).numpy() - dv).max() < 1e-12
+
+
+# ---------------------------------------------------------------- P2 special case
+def test_p2_diagonal_only_is_block_local_causal():
+    """I_s = {0}, no verticals: each block is an independent causal attention."""
+    rng = np.random.default_rng(3)
+    n, d, B = 96, 8, 32
+    q, k, v = (rng.standard_normal((n, 1, d)) for _ in range(3))
+    pos = np.arange(n)
+    idx = {(0, 0): (np.zeros(0, np.int64), np.array([0]))}
+    O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], idx, B)
+    for b in range(n // B):
+        sl = slice(b * B, (b + 1) * B)
+        t = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(q[sl, 0])[None], torch.tensor(k[sl, 0])[None], torch.tensor(v[sl, 0])[None],
+            is_causal=True)[0].numpy()
+        assert np.abs(O[sl, 0] - t).max() < 1e-12
+
+
+# ---------------------------------------------------------------- P3 closed forms
+def test_p3_zero_query_hand_derived_mask():
+    """Q = 0 makes every score 0: LSE[n] = ln|M_n|, O[n] = mean of V over the row's support.
+
+    The support sizes come from the fixture, derived by hand from the mask
+    definition (causal and (selected column or selected block-diagonal)).
+    """
+    with open(os.path.join(GOLDEN, "zero_query_mask.json")) as f:
+        fx = json.load(f)
+    n, B, d = fx["n"], fx["block"], 4
+    idx = {(0, 0): (np.array(fx["verticals"]), np.array(fx["slashes"]))}
+    rng = np.random.default_rng(4)
+    q = np.zeros((n, 1, d))
+    k, v, do = (rng.standard_normal((n, 1, d)) for _ in range(3))
+    pos = np.arange(n)
+    O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], idx, B)
+    O2, L2 = oracle.attn_fwd_support(q, k, v, pos, pos, [0, n], idx, B)
+    sizes = np.zeros(n, np.int64)
+    for lo, hi, cnt in fx["row_support_sizes"]:
+        sizes[lo:hi] = cnt
+    # rows that see column 130 only from n >= 130 on
+    for r in fx["plus_one_from"]:
+        sizes[r[0]:r[1]] += np.arange(r[1] - r[0]) >= (r[2] - r[0])
+    emp = sizes == 0
+    assert np.all(np.isneginf(L[0, emp])) and np.all(O[emp] == 0)
+    assert np.abs(L[0, ~emp] - np.log(sizes[~emp])).max() < 1e-12
+    assert np.allclose(L2, L, atol=1e-12, equal_nan=False) or np.array_equal(L2, L)
+    M = oracle.dense_mask(pos, pos, [0, n], idx, 0, B)
+    assert np.array_equal(M.sum(1), sizes)
+    mean_v = (M.astype(float) @ v[:, 0]) / np.maximum(sizes, 1)[:, None]
+    assert np.abs(O[:, 0] - mean_v).max() < 1e-12
+    # dV[m] = sum over rows n that see m of dO[n] / |M_n| (Eq. 2 with A = M / |M_n|)
+    D = (O * do).sum(-1).T
+    _, _, dv = oracle.attn_bwd_dense(q, k, v, do, L, D, pos, pos, [0, n], idx, B)
+    w = M / np.maximum(sizes, 1)[:, None]
+    assert np.abs(dv[:, 0] - w.T @ do[:, 0]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- P4 finite differences
+def test_p4_finite_differences_and_delta_identity():
+    """Gradients of L = sum(O * dO) wrt Q, K, V by central differences (index fixed)."""
+    rng = np.random.default_rng(5)
+    n, hq, hkv, d, B = 64, 2, 1, 8, 16
+    q, do = rng.standard_normal((n, hq, d)), rng.standard_normal((n, hq, d))
+    k, v = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    pos = np.arange(n)
+    idx = rand_index(rng, n, hq, B, kv=6, kg=2)
+    O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], idx, B)
+    D = (O * do).sum(-1).T
+    dq, dk, dv = oracle.attn_bwd_dense(q, k, v, do, L, D, pos, pos, [0, n], idx, B)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attn_fwd_dense(qq, kk, vv, pos, pos, [0, n], idx, B)
+        return (o * do).sum()
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        flat = x.reshape(-1)
+        picks = rng.choice(flat.size, size=40, replace=False)
+        for p in picks:
+            xp, xm = flat.copy(), flat.copy()
+            xp[p] += h
+            xm[p] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp.reshape(x.shape)
+            lp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm.reshape(x.shape)
+            lm = loss(args["q"], args["k"], args["v"])
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g.reshape(-1)[p]) <= 1e-6 * max(1.0, abs(fd)), (name, p)
+    # D = rowsum(dA * A) (Eq. 1) equals rowsum(dO * O)
+    for hh in range(hq):
+        M = oracle.dense_mask(pos, pos, [0, n], idx, hh, B)
+        S = np.where(M, (q[:, hh] @ k[:, 0].T) / math.sqrt(d), -np.inf)
+        A = np.where(M, np.exp(S - np.where(np.isfinite(L[hh]), L[hh], 0)[:, None]), 0)
+        dA = do[:, hh] @ v[:, 0].T
+        assert np.abs((dA * A).sum(1) - D[hh]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- P5 exact merge identity
+def test_p5_lse_merge_identity_over_random_partitions():
+    rng = np.random.default_rng(6)
+    n, hq, d, B = 128, 2, 8, 32
+    q = rng.standard_normal((n, hq, d))
+    k, v = rng.standard_normal((n, 1, d)), rng.standard_normal((n, 1, d))
+    pos = np.arange(n)
+    idx = rand_index(rng, n, hq, B, kv=20, kg=2)
+    O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], idx, B)
+    for nchunks in (2, 5, 32):
+        owner = rng.integers(0, nchunks, size=n)
+        acc_o = np.zeros((hq, n, d))
+        acc_l = np.full((hq, n), -np.inf)
+        for c in rng.permutation(nchunks):
+            cols = np.nonzero(owner == c)[0]
+            o, l = oracle.attn_fwd_dense(q, k[cols], v[cols], pos, cols, [0, n], idx, B)
+            acc_o, acc_l = oracle.lse_merge(acc_o, acc_l, o.transpose(1, 0, 2), l)
+        fin = np.isfinite(L)
+        assert np.array_equal(np.isneginf(acc_l), ~fin)
+        assert np.abs(acc_l[fin] - L[fin]).max() < 1e-12
+        assert np.abs(acc_o - O.transpose(1, 0, 2)).max() < 1e-12
+
+
+def test_p5_merge_algebra():
+    rng = np.random.default_rng(7)
+    o = [rng.standard_normal((5, 3)) for _ in range(3)]
+    l = [rng.standard_normal(5) * 4 for _ in range(3)]
+    l[1][2] = -np.inf
+    o[1][2] = 0
+    a = oracle.lse_merge(*oracle.lse_merge(o[0], l[0], o[1], l[1]), o[2], l[2])
+    b = oracle.lse_merge(o[0], l[0], *oracle.lse_merge(o[1], l[1], o[2], l[2]))
+    c = oracle.lse_merge(o[1], l[1], o[0], l[0])
+    d_ = oracle.lse_merge(o[0], l[0], o[1], l[1])
+    assert np.allclose(a[0], b[0], atol=1e-14) and np.allclose(a[1], b[1], atol=1e-14)
+    assert np.array_equal(c[1], d_[1]) and np.allclose(c[0], d_[0], atol=1e-15)
+    e = oracle.lse_merge(o[0], l[0], np.zeros((5, 3)), np.full(5, -np.inf))
+    assert np.array_equal(e[1], l[0]) and np.allclose(e[0], o[0], atol=1e-15)
+    z = oracle.lse_merge(np.zeros((5, 3)), np.full(5, -np.inf), np.zeros((5, 3)), np.full(5, -np.inf))
+    assert np.all(np.isneginf(z[1])) and np.all(z[0] == 0)
+    # two halves of one softmax: log-add-exp of the halves' sums
+    s = rng.standard_normal(10)
+    vv = rng.standard_normal((10, 3))
+    def part(ix):
+        m = s[ix].max()
+        p = np.exp(s[ix] - m)
+        return (p @ vv[ix]) / p.sum(), m + np.log(p.sum())
+    o1, l1 = part(np.arange(4))
+    o2, l2 = part(np.arange(4, 10))
+    om, lm = oracle.lse_merge(o1[None], np.array([l1]), o2[None], np.array([l2]))
+    p = np.exp(s - s.max())
+    assert abs(lm[0] - (s.max() + np.log(p.sum()))) < 1e-14
+    assert np.abs(om[0] - (p @ vv) / p.sum()).max() < 1e-14
+
+
+# ---------------------------------------------------------------- P6 tie pins / selection
+def test_p6_zero_query_ties_go_to_lowest_index():
+    """Q = 0: every window row is uniform over its causal keys, so v[m] is equal for
+    all m up to the first window row and sigma[g] is equal for g >= 1 (sigma[0] smaller)."""
+    rng = np.random.default_rng(8)
+    n, d, B = 512, 8, 64
+    q = np.zeros((n, 1, d))
+    k = rng.standard_normal((n, 1, d))
+    idx, sc = oracle.estimate_index(q, k, [0, n], [100], [3 * B], B, 64, return_scores=True)
+    iv, is_ = idx[(0, 0)]
+    assert np.array_equal(iv, np.arange(100))
+    assert np.array_equal(is_, np.array([1, 2, 3]))
+    v, sigma = sc[(0, 0)]
+    assert np.all(v[: n - 63] == v[0]) and np.all(v[n - 63:] < v[0])
+    assert np.allclose(sigma[1:], sigma[1]) and sigma[0] < sigma[1]
+
+
+def test_p6_duplicate_keys_lower_index_wins():
+    rng = np.random.default_rng(9)
+    n, d, B = 256, 8, 64
+    q = rng.standard_normal((n, 1, d))
+    k = rng.standard_normal((n, 1, d))
+    k[40] = k[7] * 5
+    k[7] = k[7] * 5
+    _, sc = oracle.estimate_index(q, k, [0, n], [1], [0], B, 64, return_scores=True)
+    v, _ = sc[(0, 0)]
+    assert v[7] == v[40]
+    kmax = int(np.argmax(v))
+    assert kmax == 7
+    idx = oracle.estimate_index(q, k, [0, n], [1], [0], B, 64)
+    assert idx[(0, 0)][0].tolist() == [7]
+
+
+def test_p6_topk_matches_stable_sort():
+    rng = np.random.default_rng(10)
+    for _ in range(50):
+        x = rng.integers(0, 6, size=40).astype(float)
+        kk = int(rng.integers(0, 41))
+        ref = sorted(sorted(range(40), key=lambda i: (-x[i], i))[:kk])
+        assert oracle.select_topk(x, kk).tolist() == ref
+
+
+# ---------------------------------------------------------------- P7 RoPE / Theorem 3.1
+def test_p7_rope_shift_invariance():
+    rng = np.random.default_rng(11)
+    d = 128
+    for _ in range(20):
+        q, k = rng.standard_normal(d), rng.standard_normal(d)
+        n, m = rng.integers(0, 524288, size=2)
+        t = int(rng.integers(-min(n, m), 524288 - max(n, m)))
+        z1 = orope.rope(q, n) @ orope.rope(k, m)
+        z2 = orope.rope(q, n + t) @ orope.rope(k, m + t)
+        assert abs(z1 - z2) <= 1e-10 * max(1.0, abs(z1))
+
+
+def test_p7_rope_expectation_matches_eq14():
+    """Monte Carlo mean of z at fixed n - m agrees with Eq. 14 within 5 standard errors."""
+    rng = np.random.default_rng(12)
+    d, ns = 16, 100000
+    mu_q, mu_k = rng.standard_normal(d), rng.standard_normal(d)
+    Lm = rng.standard_normal((2 * d, 2 * d)) * 0.3
+    cov = Lm @ Lm.T + np.eye(2 * d) * 0.2
+    x = rng.multivariate_normal(np.concatenate([mu_q, mu_k]), cov, size=ns)
+    qs, ks = x[:, :d], x[:, d:]
+    C = cov[:d, d:]
+    for n, m in ((7, 3), (1000, 996), (40, 0), (300, 260)):
+        z = (orope.rope(qs, np.full(ns, n)) * orope.rope(ks, np.full(ns, m))).sum(1)
+        se = z.std() / math.sqrt(ns)
+        ez = orope.expected_score(n - m, mu_q, mu_k, C)
+        assert abs(z.mean() - ez) < 5 * se, (n, m, z.mean(), ez, se)
+    # the closed form itself depends on n - m only and is not symmetric in the sign of n - m
+    assert abs(orope.expected_score(4, mu_q, mu_k, C) - orope.expected_score(-4, mu_q, mu_k, C)) > 1e-6
+
+
+# ---------------------------------------------------------------- P8 invariants
+def test_p8_score_normalisation_and_index_invariants():
+    rng = np.random.default_rng(13)
+    n, hq, hkv, d, B = 640, 4, 2, 16, 64
+    q = rng.standard_normal((n, hq, d))
+    k = rng.standard_normal((n, hkv, d))
+    cu = [0, 192, 640]
+    vb, sb = [100, 30, 640, 0], [64, 500, 7, 640]
+    idx, sc = oracle.estimate_index(q, k, cu, vb, sb, B, 64, return_scores=True)
+    for (h, s), (iv, is_) in idx.items():
+        a, e = cu[s], cu[s + 1]
+        kv, kg = oracle.capacities(vb[h], sb[h], e - a, n, B)
+        assert iv.size == kv and is_.size == kg
+        assert np.all(np.diff(iv) > 0) and np.all(np.diff(is_) > 0)
+        assert iv.size == 0 or (iv.min() >= a and iv.max() < e)
+        assert is_.size == 0 or (is_.min() >= 0 and is_.max() < -(-(e - a) // B))
+        v, sigma = sc[(h, s)]
+        w = min(64, e - a)
+        assert abs(v.sum() - w) < 1e-9 and abs(sigma.sum() - w) < 1e-9
+    # capacities: single segment gives (min(kv, N), min(ceil(ks/B), N/B))
+    assert oracle.capacities(2048, 8192, 131072, 131072, 64) == (2048, 128)
+    assert oracle.capacities(64, 64, 1024, 1024, 64) == (64, 1)
+    assert oracle.capacities(5000, 10 ** 6, 1024, 1024, 64) == (1024, 16)
+
+
+def test_estimator_window_matches_plain_softmax():
+    """The window probabilities are a plain causal softmax of the last rows (Algorithm 1)."""
+    rng = np.random.default_rng(14)
+    n, d = 200, 8
+    q, k = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    rows, P, lse = oracle.window_probs(q, k, 0, n, 0.5, 64)
+    for j, r in enumerate(rows):
+        t = torch.softmax(torch.tensor(0.5 * q[r] @ k[: r + 1].T), 0).numpy()
+        assert np.abs(P[j, : r + 1] - t).max() < 1e-14 and np.all(P[j, r + 1:] == 0)
+
+
+# ---------------------------------------------------------------- P9 layout identities
+def test_p9_striped_chunks_merge_to_global_rows():
+    rng = np.random.default_rng(15)
+    W, B, nbw = 4, 16, 3
+    n = W * nbw * B
+    hq, hkv, d = 2, 1, 8
+    q, do = rng.standard_normal((n, hq, d)), rng.standard_normal((n, hq, d))
+    k, v = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    idx = rand_index(rng, n, hq, B, kv=10, kg=4)
+    pos = np.arange(n)
+    Og, Lg = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], idx, B)
+    Dg = (Og * do).sum(-1).T
+    dqg, dkg, dvg = oracle.attn_bwd_dense(q, k, v, do, Lg, Dg, pos, pos, [0, n], idx, B)
+    dk_sum = np.zeros_like(k)
+    dv_sum = np.zeros_like(v)
+    for w in range(W):
+        rows = (np.arange(w, n // B, W)[:, None] * B + np.arange(B)).reshape(-1)
+        acc_o, acc_l = np.zeros((hq, rows.size, d)), np.full((hq, rows.size), -np.inf)
+        for t in range(W):
+            u = (w - t) % W
+            cols = (np.arange(u, n // B, W)[:, None] * B + np.arange(B)).reshape(-1)
+            o, l = oracle.attn_fwd_support(q[rows], k[cols], v[cols], rows, cols, [0, n], idx, B)
+            o2, l2 = oracle.attn_fwd_dense(q[rows], k[cols], v[cols], rows, cols, [0, n], idx, B)
+            assert np.allclose(o, o2, atol=1e-12) and np.array_equal(np.isneginf(l), np.isneginf(l2))
+            acc_o, acc_l = oracle.lse_merge(acc_o, acc_l, o.transpose(1, 0, 2), l)
+        assert np.abs(acc_o.transpose(1, 0, 2) - Og[rows]).max() < 1e-12
+        fin = np.isfinite(Lg[:, rows])
+        assert np.abs(acc_l[fin] - Lg[:, rows][fin]).max() < 1e-12
+        D = (acc_o.transpose(1, 0, 2) * do[rows]).sum(-1).T
+        dq = np.zeros((rows.size, hq, d))
+        for t in range(W):
+            u = (w - t) % W
+            cols = (np.arange(u, n // B, W)[:, None] * B + np.arange(B)).reshape(-1)
+            a, b_, c = oracle.attn_bwd_support(q[rows], k[cols], v[cols], do[rows], acc_l, D, rows,
+                                               cols, [0, n], idx, B)
+            dq += a
+            dk_sum[cols] += b_
+            dv_sum[cols] += c
+        assert np.abs(dq - dqg[rows]).max() < 1e-12
+    assert np.abs(dk_sum - dkg).max() < 1e-12 and np.abs(dv_sum - dvg).max() < 1e-12
+
+
+def test_p9_packed_documents_equal_documents_alone():
+    rng = np.random.default_rng(16)
+    B, hq, hkv, d = 16, 2, 1, 8
+    cu = [0, 48, 80, 176]
+    n = cu[-1]
+    q, do = rng.standard_normal((n, hq, d)), rng.standard_normal((n, hq, d))
+    k, v = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    vb, sb = [40, 20], [64, 30]
+    idx = oracle.estimate_index(q, k, cu, vb, sb, B, 16)
+    pos = np.arange(n)
+    O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, cu, idx, B)
+    for s in range(3):
+        a, e = cu[s], cu[s + 1]
+        sl = slice(a, e)
+        # the same document alone, with its share of the budget as the whole budget
+        kvs = [oracle.capacities(vb[h], sb[h], e - a, n, B) for h in range(hq)]
+        idx1 = oracle.estimate_index(q[sl], k[sl], [0, e - a], [c[0] for c in kvs],
+                                     [c[1] * B for c in kvs], B, 16)
+        for h in range(hq):
+            assert np.array_equal(idx1[(h, 0)][0] + a, idx[(h, s)][0])
+            assert np.array_equal(idx1[(h, 0)][1], idx[(h, s)][1])
+        p1 = np.arange(e - a)
+        O1, L1 = oracle.attn_fwd_dense(q[sl], k[sl], v[sl], p1, p1, [0, e - a], idx1, B)
+        assert np.abs(O1 - O[sl]).max() < 1e-12
+        fin = np.isfinite(L1)
+        assert np.array_equal(fin, np.isfinite(L[:, sl]))
+        assert np.abs(L1[fin] - L[:, sl][fin]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- forms (i) and (ii) agree
+def test_support_form_equals_dense_form():
+    rng = np.random.default_rng(17)
+    B, hq, hkv, d = 16, 4, 2, 8
+    cu = [0, 40, 112, 160]
+    n = cu[-1]
+    q, do = rng.standard_normal((n, hq, d)), rng.standard_normal((n, hq, d))
+    k, v = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    idx = rand_index(rng, n, hq, B, cu=cu)
+    pos = np.arange(n)
+    O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, cu, idx, B)
+    O2, L2 = oracle.attn_fwd_support(q, k, v, pos, pos, cu, idx, B)
+    assert np.array_equal(np.isneginf(L), np.isneginf(L2))
+    assert np.abs(O - O2).max() < 1e-12
+    fin = np.isfinite(L)
+    assert np.abs(L[fin] - L2[fin]).max() < 1e-12
+    D = (O * do).sum(-1).T
+    g1 = oracle.attn_bwd_dense(q, k, v, do, L, D, pos, pos, cu, idx, B)
+    g2 = oracle.attn_bwd_support(q, k, v, do, L, D, pos, pos, cu, idx, B)
+    for a, b in zip(g1, g2):
+        assert np.abs(a - b).max() < 1e-12
+
+
+# ---------------------------------------------------------------- P10 accounting
+def test_p10_mask_area_formula_equals_count():
+    rng = np.random.default_rng(18)
+    for cu, B in (([0, 256], 64), ([0, 100, 164, 300], 32), ([0, 1000], 64)):
+        n = cu[-1]
+        idx = rand_index(rng, n, 3, B, cu=cu)
+        pos = np.arange(n)
+        assert oracle.mask_area_bruteforce(pos, pos, cu, idx, 3, B) == \
+            oracle.mask_area_formula(cu, idx, 3, B)
+
+
+def test_p10_golden_mask_areas():
+    """The cost-model examples: full block S_q*S_k, causal diagonal S_q(S_q+1)/2, and
+    the two-sample varlen causal mask of lengths 21 and 11."""
+    with open(os.path.join(GOLDEN, "mask_area.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        cu, B = case["cu_seqlens"], case["block"]
+        n = cu[-1]
+        idx = full_index(n, 1, B, cu) if case["mask"] == "causal" else None
+        pos = np.arange(n)
+        assert oracle.mask_area_bruteforce(pos, pos, cu, idx, 1, B)[0] == case["area"]
+        assert oracle.dense_causal_area(pos, cu) == case["area"]
