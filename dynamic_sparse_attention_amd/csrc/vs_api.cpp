@@ -1,0 +1,402 @@
+// vs_api.cpp — the C ABI: argument validation, workspace layout and launches.
+//
+// Every entry point validates all host-visible arguments before the first
+// HIP call, so a rejected call enqueues nothing (and needs no GPU).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/vs.h"
+#include "vs_attn_common.h"
+
+namespace vs {
+hipError_t launch_fwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st);
+hipError_t launch_prep_vertical(const AttnParams& p, int n_lists, const int* v_ptr, const int* v_idx,
+                                hipStream_t st);
+hipError_t launch_delta(const void* o, int o_f32, int bf16, const void* dout, float* delta, int batch,
+                        int n, int h, int d, hipStream_t st);
+hipError_t launch_lse_merge(int batch, int n, int heads, int d, float* o_acc, float* lse_acc,
+                            const float* o_part, const float* lse_part, hipStream_t st);
+hipError_t launch_bwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st);
+struct EstParams;
+hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int* v_ptr, int* v_idx,
+                           const int* s_ptr, int* s_idx, float* v_score, float* s_score,
+                           float2* partials, float* lse2, int tiles_total, const int* tile_prefix,
+                           hipStream_t st);
+constexpr int kEstKeyTile = 256;
+}  // namespace vs
+
+namespace {
+
+thread_local std::string g_err;
+
+vs_status fail(vs_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+vs_status ok() {
+  g_err.clear();
+  return VS_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Prob {
+  int batch, h_q, h_kv, d, n_q, n_k, block, bf16, n_seg, W, q_rank, k_rank, n_global, nqb, nkb;
+  float scale;
+  std::vector<int> cu;
+  int n_lists() const { return batch * h_q * n_seg; }
+};
+
+vs_status check_problem(const vs_problem* p, Prob* c) {
+  if (!p) return fail(VS_ERR_NULL, "problem is NULL");
+  if (!p->cu_seqlens) return fail(VS_ERR_NULL, "cu_seqlens is NULL");
+  if (p->batch < 1 || p->h_q < 1 || p->h_kv < 1)
+    return fail(VS_ERR_SHAPE, "batch, h_q, h_kv must be >= 1 (got %d, %d, %d)", p->batch, p->h_q,
+                p->h_kv);
+  if (p->h_q % p->h_kv != 0)
+    return fail(VS_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", p->h_q, p->h_kv);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(VS_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", p->head_dim);
+  if (p->block != 64) return fail(VS_ERR_UNSUPPORTED, "block %d unsupported (64)", p->block);
+  if (p->dtype != VS_F32 && p->dtype != VS_BF16)
+    return fail(VS_ERR_UNSUPPORTED, "dtype %d unsupported", p->dtype);
+  if (p->n_seg < 1) return fail(VS_ERR_SHAPE, "n_seg must be >= 1 (got %d)", p->n_seg);
+  if (p->n_seg > VS_MAX_SEGMENTS)
+    return fail(VS_ERR_UNSUPPORTED, "n_seg %d exceeds %d", p->n_seg, VS_MAX_SEGMENTS);
+  if (!(std::isfinite(p->scale))) return fail(VS_ERR_SHAPE, "scale is not finite");
+  if (p->n_q < 0 || p->n_k < 0) return fail(VS_ERR_SHAPE, "n_q, n_k must be >= 0");
+  c->cu.assign(p->cu_seqlens, p->cu_seqlens + p->n_seg + 1);
+  if (c->cu[0] != 0) return fail(VS_ERR_SHAPE, "cu_seqlens[0] must be 0");
+  for (int s = 0; s < p->n_seg; ++s) {
+    const long long L = (long long)c->cu[s + 1] - c->cu[s];
+    if (L <= 0) return fail(VS_ERR_SHAPE, "segment %d has length %lld", s, L);
+    if (L % p->block != 0)
+      return fail(VS_ERR_UNSUPPORTED, "segment %d length %lld is not a multiple of %d", s, L,
+                  p->block);
+    if (L / p->block > 65536)
+      return fail(VS_ERR_UNSUPPORTED, "segment %d longer than 65536 blocks", s);
+  }
+  c->n_global = c->cu[p->n_seg];
+  c->W = p->stripe_world;
+  if (c->W < 1) return fail(VS_ERR_SHAPE, "stripe_world must be >= 1");
+  if (c->W == 1) {
+    if (p->n_q != c->n_global || p->n_k != c->n_global)
+      return fail(VS_ERR_SHAPE, "contiguous call needs n_q == n_k == cu_seqlens[n_seg] (%d, %d, %d)",
+                  p->n_q, p->n_k, c->n_global);
+  } else {
+    if (p->n_seg != 1) return fail(VS_ERR_UNSUPPORTED, "striped calls take one segment");
+    if (c->n_global % (p->block * c->W) != 0)
+      return fail(VS_ERR_SHAPE, "n_global %d not a multiple of block*stripe_world", c->n_global);
+    if (p->n_q != c->n_global / c->W || p->n_k != c->n_global / c->W)
+      return fail(VS_ERR_SHAPE, "striped call needs n_q == n_k == n_global/stripe_world");
+    if (p->q_rank < 0 || p->q_rank >= c->W || p->k_rank < 0 || p->k_rank >= c->W)
+      return fail(VS_ERR_SHAPE, "q_rank/k_rank outside [0, stripe_world)");
+  }
+  if ((long long)p->batch * p->n_q > (1ll << 31) / 64 || (long long)p->batch * p->n_k > (1ll << 31) / 64)
+    return fail(VS_ERR_UNSUPPORTED, "batch * tokens too large");
+  c->batch = p->batch;
+  c->h_q = p->h_q;
+  c->h_kv = p->h_kv;
+  c->d = p->head_dim;
+  c->n_q = p->n_q;
+  c->n_k = p->n_k;
+  c->block = p->block;
+  c->bf16 = p->dtype == VS_BF16;
+  c->n_seg = p->n_seg;
+  c->q_rank = c->W == 1 ? 0 : p->q_rank;
+  c->k_rank = c->W == 1 ? 0 : p->k_rank;
+  c->nqb = p->n_q / p->block;
+  c->nkb = p->n_k / p->block;
+  c->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
+  return VS_OK;
+}
+
+vs_status check_index(const Prob& c, const vs_index* idx) {
+  if (!idx) return fail(VS_ERR_NULL, "index is NULL");
+  if (!idx->v_ptr || !idx->s_ptr) return fail(VS_ERR_NULL, "index v_ptr/s_ptr is NULL");
+  if (idx->v_cap_max < 0 || idx->s_cap_max < 0)
+    return fail(VS_ERR_INDEX, "negative index capacity bound");
+  if (idx->v_cap_max > 0 && !idx->v_idx) return fail(VS_ERR_NULL, "index v_idx is NULL");
+  if (idx->s_cap_max > 0 && !idx->s_idx) return fail(VS_ERR_NULL, "index s_idx is NULL");
+  int max_seg = 0;
+  for (int s = 0; s < c.n_seg; ++s) max_seg = std::max(max_seg, c.cu[s + 1] - c.cu[s]);
+  if (idx->v_cap_max > max_seg)
+    return fail(VS_ERR_INDEX, "v_cap_max %d exceeds the longest segment %d", idx->v_cap_max, max_seg);
+  if (idx->s_cap_max > max_seg / c.block)
+    return fail(VS_ERR_INDEX, "s_cap_max %d exceeds the block count %d", idx->s_cap_max,
+                max_seg / c.block);
+  return VS_OK;
+}
+
+void fill_params(const Prob& c, vs::AttnParams* a) {
+  std::memset(a, 0, sizeof *a);
+  a->batch = c.batch;
+  a->h_q = c.h_q;
+  a->h_kv = c.h_kv;
+  a->n_q = c.n_q;
+  a->n_k = c.n_k;
+  a->nqb = c.nqb;
+  a->nkb = c.nkb;
+  a->scale = c.scale;
+  a->sl2 = c.scale * vs::kLog2e;
+  a->W = c.W;
+  a->q_rank = c.q_rank;
+  a->k_rank = c.k_rank;
+  a->n_global = c.n_global;
+  a->seg.n_seg = c.n_seg;
+  for (int s = 0; s <= c.n_seg; ++s) a->seg.start_blk[s] = c.cu[s] / c.block;
+}
+
+// Workspace layouts.
+struct AttnWs {
+  size_t vsel, vcnt, delta, total;
+};
+AttnWs attn_ws(const Prob& c, int v_cap_max, bool with_delta) {
+  AttnWs w;
+  size_t off = 0;
+  w.vsel = off;
+  off += align256((size_t)c.n_lists() * std::max(v_cap_max, 1) * 4);
+  w.vcnt = off;
+  off += align256((size_t)c.n_lists() * 4);
+  w.delta = off;
+  if (with_delta) off += align256((size_t)c.batch * c.h_q * c.n_q * 4);
+  w.total = off;
+  return w;
+}
+
+struct EstWs {
+  size_t part, lse2, vscore, sscore, tprefix, total;
+  int tiles_total;
+  std::vector<int> tile_prefix;
+};
+EstWs est_ws(const Prob& c) {
+  EstWs w;
+  w.tile_prefix.assign(c.n_seg + 1, 0);
+  for (int s = 0; s < c.n_seg; ++s)
+    w.tile_prefix[s + 1] =
+        w.tile_prefix[s] + (c.cu[s + 1] - c.cu[s] + vs::kEstKeyTile - 1) / vs::kEstKeyTile;
+  w.tiles_total = w.tile_prefix[c.n_seg];
+  size_t off = 0;
+  w.part = off;
+  off += align256((size_t)c.batch * c.h_q * w.tiles_total * 64 * 8);
+  w.lse2 = off;
+  off += align256((size_t)c.n_lists() * 64 * 4);
+  w.vscore = off;
+  off += align256((size_t)c.batch * c.h_q * c.n_global * 4);
+  w.sscore = off;
+  off += align256((size_t)c.batch * c.h_q * (c.n_global / c.block) * 4);
+  w.tprefix = off;
+  w.total = off;
+  return w;
+}
+
+vs_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(VS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vs_last_error(void) { return g_err.c_str(); }
+
+vs_status vs_index_capacity(const vs_problem* p, const int32_t* v_budget, const int32_t* s_budget,
+                            int32_t* v_ptr_host, int32_t* s_ptr_host, int32_t* v_cap_max,
+                            int32_t* s_cap_max) {
+  Prob c;
+  vs_status st = check_problem(p, &c);
+  if (st) return st;
+  if (!v_budget || !s_budget || !v_ptr_host || !s_ptr_host)
+    return fail(VS_ERR_NULL, "budget or pointer array is NULL");
+  for (int h = 0; h < c.h_q; ++h)
+    if (v_budget[h] < 0 || s_budget[h] < 0)
+      return fail(VS_ERR_BUDGET, "head %d has a negative budget", h);
+  long long vo = 0, so = 0;
+  int vmax = 0, smax = 0;
+  const long long N = c.n_global;
+  v_ptr_host[0] = 0;
+  s_ptr_host[0] = 0;
+  for (int b = 0; b < c.batch; ++b)
+    for (int h = 0; h < c.h_q; ++h)
+      for (int s = 0; s < c.n_seg; ++s) {
+        const long long L = c.cu[s + 1] - c.cu[s];
+        const long long nb = (L + c.block - 1) / c.block;
+        const long long sv = ((long long)v_budget[h] * L + N - 1) / N;
+        const long long ss = ((long long)s_budget[h] * L + N - 1) / N;
+        const long long kv = std::min(sv, L);
+        const long long kg = std::min((ss + c.block - 1) / c.block, nb);
+        vo += kv;
+        so += kg;
+        if (vo > INT32_MAX || so > INT32_MAX) return fail(VS_ERR_SHAPE, "index too large");
+        const int l = (b * c.h_q + h) * c.n_seg + s;
+        v_ptr_host[l + 1] = (int32_t)vo;
+        s_ptr_host[l + 1] = (int32_t)so;
+        vmax = std::max(vmax, (int)kv);
+        smax = std::max(smax, (int)kg);
+      }
+  if (v_cap_max) *v_cap_max = vmax;
+  if (s_cap_max) *s_cap_max = smax;
+  return ok();
+}
+
+vs_status vs_workspace_size(const vs_problem* p, int32_t op, const vs_index* idx, size_t* bytes) {
+  Prob c;
+  vs_status st = check_problem(p, &c);
+  if (st) return st;
+  if (!bytes) return fail(VS_ERR_NULL, "bytes is NULL");
+  if (op == 0) {
+    *bytes = est_ws(c).total;
+    return ok();
+  }
+  if (op != 1 && op != 2) return fail(VS_ERR_SHAPE, "op %d is not 0, 1 or 2", op);
+  if ((st = check_index(c, idx))) return st;
+  *bytes = attn_ws(c, idx->v_cap_max, op == 2).total;
+  return ok();
+}
+
+vs_status vs_estimate_index(const vs_problem* p, const void* q, const void* k, int32_t last_q,
+                            const int32_t* v_ptr, int32_t* v_idx, const int32_t* s_ptr,
+                            int32_t* s_idx, float* v_score, float* s_score, void* ws,
+                            size_t ws_bytes, vs_stream_t stream) {
+  Prob c;
+  vs_status st = check_problem(p, &c);
+  if (st) return st;
+  if (c.W != 1) return fail(VS_ERR_UNSUPPORTED, "estimation runs on the contiguous layout");
+  if (last_q != 0 && last_q != c.block)
+    return fail(VS_ERR_UNSUPPORTED, "last_q %d unsupported (0 or %d)", last_q, c.block);
+  if (!q || !k || !v_ptr || !s_ptr || !v_idx || !s_idx)
+    return fail(VS_ERR_NULL, "q, k, v_ptr, v_idx, s_ptr or s_idx is NULL");
+  const EstWs w = est_ws(c);
+  if (!ws || ws_bytes < w.total)
+    return fail(VS_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  vs::AttnParams a;
+  fill_params(c, &a);
+  a.q = q;
+  a.k = k;
+  char* base = static_cast<char*>(ws);
+  float* vsc = v_score ? v_score : reinterpret_cast<float*>(base + w.vscore);
+  float* ssc = s_score ? s_score : reinterpret_cast<float*>(base + w.sscore);
+  return hip_status(vs::launch_estimate(a, c.bf16, c.d, v_ptr, v_idx, s_ptr, s_idx, vsc, ssc,
+                                        reinterpret_cast<float2*>(base + w.part),
+                                        reinterpret_cast<float*>(base + w.lse2), w.tiles_total,
+                                        w.tile_prefix.data(), (hipStream_t)stream),
+                    "vs_estimate_index");
+}
+
+vs_status vs_sparse_attn_fwd(const vs_problem* p, const void* q, const void* k, const void* v,
+                             const vs_index* idx, void* o, int32_t o_f32, float* lse, void* ws,
+                             size_t ws_bytes, vs_stream_t stream) {
+  Prob c;
+  vs_status st = check_problem(p, &c);
+  if (st) return st;
+  if ((st = check_index(c, idx))) return st;
+  if (!q || !k || !v || !o || !lse) return fail(VS_ERR_NULL, "q, k, v, o or lse is NULL");
+  const AttnWs w = attn_ws(c, idx->v_cap_max, false);
+  if (!ws || ws_bytes < w.total)
+    return fail(VS_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  vs::AttnParams a;
+  fill_params(c, &a);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.s_ptr = idx->s_ptr;
+  a.s_idx = idx->s_idx;
+  char* base = static_cast<char*>(ws);
+  a.vsel = reinterpret_cast<int*>(base + w.vsel);
+  a.vcnt = reinterpret_cast<int*>(base + w.vcnt);
+  a.vsel_stride = std::max(idx->v_cap_max, 1);
+  a.o_out = o;
+  a.o_f32 = o_f32 != 0;
+  a.lse = lse;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = vs::launch_prep_vertical(a, c.n_lists(), idx->v_ptr, idx->v_idx, s);
+  if (e == hipSuccess) e = vs::launch_fwd(a, c.bf16, c.d, s);
+  return hip_status(e, "vs_sparse_attn_fwd");
+}
+
+vs_status vs_attn_bwd_delta(const vs_problem* p, const void* o, int32_t o_f32, const void* dout,
+                            float* delta, vs_stream_t stream) {
+  Prob c;
+  vs_status st = check_problem(p, &c);
+  if (st) return st;
+  if (!o || !dout || !delta) return fail(VS_ERR_NULL, "o, dout or delta is NULL");
+  return hip_status(vs::launch_delta(o, o_f32 != 0, c.bf16, dout, delta, c.batch, c.n_q, c.h_q, c.d,
+                                     (hipStream_t)stream),
+                    "vs_attn_bwd_delta");
+}
+
+vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, const void* v,
+                             const void* o, int32_t o_f32, const void* dout, const float* lse,
+                             const float* delta, const vs_index* idx, float* dq,
+                             int32_t dq_accumulate, float* dk, float* dv, void* ws,
+                             size_t ws_bytes, vs_stream_t stream) {
+  Prob c;
+  vs_status st = check_problem(p, &c);
+  if (st) return st;
+  if ((st = check_index(c, idx))) return st;
+  if (!q || !k || !v || !dout || !lse || !dq || !dk || !dv)
+    return fail(VS_ERR_NULL, "q, k, v, dout, lse, dq, dk or dv is NULL");
+  if (!delta && !o) return fail(VS_ERR_NULL, "o is NULL and no delta was given");
+  const AttnWs w = attn_ws(c, idx->v_cap_max, true);
+  if (!ws || ws_bytes < w.total)
+    return fail(VS_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  vs::AttnParams a;
+  fill_params(c, &a);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.s_ptr = idx->s_ptr;
+  a.s_idx = idx->s_idx;
+  char* base = static_cast<char*>(ws);
+  a.vsel = reinterpret_cast<int*>(base + w.vsel);
+  a.vcnt = reinterpret_cast<int*>(base + w.vcnt);
+  a.vsel_stride = std::max(idx->v_cap_max, 1);
+  a.lse = const_cast<float*>(lse);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dq_accumulate = dq_accumulate != 0;
+  a.col_tiles = (idx->v_cap_max + 63) / 64;
+  a.qrange_len = 32;
+  a.qranges = (c.nqb + a.qrange_len - 1) / a.qrange_len;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (!delta) {
+    float* dws = reinterpret_cast<float*>(base + w.delta);
+    e = vs::launch_delta(o, o_f32 != 0, c.bf16, dout, dws, c.batch, c.n_q, c.h_q, c.d, s);
+    delta = dws;
+  }
+  a.delta = delta;
+  if (e == hipSuccess) e = vs::launch_prep_vertical(a, c.n_lists(), idx->v_ptr, idx->v_idx, s);
+  if (e == hipSuccess) e = vs::launch_bwd(a, c.bf16, c.d, s);
+  return hip_status(e, "vs_sparse_attn_bwd");
+}
+
+vs_status lse_merge(int32_t batch, int32_t n, int32_t heads, int32_t head_dim, float* o_acc,
+                    float* lse_acc, const float* o_part, const float* lse_part,
+                    vs_stream_t stream) {
+  if (!o_acc || !lse_acc || !o_part || !lse_part)
+    return fail(VS_ERR_NULL, "lse_merge pointer is NULL");
+  if (batch < 0 || n < 0 || heads < 0) return fail(VS_ERR_SHAPE, "negative size");
+  if (head_dim < 4 || head_dim > 256 || (head_dim & (head_dim - 1)) != 0)
+    return fail(VS_ERR_UNSUPPORTED, "head_dim %d unsupported (power of two, 4..256)", head_dim);
+  return hip_status(vs::launch_lse_merge(batch, n, heads, head_dim, o_acc, lse_acc, o_part,
+                                         lse_part, (hipStream_t)stream),
+                    "lse_merge");
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// vs_attn_common.h — argument block and tile descriptors shared by the sparse
+// attention forward and backward kernels.
+//
+// The Vertical-Slash support of a query block (MTraining paper note,
+// Algorithm 1, sparseformat; MTraining §4.1 (ii)-(iii)):
+//   * slash tiles: for each selected block-diagonal g, the key block
+//     beta - g of the same segment, if this call holds it (a causal mask
+//     applies only when g == 0);
+//   * column tiles: the selected vertical columns m <= the block's last row
+//     whose block offset beta - beta(m) is not selected (those entries are
+//     already inside a slash tile), 64 columns per tile, causal per row.
+// Positions in the index are global (index coordinates); a block-striped
+// call relabels global key block k_rank + W*j to local block j.
+#pragma once
+
+#include "vs_device.h"
+
+namespace vs {
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;      // forward: output; backward: saved output (delta only)
+  const void* dout;   // backward only
+  const int* s_ptr;
+  const int* s_idx;
+  const int* vsel;    // prepared vertical lists: global positions held by this call
+  const int* vcnt;
+  int vsel_stride;
+  void* o_out;
+  float* lse;         // forward: written; backward: read
+  const float* delta; // backward only
+  float* dq;
+  float* dk;
+  float* dv;
+  int o_f32;
+  int dq_accumulate;
+  int batch, h_q, h_kv, n_q, n_k, nqb, nkb;
+  float scale;
+  float sl2;          // scale * log2(e)
+  int W, q_rank, k_rank;
+  int n_global;
+  int qranges;        // backward column units: query-block ranges per column tile
+  int qrange_len;
+  int col_tiles;      // backward column units: column tiles per list
+  SegTable seg;
+};
+
+// Global block of local query block i, and its segment / in-segment block.
+struct RowBlock {
+  int i_local;
+  int qb_glob;
+  int seg;
+  int a_blk;   // segment start, in blocks
+  int beta;    // block index inside the segment
+  int nb_seg;  // blocks in the segment
+};
+
+__device__ __forceinline__ RowBlock row_block(const AttnParams& p, int i_local) {
+  RowBlock rb;
+  rb.i_local = i_local;
+  if (p.W == 1) {
+    rb.seg = seg_of_block(p.seg, i_local);
+    rb.a_blk = p.seg.start_blk[rb.seg];
+    rb.qb_glob = i_local;
+    rb.nb_seg = p.seg.start_blk[rb.seg + 1] - rb.a_blk;
+  } else {
+    rb.seg = 0;
+    rb.a_blk = 0;
+    rb.qb_glob = p.q_rank + p.W * i_local;
+    rb.nb_seg = p.n_global / kBlock;
+  }
+  rb.beta = rb.qb_glob - rb.a_blk;
+  return rb;
+}
+
+// Local key block of global key block kb_glob, or -1 if this call does not hold it.
+__device__ __forceinline__ int local_key_block(const AttnParams& p, int kb_glob) {
+  if (p.W == 1) return (kb_glob >= 0 && kb_glob < p.nkb) ? kb_glob : -1;
+  const int d = kb_glob - p.k_rank;
+  if (d < 0 || d % p.W != 0) return -1;
+  const int j = d / p.W;
+  return j < p.nkb ? j : -1;
+}
+
+// Local key position of a global position held by this call.
+__device__ __forceinline__ int local_key_pos(const AttnParams& p, int m_glob) {
+  if (p.W == 1) return m_glob;
+  const int kb = m_glob / kBlock;
+  return ((kb - p.k_rank) / p.W) * kBlock + (m_glob % kBlock);
+}
+
+// Tile of 64 keys of one contiguous local key block; causal inside when diag.
+struct SlashTile {
+  int j;
+  bool diag;
+  __device__ __forceinline__ int key_pos(int e) const { return j * kBlock + e; }
+  __device__ __forceinline__ bool valid(int e, int r) const { return !diag || e <= r; }
+};
+
+// Tile of up to 64 gathered vertical columns (local positions in cols[],
+// per-column row threshold in coff[]: -1 = every row, else rows r >= coff).
+struct ColTile {
+  const int* cols;
+  const int* coff;
+  int ncols;
+  __device__ __forceinline__ int key_pos(int e) const { return cols[e < ncols ? e : 0]; }
+  __device__ __forceinline__ bool valid(int e, int r) const {
+    if (e >= ncols) return false;
+    const int c = coff[e];
+    return c < 0 || c <= r;
+  }
+};
+
+}  // namespace vs

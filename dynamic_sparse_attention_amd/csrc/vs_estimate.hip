@@ -1,0 +1,314 @@
+// vs_estimate.hip — online Vertical-Slash index estimation.
+//
+// MTraining paper note, Algorithm 1 (first six steps) and MTraining §4.1
+// (i)-(ii): the last query block of each segment is the observation window;
+// its causal softmax A_hat over all keys of the segment gives the vertical
+// scores (column sums, per token) and the slash scores (window mass on each
+// block-diagonal of the 64x64 grid); argtopk keeps the highest of each, ties
+// to the lowest index.
+//
+// gfx950 design, three passes over K plus a selection:
+//   pass 1: one workgroup per (batch, KV head, 256-key tile); each wave takes
+//           Q heads of the group, holds the 64 window rows as the B operand
+//           and streams the tile's keys through S^T = K Q^T, keeping a
+//           running (max, sum of exp) per row -> per-tile partials;
+//   combine: per (list, row) the partials merge into the row's LSE;
+//   pass 2: same grid, S = Q K^T so that a lane owns a key column; the
+//           column sum of exp(S - LSE) is the vertical score and the sum
+//           over a 64-key block is the slash score of its block-diagonal;
+//   top-k:  one workgroup per (list, kind): 4-pass radix select on the fp32
+//           score bits (scores are >= 0, so the bits order like the values),
+//           then an ordered compaction that writes the chosen indices
+//           ascending, taking the lowest indices among scores equal to the
+//           threshold.
+#include "vs_attn_common.h"
+
+namespace vs {
+
+constexpr int kEstKeyTile = 256;
+
+struct TilePrefix {
+  int v[129];
+};
+
+__device__ __forceinline__ int tile_seg(const TilePrefix& tp, int n_seg, int t) {
+  int s = 0;
+  while (s + 1 < n_seg && tp.v[s + 1] <= t) ++s;
+  return s;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vs_est_pass1_kernel(AttnParams p, TilePrefix tp, int tiles_total,
+                                                           float2* part) {
+  typedef Mfma<T> MF;
+  typedef typename MF::frag frag;
+  constexpr int KPL = MF::KPL, KC = 2 * KPL, NCD = D / KC;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int tg = blockIdx.x % tiles_total;
+  const int bh = blockIdx.x / tiles_total;
+  const int b = bh / p.h_kv, kvh = bh % p.h_kv;
+  const int s = tile_seg(tp, p.seg.n_seg, tg);
+  const int a = p.seg.start_blk[s] * kBlock, e = p.seg.start_blk[s + 1] * kBlock;
+  const int k0 = a + (tg - tp.v[s]) * kEstKeyTile;
+  const int k1 = min(k0 + kEstKeyTile, e);
+  const int G = p.h_q / p.h_kv;
+  const int kvs = p.h_kv * D;
+  const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)b * p.n_k * kvs + (size_t)kvh * D;
+  const T* q = reinterpret_cast<const T*>(p.q);
+  for (int hg = wave; hg < G; hg += 4) {
+    const int h = kvh * G + hg;
+    frag qf[2][NCD];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const T* qr = q + (((size_t)b * p.n_q + (e - 64 + 32 * rg + l32)) * p.h_q + h) * D;
+#pragma unroll
+      for (int c = 0; c < NCD; ++c) qf[rg][c] = load_frag<T>(qr + c * KC + hl * KPL);
+    }
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    for (int kc = k0; kc < k1; kc += 32) {
+      const int key_l = min(kc + l32, k1 - 1);
+      const T* kr = kb + (size_t)key_l * kvs;
+      frag kf[NCD];
+#pragma unroll
+      for (int c = 0; c < NCD; ++c) kf[c] = load_frag<T>(kr + c * KC + hl * KPL);
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        f32x16 sc = f32x16{0};
+#pragma unroll
+        for (int c = 0; c < NCD; ++c) sc = MF::mma(kf[c], qf[rg][c], sc);
+        const int row = e - 64 + 32 * rg + l32;
+        float tt[16], mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kc + c_row(i, hl);
+          tt[i] = (key < k1 && key <= row) ? sc[i] * p.sl2 : -INFINITY;
+          mx = fmaxf(mx, tt[i]);
+        }
+        mx = fmaxf(mx, xor32(mx));
+        const float mn = fmaxf(m[rg], mx);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rs += fast_exp2(tt[i] - mu);
+        rs += xor32(rs);
+        l[rg] = l[rg] * fast_exp2(m[rg] - mu) + rs;
+        m[rg] = mn;
+      }
+    }
+    if (hl == 0) {
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+        part[(((size_t)b * p.h_q + h) * tiles_total + tg) * 64 + 32 * rg + l32] = make_float2(m[rg], l[rg]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void vs_est_combine_kernel(AttnParams p, TilePrefix tp, int tiles_total,
+                                                            const float2* part, float* lse2) {
+  const int list = blockIdx.x;
+  const int s = list % p.seg.n_seg;
+  const int bh = list / p.seg.n_seg;
+  const int r = threadIdx.x;
+  const float2* pp = part + (size_t)bh * tiles_total * 64;
+  float M = -INFINITY;
+  for (int t = tp.v[s]; t < tp.v[s + 1]; ++t) M = fmaxf(M, pp[(size_t)t * 64 + r].x);
+  const float mu = M == -INFINITY ? 0.f : M;
+  float L = 0.f;
+  for (int t = tp.v[s]; t < tp.v[s + 1]; ++t) {
+    const float2 v = pp[(size_t)t * 64 + r];
+    L += v.y * fast_exp2(v.x - mu);
+  }
+  lse2[(size_t)list * 64 + r] = L > 0.f ? M + __log2f(L) : INFINITY;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePrefix tp, int tiles_total,
+                                                           const float* lse2, float* v_score,
+                                                           float* s_score) {
+  typedef Mfma<T> MF;
+  typedef typename MF::frag frag;
+  constexpr int KPL = MF::KPL, KC = 2 * KPL, NCD = D / KC;
+  __shared__ float s_lse[4][64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int tg = blockIdx.x % tiles_total;
+  const int bh = blockIdx.x / tiles_total;
+  const int b = bh / p.h_kv, kvh = bh % p.h_kv;
+  const int s = tile_seg(tp, p.seg.n_seg, tg);
+  const int a = p.seg.start_blk[s] * kBlock, e = p.seg.start_blk[s + 1] * kBlock;
+  const int nb_s = (e - a) / kBlock;
+  const int k0 = a + (tg - tp.v[s]) * kEstKeyTile;
+  const int k1 = min(k0 + kEstKeyTile, e);
+  const int G = p.h_q / p.h_kv;
+  const int kvs = p.h_kv * D;
+  const int nbt = p.n_global / kBlock;
+  const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)b * p.n_k * kvs + (size_t)kvh * D;
+  const T* q = reinterpret_cast<const T*>(p.q);
+  for (int hg = wave; hg < G; hg += 4) {
+    const int h = kvh * G + hg;
+    const int list = (b * p.h_q + h) * p.seg.n_seg + s;
+    s_lse[wave][lane] = lse2[(size_t)list * 64 + lane];
+    wave_sync();
+    // A operand: window rows in natural order (row slot m -> row e-64+32rg+m).
+    frag qa[2][NCD];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const T* qr = q + (((size_t)b * p.n_q + (e - 64 + 32 * rg + l32)) * p.h_q + h) * D;
+#pragma unroll
+      for (int c = 0; c < NCD; ++c) qa[rg][c] = load_frag<T>(qr + c * KC + hl * KPL);
+    }
+    float blk_acc = 0.f;
+    for (int kc = k0; kc < k1; kc += 32) {
+      const int key = kc + l32;
+      const T* kr = kb + (size_t)min(key, k1 - 1) * kvs;
+      frag kf[NCD];
+#pragma unroll
+      for (int c = 0; c < NCD; ++c) kf[c] = load_frag<T>(kr + c * KC + hl * KPL);
+      float col = 0.f;
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        f32x16 sc = f32x16{0};
+#pragma unroll
+        for (int c = 0; c < NCD; ++c) sc = MF::mma(qa[rg][c], kf[c], sc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int rr = 32 * rg + c_row(i, hl);
+          const int row = e - 64 + rr;
+          col += (key < k1 && key <= row) ? fast_exp2(sc[i] * p.sl2 - s_lse[wave][rr]) : 0.f;
+        }
+      }
+      col += xor32(col);
+      if (hl == 0 && key < k1) v_score[((size_t)b * p.h_q + h) * p.n_global + key] = col;
+      float bs = hl == 0 ? col : 0.f;
+#pragma unroll
+      for (int w = 16; w >= 1; w >>= 1) bs += __shfl_xor(bs, w, 64);
+      blk_acc += bs;
+      if (((kc - a) & 63) == 32) {  // second half of a 64-key block
+        if (lane == 0) {
+          const int beta = (kc - a) / kBlock;
+          s_score[((size_t)b * p.h_q + h) * nbt + p.seg.start_blk[s] + (nb_s - 1 - beta)] = blk_acc;
+        }
+        blk_acc = 0.f;
+      }
+    }
+    wave_sync();
+  }
+}
+
+constexpr int kTopkThreads = 1024;
+
+__device__ __forceinline__ int block_excl_scan_count(bool flag, int* wsum, int* total) {
+  return block_compact<kTopkThreads>(flag, wsum, total);
+}
+
+__global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p, const float* v_score,
+                                                                   const float* s_score, const int* v_ptr,
+                                                                   int* v_idx, const int* s_ptr,
+                                                                   int* s_idx) {
+  __shared__ int hist[256];
+  __shared__ int wsum[kTopkThreads / 64];
+  __shared__ int sel[2];
+  const int kind = blockIdx.x & 1;
+  const int list = blockIdx.x >> 1;
+  const int s = list % p.seg.n_seg;
+  const int bh = list / p.seg.n_seg;
+  const int a_blk = p.seg.start_blk[s];
+  const int nb_s = p.seg.start_blk[s + 1] - a_blk;
+  const int nbt = p.n_global / kBlock;
+  const float* sc;
+  int L, k, add;
+  int* out;
+  if (kind == 0) {
+    sc = v_score + (size_t)bh * p.n_global + (size_t)a_blk * kBlock;
+    L = nb_s * kBlock;
+    k = v_ptr[list + 1] - v_ptr[list];
+    out = v_idx + v_ptr[list];
+    add = a_blk * kBlock;
+  } else {
+    sc = s_score + (size_t)bh * nbt + a_blk;
+    L = nb_s;
+    k = s_ptr[list + 1] - s_ptr[list];
+    out = s_idx + s_ptr[list];
+    add = 0;
+  }
+  const int tid = threadIdx.x;
+  if (k >= L) {
+    for (int x = tid; x < k; x += kTopkThreads) out[x] = x < L ? x + add : -1;
+    return;
+  }
+  if (k <= 0) return;
+  const uint32_t* u = reinterpret_cast<const uint32_t*>(sc);
+  uint32_t prefix = 0, pmask = 0;
+  int kr = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int x = tid; x < L; x += kTopkThreads) {
+      const uint32_t v = u[x];
+      if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0, d = 255;
+      for (; d >= 0; --d) {
+        if (cum + hist[d] >= kr) break;
+        cum += hist[d];
+      }
+      sel[0] = d;
+      sel[1] = kr - cum;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sel[0] << shift;
+    pmask |= 255u << shift;
+    kr = sel[1];
+    __syncthreads();
+  }
+  // prefix is the k-th largest value; take everything above it and the kr
+  // lowest-index entries equal to it, in index order.
+  int count = 0, eq_seen = 0;
+  for (int base = 0; base < L; base += kTopkThreads) {
+    const int x = base + tid;
+    const uint32_t v = x < L ? u[x] : 0u;
+    const bool gt = x < L && v > prefix;
+    const bool eq = x < L && v == prefix;
+    int eq_tot;
+    const int eq_before = block_excl_scan_count(eq, wsum, &eq_tot);
+    __syncthreads();
+    const bool take = gt || (eq && eq_seen + eq_before < kr);
+    int tot;
+    const int slot = block_compact<kTopkThreads>(take, wsum, &tot);
+    if (take) out[count + slot] = x + add;
+    count += tot;
+    eq_seen += eq_tot;
+    __syncthreads();
+  }
+}
+
+hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int* v_ptr, int* v_idx,
+                           const int* s_ptr, int* s_idx, float* v_score, float* s_score,
+                           float2* partials, float* lse2, int tiles_total, const int* tile_prefix,
+                           hipStream_t st) {
+  TilePrefix tp;
+  for (int s = 0; s <= p.seg.n_seg; ++s) tp.v[s] = tile_prefix[s];
+  const int n_lists = p.batch * p.h_q * p.seg.n_seg;
+  const dim3 g1((unsigned)(p.batch * p.h_kv * tiles_total));
+#define VS_EST(T, DD)                                                                                   \
+  do {                                                                                                  \
+    hipLaunchKernelGGL((vs_est_pass1_kernel<T, DD>), g1, dim3(256), 0, st, p, tp, tiles_total, partials); \
+    hipLaunchKernelGGL(vs_est_combine_kernel, dim3(n_lists), dim3(64), 0, st, p, tp, tiles_total,        \
+                       (const float2*)partials, lse2);                                                 \
+    hipLaunchKernelGGL((vs_est_pass2_kernel<T, DD>), g1, dim3(256), 0, st, p, tp, tiles_total,          \
+                       (const float*)lse2, v_score, s_score);                                           \
+  } while (0)
+  if (g1.x == 0) return hipSuccess;
+  if (dtype_bf16 && d == 128) VS_EST(__bf16, 128);
+  else if (dtype_bf16 && d == 64) VS_EST(__bf16, 64);
+  else if (!dtype_bf16 && d == 128) VS_EST(float, 128);
+  else VS_EST(float, 64);
+#undef VS_EST
+  hipLaunchKernelGGL(vs_est_topk_kernel, dim3(2 * n_lists), dim3(kTopkThreads), 0, st, p,
+                     (const float*)v_score, (const float*)s_score, v_ptr, v_idx, s_ptr, s_idx);
+  return hipGetLastError();
+}
+
+}  // namespace vs

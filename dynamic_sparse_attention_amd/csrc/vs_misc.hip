@@ -1,0 +1,154 @@
+// vs_misc.hip — memory-bound helper kernels: vertical-list preparation,
+// the backward row term delta, and the LSE merge of chunk partials.
+#include "vs_attn_common.h"
+
+namespace vs {
+
+// convert_index for verticals (MTraining paper note, Algorithm 2): keep the
+// selected columns of list l that this call holds (inside the list's segment;
+// for a block-striped call, in a key block of rank k_rank), in ascending
+// order, as global positions.  One workgroup per list, ordered compaction.
+__global__ __launch_bounds__(256) void vs_prep_vertical_kernel(AttnParams p, const int* v_ptr,
+                                                               const int* v_idx) {
+  __shared__ int wsum[4];
+  const int l = blockIdx.x;
+  const int s = l % p.seg.n_seg;
+  int a, e;
+  if (p.W == 1) {
+    a = p.seg.start_blk[s] * kBlock;
+    e = p.seg.start_blk[s + 1] * kBlock;
+  } else {
+    a = 0;
+    e = p.n_global;
+  }
+  const int v0 = v_ptr[l];
+  const int nv = v_ptr[l + 1] - v0;
+  int* out = const_cast<int*>(p.vsel) + (size_t)l * p.vsel_stride;
+  int count = 0;
+  for (int base = 0; base < nv; base += 256) {
+    const int i = base + threadIdx.x;
+    int m = -1;
+    bool keep = false;
+    if (i < nv) {
+      m = v_idx[v0 + i];
+      keep = m >= a && m < e && local_key_block(p, m / kBlock) >= 0;
+    }
+    int tot;
+    const int slot = block_compact<256>(keep, wsum, &tot);
+    if (keep && count + slot < p.vsel_stride) out[count + slot] = m;
+    count += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) const_cast<int*>(p.vcnt)[l] = count < p.vsel_stride ? count : p.vsel_stride;
+}
+
+hipError_t launch_prep_vertical(const AttnParams& p, int n_lists, const int* v_ptr, const int* v_idx,
+                                hipStream_t st) {
+  if (n_lists == 0) return hipSuccess;
+  hipLaunchKernelGGL(vs_prep_vertical_kernel, dim3(n_lists), dim3(256), 0, st, p, v_ptr, v_idx);
+  return hipGetLastError();
+}
+
+// delta[b, h, n] = sum_c dO[b, n, h, c] * O[b, n, h, c]  (MTraining §3.2 Eq. 1:
+// rowsum(dA * A) = rowsum(dO * O)).  D/4 threads per row, 4 channels each.
+template <typename TO, typename TD, int D>
+__global__ __launch_bounds__(256) void vs_delta_kernel(const TO* o, const TD* dout, float* delta,
+                                                       int batch, int n, int h, size_t rows) {
+  constexpr int TPR = D / 4;
+  const size_t gt = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t row = gt / TPR;
+  const int c4 = (int)(gt % TPR) * 4;
+  float acc = 0.f;
+  if (row < rows) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += to_f32(o[row * D + c4 + u]) * to_f32(dout[row * D + c4 + u]);
+  }
+#pragma unroll
+  for (int w = TPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, 64);
+  if (row < rows && (gt % TPR) == 0) {
+    // row = (b * n + pos) * h + head  ->  delta[(b * h + head) * n + pos]
+    const size_t head = row % h;
+    const size_t bp = row / h;
+    const size_t pos = bp % n;
+    const size_t b = bp / n;
+    delta[(b * h + head) * n + pos] = acc;
+  }
+}
+
+hipError_t launch_delta(const void* o, int o_f32, int bf16, const void* dout, float* delta, int batch,
+                        int n, int h, int d, hipStream_t st) {
+  const size_t rows = (size_t)batch * n * h;
+  if (rows == 0) return hipSuccess;
+  const size_t threads = rows * (d / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+#define VS_DELTA(TO, TD, DD)                                                                        \
+  hipLaunchKernelGGL((vs_delta_kernel<TO, TD, DD>), grid, dim3(256), 0, st, (const TO*)o,          \
+                     (const TD*)dout, delta, batch, n, h, rows)
+  if (d == 128) {
+    if (o_f32 && bf16) VS_DELTA(float, __bf16, 128);
+    else if (o_f32) VS_DELTA(float, float, 128);
+    else if (bf16) VS_DELTA(__bf16, __bf16, 128);
+    else VS_DELTA(float, float, 128);
+  } else {
+    if (o_f32 && bf16) VS_DELTA(float, __bf16, 64);
+    else if (o_f32) VS_DELTA(float, float, 64);
+    else if (bf16) VS_DELTA(__bf16, __bf16, 64);
+    else VS_DELTA(float, float, 64);
+  }
+#undef VS_DELTA
+  return hipGetLastError();
+}
+
+// merge_out_and_lse (MTraining paper note, Algorithm 2), in place on the
+// accumulator; a partial with LSE = -inf is the identity.  d/4 threads per
+// row (one wave holds a whole row, so every lane reads lse_acc before any
+// lane of the row writes it).
+__global__ __launch_bounds__(256) void vs_lse_merge_kernel(int tpr, int n, int heads, size_t rows,
+                                                           float* o_acc, float* lse_acc,
+                                                           const float* o_part,
+                                                           const float* lse_part) {
+  const size_t gt = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t row = gt / tpr;
+  if (row >= rows) return;
+  const int c4 = (int)(gt % tpr) * 4;
+  const size_t head = row % heads;
+  const size_t bp = row / heads;
+  const size_t pos = bp % n;
+  const size_t b = bp / n;
+  const size_t li = (b * heads + head) * n + pos;
+  const float l1 = lse_acc[li];
+  const float l2 = lse_part[li];
+  const float mx = fmaxf(l1, l2);
+  const size_t oi = row * (size_t)(tpr * 4) + c4;
+  f32x4 r;
+  float lse;
+  if (mx == -INFINITY) {
+    r = f32x4{0.f, 0.f, 0.f, 0.f};
+    lse = -INFINITY;
+  } else {
+    const float w1 = expf(l1 - mx);
+    const float w2 = expf(l2 - mx);
+    const float tot = w1 + w2;
+    lse = mx + logf(tot);
+    const float a1 = w1 / tot;
+    const float a2 = w2 / tot;
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(o_acc + oi);
+    const f32x4 x2 = *reinterpret_cast<const f32x4*>(o_part + oi);
+    r = x1 * a1 + x2 * a2;
+  }
+  *reinterpret_cast<f32x4*>(o_acc + oi) = r;
+  if (c4 == 0) lse_acc[li] = lse;
+}
+
+hipError_t launch_lse_merge(int batch, int n, int heads, int d, float* o_acc, float* lse_acc,
+                            const float* o_part, const float* lse_part, hipStream_t st) {
+  const size_t rows = (size_t)batch * n * heads;
+  if (rows == 0) return hipSuccess;
+  const int tpr = d / 4;
+  const size_t threads = rows * tpr;
+  hipLaunchKernelGGL(vs_lse_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     tpr, n, heads, rows, o_acc, lse_acc, o_part, lse_part);
+  return hipGetLastError();
+}
+
+}  // namespace vs

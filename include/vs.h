@@ -1,0 +1,220 @@
+/*
+ * vs.h — C ABI of the Vertical-Slash dynamic sparse attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is MTraining's dynamic sparse attention (MTraining, arXiv
+ * 2510.18830, §3.2 and §4.1; the MTraining paper note, Algorithm 1 and
+ * Algorithm 2): an online estimator scores the last query block against all
+ * keys, keeps the top-k vertical key columns and the top-k slash
+ * block-diagonals of the 64x64 block grid, and causal attention forward and
+ * backward then run over that support only.  Partial results over successive
+ * KV chunks combine with lse_merge.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every call validates all host-visible arguments before it enqueues
+ *   anything; on error it returns a negative vs_status, enqueues nothing and
+ *   records a message readable with vs_last_error().  No call allocates or
+ *   frees device memory, and no call synchronises the stream: work is
+ *   enqueued on the caller's hipStream_t (NULL = the default stream).
+ * - Device buffers are caller-owned and must stay valid until the enqueued
+ *   work completes.  Host arrays (vs_problem.cu_seqlens, budgets) are read
+ *   only during the call.
+ * - Tensor layout is contiguous [batch, token, head, head_dim] ("BSHD") for
+ *   Q, K, V, O, dO, dQ, dK, dV and contiguous [batch, head, token] for LSE and
+ *   delta.  Element types: Q, K, V, dO in vs_problem.dtype; O in that dtype or
+ *   fp32 (o_f32); LSE, delta, dQ, dK, dV are fp32.
+ * - LSE is the natural-log log-sum-exp of the scaled scores of a row over its
+ *   support.  A row with an empty support has O = 0 and LSE = -inf and
+ *   contributes no gradient.
+ * - The index is a constant for the backward pass (the estimator is not
+ *   differentiated), as in Algorithm 1 where the index is built from the
+ *   observation window before the sparse attention call.
+ */
+#ifndef VS_H_
+#define VS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* vs_stream_t; /* the same object as hipStream_t */
+
+typedef int32_t vs_status;
+enum {
+  VS_OK = 0,
+  VS_ERR_NULL = -1,        /* a required pointer is NULL                               */
+  VS_ERR_SHAPE = -2,       /* inconsistent sizes, heads, segments or stripes           */
+  VS_ERR_UNSUPPORTED = -3, /* valid request outside what the GPU path implements       */
+  VS_ERR_BUDGET = -4,      /* negative budget                                          */
+  VS_ERR_WORKSPACE = -5,   /* workspace smaller than vs_workspace_size()               */
+  VS_ERR_HIP = -6,         /* a HIP launch failed; vs_last_error() has its message     */
+  VS_ERR_INDEX = -7        /* index capacities inconsistent with the problem           */
+};
+
+typedef enum { VS_F32 = 0, VS_BF16 = 1 } vs_dtype;
+
+/* Which rows and keys one call holds, in the coordinates of the index.
+ *
+ * Index coordinates are token positions 0..n_global-1 of one batch row,
+ * n_global = cu_seqlens[n_seg].  Segments [cu_seqlens[s], cu_seqlens[s+1])
+ * are packed documents: attention never crosses a segment boundary and each
+ * segment has its own index.  Inside a segment starting at a, the block of
+ * position p is beta(p) = (p - a) / block.
+ *
+ * Contiguous layout (stripe_world == 1): the call holds every row and key,
+ * n_q == n_k == n_global.
+ * Block-striped layout (stripe_world = W > 1, one segment only; MTraining
+ * §4.2 (ii): 64-token stripes): local row block i is global block
+ * q_rank + W*i and local key block j is global block k_rank + W*j, so
+ * n_global == W*n_q == W*n_k.  A striped call computes the global mask
+ * restricted to its rows and keys; one worker's ring step on KV chunk u is
+ * the call with q_rank = worker, k_rank = u.
+ */
+typedef struct vs_problem {
+  int32_t batch;        /* >= 1                                                   */
+  int32_t h_q;          /* query heads, a multiple of h_kv                         */
+  int32_t h_kv;         /* key/value heads; Q head h reads KV head h*h_kv/h_q      */
+  int32_t head_dim;     /* 64 or 128                                              */
+  int32_t n_q;          /* rows per batch row held by this call                   */
+  int32_t n_k;          /* keys per batch row held by this call                   */
+  int32_t block;        /* B, 64 (the slash granularity of MTraining §4.1 (ii))    */
+  int32_t dtype;        /* vs_dtype of Q, K, V, dO (and O unless o_f32)            */
+  float scale;          /* score scale; <= 0 selects 1/sqrt(head_dim)             */
+  int32_t n_seg;        /* 1..VS_MAX_SEGMENTS segments per batch row               */
+  const int32_t* cu_seqlens; /* HOST, n_seg+1 ascending token offsets, [0]=0;
+                                every segment length a multiple of block (>0) */
+  int32_t stripe_world; /* 1 = contiguous, W > 1 = block-striped                   */
+  int32_t q_rank;       /* striped: rank whose row blocks this call holds          */
+  int32_t k_rank;       /* striped: rank whose key blocks this call holds          */
+} vs_problem;
+
+#define VS_MAX_SEGMENTS 128
+
+/* The Vertical-Slash index, one list pair per (batch b, Q head h, segment s),
+ * list number l = (b*h_q + h)*n_seg + s.  All four arrays are DEVICE memory.
+ * v_idx[v_ptr[l] .. v_ptr[l+1]) are the selected vertical key columns as
+ * index-coordinate token positions inside segment s, strictly ascending;
+ * s_idx[s_ptr[l] .. s_ptr[l+1]) are the selected block-diagonal offsets
+ * g = beta(row) - beta(key) >= 0, strictly ascending.  Entries < 0 (padding
+ * written by vs_estimate_index when a capacity exceeds the candidates) are
+ * ignored.  v_cap_max / s_cap_max are HOST-known upper bounds of the list
+ * lengths (vs_index_capacity returns them) used to size launches.
+ */
+typedef struct vs_index {
+  const int32_t* v_ptr;
+  const int32_t* v_idx;
+  const int32_t* s_ptr;
+  const int32_t* s_idx;
+  int32_t v_cap_max;
+  int32_t s_cap_max;
+} vs_index;
+
+/* List offsets for budgets (MTraining paper note, Algorithm 1: argtopk with
+ * budgets k_v and k_s; MTraining §4.1 (ii): verticals per token, slashes per
+ * 64x64 block-diagonal).  v_budget[h], s_budget[h] (HOST, h_q entries) are
+ * tokens for the whole batch row.  Segment s of length L receives
+ * ceil(k*L/n_global) of each; the vertical share is clipped to L columns and
+ * the slash share becomes min(ceil(share/block), ceil(L/block))
+ * block-diagonals.  Writes v_ptr_host / s_ptr_host (HOST, batch*h_q*n_seg+1
+ * entries each) and, when not NULL, the largest list lengths.
+ * Errors: VS_ERR_NULL, VS_ERR_SHAPE, VS_ERR_BUDGET (a budget < 0). */
+vs_status vs_index_capacity(const vs_problem* p, const int32_t* v_budget,
+                            const int32_t* s_budget, int32_t* v_ptr_host,
+                            int32_t* s_ptr_host, int32_t* v_cap_max,
+                            int32_t* s_cap_max);
+
+/* Workspace bytes an entry point needs: op 0 = vs_estimate_index,
+ * 1 = vs_sparse_attn_fwd, 2 = vs_sparse_attn_bwd.  idx may be NULL for op 0;
+ * for ops 1 and 2 it supplies the capacity bounds.  The workspace is DEVICE
+ * memory, 256-byte aligned, owned by the caller, and may be reused across
+ * calls on the same stream. */
+vs_status vs_workspace_size(const vs_problem* p, int32_t op, const vs_index* idx,
+                            size_t* bytes);
+
+/* Online index estimation (MTraining paper note, Algorithm 1, first six
+ * steps; MTraining §4.1 (i)-(ii)).  For every (b, h, s): the last block of
+ * segment s (last_q = block rows) is the observation window; each window
+ * row r gets a causal softmax A_hat[r, m] over the segment's keys m <= r;
+ * the vertical score of column m is sum_r A_hat[r, m] and the slash score of
+ * block-diagonal g is the window mass on it; the v_ptr/s_ptr capacities of
+ * the highest scores are kept (ties to the lowest index) and written
+ * ascending into v_idx / s_idx (padding -1 when a capacity exceeds the
+ * candidates).  Scores are computed from bf16/fp32 inputs with fp32
+ * accumulation.
+ * q: [batch, n, h_q, d]; k: [batch, n, h_kv, d] (DEVICE, contiguous layout
+ * only: stripe_world must be 1).  v_ptr, s_ptr: DEVICE offsets from
+ * vs_index_capacity.  v_score [batch, h_q, n] and s_score
+ * [batch, h_q, n/block] (fp32, DEVICE, nullable) receive the scores; s_score
+ * entry of segment s, offset g, is at [b, h, cu_seqlens[s]/block + g].
+ * last_q: 0 or block (other window sizes are VS_ERR_UNSUPPORTED).
+ * Errors: VS_ERR_NULL, VS_ERR_SHAPE, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE,
+ * VS_ERR_HIP. */
+vs_status vs_estimate_index(const vs_problem* p, const void* q, const void* k,
+                            int32_t last_q, const int32_t* v_ptr, int32_t* v_idx,
+                            const int32_t* s_ptr, int32_t* s_idx, float* v_score,
+                            float* s_score, void* ws, size_t ws_bytes,
+                            vs_stream_t stream);
+
+/* Sparse attention forward (MTraining paper note, Algorithm 1 last step and
+ * Algorithm 2 block_bar_sparse_attention_forward; online softmax as in
+ * "Ring Attention Paper Analysis", "The Blockwise Partitioning Strategy").
+ * Row n attends to key m iff they share a segment, m <= n, and m is a
+ * selected vertical or beta(n) - beta(m) a selected block-diagonal of the
+ * row's (b, h, s) list.  q [batch, n_q, h_q, d], k/v [batch, n_k, h_kv, d]
+ * (DEVICE, dtype).  o [batch, n_q, h_q, d] (fp32 if o_f32 else dtype),
+ * lse [batch, h_q, n_q] fp32.  Rows are fully overwritten.
+ * Errors: VS_ERR_NULL, VS_ERR_SHAPE, VS_ERR_UNSUPPORTED, VS_ERR_INDEX,
+ * VS_ERR_WORKSPACE, VS_ERR_HIP. */
+vs_status vs_sparse_attn_fwd(const vs_problem* p, const void* q, const void* k,
+                             const void* v, const vs_index* idx, void* o, int32_t o_f32,
+                             float* lse, void* ws, size_t ws_bytes, vs_stream_t stream);
+
+/* delta[b, h, n] = sum_c dout[b, n, h, c] * o[b, n, h, c], the row term
+ * rowsum(dA * A) of MTraining §3.2 Eq. 1 (it equals rowsum(dO * O)).
+ * o is fp32 if o_f32 else dtype; dout is dtype; delta fp32 [batch, h_q, n_q].
+ * Errors: VS_ERR_NULL, VS_ERR_SHAPE, VS_ERR_UNSUPPORTED, VS_ERR_HIP. */
+vs_status vs_attn_bwd_delta(const vs_problem* p, const void* o, int32_t o_f32,
+                            const void* dout, float* delta, vs_stream_t stream);
+
+/* Sparse attention backward over the same support (MTraining §3.2 Eq. 1-2;
+ * paper note Appendix B.1): P = exp(S - lse), dP = dO V^T,
+ * dS = P * (dP - delta), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO,
+ * dK and dV summed over the Q heads of a KV group.  lse and delta are the
+ * FINAL values of the rows (after every KV chunk was merged); delta may be
+ * NULL, then it is computed from o and dout into the workspace (o and dout
+ * are read only in that case).  dq [batch, n_q, h_q, d] fp32 is overwritten,
+ * or accumulated into when dq_accumulate != 0; dk, dv [batch, n_k, h_kv, d]
+ * fp32 are overwritten.
+ * Errors: VS_ERR_NULL, VS_ERR_SHAPE, VS_ERR_UNSUPPORTED, VS_ERR_INDEX,
+ * VS_ERR_WORKSPACE, VS_ERR_HIP. */
+vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k,
+                             const void* v, const void* o, int32_t o_f32,
+                             const void* dout, const float* lse, const float* delta,
+                             const vs_index* idx, float* dq, int32_t dq_accumulate,
+                             float* dk, float* dv, void* ws, size_t ws_bytes,
+                             vs_stream_t stream);
+
+/* merge_out_and_lse (MTraining paper note, Algorithm 2): combine a partial
+ * result over a disjoint key set into an accumulator, in place:
+ * L = max(l1, l2) + log(e^(l1-max) + e^(l2-max)),
+ * O = e^(l1-L) O1 + e^(l2-L) O2, where a partial with LSE = -inf is the
+ * identity and two empty partials stay (O = 0, LSE = -inf).
+ * o_acc, o_part: fp32 [batch, n, heads, head_dim]; lse_acc, lse_part: fp32
+ * [batch, heads, n] (DEVICE).  head_dim a power of two from 4 to 256.
+ * Errors: VS_ERR_NULL, VS_ERR_SHAPE, VS_ERR_UNSUPPORTED, VS_ERR_HIP. */
+vs_status lse_merge(int32_t batch, int32_t n, int32_t heads, int32_t head_dim,
+                    float* o_acc, float* lse_acc, const float* o_part,
+                    const float* lse_part, vs_stream_t stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* vs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VS_H_ */

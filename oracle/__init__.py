@@ -25,12 +25,14 @@ steps are listed in the repository's design notes.
 from .index import (capacities, window_probs, window_scores, select_topk, estimate_index,
                     dense_mask)
 from .attention import (attn_fwd_dense, attn_bwd_dense, attn_fwd_support, attn_bwd_support,
-                        lse_merge, row_groups, support_candidates, bwd_delta)
+                        lse_merge, row_groups, support_candidates, bwd_delta,
+                        bwd_rounding_bounds)
 from .accounting import mask_area_bruteforce, mask_area_formula, dense_causal_area
 
 __all__ = [
     "capacities", "window_probs", "window_scores", "select_topk", "estimate_index",
     "dense_mask", "attn_fwd_dense", "attn_bwd_dense", "attn_fwd_support", "attn_bwd_support",
-    "lse_merge", "row_groups", "support_candidates", "bwd_delta", "mask_area_bruteforce",
+    "lse_merge", "row_groups", "support_candidates", "bwd_delta", "bwd_rounding_bounds",
+    "mask_area_bruteforce",
     "mask_area_formula", "dense_causal_area",
 ]

@@ -183,8 +183,12 @@ def attn_fwd_support(q, k, v, rows_pos, cols_pos, cu_seqlens, index, block=64, s
 
 
 def attn_bwd_support(q, k, v, do, lse, delta, rows_pos, cols_pos, cu_seqlens, index, block=64,
-                     scale=None, heads=None):
-    """Form (ii) backward over the support.  Same contract as ``attn_bwd_dense``."""
+                     scale=None, heads=None, row_filter=None):
+    """Form (ii) backward over the support.  Same contract as ``attn_bwd_dense``.
+
+    ``row_filter(seg, beta)`` limits the row groups (sampling): dQ is then exact
+    for the kept rows, and dK / dV hold only the kept rows' contributions.
+    """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     lse, delta = _f64(lse), _f64(delta)
     rows_pos = np.asarray(rows_pos)
@@ -200,6 +204,8 @@ def attn_bwd_support(q, k, v, do, lse, delta, rows_pos, cols_pos, cu_seqlens, in
     for h in heads:
         g = h * hkv // hq
         for ri, seg, beta in groups:
+            if row_filter is not None and not row_filter(seg, beta):
+                continue
             ci = support_candidates(seg, beta, rows_pos[ri].max(), cols_pos, cu_seqlens,
                                     index[(h, seg)], block)
             if ci.size == 0:
@@ -244,3 +250,59 @@ def bwd_delta(o, do):
     o, do: [rows, Hq, d].  Returns [Hq, rows] float64.
     """
     return (_f64(o) * _f64(do)).sum(-1).T
+
+
+def bwd_rounding_bounds(q, k, v, do, o, lse, rows_pos, cols_pos, cu_seqlens, index, block=64,
+                        scale=None, u_op=2.0 ** -8, u_o=2.0 ** -8, support=None):
+    """First-order error bounds of a backward whose matrix-core operands P and dS
+    are rounded to a format of unit roundoff u_op, with delta formed from an
+    output O stored with unit roundoff u_o (bf16: 2^-8 each; MTraining §5.1
+    trains in bfloat16).  Inputs are taken as exact.
+
+    With D~ = D + e_D, |e_D| <= u_o * sum_c |dO O| and dS~ = P (dP - D~) rounded:
+      |dQ~ - dQ| <= scale * (u_op |dS| |K| + |e_D| P |K|)
+      |dK~ - dK| <= scale * (u_op |dS|^T |Q| + (P |e_D|)^T |Q|)
+      |dV~ - dV| <= u_op P^T |dO|
+    (row-wise sums over the support; GQA sums over the group).  Returns
+    (bq, bk, bv) shaped like dQ, dK, dV.  ``support`` selects form (ii) when
+    True (default: form (i) for at most 4096 rows).
+    """
+    q, k, v, do, o = _f64(q), _f64(k), _f64(v), _f64(do), _f64(o)
+    lse = _f64(lse)
+    rows_pos = np.asarray(rows_pos)
+    cols_pos = np.asarray(cols_pos)
+    nr, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    use_support = (nr > 4096) if support is None else support
+    D = bwd_delta(o, do)
+    eD = u_o * np.abs(do * o).sum(-1).T
+    bq = np.zeros_like(q)
+    bk = np.zeros_like(k)
+    bv = np.zeros_like(v)
+    aq, ak, ado = np.abs(q), np.abs(k), np.abs(do)
+
+    def accumulate(h, g, ri, ci, M):
+        S = np.where(M, scale * (q[ri, h] @ k[ci, g].T), -np.inf)
+        A = _probs(S, lse[h, ri])
+        dA = do[ri, h] @ v[ci, g].T
+        adS = np.abs(A * (dA - D[h, ri][:, None]))
+        e = eD[h, ri]
+        bq[ri, h] = scale * (u_op * adS @ ak[ci, g] + e[:, None] * (A @ ak[ci, g]))
+        bk[ci, g] += scale * (u_op * adS.T @ aq[ri, h] + (A * e[:, None]).T @ aq[ri, h])
+        bv[ci, g] += u_op * A.T @ ado[ri, h]
+
+    for h in range(hq):
+        g = h * hkv // hq
+        if not use_support:
+            M = dense_mask(rows_pos, cols_pos, cu_seqlens, index, h, block)
+            accumulate(h, g, np.arange(nr), np.arange(cols_pos.size), M)
+            continue
+        for ri, seg, beta in row_groups(rows_pos, cu_seqlens, block):
+            ci = support_candidates(seg, beta, rows_pos[ri].max(), cols_pos, cu_seqlens,
+                                    index[(h, seg)], block)
+            if ci.size == 0:
+                continue
+            M = _group_mask(rows_pos[ri], cols_pos[ci], seg, cu_seqlens, index[(h, seg)], block)
+            accumulate(h, g, ri, ci, M)
+    return bq, bk, bv

@@ -1,0 +1,168 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vs.h")
+
+
+@pytest.fixture(scope="module")
+def abi():
+    from dynamic_sparse_attention_amd import _abi
+    if not os.path.exists(_abi.LIB_PATH):
+        from dynamic_sparse_attention_amd import build
+        build.build()
+    _abi.lib()
+    return _abi
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:vs_status|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_symbols_exported(abi):
+    names = declared_functions()
+    assert set(names) == set(abi.SIGNATURES), (names, list(abi.SIGNATURES))
+    L = abi.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def prob(abi, **kw):
+    cu = kw.pop("cu", [0, 4096])
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    base = dict(batch=1, h_q=16, h_kv=2, head_dim=128, n_q=cu[-1], n_k=cu[-1], block=64,
+                dtype=abi.VS_BF16, scale=0.0, n_seg=len(cu) - 1, stripe_world=1, q_rank=0, k_rank=0)
+    base.update(kw)
+    p = abi.VsProblem(**{k: v for k, v in base.items()})
+    p.cu_seqlens = ctypes.cast(arr, abi.i32p)
+    p._keep = arr
+    return p
+
+
+def capacity(abi, p, vb, sb):
+    nl = p.batch * p.h_q * p.n_seg
+    vp = (ctypes.c_int32 * (nl + 1))()
+    sp = (ctypes.c_int32 * (nl + 1))()
+    a = (ctypes.c_int32 * p.h_q)(*vb)
+    b = (ctypes.c_int32 * p.h_q)(*sb)
+    vm, sm = ctypes.c_int32(), ctypes.c_int32()
+    st = abi.lib().vs_index_capacity(ctypes.byref(p), a, b, vp, sp, ctypes.byref(vm), ctypes.byref(sm))
+    return st, list(vp), list(sp), vm.value, sm.value
+
+
+@pytest.mark.parametrize("cu,vb,sb", [
+    ([0, 131072], 2048, 8192),
+    ([0, 1024], 64, 64),
+    ([0, 1024], 5000, 10 ** 6),
+    ([0, 640, 4096, 8192], 1000, 3000),
+    ([0, 64, 128], 1, 1),
+])
+def test_capacity_matches_oracle(abi, cu, vb, sb):
+    hq = 4
+    p = prob(abi, cu=cu, h_q=hq, h_kv=1)
+    vbs = [vb + h for h in range(hq)]
+    sbs = [sb * (h + 1) for h in range(hq)]
+    st, vp, sp, vm, sm = capacity(abi, p, vbs, sbs)
+    assert st == abi.VS_OK
+    for h in range(hq):
+        for s in range(len(cu) - 1):
+            l = h * (len(cu) - 1) + s
+            kv, kg = oracle.capacities(vbs[h], sbs[h], cu[s + 1] - cu[s], cu[-1], 64)
+            assert vp[l + 1] - vp[l] == kv and sp[l + 1] - sp[l] == kg
+    assert vm == max(vp[i + 1] - vp[i] for i in range(len(vp) - 1))
+    assert sm == max(sp[i + 1] - sp[i] for i in range(len(sp) - 1))
+
+
+def status_of(abi, p, vb=None, sb=None):
+    return capacity(abi, p, vb or [1] * p.h_q, sb or [1] * p.h_q)[0]
+
+
+def test_problem_validation(abi):
+    L = abi.lib()
+    assert L.vs_index_capacity(None, None, None, None, None, None, None) == abi.VS_ERR_NULL
+    assert "NULL" in L.vs_last_error().decode()
+    assert status_of(abi, prob(abi, h_q=6, h_kv=4)) == abi.VS_ERR_SHAPE
+    assert status_of(abi, prob(abi, head_dim=96)) == abi.VS_ERR_UNSUPPORTED
+    assert status_of(abi, prob(abi, block=32)) == abi.VS_ERR_UNSUPPORTED
+    assert status_of(abi, prob(abi, dtype=7)) == abi.VS_ERR_UNSUPPORTED
+    assert status_of(abi, prob(abi, cu=[0, 100])) == abi.VS_ERR_UNSUPPORTED
+    assert status_of(abi, prob(abi, cu=[64, 128])) == abi.VS_ERR_SHAPE
+    assert status_of(abi, prob(abi, cu=[0, 128, 128])) == abi.VS_ERR_SHAPE
+    assert status_of(abi, prob(abi, n_q=2048)) == abi.VS_ERR_SHAPE
+    assert status_of(abi, prob(abi, batch=0)) == abi.VS_ERR_SHAPE
+    assert status_of(abi, prob(abi, h_q=16), [-1] * 16) == abi.VS_ERR_BUDGET
+    assert status_of(abi, prob(abi, scale=float("nan"))) == abi.VS_ERR_SHAPE
+    many = list(range(0, 64 * 130, 64))
+    assert status_of(abi, prob(abi, cu=many)) == abi.VS_ERR_UNSUPPORTED
+    # block striping
+    assert status_of(abi, prob(abi, cu=[0, 8192], n_q=1024, n_k=1024, stripe_world=8, q_rank=1,
+                               k_rank=7)) == abi.VS_OK
+    assert status_of(abi, prob(abi, cu=[0, 8192], n_q=1024, n_k=1024, stripe_world=8, q_rank=8)) == \
+        abi.VS_ERR_SHAPE
+    assert status_of(abi, prob(abi, cu=[0, 4096, 8192], n_q=1024, n_k=1024, stripe_world=8)) == \
+        abi.VS_ERR_UNSUPPORTED
+    assert status_of(abi, prob(abi, cu=[0, 8192], n_q=2048, n_k=1024, stripe_world=8)) == abi.VS_ERR_SHAPE
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def test_entry_points_reject_before_launch(abi):
+    L = abi.lib()
+    p = prob(abi)
+    P = ctypes.byref(p)
+    ix = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 64, 4)
+    nb = ctypes.c_size_t()
+    assert L.vs_workspace_size(P, 0, None, ctypes.byref(nb)) == abi.VS_OK and nb.value > 0
+    assert L.vs_workspace_size(P, 1, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_OK
+    fwd_ws = nb.value
+    assert L.vs_workspace_size(P, 2, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_OK
+    assert nb.value > fwd_ws
+    assert L.vs_workspace_size(P, 3, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_ERR_SHAPE
+    assert L.vs_workspace_size(P, 1, None, ctypes.byref(nb)) == abi.VS_ERR_NULL
+    # estimate
+    st = L.vs_estimate_index(P, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_UNSUPPORTED
+    st = L.vs_estimate_index(P, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 16, None)
+    assert st == abi.VS_ERR_WORKSPACE
+    st = L.vs_estimate_index(P, None, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_NULL
+    ps = prob(abi, cu=[0, 8192], n_q=1024, n_k=1024, stripe_world=8)
+    st = L.vs_estimate_index(ctypes.byref(ps), FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                             1 << 40, None)
+    assert st == abi.VS_ERR_UNSUPPORTED
+    # forward
+    st = L.vs_sparse_attn_fwd(P, FAKE, FAKE, FAKE, ctypes.byref(ix), FAKE, 0, FAKE, FAKE, 16, None)
+    assert st == abi.VS_ERR_WORKSPACE
+    st = L.vs_sparse_attn_fwd(P, FAKE, FAKE, None, ctypes.byref(ix), FAKE, 0, FAKE, FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_NULL
+    bad = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 5000, 4)
+    st = L.vs_sparse_attn_fwd(P, FAKE, FAKE, FAKE, ctypes.byref(bad), FAKE, 0, FAKE, FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_INDEX
+    bad = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 64, 65)
+    st = L.vs_sparse_attn_fwd(P, FAKE, FAKE, FAKE, ctypes.byref(bad), FAKE, 0, FAKE, FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_INDEX
+    bad = abi.VsIndex(0x1000, None, 0x1000, 0x1000, 64, 4)
+    st = L.vs_sparse_attn_fwd(P, FAKE, FAKE, FAKE, ctypes.byref(bad), FAKE, 0, FAKE, FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_NULL
+    # backward
+    st = L.vs_sparse_attn_bwd(P, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, None, ctypes.byref(ix), FAKE, 0,
+                              FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_NULL
+    st = L.vs_sparse_attn_bwd(P, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, ctypes.byref(ix), FAKE, 0,
+                              FAKE, FAKE, FAKE, fwd_ws, None)
+    assert st == abi.VS_ERR_WORKSPACE
+    st = L.vs_attn_bwd_delta(P, None, 0, FAKE, FAKE, None)
+    assert st == abi.VS_ERR_NULL
+    # merge
+    assert L.lse_merge(1, 16, 2, 96, FAKE, FAKE, FAKE, FAKE, None) == abi.VS_ERR_UNSUPPORTED
+    assert L.lse_merge(1, 16, 2, 128, None, FAKE, FAKE, FAKE, None) == abi.VS_ERR_NULL
+    assert L.lse_merge(-1, 16, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == abi.VS_ERR_SHAPE

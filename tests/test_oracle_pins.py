@@ -476,3 +476,38 @@ def test_p10_golden_mask_areas():
         pos = np.arange(n)
         assert oracle.mask_area_bruteforce(pos, pos, cu, idx, 1, B)[0] == case["area"]
         assert oracle.dense_causal_area(pos, cu) == case["area"]
+
+
+# ---------------------------------------------------------------- rounding bound of the bf16 backward
+def test_bwd_rounding_bound_holds_for_simulated_bf16():
+    """A backward that rounds P, dS and O to bf16 (simulated here with torch on the CPU)
+    stays inside oracle.bwd_rounding_bounds element by element, and the bound is
+    not vacuous (the simulated error reaches a visible fraction of it)."""
+    rng = np.random.default_rng(19)
+    n, hq, hkv, d, B = 256, 2, 1, 32, 32
+    bf = lambda x: torch.tensor(x).to(torch.bfloat16).to(torch.float64).numpy()
+    q, do = bf(rng.standard_normal((n, hq, d))), bf(rng.standard_normal((n, hq, d)))
+    k, v = bf(rng.standard_normal((n, hkv, d))), bf(rng.standard_normal((n, hkv, d)))
+    k[17] *= 6
+    pos = np.arange(n)
+    idx = rand_index(rng, n, hq, B, kv=20, kg=3)
+    O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], idx, B)
+    D = oracle.bwd_delta(O, do)
+    dq, dk, dv = oracle.attn_bwd_dense(q, k, v, do, L, D, pos, pos, [0, n], idx, B)
+    bq, bk, bv = oracle.bwd_rounding_bounds(q, k, v, do, O, L, pos, pos, [0, n], idx, B)
+    scale = 1 / math.sqrt(d)
+    Ob = bf(O)
+    Dt = (Ob * do).sum(-1).T
+    sq, sk, sv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h in range(hq):
+        M = oracle.dense_mask(pos, pos, [0, n], idx, h, B)
+        S = np.where(M, scale * q[:, h] @ k[:, 0].T, -np.inf)
+        A = np.where(M, np.exp(S - np.where(np.isfinite(L[h]), L[h], 0)[:, None]), 0)
+        dS = bf(A * (do[:, h] @ v[:, 0].T - Dt[h][:, None]))
+        sq[:, h] = scale * dS @ k[:, 0]
+        sk[:, 0] += scale * dS.T @ q[:, h]
+        sv[:, 0] += bf(A).T @ do[:, h]
+    for sim, ref, b in ((sq, dq, bq), (sk, dk, bk), (sv, dv, bv)):
+        err = np.abs(sim - ref)
+        assert np.all(err <= 1.01 * b + 1e-12)
+        assert (err / (b + 1e-30)).max() > 0.05

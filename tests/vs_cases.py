@@ -1,0 +1,137 @@
+"""Shared helpers for the GPU parity tests: seeded problems, oracle runs, comparisons.
+
+Inputs come from the seeded generator (``workloads``); expected values come
+from the CPU oracle only.  The oracle's index is handed to the GPU attention
+calls, so attention parity does not depend on the estimator's near-ties.
+"""
+from __future__ import annotations
+
+import math
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def oracle_index(prob: workloads.Problem, last_q=64):
+    """Oracle index {(h, seg): (iv, is)} for batch row 0 (float64 estimator)."""
+    return oracle.estimate_index(np64(prob.q[0]), np64(prob.k[0]), prob.cu_seqlens, prob.v_budget,
+                                 prob.s_budget, prob.block, last_q, return_scores=True)
+
+
+def lists_for_gpu(index, h_q, n_seg):
+    """Oracle index -> list order of the C ABI (l = h * n_seg + s, batch 1)."""
+    return [(index[(h, s)][0].tolist(), index[(h, s)][1].tolist())
+            for h in range(h_q) for s in range(n_seg)]
+
+
+def bf16_tol(ref: np.ndarray, got: np.ndarray):
+    """(max-abs, relative L2) of got vs ref."""
+    err = np.abs(got - ref)
+    rel = np.linalg.norm((got - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-30)
+    return float(err.max(initial=0.0)), float(rel)
+
+
+def check_close(name, ref, got, dtype, kind="out", bound=None):
+    """Compare got with ref; returns an error string or None.
+
+    fp32: max-abs <= 1e-4.  bf16 outputs (O, LSE): max-abs <= 2e-2.
+    bf16 gradients: relative L2 <= 1e-2 and, element by element,
+    |err| <= 2 * bound, the first-order bf16 rounding bound of the backward
+    (oracle.bwd_rounding_bounds); the literal max-abs is printed.
+    """
+    ref = np.asarray(ref, np.float64)
+    got = np.asarray(got, np.float64)
+    if ref.shape != got.shape:
+        return f"{name}: shape {got.shape} != {ref.shape}"
+    fin_r = np.isfinite(ref)
+    fin_g = np.isfinite(got)
+    if not np.array_equal(fin_r, fin_g):
+        return f"{name}: finite pattern differs ({int((fin_r != fin_g).sum())} entries)"
+    if not np.array_equal(ref[~fin_r], got[~fin_g]):
+        return f"{name}: infinities differ"
+    r, g = ref[fin_r], got[fin_g]
+    mx, rel = bf16_tol(r, g)
+    extra = ""
+    if bound is not None:
+        b = np.asarray(bound, np.float64)[fin_r]
+        ratio = float((np.abs(g - r) / (b + 1e-30)).max(initial=0.0))
+        extra = f" err/bound {ratio:.3f}"
+    log(f"  {name}: max-abs {mx:.3e} rel-L2 {rel:.3e}{extra} (n={r.size})")
+    if dtype == "f32":
+        return None if mx <= 1e-4 else f"{name}: max-abs {mx}"
+    if kind == "out":
+        return None if mx <= 2e-2 else f"{name}: max-abs {mx}"
+    if rel > 1e-2:
+        return f"{name}: rel-L2 {rel}"
+    if bound is not None:
+        bad = np.abs(g - r) > 2.0 * b + 1e-6
+        if bad.any():
+            return f"{name}: {int(bad.sum())} entries beyond 2x rounding bound (worst ratio {ratio:.2f})"
+    return None
+
+
+def assert_close(name, ref, got, dtype, kind="out", bound=None):
+    err = check_close(name, ref, got, dtype, kind, bound)
+    assert err is None, err
+
+
+def index_parity(name, o_index, o_scores, g_lists, g_vscore, g_sscore, prob, rel_tie=1e-4):
+    """Estimator parity.
+
+    1. scores: GPU fp32 vertical / slash scores against the oracle's fp64 ones;
+    2. selection: each GPU list is exactly the top-k of the GPU's own scores
+       (ties to the lowest index) — the integer decision in the kernel's
+       precision, checked with a plain stable sort;
+    3. sets: each GPU list equals the oracle's; a difference is accepted only
+       as certified near-ties (oracle scores of every swapped element within
+       rel_tie of the k-th score) and is reported.
+    Returns the number of near-tie swaps.
+    """
+    n_seg = len(prob.cu_seqlens) - 1
+    swaps = 0
+    vmax = 0.0
+    for h in range(prob.h_q):
+        for s in range(n_seg):
+            a, e = prob.cu_seqlens[s], prob.cu_seqlens[s + 1]
+            l = h * n_seg + s
+            ov, osg = o_scores[(h, s)]
+            gv = g_vscore[h, a:e].astype(np.float64)
+            gs = g_sscore[h, a // 64: e // 64].astype(np.float64)
+            vmax = max(vmax, float(np.abs(gv - ov).max() / max(ov.max(), 1e-30)))
+            assert np.abs(gv - ov).max() <= 1e-3 * max(ov.max(), 1e-30) + 1e-6, (name, h, s, "v")
+            assert np.abs(gs - osg).max() <= 1e-3 * max(osg.max(), 1e-30) + 1e-6, (name, h, s, "sigma")
+            gvl = np.asarray(g_lists[l][0])
+            gsl = np.asarray(g_lists[l][1])
+            for kind, glist, gsc, olist, osc, off in (("v", gvl, g_vscore[h, a:e], o_index[(h, s)][0], ov, a),
+                                                      ("s", gsl, g_sscore[h, a // 64:e // 64], o_index[(h, s)][1], osg, 0)):
+                k = olist.size
+                assert glist.size == k, (name, kind, h, s, glist.size, k)
+                assert np.all(np.diff(glist) > 0), (name, kind, "not ascending")
+                # selection in the kernel's precision
+                sc32 = np.asarray(gsc, np.float32)
+                order = np.lexsort((np.arange(sc32.size), -sc32.astype(np.float64)))
+                assert np.array_equal(np.sort(order[:k]) + off, glist), (name, kind, h, s, "not top-k of own scores")
+                if not np.array_equal(glist, olist):
+                    extra = np.setdiff1d(glist, olist) - off
+                    miss = np.setdiff1d(olist, glist) - off
+                    kth = np.sort(osc)[::-1][k - 1]
+                    tol = rel_tie * max(kth, 1e-30)
+                    assert np.all(np.abs(osc[extra] - kth) <= tol) and np.all(np.abs(osc[miss] - kth) <= tol), \
+                        (name, kind, h, s, "non-tie mismatch", extra[:5], miss[:5])
+                    swaps += extra.size
+    log(f"  {name}: index sets match oracle, near-tie swaps={swaps}, max rel score err={vmax:.2e}")
+    return swaps
