@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark: Vertical-Slash sparse attention (index estimate + forward + backward) on one MI355X.
+
+Workload (default): one Qwen2.5-3B-shaped attention layer at N = 131072, bf16,
+16 Q / 2 KV heads, head_dim 128, causal, 64-token blocks, vertical budget 2048
+and slash budget 8192 tokens, seeded synthetic Q/K/V/dO with RoPE and 0.1%
+outlier keys.  One step = vs_estimate_index + vs_sparse_attn_fwd +
+vs_sparse_attn_bwd over inputs already resident in HBM.
+
+Prints one JSON line.  value = executed TFLOP/s = 14 * d * H_q * |M| / t_step
+(|M| = valid entries of the estimated index per head; 4d forward + 10d
+backward per entry); also dense-equivalent TFLOP/s over the causal area and
+the fraction of the bf16 matrix-core peak.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd sparse attn TFLOP/s (executed & dense-equiv), % bf16 MFMA peak, N=128K"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (published)
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def trace_read(vs):
+    buf = ctypes.create_string_buffer(1 << 16)
+    vs._abi.check(vs._abi.lib().vs_trace_collect(buf, len(buf)))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, tot = line.split()
+        out[name] = (int(cnt), float(tot))
+    return out
+
+
+def cpu_baseline(prob, lists, target_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload.
+
+    Sample: the estimator for one Q head (window scoring over all keys) and the
+    support-form forward + backward for evenly spaced query blocks of that
+    head, until about target_s seconds have passed.  The job time is
+    extrapolated: estimator time x heads + (sample time / sample entries) x |M|.
+    """
+    import numpy as np
+    import oracle
+    from dynamic_sparse_attention_amd import accounting
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    h = 0
+    g = h * prob.h_kv // prob.h_q
+    q = prob.q[0].to(dtype=__import__("torch").float64).numpy()
+    k = prob.k[0].to(dtype=__import__("torch").float64).numpy()
+    v = prob.v[0].to(dtype=__import__("torch").float64).numpy()
+    do = prob.do[0].to(dtype=__import__("torch").float64).numpy()
+    n = prob.n
+    t0 = time.perf_counter()
+    oracle.estimate_index(q[:, h:h + 1], k[:, g:g + 1], prob.cu_seqlens, prob.v_budget[:1],
+                          prob.s_budget[:1])
+    t_est = time.perf_counter() - t0
+    index = {(0, 0): (np.asarray(lists[h][0]), np.asarray(lists[h][1]))}
+    nb = n // 64
+    order = np.concatenate([np.arange(s, nb, 64) for s in range(64)])  # spread over the sequence
+    pos = np.arange(n)
+    done, t_fb = [], 0.0
+    qh, doh = q[:, h:h + 1], do[:, h:h + 1]
+    kg, vg = k[:, g:g + 1], v[:, g:g + 1]
+    for blk in order:
+        rows = pos[blk * 64:(blk + 1) * 64]
+        t1 = time.perf_counter()
+        O, L = oracle.attn_fwd_support(qh[rows], kg, vg, rows, pos, prob.cu_seqlens, index)
+        D = oracle.bwd_delta(O, doh[rows])
+        oracle.attn_bwd_support(qh[rows], kg, vg, doh[rows], L, D, rows, pos, prob.cu_seqlens, index)
+        t_fb += time.perf_counter() - t1
+        done.append(blk)
+        if t_est + t_fb >= target_s:
+            break
+    ent = int(accounting.executed_area([lists[h]], prob.cu_seqlens, 1,
+                                       row_blocks=np.asarray(done))[0])
+    total_ent = int(sum(accounting.executed_area(lists, prob.cu_seqlens, prob.h_q)))
+    job_s = t_est * prob.h_q + t_fb / max(ent, 1) * total_ent
+    flops = 14 * prob.d * total_ent
+    return {"value": round(flops / job_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle: estimator for 1 of {prob.h_q} heads ({t_est:.2f} s) and "
+                       f"support-form fwd+bwd of {len(done)} of {nb} query blocks of that head "
+                       f"({ent} entries, {t_fb:.2f} s); job time extrapolated to {job_s:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="workload id (3 = N=131072)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dynamic_sparse_attention_amd as vs
+    from dynamic_sparse_attention_amd import accounting
+    import workloads
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    prob = workloads.make_problem(args.workload)
+    log(f"inputs {prob.name}: n={prob.n} in {time.time() - t0:.1f} s")
+    cu = prob.cu_seqlens
+    q, k, v, do = (t.to(dev) for t in (prob.q, prob.k, prob.v, prob.do))
+    B, N, Hq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq = torch.empty((B, N, Hq, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, N, prob.h_kv, d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+
+    idx = vs.estimate_index(q, k, prob.v_budget, prob.s_budget, cu)
+    lists = [(a.numpy(), b.numpy()) for a, b in idx.lists()]
+    ent_heads = accounting.executed_area(lists, cu, Hq)
+    ent = int(ent_heads.sum())
+    dense = accounting.dense_causal_area(cu) * Hq
+    log(f"index: executed entries {ent} of {dense} causal ({ent / dense:.4f})")
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ix = vs.estimate_index(q, k, prob.v_budget, prob.s_budget, cu)
+        if ev is not None:
+            ev[1].record(stream)
+        vs.sparse_attn_fwd(q, k, v, ix, cu, out=o, lse=lse)
+        if ev is not None:
+            ev[2].record(stream)
+        vs.sparse_attn_bwd(q, k, v, o, do, lse, ix, cu_seqlens=cu, dq=dq, dk=dk, dv=dv)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    lib = vs._abi.lib()
+    lib.vs_trace_enable(1)
+    trace_read(vs)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    lib.vs_trace_enable(0)
+    kern = trace_read(vs)
+    ms = start.elapsed_time(stop) / args.steps
+    phases = {"estimate": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+              "fwd": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+              "bwd": float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))}
+    exec_tf = 14 * d * ent / (ms * 1e-3) / 1e12
+    dense_tf = 14 * d * dense / (ms * 1e-3) / 1e12
+    log(f"step {ms:.3f} ms; phases {phases}")
+    for name, (cnt, tot) in sorted(kern.items(), key=lambda x: -x[1][1]):
+        log(f"  kernel {name}: {cnt} launches, avg {tot / cnt:.4f} ms")
+
+    # Roofline of the dominant kernel: algorithmic matrix-core FLOPs per launch.
+    split = accounting.executed_split(lists, cu, Hq)
+    alg = {"vs_fwd": 4 * d * ent,
+           "vs_bwd_dq": 6 * d * ent,
+           "vs_bwd_dkdv_slash": 8 * d * int(split["slash"].sum()),
+           "vs_bwd_dkdv_cols": 8 * d * int(split["vertical"].sum())}
+    dom = max(kern.items(), key=lambda x: x[1][1])[0]
+    cnt, tot = kern[dom]
+    avg_s = tot / cnt * 1e-3
+    if dom in alg:
+        ach = alg[dom] / avg_s / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_ms": round(tot / cnt, 4)}
+    else:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": None, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": None, "traffic": None, "avg_ms": round(tot / cnt, 4)}
+    per_kernel = {n: round(t / c, 4) for n, (c, t) in kern.items()}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t1 = time.time()
+        cpu = cpu_baseline(prob, lists, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']} TFLOP/s in {time.time() - t1:.1f} s")
+
+    out = {
+        "metric": METRIC, "value": round(exec_tf, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "dense_equiv_tflops": round(dense_tf, 3),
+        "pct_bf16_peak_executed": round(100 * exec_tf / PEAK_BF16_TFLOPS, 3),
+        "config": {"workload": prob.name, "batch": 1, "seq_len": N, "h_q": Hq, "h_kv": prob.h_kv,
+                   "head_dim": d, "block": 64, "v_budget": prob.v_budget[0],
+                   "s_budget": prob.s_budget[0], "executed_entries": ent, "causal_entries": dense,
+                   "density": round(ent / dense, 5), "phases_ms": {k_: round(v_, 4) for k_, v_ in phases.items()},
+                   "kernels_avg_ms": per_kernel, "parallelism": "none"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -209,11 +209,13 @@ def attn_bwd_delta(o: torch.Tensor, do: torch.Tensor, out: Optional[torch.Tensor
 
 
 def sparse_attn_bwd(q, k, v, o, do, lse, index: VsIndexT, delta=None, dq=None,
-                    cu_seqlens=None, stripe=None, scale=None, dk=None, dv=None):
+                    cu_seqlens=None, stripe=None, scale=None, dk=None, dv=None,
+                    accumulate: bool = False):
     """Sparse attention backward.  Returns (dq, dk, dv), fp32.
 
-    lse (and delta, if given) are the rows' final values.  If dq is given it
-    is accumulated into (chunked KV); otherwise a new dq is returned.
+    lse (and delta, if given) are the rows' final values.  dq / dk / dv are
+    optional output buffers; with accumulate=True the gradient of Q is added
+    to dq (chunked KV) instead of overwriting it.
     """
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
@@ -222,7 +224,9 @@ def sparse_attn_bwd(q, k, v, o, do, lse, index: VsIndexT, delta=None, dq=None,
     B, Nq, Hq, d = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
     P = _Problem(B, Hq, Hkv, d, Nq, Nk, _dtype_code(q), cu_seqlens, stripe, scale)
-    acc = dq is not None
+    acc = bool(accumulate)
+    if acc and dq is None:
+        raise ValueError("accumulate=True needs dq")
     if dq is None:
         dq = torch.empty((B, Nq, Hq, d), dtype=torch.float32, device=dev)
     dk = dk if dk is not None else torch.empty((B, Nk, Hkv, d), dtype=torch.float32, device=dev)

@@ -1,0 +1,91 @@
+"""Work accounting of a Vertical-Slash index (host side, numpy).
+
+The work of sparse attention is the number of valid (row, key) entries, the
+"effective mask area" of the MagiAttention "Dynamic Attention Solver" docs
+("Computation Cost Estimation"): each selected block-diagonal g > 0 adds one
+full 64x64 block per query block i >= g, g = 0 adds the causal triangle
+64*65/2 per block, and each selected column m adds, for every query block at
+or below it whose offset to m's block is not selected, its rows n >= m.
+
+FLOP conventions: forward 4*d per entry (two products), backward 10*d per
+entry (five products: S recompute, dP, dV, dQ, dK).
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+FWD_FLOPS_PER_ENTRY_PER_DIM = 4
+BWD_FLOPS_PER_ENTRY_PER_DIM = 10
+
+
+def executed_split(lists, cu_seqlens: Sequence[int], h_q: int, block: int = 64,
+                   row_blocks: Optional[np.ndarray] = None):
+    """Valid entries per Q head, split into slash-block entries and vertical-column
+    entries (columns inside a selected block count once, as slash entries).
+
+    lists[l] = (verticals, block-diagonals), l = h * n_seg + s (batch 1).
+    row_blocks: optional global block indices of the rows actually held
+    (one segment only, e.g. a block-striped worker); default all rows.
+    Returns {"slash": int64[h_q], "vertical": int64[h_q]}.
+    """
+    n_seg = len(cu_seqlens) - 1
+    sl = np.zeros(h_q, dtype=np.int64)
+    ve = np.zeros(h_q, dtype=np.int64)
+    tri = block * (block + 1) // 2
+    for h in range(h_q):
+        for s in range(n_seg):
+            a, e = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+            nb = (e - a) // block
+            iv, is_ = lists[h * n_seg + s]
+            iv = np.asarray(iv, dtype=np.int64)
+            iv = iv[iv >= 0]
+            is_ = np.asarray(is_, dtype=np.int64)
+            is_ = np.sort(is_[(is_ >= 0) & (is_ < nb)])
+            rows = np.arange(nb, dtype=np.int64) if row_blocks is None else \
+                np.asarray(row_blocks, dtype=np.int64)
+            # slash part: blocks (i, i - g) for g <= i
+            cnt_le = np.searchsorted(is_, rows, side="right")      # #g <= i
+            has0 = is_.size > 0 and is_[0] == 0
+            sl[h] += int((cnt_le - (1 if has0 else 0)).clip(min=0).sum()) * block * block
+            if has0:
+                sl[h] += rows.size * tri
+            if iv.size == 0:
+                continue
+            bm = (iv - a) // block
+            if row_blocks is None:
+                # rows of m's own block at or below m, unless offset 0 is selected
+                if not has0:
+                    ve[h] += int((a + (bm + 1) * block - iv).sum())
+                # later blocks: offsets 1 .. nb-1-bm not selected
+                span = nb - 1 - bm
+                nsel = np.searchsorted(is_, span, side="right") - np.searchsorted(is_, 1, side="left")
+                ve[h] += int(((span - nsel).clip(min=0)).sum()) * block
+            else:
+                selset = np.zeros(nb + 1, dtype=bool)
+                selset[is_] = True
+                for i in rows:
+                    off = i - bm
+                    ok = (off >= 0) & ~selset[np.clip(off, 0, nb)]
+                    full = ok & (off > 0)
+                    same = ok & (off == 0)
+                    ve[h] += int(full.sum()) * block
+                    ve[h] += int((a + (i + 1) * block - iv[same]).sum())
+    return {"slash": sl, "vertical": ve}
+
+
+def executed_area(lists, cu_seqlens: Sequence[int], h_q: int, block: int = 64,
+                  row_blocks: Optional[np.ndarray] = None) -> np.ndarray:
+    """Valid entries per Q head (slash and vertical entries together)."""
+    sp = executed_split(lists, cu_seqlens, h_q, block, row_blocks)
+    return sp["slash"] + sp["vertical"]
+
+
+def dense_causal_area(cu_seqlens: Sequence[int], row_positions: Optional[np.ndarray] = None) -> int:
+    """Causal entries per head: sum over rows of (position - segment start + 1)."""
+    if row_positions is None:
+        return int(sum((e - a) * (e - a + 1) // 2 for a, e in zip(cu_seqlens[:-1], cu_seqlens[1:])))
+    rp = np.asarray(row_positions, dtype=np.int64)
+    seg = np.searchsorted(np.asarray(cu_seqlens), rp, side="right") - 1
+    return int((rp - np.asarray(cu_seqlens, dtype=np.int64)[seg] + 1).sum())

@@ -8,11 +8,14 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/vs.h"
 #include "vs_attn_common.h"
+#include "vs_trace.h"
 
 namespace vs {
 hipError_t launch_fwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st);
@@ -209,6 +212,53 @@ vs_status hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+
+// ---------------------------------------------------------------------------
+// Per-kernel timing (vs_trace_enable / vs_trace_collect).
+namespace {
+struct TraceRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_tmu;
+bool g_trace = false;
+std::vector<TraceRec> g_pending;
+std::vector<hipEvent_t> g_pool;
+thread_local hipEvent_t t_start = nullptr;
+thread_local const char* t_name = nullptr;
+
+hipEvent_t pool_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+namespace vs {
+void trace_begin(hipStream_t st, const char* name) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  t_start = nullptr;
+  if (!g_trace) return;
+  t_start = pool_event();
+  t_name = name;
+  if (t_start) (void)hipEventRecord(t_start, st);
+}
+void trace_end(hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_trace || !t_start) return;
+  hipEvent_t stop = pool_event();
+  if (!stop) return;
+  (void)hipEventRecord(stop, st);
+  g_pending.push_back({t_name, t_start, stop});
+  t_start = nullptr;
+}
+}  // namespace vs
+
 extern "C" {
 
 const char* vs_last_error(void) { return g_err.c_str(); }
@@ -397,6 +447,48 @@ vs_status lse_merge(int32_t batch, int32_t n, int32_t heads, int32_t head_dim, f
   return hip_status(vs::launch_lse_merge(batch, n, heads, head_dim, o_acc, lse_acc, o_part,
                                          lse_part, (hipStream_t)stream),
                     "lse_merge");
+}
+
+vs_status vs_trace_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_trace = on != 0;
+  return ok();
+}
+
+vs_status vs_trace_collect(char* buf, size_t len) {
+  if (!buf || len == 0) return fail(VS_ERR_NULL, "trace buffer is NULL");
+  std::vector<TraceRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    recs.swap(g_pending);
+  }
+  std::map<std::string, std::pair<long, double>> agg;
+  hipError_t err = hipSuccess;
+  for (const TraceRec& r : recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) err = e;
+    auto& a = agg[r.name];
+    a.first += 1;
+    a.second += ms;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    for (const TraceRec& r : recs) {
+      g_pool.push_back(r.start);
+      g_pool.push_back(r.stop);
+    }
+  }
+  std::string out;
+  for (const auto& kv : agg) {
+    char line[256];
+    snprintf(line, sizeof line, "%s %ld %.6f\n", kv.first.c_str(), kv.second.first, kv.second.second);
+    out += line;
+  }
+  std::snprintf(buf, len, "%s", out.c_str());
+  if (err != hipSuccess) return fail(VS_ERR_HIP, "trace events: %s", hipGetErrorString(err));
+  return ok();
 }
 
 }  // extern "C"

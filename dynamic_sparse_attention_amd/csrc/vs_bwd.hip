@@ -21,6 +21,7 @@
 //     slash kernel has stored its blocks (stream order).
 #include "vs_qmajor.h"
 #include "vs_stage.h"
+#include "vs_trace.h"
 
 namespace vs {
 
@@ -514,9 +515,9 @@ hipError_t launch_bwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st
   const dim3 gc((unsigned)(p.batch * p.h_q * p.seg.n_seg * p.col_tiles * p.qranges));
 #define VS_BWD(T, DD)                                                                           \
   do {                                                                                          \
-    if (gs.x) hipLaunchKernelGGL((vs_bwd_dkdv_slash_kernel<T, DD>), gs, dim3(kKThreads), 0, st, p); \
-    if (gc.x) hipLaunchKernelGGL((vs_bwd_dkdv_cols_kernel<T, DD>), gc, dim3(kKThreads), 0, st, p);  \
-    if (gq.x) hipLaunchKernelGGL((vs_bwd_dq_kernel<T, DD>), gq, dim3(kQThreads), 0, st, p);         \
+    if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_dkdv_slash_kernel<T, DD>), gs, dim3(kKThreads), 0, st, p)); \
+    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_dkdv_cols_kernel<T, DD>), gc, dim3(kKThreads), 0, st, p));   \
+    if (gq.x) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_kernel<T, DD>), gq, dim3(kQThreads), 0, st, p));                 \
   } while (0)
   if (dtype_bf16 && d == 128) VS_BWD(__bf16, 128);
   else if (dtype_bf16 && d == 64) VS_BWD(__bf16, 64);

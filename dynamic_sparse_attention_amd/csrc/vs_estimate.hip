@@ -22,6 +22,7 @@
 //           ascending, taking the lowest indices among scores equal to the
 //           threshold.
 #include "vs_attn_common.h"
+#include "vs_trace.h"
 
 namespace vs {
 
@@ -294,11 +295,11 @@ hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int
   const dim3 g1((unsigned)(p.batch * p.h_kv * tiles_total));
 #define VS_EST(T, DD)                                                                                   \
   do {                                                                                                  \
-    hipLaunchKernelGGL((vs_est_pass1_kernel<T, DD>), g1, dim3(256), 0, st, p, tp, tiles_total, partials); \
-    hipLaunchKernelGGL(vs_est_combine_kernel, dim3(n_lists), dim3(64), 0, st, p, tp, tiles_total,        \
-                       (const float2*)partials, lse2);                                                 \
-    hipLaunchKernelGGL((vs_est_pass2_kernel<T, DD>), g1, dim3(256), 0, st, p, tp, tiles_total,          \
-                       (const float*)lse2, v_score, s_score);                                           \
+    VS_TRACED(st, "vs_est_pass1", hipLaunchKernelGGL((vs_est_pass1_kernel<T, DD>), g1, dim3(256), 0, st, p, tp, tiles_total, partials)); \
+    VS_TRACED(st, "vs_est_combine", hipLaunchKernelGGL(vs_est_combine_kernel, dim3(n_lists), dim3(64), 0, st, p, tp, tiles_total,        \
+                       (const float2*)partials, lse2));                                                 \
+    VS_TRACED(st, "vs_est_pass2", hipLaunchKernelGGL((vs_est_pass2_kernel<T, DD>), g1, dim3(256), 0, st, p, tp, tiles_total,          \
+                       (const float*)lse2, v_score, s_score));                                           \
   } while (0)
   if (g1.x == 0) return hipSuccess;
   if (dtype_bf16 && d == 128) VS_EST(__bf16, 128);
@@ -306,8 +307,8 @@ hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int
   else if (!dtype_bf16 && d == 128) VS_EST(float, 128);
   else VS_EST(float, 64);
 #undef VS_EST
-  hipLaunchKernelGGL(vs_est_topk_kernel, dim3(2 * n_lists), dim3(kTopkThreads), 0, st, p,
-                     (const float*)v_score, (const float*)s_score, v_ptr, v_idx, s_ptr, s_idx);
+  VS_TRACED(st, "vs_est_topk", hipLaunchKernelGGL(vs_est_topk_kernel, dim3(2 * n_lists), dim3(kTopkThreads), 0, st, p,
+                     (const float*)v_score, (const float*)s_score, v_ptr, v_idx, s_ptr, s_idx));
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@
 // to bf16 for the matrix cores when the inputs are bf16.  The four waves'
 // (max, sum, O) merge through LDS at the end.
 #include "vs_qmajor.h"
+#include "vs_trace.h"
 
 namespace vs {
 
@@ -262,10 +263,10 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
 hipError_t launch_fwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st) {
   const dim3 grid((unsigned)(p.batch * p.h_q * p.nqb));
   if (grid.x == 0) return hipSuccess;
-  if (dtype_bf16 && d == 128) hipLaunchKernelGGL((vs_fwd_kernel<__bf16, 128>), grid, dim3(kQThreads), 0, st, p);
-  else if (dtype_bf16 && d == 64) hipLaunchKernelGGL((vs_fwd_kernel<__bf16, 64>), grid, dim3(kQThreads), 0, st, p);
-  else if (!dtype_bf16 && d == 128) hipLaunchKernelGGL((vs_fwd_kernel<float, 128>), grid, dim3(kQThreads), 0, st, p);
-  else hipLaunchKernelGGL((vs_fwd_kernel<float, 64>), grid, dim3(kQThreads), 0, st, p);
+  if (dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<__bf16, 128>), grid, dim3(kQThreads), 0, st, p));
+  else if (dtype_bf16 && d == 64) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<__bf16, 64>), grid, dim3(kQThreads), 0, st, p));
+  else if (!dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<float, 128>), grid, dim3(kQThreads), 0, st, p));
+  else VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<float, 64>), grid, dim3(kQThreads), 0, st, p));
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // vs_misc.hip — memory-bound helper kernels: vertical-list preparation,
 // the backward row term delta, and the LSE merge of chunk partials.
 #include "vs_attn_common.h"
+#include "vs_trace.h"
 
 namespace vs {
 
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void vs_prep_vertical_kernel(AttnParams p, con
 hipError_t launch_prep_vertical(const AttnParams& p, int n_lists, const int* v_ptr, const int* v_idx,
                                 hipStream_t st) {
   if (n_lists == 0) return hipSuccess;
-  hipLaunchKernelGGL(vs_prep_vertical_kernel, dim3(n_lists), dim3(256), 0, st, p, v_ptr, v_idx);
+  VS_TRACED(st, "vs_prep_vertical", hipLaunchKernelGGL(vs_prep_vertical_kernel, dim3(n_lists), dim3(256), 0, st, p, v_ptr, v_idx));
   return hipGetLastError();
 }
 
@@ -82,8 +83,8 @@ hipError_t launch_delta(const void* o, int o_f32, int bf16, const void* dout, fl
   const size_t threads = rows * (d / 4);
   const dim3 grid((unsigned)((threads + 255) / 256));
 #define VS_DELTA(TO, TD, DD)                                                                        \
-  hipLaunchKernelGGL((vs_delta_kernel<TO, TD, DD>), grid, dim3(256), 0, st, (const TO*)o,          \
-                     (const TD*)dout, delta, batch, n, h, rows)
+  VS_TRACED(st, "vs_delta", hipLaunchKernelGGL((vs_delta_kernel<TO, TD, DD>), grid, dim3(256), 0, st, (const TO*)o, \
+                     (const TD*)dout, delta, batch, n, h, rows))
   if (d == 128) {
     if (o_f32 && bf16) VS_DELTA(float, __bf16, 128);
     else if (o_f32) VS_DELTA(float, float, 128);
@@ -146,8 +147,8 @@ hipError_t launch_lse_merge(int batch, int n, int heads, int d, float* o_acc, fl
   if (rows == 0) return hipSuccess;
   const int tpr = d / 4;
   const size_t threads = rows * tpr;
-  hipLaunchKernelGGL(vs_lse_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                     tpr, n, heads, rows, o_acc, lse_acc, o_part, lse_part);
+  VS_TRACED(st, "vs_lse_merge", hipLaunchKernelGGL(vs_lse_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     tpr, n, heads, rows, o_acc, lse_acc, o_part, lse_part));
   return hipGetLastError();
 }
 

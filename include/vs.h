@@ -210,6 +210,16 @@ vs_status lse_merge(int32_t batch, int32_t n, int32_t heads, int32_t head_dim,
                     float* o_acc, float* lse_acc, const float* o_part,
                     const float* lse_part, vs_stream_t stream);
 
+/* Per-kernel timing, a profiling aid.  While enabled, every kernel the library
+ * launches is bracketed by two HIP events on its stream (the launch itself is
+ * unchanged).  vs_trace_collect waits for the recorded events and writes one
+ * line per kernel name, "name launches total_ms\n", into buf (HOST,
+ * NUL-terminated, truncated to len bytes), then forgets them.  Events are
+ * created on first use and reused; tracing adds no device allocation.
+ * Errors: VS_ERR_NULL (buf), VS_ERR_HIP (an event failed). */
+vs_status vs_trace_enable(int32_t on);
+vs_status vs_trace_collect(char* buf, size_t len);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char* vs_last_error(void);
 

@@ -256,10 +256,12 @@ def bwd_rounding_bounds(q, k, v, do, o, lse, rows_pos, cols_pos, cu_seqlens, ind
                         scale=None, u_op=2.0 ** -8, u_o=2.0 ** -8, support=None):
     """First-order error bounds of a backward whose matrix-core operands P and dS
     are rounded to a format of unit roundoff u_op, with delta formed from an
-    output O stored with unit roundoff u_o (bf16: 2^-8 each; MTraining §5.1
-    trains in bfloat16).  Inputs are taken as exact.
+    output O that was itself computed with P rounded to u_op (O = P V) and
+    stored with unit roundoff u_o (bf16: 2^-8 each; MTraining §5.1 trains in
+    bfloat16).  Inputs are taken as exact.
 
-    With D~ = D + e_D, |e_D| <= u_o * sum_c |dO O| and dS~ = P (dP - D~) rounded:
+    With |e_O| <= u_o |O| + u_op P |V| and D~ = D + e_D,
+    |e_D| <= sum_c |dO| e_O, and dS~ = P (dP - D~) rounded:
       |dQ~ - dQ| <= scale * (u_op |dS| |K| + |e_D| P |K|)
       |dK~ - dK| <= scale * (u_op |dS|^T |Q| + (P |e_D|)^T |Q|)
       |dV~ - dV| <= u_op P^T |dO|
@@ -276,18 +278,18 @@ def bwd_rounding_bounds(q, k, v, do, o, lse, rows_pos, cols_pos, cu_seqlens, ind
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     use_support = (nr > 4096) if support is None else support
     D = bwd_delta(o, do)
-    eD = u_o * np.abs(do * o).sum(-1).T
     bq = np.zeros_like(q)
     bk = np.zeros_like(k)
     bv = np.zeros_like(v)
-    aq, ak, ado = np.abs(q), np.abs(k), np.abs(do)
+    aq, ak, av, ado, ao = np.abs(q), np.abs(k), np.abs(v), np.abs(do), np.abs(o)
 
     def accumulate(h, g, ri, ci, M):
         S = np.where(M, scale * (q[ri, h] @ k[ci, g].T), -np.inf)
         A = _probs(S, lse[h, ri])
         dA = do[ri, h] @ v[ci, g].T
         adS = np.abs(A * (dA - D[h, ri][:, None]))
-        e = eD[h, ri]
+        eO = u_o * ao[ri, h] + u_op * (A @ av[ci, g])
+        e = (ado[ri, h] * eO).sum(-1)
         bq[ri, h] = scale * (u_op * adS @ ak[ci, g] + e[:, None] * (A @ ak[ci, g]))
         bk[ci, g] += scale * (u_op * adS.T @ aq[ri, h] + (A * e[:, None]).T @ aq[ri, h])
         bv[ci, g] += u_op * A.T @ ado[ri, h]

@@ -166,3 +166,29 @@ def test_entry_points_reject_before_launch(abi):
     assert L.lse_merge(1, 16, 2, 96, FAKE, FAKE, FAKE, FAKE, None) == abi.VS_ERR_UNSUPPORTED
     assert L.lse_merge(1, 16, 2, 128, None, FAKE, FAKE, FAKE, None) == abi.VS_ERR_NULL
     assert L.lse_merge(-1, 16, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == abi.VS_ERR_SHAPE
+
+
+def test_executed_area_matches_oracle():
+    """Host work accounting of the package equals the oracle's mask-area count."""
+    import numpy as np
+    from dynamic_sparse_attention_amd import accounting
+    from test_oracle_pins import rand_index
+    rng = np.random.default_rng(21)
+    for cu in ([0, 1024], [0, 256, 640, 1024], [0, 4096]):
+        n = cu[-1]
+        idx = rand_index(rng, n, 3, 64, cu=cu)
+        lists = [idx[(h, s)] for h in range(3) for s in range(len(cu) - 1)]
+        got = accounting.executed_area(lists, cu, 3)
+        assert got.tolist() == oracle.mask_area_formula(cu, idx, 3)
+        pos = np.arange(n)
+        assert accounting.dense_causal_area(cu) == oracle.dense_causal_area(pos, cu)
+    # a block-striped worker's rows
+    n, W, w = 2048, 4, 1
+    idx = rand_index(rng, n, 2, 64, kv=50, kg=5)
+    rows_b = np.arange(w, n // 64, W)
+    rows = (rows_b[:, None] * 64 + np.arange(64)).reshape(-1)
+    lists = [idx[(h, 0)] for h in range(2)]
+    got = accounting.executed_area(lists, [0, n], 2, row_blocks=rows_b)
+    ref = [int(oracle.dense_mask(rows, np.arange(n), [0, n], idx, h).sum()) for h in range(2)]
+    assert got.tolist() == ref
+    assert accounting.dense_causal_area([0, n], rows) == oracle.dense_causal_area(rows, [0, n])

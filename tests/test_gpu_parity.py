@@ -148,7 +148,7 @@ def test_striped_ring_share():
     dv_all = np.zeros_like(dvg)
     for u, gk, gv in chunks:
         _, dk, dv = vs.sparse_attn_bwd(gq, gk, gv, None, gdo, acc_l, idx, delta=delta, dq=dq,
-                                       stripe=(W, w, u))
+                                       stripe=(W, w, u), accumulate=True)
         cols = workloads.stripe_positions(prob.n, W, u).numpy()
         torch.cuda.synchronize()
         dk_all[cols] += np64(dk[0])

@@ -496,7 +496,13 @@ def test_bwd_rounding_bound_holds_for_simulated_bf16():
     dq, dk, dv = oracle.attn_bwd_dense(q, k, v, do, L, D, pos, pos, [0, n], idx, B)
     bq, bk, bv = oracle.bwd_rounding_bounds(q, k, v, do, O, L, pos, pos, [0, n], idx, B)
     scale = 1 / math.sqrt(d)
-    Ob = bf(O)
+    # forward as the GPU does it: P rounded before P V, O stored in bf16
+    Ob = np.zeros_like(O)
+    for h in range(hq):
+        M = oracle.dense_mask(pos, pos, [0, n], idx, h, B)
+        S = np.where(M, scale * q[:, h] @ k[:, 0].T, -np.inf)
+        A = np.where(M, np.exp(S - np.where(np.isfinite(L[h]), L[h], 0)[:, None]), 0)
+        Ob[:, h] = bf(bf(A) @ v[:, 0])
     Dt = (Ob * do).sum(-1).T
     sq, sk, sv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for h in range(hq):
