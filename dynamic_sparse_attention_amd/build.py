@@ -13,7 +13,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvs.so")
-SOURCES = ["vs_api.cpp", "vs_fwd.hip", "vs_bwd.hip", "vs_estimate.hip", "vs_misc.hip"]
+SOURCES = ["vs_api.cpp", "vs_fwd.hip", "vs_bwd.hip", "vs_bwd_kv.hip", "vs_bwd_dq.hip", "vs_estimate.hip", "vs_misc.hip"]
 
 
 def hipcc() -> str:
@@ -30,6 +30,15 @@ def flags(arch: str = "gfx950"):
             "-Wno-unused-result", "-munsafe-fp-atomics"]
 
 
+# Per-source extra flags.  The forward keeps its matrix-core accumulators in
+# the VGPR file: the online softmax rescales them with vector ALU
+# instructions, and AGPR residency made the compiler copy the whole output
+# tile back and forth on every iteration.
+EXTRA = {"vs_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "vs_bwd_kv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "vs_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every source for gfx950 and link libvs.so next to this file."""
     cc = hipcc()
@@ -39,7 +48,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            cmd = [cc, *flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *flags(), *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -84,33 +84,20 @@ __device__ __forceinline__ int local_key_block(const AttnParams& p, int kb_glob)
   return j < p.nkb ? j : -1;
 }
 
+// Local query block of global block qb_glob, or -1 if this call does not hold it.
+__device__ __forceinline__ int local_query_block(const AttnParams& p, int qb_glob) {
+  if (p.W == 1) return (qb_glob >= 0 && qb_glob < p.nqb) ? qb_glob : -1;
+  const int d = qb_glob - p.q_rank;
+  if (d < 0 || d % p.W != 0) return -1;
+  const int i = d / p.W;
+  return i < p.nqb ? i : -1;
+}
+
 // Local key position of a global position held by this call.
 __device__ __forceinline__ int local_key_pos(const AttnParams& p, int m_glob) {
   if (p.W == 1) return m_glob;
   const int kb = m_glob / kBlock;
   return ((kb - p.k_rank) / p.W) * kBlock + (m_glob % kBlock);
 }
-
-// Tile of 64 keys of one contiguous local key block; causal inside when diag.
-struct SlashTile {
-  int j;
-  bool diag;
-  __device__ __forceinline__ int key_pos(int e) const { return j * kBlock + e; }
-  __device__ __forceinline__ bool valid(int e, int r) const { return !diag || e <= r; }
-};
-
-// Tile of up to 64 gathered vertical columns (local positions in cols[],
-// per-column row threshold in coff[]: -1 = every row, else rows r >= coff).
-struct ColTile {
-  const int* cols;
-  const int* coff;
-  int ncols;
-  __device__ __forceinline__ int key_pos(int e) const { return cols[e < ncols ? e : 0]; }
-  __device__ __forceinline__ bool valid(int e, int r) const {
-    if (e >= ncols) return false;
-    const int c = coff[e];
-    return c < 0 || c <= r;
-  }
-};
 
 }  // namespace vs

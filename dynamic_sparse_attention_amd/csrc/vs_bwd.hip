@@ -49,12 +49,12 @@ struct DqWorker {
   T* kt;           // this wave's K^T staging area [D][KTP]
   float sl2;
 
-  template <class Tile>
-  __device__ __forceinline__ void half(const Tile& t, int kk) {
+  template <class Set>
+  __device__ __forceinline__ void half(const Set& S, int n) {
     const int lane = threadIdx.x & 63;
     const int hl = lane >> 5;
     const int l32 = lane & 31;
-    const int kpos = t.key_pos(32 * kk + slot_perm<KPL>(l32));
+    const int kpos = S.key_pos(n, slot_perm<KPL>(l32));
     const T* krow = kb + (size_t)kpos * kvs;
     const T* vrow = vb + (size_t)kpos * kvs;
     frag kf[NCD], vf[NCD];
@@ -63,7 +63,7 @@ struct DqWorker {
       kf[c] = load_frag<T>(krow + c * KC + hl * KPL);
       vf[c] = load_frag<T>(vrow + c * KC + hl * KPL);
     }
-    stage_transposed<T, D, 32, KTP, 64>(kt, kb, [&](int r) { return (size_t)t.key_pos(32 * kk + r) * kvs; },
+    stage_transposed<T, D, 32, KTP, 64>(kt, kb, [&](int r) { return (size_t)S.key_pos(n, r) * kvs; },
                                         lane);
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -76,6 +76,7 @@ struct DqWorker {
         dp[rg] = MF::mma(vf[c], dof[rg][c], dp[rg]);
       }
     }
+    const bool full = S.full(n);
     frag dsf[2][NCK];
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
@@ -83,8 +84,8 @@ struct DqWorker {
       float ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int e = 32 * kk + reg_row<KPL>(i, hl);
-        const float pr = t.valid(e, r) ? fast_exp2(s[rg][i] * sl2 - lse2[rg]) : 0.f;
+        const bool ok = full || S.valid(n, reg_row<KPL>(i, hl), r);
+        const float pr = ok ? fast_exp2(__builtin_fmaf(s[rg][i], sl2, -lse2[rg])) : 0.f;
         ds[i] = pr * (dp[rg][i] - dl[rg]);
       }
 #pragma unroll
@@ -103,10 +104,10 @@ struct DqWorker {
     wave_sync();
   }
 
-  template <class Tile>
-  __device__ __forceinline__ void tile(const Tile& t) {
-    half(t, 0);
-    half(t, 1);
+  template <class Set>
+  __device__ __forceinline__ void run(const Set& S) {
+    const int N = S.n_halves();
+    for (int n = 0; n < N; ++n) half(S, n);
   }
 };
 
@@ -349,15 +350,6 @@ __device__ __forceinline__ void kv_store(const KvWorker<T, D>& wk, const AttnPar
     }
 }
 
-// Local query block of global block qb_glob, or -1 if this call does not hold it.
-__device__ __forceinline__ int local_query_block(const AttnParams& p, int qb_glob) {
-  if (p.W == 1) return (qb_glob >= 0 && qb_glob < p.nqb) ? qb_glob : -1;
-  const int d = qb_glob - p.q_rank;
-  if (d < 0 || d % p.W != 0) return -1;
-  const int i = d / p.W;
-  return i < p.nqb ? i : -1;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(kKThreads) void vs_bwd_dkdv_slash_kernel(AttnParams p) {
   typedef KvWorker<T, D> W;
@@ -509,7 +501,17 @@ __global__ __launch_bounds__(kKThreads) void vs_bwd_dkdv_cols_kernel(AttnParams 
   if (col_ok) kv_store<T, D>(wk, p, b, kvh, kpos, true);
 }
 
+hipError_t launch_bwd_kv_bf16(const AttnParams& p, int d, hipStream_t st);
+hipError_t launch_bwd_dq_bf16(const AttnParams& p, int d, hipStream_t st);
+
+// bf16 inputs take the direct-load kernels (vs_bwd_kv.hip, vs_bwd_dq.hip);
+// fp32 inputs the kernels of this file.
 hipError_t launch_bwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st) {
+  if (dtype_bf16) {
+    hipError_t e = launch_bwd_kv_bf16(p, d, st);
+    if (e != hipSuccess) return e;
+    return launch_bwd_dq_bf16(p, d, st);
+  }
   const dim3 gq((unsigned)(p.batch * p.h_q * p.nqb));
   const dim3 gs((unsigned)(p.batch * p.h_kv * p.nkb));
   const dim3 gc((unsigned)(p.batch * p.h_q * p.seg.n_seg * p.col_tiles * p.qranges));
@@ -519,9 +521,7 @@ hipError_t launch_bwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st
     if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_dkdv_cols_kernel<T, DD>), gc, dim3(kKThreads), 0, st, p));   \
     if (gq.x) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_kernel<T, DD>), gq, dim3(kQThreads), 0, st, p));                 \
   } while (0)
-  if (dtype_bf16 && d == 128) VS_BWD(__bf16, 128);
-  else if (dtype_bf16 && d == 64) VS_BWD(__bf16, 64);
-  else if (!dtype_bf16 && d == 128) VS_BWD(float, 128);
+  if (d == 128) VS_BWD(float, 128);
   else VS_BWD(float, 64);
 #undef VS_BWD
   return hipGetLastError();

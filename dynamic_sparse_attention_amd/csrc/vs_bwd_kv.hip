@@ -1,0 +1,414 @@
+// vs_bwd_kv.hip — dK / dV of the sparse backward, key-major, bf16 inputs.
+//
+// MTraining §3.2 Eq. 1-2 and the paper note's Appendix B.1: for the keys of a
+// unit, dV += P^T dO and dK += scale * dS^T Q over every query row that reads
+// them, with P = exp(S - LSE) recomputed from the final LSE and
+// dS = P * (dP - delta), dP = dO V^T.
+//
+// A workgroup is two waves; wave kh owns 32 keys (held as the B operands K^T,
+// V^T) and accumulates dK^T, dV^T for them.  The query tiles the unit reads
+// (64 rows of Q and dO of one Q head, plus their LSE and delta) stream
+// through two LDS buffers: while the waves compute on one tile the next one
+// arrives by direct global -> LDS loads (no registers, no packing).  Q and dO
+// are stored row-major with the 16-byte chunks of row r at chunk index
+// c ^ 2*(r % 4); the S = Q K^T and dP = dO V^T operands are plain 16-byte
+// reads, the dK^T = Q^T dS and dV^T = dO^T P operands transposed reads
+// (ds_read_b64_tr_b16) that hit distinct banks thanks to the swizzle.
+//
+//   * slash units: (batch, KV head, key block j); the tiles are every
+//     (Q head of the group, selected block-diagonal g) with query block j + g;
+//     dK, dV of the block are complete at the end and are stored.
+//   * column units: (list, 64 gathered vertical columns, range of query
+//     blocks); added to dK, dV with fp32 atomics after the slash kernel.
+#include "vs_attn_common.h"
+#include "vs_trace.h"
+
+namespace vs {
+
+constexpr int kKvThreads = 128;
+constexpr int kKvTiles = 512;  // tile list capacity per pass
+
+template <int D>
+struct RowTile {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;       // rows per 1 KiB direct-load instruction
+  static constexpr int BYTES = 64 * D * 2;   // 64 rows
+  static constexpr int NDMA = 64 / RPI;      // direct-load instructions per 64 rows
+  __device__ static __forceinline__ int off(int row, int chunk) {
+    return (row / RPI) * 1024 + (row % RPI) * (CPR * 16) + 16 * (chunk ^ (2 * (row & 3)));
+  }
+};
+
+template <int D>
+struct KvBuf {
+  char q[RowTile<D>::BYTES];
+  char dout[RowTile<D>::BYTES];
+  float lse[64];
+  float del[64];
+};
+
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef __attribute__((address_space(1))) void* glb_vptr;
+
+// Direct loads of query tile (local block i, Q head h) into B; each of the two
+// waves issues half of the rows (NDMA instructions) plus one of LSE / delta.
+template <int D>
+__device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, int b, int h, int i) {
+  typedef RowTile<D> RT;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const unsigned rstride = (unsigned)(p.h_q * D);
+  const size_t base = (((size_t)b * p.n_q + (size_t)i * kBlock) * p.h_q + h) * D;
+  const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + base;
+  const __bf16* db = reinterpret_cast<const __bf16*>(p.dout) + base;
+  const int rsub = lane / RT::CPR;
+  const int chunk = (lane % RT::CPR) ^ (2 * (rsub & 3));
+#pragma unroll
+  for (int u0 = 0; u0 < RT::NDMA / 2; ++u0) {
+    const int u = w * (RT::NDMA / 2) + u0;
+    const unsigned eoff = (unsigned)(u * RT::RPI + rsub) * rstride + chunk * 8;
+    __builtin_amdgcn_global_load_lds((glb_vptr)(qb + eoff), (lds_vptr)(B.q + u * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_vptr)(db + eoff), (lds_vptr)(B.dout + u * 1024), 16, 0, 0);
+  }
+  const size_t li = ((size_t)b * p.h_q + h) * p.n_q + (size_t)i * kBlock + lane;
+  if (w == 0)
+    __builtin_amdgcn_global_load_lds((glb_vptr)(p.lse + li), (lds_vptr)B.lse, 4, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((glb_vptr)(p.delta + li), (lds_vptr)B.del, 4, 0, 0);
+}
+
+template <int D>
+struct KvWorkerB {
+  typedef Mfma<__bf16> MF;
+  typedef MF::frag frag;
+  typedef RowTile<D> RT;
+  static constexpr int KPL = 8, KC = 16;
+  static constexpr int NCD = D / KC;   // k chunks over head_dim
+  static constexpr int NCT = D / 32;   // 32-channel tiles of dK^T / dV^T
+  static constexpr int DMA_PER_TILE = RT::NDMA + 1;  // per wave
+
+  frag kB[NCD];     // B operand K^T of this lane's key column
+  frag vB[NCD];     // B operand V^T
+  f32x16 dk[NCT];   // dK^T [channel][key]
+  f32x16 dv[NCT];   // dV^T [channel][key]
+
+  __device__ __forceinline__ void load_keys(const AttnParams& p, int b, int kvh, int kpos) {
+    const int hl = (threadIdx.x & 63) >> 5;
+    const size_t off = (((size_t)b * p.n_k + kpos) * p.h_kv + kvh) * D + hl * KPL;
+    const __bf16* kr = reinterpret_cast<const __bf16*>(p.k) + off;
+    const __bf16* vr = reinterpret_cast<const __bf16*>(p.v) + off;
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) {
+      kB[c] = load_frag<__bf16>(kr + c * KC);
+      vB[c] = load_frag<__bf16>(vr + c * KC);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      dk[ct] = f32x16{0};
+      dv[ct] = f32x16{0};
+    }
+  }
+
+  // A operand from a row-major tile: rows 32*rg + slot_perm(L%32), chunk c.
+  __device__ __forceinline__ static frag row_frag(const char* t, int rg, int c) {
+    const int lane = threadIdx.x & 63;
+    const int row = 32 * rg + slot_perm<KPL>(lane & 31);
+    return *reinterpret_cast<const frag*>(t + RT::off(row, 2 * c + (lane >> 5)));
+  }
+
+  // A operand of a transposed tile: channels 32*ct + L%32, rows of k chunk c
+  // (16 rows).  ds_read_b64_tr_b16: in each 16-lane group, lane i receives
+  // element i%4 of the 8 bytes read by lanes i/4, 4+i/4, 8+i/4, 12+i/4.
+  __device__ __forceinline__ static frag tr_frag(const char* t, int ct, int c) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int sg = lane & 15;
+    const int hl = lane >> 5;
+    const int cb = 32 * ct + 16 * (g & 1) + 4 * (sg & 3);
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    v4s part[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = c * 16 + 8 * hl + 4 * q + (sg >> 2);
+      part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(t + RT::off(row, cb >> 3) + 2 * (cb & 7)));
+    }
+    const v8s both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(frag, both);
+  }
+
+  // One query tile.  valid(r): this lane's key column is visible to row r.
+  template <class ValidF>
+  __device__ __forceinline__ void tile(const KvBuf<D>& B, float sl2, ValidF valid) {
+    const int lane = threadIdx.x & 63;
+    const int hl = lane >> 5;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      s[rg] = f32x16{0};
+      dp[rg] = f32x16{0};
+#pragma unroll
+      for (int c = 0; c < NCD; ++c) {
+        s[rg] = MF::mma(row_frag(B.q, rg, c), kB[c], s[rg]);
+        dp[rg] = MF::mma(row_frag(B.dout, rg, c), vB[c], dp[rg]);
+      }
+    }
+    frag pf[2][2], dsf[2][2];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        // register i = 8c + e holds row 32rg + 16c + 8hl + e
+        const int r0 = 32 * rg + 16 * c + 8 * hl;
+        const f32x4 la = *reinterpret_cast<const f32x4*>(B.lse + r0);
+        const f32x4 lb = *reinterpret_cast<const f32x4*>(B.lse + r0 + 4);
+        const f32x4 da = *reinterpret_cast<const f32x4*>(B.del + r0);
+        const f32x4 db = *reinterpret_cast<const f32x4*>(B.del + r0 + 4);
+        float pr[8], ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lse = e < 4 ? la[e] : lb[e - 4];
+          const float dl = e < 4 ? da[e] : db[e - 4];
+          const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+          const float x = valid(r0 + e) ? fast_exp2(__builtin_fmaf(s[rg][8 * c + e], sl2, -l2)) : 0.f;
+          pr[e] = x;
+          ds[e] = x * (dp[rg][8 * c + e] - dl);
+        }
+        pf[rg][c] = MF::pack(pr);
+        dsf[rg][c] = MF::pack(ds);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        dv[ct] = MF::mma(tr_frag(B.dout, ct, c), pf[c >> 1][c & 1], dv[ct]);
+        dk[ct] = MF::mma(tr_frag(B.q, ct, c), dsf[c >> 1][c & 1], dk[ct]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(const AttnParams& p, int b, int kvh, int kpos, bool atomic) const {
+    const int hl = (threadIdx.x & 63) >> 5;
+    const size_t off = (((size_t)b * p.n_k + kpos) * p.h_kv + kvh) * D;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int ch = 32 * ct + 8 * i4 + 4 * hl;
+        f32x4 a, v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a[u] = dk[ct][4 * i4 + u] * p.scale;
+          v[u] = dv[ct][4 * i4 + u];
+        }
+        if (atomic) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            atomicAdd(p.dk + off + ch + u, a[u]);
+            atomicAdd(p.dv + off + ch + u, v[u]);
+          }
+        } else {
+          *reinterpret_cast<f32x4*>(p.dk + off + ch) = a;
+          *reinterpret_cast<f32x4*>(p.dv + off + ch) = v;
+        }
+      }
+  }
+};
+
+template <int D>
+struct KvLdsB {
+  KvBuf<D> buf[2];
+  int tiles[kKvTiles];
+  int wsum[2];
+};
+
+// Double-buffered walk over ntiles query tiles: tile_of(t) -> (h, i, flags),
+// body(B, t, flags) computes on the staged tile t.
+template <int D, class TileF, class BodyF>
+__device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D>& L, int b, int ntiles,
+                                            TileF tile_of, BodyF body) {
+  if (ntiles == 0) return;
+  int h, i, fl;
+  tile_of(0, &h, &i, &fl);
+  kv_tile_dma<D>(p, L.buf[0], b, h, i);
+  for (int t = 0; t < ntiles; ++t) {
+    // this wave's loads of tile t are done; the barrier makes every wave's
+    // loads visible and frees the other buffer (its tile t-1 compute is over)
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+    __syncthreads();
+    int h1, i1, fl1;
+    if (t + 1 < ntiles) {
+      tile_of(t + 1, &h1, &i1, &fl1);
+      kv_tile_dma<D>(p, L.buf[(t + 1) & 1], b, h1, i1);
+    }
+    tile_of(t, &h, &i, &fl);
+    body(L.buf[t & 1], t, fl);
+  }
+  __syncthreads();
+}
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_slash_bf16_kernel(AttnParams p) {
+  typedef KvWorkerB<D> W;
+  __shared__ KvLdsB<D> L;
+  const int tid = threadIdx.x;
+  const int kh = tid >> 6;
+  const int l32 = tid & 31;
+  const int BH = p.batch * p.h_kv;
+  const int bh = blockIdx.x % BH;
+  const int j = blockIdx.x / BH;
+  const int b = bh / p.h_kv;
+  const int kvh = bh % p.h_kv;
+  const int G = p.h_q / p.h_kv;
+  int kb_glob, seg, a_blk, nb_seg;
+  if (p.W == 1) {
+    kb_glob = j;
+    seg = seg_of_block(p.seg, j);
+    a_blk = p.seg.start_blk[seg];
+    nb_seg = p.seg.start_blk[seg + 1] - a_blk;
+  } else {
+    kb_glob = p.k_rank + p.W * j;
+    seg = 0;
+    a_blk = 0;
+    nb_seg = p.n_global / kBlock;
+  }
+  const int beta_k = kb_glob - a_blk;
+  const int kpos = j * kBlock + 32 * kh + l32;
+  const int kin = 32 * kh + l32;
+
+  W wk;
+  wk.load_keys(p, b, kvh, kpos);
+  int count = 0;
+  auto tile_of = [&](int t, int* h, int* i, int* fl) {
+    const int v = L.tiles[t];
+    *h = kvh * G + (v >> 26);
+    *i = (v >> 1) & ((1 << 25) - 1);
+    *fl = v & 1;
+  };
+  auto body = [&](const KvBuf<D>& B, int, int diag) {
+    wk.tile(B, p.sl2, [&](int r) { return !diag || kin <= r; });
+  };
+  for (int hh = 0; hh < G; ++hh) {
+    const int list = (b * p.h_q + kvh * G + hh) * p.seg.n_seg + seg;
+    const int sp0 = p.s_ptr[list];
+    const int ns = p.s_ptr[list + 1] - sp0;
+    for (int base = 0; base < ns; base += kKvThreads) {
+      const int e = base + tid;
+      int i = -1, diag = 0;
+      if (e < ns) {
+        const int g = p.s_idx[sp0 + e];
+        if (g >= 0 && beta_k + g < nb_seg) {
+          i = local_query_block(p, kb_glob + g);
+          diag = g == 0;
+        }
+      }
+      int tot;
+      const int slot = block_compact<kKvThreads>(i >= 0, L.wsum, &tot);
+      if (i >= 0) L.tiles[count + slot] = (hh << 26) | (i << 1) | diag;
+      count += tot;
+      __syncthreads();
+      if (count > kKvTiles - kKvThreads) {
+        kv_pipeline<D>(p, L, b, count, tile_of, body);
+        count = 0;
+      }
+    }
+  }
+  kv_pipeline<D>(p, L, b, count, tile_of, body);
+  wk.store(p, b, kvh, kpos, false);
+}
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_cols_bf16_kernel(AttnParams p) {
+  typedef KvWorkerB<D> W;
+  __shared__ KvLdsB<D> L;
+  __shared__ uint32_t bits[2048];
+  const int tid = threadIdx.x;
+  const int kh = tid >> 6;
+  const int l32 = tid & 31;
+  int u = blockIdx.x;
+  const int qr = u % p.qranges;
+  u /= p.qranges;
+  const int ctile = u % p.col_tiles;
+  const int list = u / p.col_tiles;
+  const int vc = p.vcnt[list];
+  if (64 * ctile >= vc) return;
+  const int seg = list % p.seg.n_seg;
+  const int bh = list / p.seg.n_seg;
+  const int b = bh / p.h_q;
+  const int h = bh % p.h_q;
+  const int kvh = h * p.h_kv / p.h_q;
+  int a_blk, nb_seg, i_lo, i_hi;
+  if (p.W == 1) {
+    a_blk = p.seg.start_blk[seg];
+    nb_seg = p.seg.start_blk[seg + 1] - a_blk;
+    i_lo = a_blk;
+    i_hi = a_blk + nb_seg;
+  } else {
+    a_blk = 0;
+    nb_seg = p.n_global / kBlock;
+    i_lo = 0;
+    i_hi = p.nqb;
+  }
+  const int* vs = p.vsel + (size_t)list * p.vsel_stride + 64 * ctile;
+  const int ncol = min(64, vc - 64 * ctile);
+  const int first_blk = vs[0] / kBlock;  // global block of the first column
+  // first local query block whose global block is >= first_blk
+  int i_first = p.W == 1 ? first_blk : (first_blk <= p.q_rank ? 0 : (first_blk - p.q_rank + p.W - 1) / p.W);
+  const int r_lo = max(max(i_lo, qr * p.qrange_len), i_first);
+  const int r_hi = min(i_hi, (qr + 1) * p.qrange_len);
+  if (r_lo >= r_hi) return;
+
+  const int col = 32 * kh + l32;
+  const bool col_ok = col < ncol;
+  const int m = vs[col_ok ? col : 0];
+  const int bm = m / kBlock - a_blk;
+  const int kpos = local_key_pos(p, m);
+
+  const int sp0 = p.s_ptr[list];
+  const int ns = p.s_ptr[list + 1] - sp0;
+  const int nwords = (nb_seg + 31) >> 5;
+  for (int w = tid; w < nwords; w += kKvThreads) bits[w] = 0u;
+  __syncthreads();
+  for (int e = tid; e < ns; e += kKvThreads) {
+    const int g = p.s_idx[sp0 + e];
+    if (g >= 0 && g < nb_seg) atomicOr(&bits[g >> 5], 1u << (g & 31));
+  }
+  __syncthreads();
+
+  W wk;
+  wk.load_keys(p, b, kvh, kpos);
+  auto qglob = [&](int i) { return p.W == 1 ? i : p.q_rank + p.W * i; };
+  auto tile_of = [&](int t, int* hh, int* i, int* fl) {
+    *hh = h;
+    *i = r_lo + t;
+    *fl = 0;
+  };
+  const int ntiles = r_hi - r_lo;
+  auto body = [&](const KvBuf<D>& B, int t, int) {
+    const int qbg = qglob(r_lo + t);
+    const int beta_q = qbg - a_blk;
+    const int off = beta_q - bm;
+    const bool lane_ok = col_ok && off >= 0 && ((bits[off >> 5] >> (off & 31)) & 1u) == 0u;
+    const int row0 = qbg * kBlock;
+    wk.tile(B, p.sl2, [&](int r) { return lane_ok && m <= row0 + r; });
+  };
+  kv_pipeline<D>(p, L, b, ntiles, tile_of, body);
+  if (col_ok) wk.store(p, b, kvh, kpos, true);
+}
+
+hipError_t launch_bwd_kv_bf16(const AttnParams& p, int d, hipStream_t st) {
+  const dim3 gs((unsigned)(p.batch * p.h_kv * p.nkb));
+  const dim3 gc((unsigned)(p.batch * p.h_q * p.seg.n_seg * p.col_tiles * p.qranges));
+  if (d == 128) {
+    if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128>), gs, dim3(kKvThreads), 0, st, p));
+    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128>), gc, dim3(kKvThreads), 0, st, p));
+  } else {
+    if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64>), gs, dim3(kKvThreads), 0, st, p));
+    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64>), gc, dim3(kKvThreads), 0, st, p));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vs

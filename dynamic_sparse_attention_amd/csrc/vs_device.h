@@ -85,6 +85,11 @@ __device__ __forceinline__ typename Mfma<T>::frag load_frag(const T* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding and leaves the other counters alone (gfx9 layout:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 __device__ __forceinline__ void wave_sync() {

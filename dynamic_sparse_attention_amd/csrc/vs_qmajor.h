@@ -17,6 +17,49 @@ namespace vs {
 constexpr int kQThreads = 256;
 constexpr int kMaxBitWords = 2048;  // block offsets < 65536 (segments up to 4M tokens)
 
+// The half-tiles (32 keys) one wave consumes from the current tile list: tiles
+// wave, wave + 4, ... (round-robin over the 4 waves), two halves each.
+// key_pos(n, r): local key position of key r (0..31) of half-tile n;
+// full(n): no masking needed; valid(n, e, r): key e of the half for row r.
+struct SlashSet {
+  static constexpr bool kContiguous = true;  // the 32 keys of a half are consecutive
+  const int* tiles;  // 2 * local key block + (g == 0)
+  int tot;
+  int wave;
+  __device__ __forceinline__ int n_halves() const { return tot > wave ? 2 * ((tot - wave + 3) >> 2) : 0; }
+  __device__ __forceinline__ int tv(int n) const { return tiles[wave + 4 * (n >> 1)]; }
+  __device__ __forceinline__ int key_pos(int n, int r) const { return (tv(n) >> 1) * kBlock + 32 * (n & 1) + r; }
+  __device__ __forceinline__ bool full(int n) const { return (tv(n) & 1) == 0; }
+  __device__ __forceinline__ bool valid(int n, int e, int r) const { return 32 * (n & 1) + e <= r; }
+};
+
+struct ColSet {
+  static constexpr bool kContiguous = false;
+  const int* cols;   // local key positions of the gathered columns
+  const int* coff;   // -1, or the first row (0..63) that may see the column
+  int count;         // columns in the list
+  int nt;            // 64-column tiles in the list
+  int wave;
+  __device__ __forceinline__ int n_halves() const { return nt > wave ? 2 * ((nt - wave + 3) >> 2) : 0; }
+  __device__ __forceinline__ int base(int n) const { return 64 * (wave + 4 * (n >> 1)) + 32 * (n & 1); }
+  __device__ __forceinline__ int key_pos(int n, int r) const {
+    const int i = base(n) + r;
+    return cols[i < count ? i : 64 * (wave + 4 * (n >> 1))];
+  }
+  // Columns are in ascending position, so those with a per-row limit (inside
+  // the query block) come last: a half is unmasked if its last column has none.
+  __device__ __forceinline__ bool full(int n) const {
+    const int i = base(n) + 31;
+    return i < count && coff[i] < 0;
+  }
+  __device__ __forceinline__ bool valid(int n, int e, int r) const {
+    const int i = base(n) + e;
+    if (i >= count) return false;
+    const int c = coff[i];
+    return c < 0 || c <= r;
+  }
+};
+
 struct QMajorLds {
   uint32_t bits[kMaxBitWords];
   int tiles[kQThreads];
@@ -30,7 +73,6 @@ __device__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list, 
                              Worker& wk) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  constexpr int NW = kQThreads / 64;
   const int sp0 = p.s_ptr[list];
   const int ns = p.s_ptr[list + 1] - sp0;
 
@@ -59,10 +101,7 @@ __device__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list, 
     const int slot = block_compact<kQThreads>(j >= 0, L.wsum, &tot);
     if (j >= 0) L.tiles[slot] = 2 * j + diag;
     __syncthreads();
-    for (int t = wave; t < tot; t += NW) {
-      const int v = L.tiles[t];
-      wk.tile(SlashTile{v >> 1, (v & 1) != 0});
-    }
+    wk.run(SlashSet{L.tiles, tot, wave});
     __syncthreads();
   }
 
@@ -100,10 +139,7 @@ __device__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list, 
     }
     const bool last = e0 >= vlimit;
     const int nt = last ? (count + 63) / 64 : count / 64;
-    for (int t = wave; t < nt; t += NW) {
-      const int nc = count - 64 * t < 64 ? count - 64 * t : 64;
-      wk.tile(ColTile{&L.cols[64 * t], &L.coff[64 * t], nc});
-    }
+    wk.run(ColSet{L.cols, L.coff, last ? count : 64 * nt, nt, wave});
     if (last) break;
     __syncthreads();
     const int rem = count - 64 * nt;
