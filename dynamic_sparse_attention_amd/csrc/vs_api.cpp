@@ -23,6 +23,7 @@ hipError_t launch_prep_vertical(const AttnParams& p, int n_lists, const int* v_p
                                 hipStream_t st);
 hipError_t launch_delta(const void* o, int o_f32, int bf16, const void* dout, float* delta, int batch,
                         int n, int h, int d, hipStream_t st);
+hipError_t launch_lse_log2(const float* lse, float* lse2, size_t count, hipStream_t st);
 hipError_t launch_lse_merge(int batch, int n, int heads, int d, float* o_acc, float* lse_acc,
                             const float* o_part, const float* lse_part, hipStream_t st);
 hipError_t launch_bwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st);
@@ -164,17 +165,22 @@ void fill_params(const Prob& c, vs::AttnParams* a) {
 
 // Workspace layouts.
 struct AttnWs {
-  size_t vsel, vcnt, delta, total;
+  size_t vsel, vcnt, delta, lse2, total;
 };
-AttnWs attn_ws(const Prob& c, int v_cap_max, bool with_delta) {
+// Forward: prepared vertical lists.  Backward: also delta (when the caller
+// gives none) and LSE * log2(e), one fp32 per (batch, Q head, row) each.
+AttnWs attn_ws(const Prob& c, int v_cap_max, bool backward) {
   AttnWs w;
   size_t off = 0;
   w.vsel = off;
   off += align256((size_t)c.n_lists() * std::max(v_cap_max, 1) * 4);
   w.vcnt = off;
   off += align256((size_t)c.n_lists() * 4);
+  const size_t rows = align256((size_t)c.batch * c.h_q * c.n_q * 4);
   w.delta = off;
-  if (with_delta) off += align256((size_t)c.batch * c.h_q * c.n_q * 4);
+  if (backward) off += rows;
+  w.lse2 = off;
+  if (backward) off += rows;
   w.total = off;
   return w;
 }
@@ -421,7 +427,7 @@ vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, 
   a.dv = dv;
   a.dq_accumulate = dq_accumulate != 0;
   a.col_tiles = (idx->v_cap_max + 63) / 64;
-  a.qrange_len = 32;
+  a.qrange_len = 128;
   a.qranges = (c.nqb + a.qrange_len - 1) / a.qrange_len;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
@@ -431,6 +437,9 @@ vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, 
     delta = dws;
   }
   a.delta = delta;
+  float* l2 = reinterpret_cast<float*>(base + w.lse2);
+  if (e == hipSuccess) e = vs::launch_lse_log2(lse, l2, (size_t)c.batch * c.h_q * c.n_q, s);
+  a.lse2 = l2;
   if (e == hipSuccess) e = vs::launch_prep_vertical(a, c.n_lists(), idx->v_ptr, idx->v_idx, s);
   if (e == hipSuccess) e = vs::launch_bwd(a, c.bf16, c.d, s);
   return hip_status(e, "vs_sparse_attn_bwd");

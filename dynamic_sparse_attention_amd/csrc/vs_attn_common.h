@@ -31,6 +31,7 @@ struct AttnParams {
   void* o_out;
   float* lse;         // forward: written; backward: read
   const float* delta; // backward only
+  const float* lse2;  // backward only: LSE * log2(e), +inf for an empty row
   float* dq;
   float* dk;
   float* dv;

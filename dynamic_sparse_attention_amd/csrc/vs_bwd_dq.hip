@@ -42,8 +42,12 @@ struct DqWorkerB {
   char* kt;             // this wave's two K buffers [2][HBYTES]
   float sl2;
 
+  // Chunk c of row r sits at chunk index c ^ swz(r): the row reads (rows
+  // {0-3, 8-11} + 4k, eight lanes at a time) and the transposed reads (four
+  // consecutive rows, sixteen lanes) both hit eight distinct bank groups.
+  __device__ static __forceinline__ constexpr int swz(int row) { return 2 * (row & 3) + ((row >> 3) & 1); }
   __device__ static __forceinline__ int off(int row, int chunk) {
-    return (row / RPI) * 1024 + (row % RPI) * (CPR * 16) + 16 * (chunk ^ (2 * (row & 3)));
+    return (row / RPI) * 1024 + (row % RPI) * (CPR * 16) + 16 * (chunk ^ swz(row));
   }
 
   template <class Set>
@@ -62,19 +66,22 @@ struct DqWorkerB {
     typedef __attribute__((address_space(1))) void* glb_ptr;
     const int lane = threadIdx.x & 63;
     const int rr = lane / CPR;
-    const int chunk = (lane % CPR) ^ (2 * (rr & 3));
     if constexpr (Set::kContiguous) {
-      const __bf16* p0 = kb + (unsigned)S.key_pos(n, rr) * (unsigned)kvs + chunk * 8;
+      const __bf16* p0 = kb + (unsigned)S.key_pos(n, rr) * (unsigned)kvs;
 #pragma unroll
-      for (int u = 0; u < NVL; ++u)
-        __builtin_amdgcn_global_load_lds((glb_ptr)(p0 + (unsigned)(u * RPI * kvs)), (lds_ptr)(dst + u * 1024),
-                                         16, 0, 0);
+      for (int u = 0; u < NVL; ++u) {
+        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
+        __builtin_amdgcn_global_load_lds((glb_ptr)(p0 + (unsigned)(u * RPI * kvs) + chunk * 8),
+                                         (lds_ptr)(dst + u * 1024), 16, 0, 0);
+      }
     } else {
 #pragma unroll
-      for (int u = 0; u < NVL; ++u)
+      for (int u = 0; u < NVL; ++u) {
+        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
         __builtin_amdgcn_global_load_lds(
             (glb_ptr)(kb + (unsigned)S.key_pos(n, rr + u * RPI) * (unsigned)kvs + chunk * 8),
             (lds_ptr)(dst + u * 1024), 16, 0, 0);
+      }
     }
   }
 

@@ -7,13 +7,15 @@
 //
 // A workgroup is two waves; wave kh owns 32 keys (held as the B operands K^T,
 // V^T) and accumulates dK^T, dV^T for them.  The query tiles the unit reads
-// (64 rows of Q and dO of one Q head, plus their LSE and delta) stream
-// through two LDS buffers: while the waves compute on one tile the next one
-// arrives by direct global -> LDS loads (no registers, no packing).  Q and dO
-// are stored row-major with the 16-byte chunks of row r at chunk index
-// c ^ 2*(r % 4); the S = Q K^T and dP = dO V^T operands are plain 16-byte
-// reads, the dK^T = Q^T dS and dV^T = dO^T P operands transposed reads
-// (ds_read_b64_tr_b16) that hit distinct banks thanks to the swizzle.
+// (64 rows of Q and dO of one Q head, plus their LSE * log2(e) and delta)
+// stream through two LDS buffers: while the waves compute on one tile the
+// next one arrives by direct global -> LDS loads (no registers, no packing).
+// Q and dO are stored row-major with the 16-byte chunks of row r at chunk
+// index c ^ f(r), f(r) = 2*(r % 4) + (r / 8) % 2.  The S = Q K^T and
+// dP = dO V^T operands are 16-byte reads of rows {0-3, 8-11} + 4k by eight
+// lanes at a time, the dK^T = Q^T dS and dV^T = dO^T P operands transposed
+// reads (ds_read_b64_tr_b16) of four consecutive rows by sixteen lanes; f
+// sends both to eight distinct 16-byte bank groups.
 //
 //   * slash units: (batch, KV head, key block j); the tiles are every
 //     (Q head of the group, selected block-diagonal g) with query block j + g;
@@ -34,16 +36,17 @@ struct RowTile {
   static constexpr int RPI = 64 / CPR;       // rows per 1 KiB direct-load instruction
   static constexpr int BYTES = 64 * D * 2;   // 64 rows
   static constexpr int NDMA = 64 / RPI;      // direct-load instructions per 64 rows
+  __device__ static __forceinline__ constexpr int swz(int row) { return 2 * (row & 3) + ((row >> 3) & 1); }
   __device__ static __forceinline__ int off(int row, int chunk) {
-    return (row / RPI) * 1024 + (row % RPI) * (CPR * 16) + 16 * (chunk ^ (2 * (row & 3)));
+    return (row / RPI) * 1024 + (row % RPI) * (CPR * 16) + 16 * (chunk ^ swz(row));
   }
 };
 
 template <int D>
-struct KvBuf {
+struct __attribute__((aligned(16))) KvBuf {
   char q[RowTile<D>::BYTES];
   char dout[RowTile<D>::BYTES];
-  float lse[64];
+  float lse2[64];  // LSE * log2(e)
   float del[64];
 };
 
@@ -62,17 +65,17 @@ __device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, in
   const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + base;
   const __bf16* db = reinterpret_cast<const __bf16*>(p.dout) + base;
   const int rsub = lane / RT::CPR;
-  const int chunk = (lane % RT::CPR) ^ (2 * (rsub & 3));
 #pragma unroll
   for (int u0 = 0; u0 < RT::NDMA / 2; ++u0) {
     const int u = w * (RT::NDMA / 2) + u0;
+    const int chunk = (lane % RT::CPR) ^ RT::swz(u * RT::RPI + rsub);
     const unsigned eoff = (unsigned)(u * RT::RPI + rsub) * rstride + chunk * 8;
     __builtin_amdgcn_global_load_lds((glb_vptr)(qb + eoff), (lds_vptr)(B.q + u * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((glb_vptr)(db + eoff), (lds_vptr)(B.dout + u * 1024), 16, 0, 0);
   }
   const size_t li = ((size_t)b * p.h_q + h) * p.n_q + (size_t)i * kBlock + lane;
   if (w == 0)
-    __builtin_amdgcn_global_load_lds((glb_vptr)(p.lse + li), (lds_vptr)B.lse, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_vptr)(p.lse2 + li), (lds_vptr)B.lse2, 4, 0, 0);
   else
     __builtin_amdgcn_global_load_lds((glb_vptr)(p.delta + li), (lds_vptr)B.del, 4, 0, 0);
 }
@@ -109,83 +112,105 @@ struct KvWorkerB {
     }
   }
 
-  // A operand from a row-major tile: rows 32*rg + slot_perm(L%32), chunk c.
-  __device__ __forceinline__ static frag row_frag(const char* t, int rg, int c) {
-    const int lane = threadIdx.x & 63;
-    const int row = 32 * rg + slot_perm<KPL>(lane & 31);
-    return *reinterpret_cast<const frag*>(t + RT::off(row, 2 * c + (lane >> 5)));
-  }
+  // LDS reads of a tile with per-lane offsets computed once, so that the
+  // per-read part is a constant the ds_read offset field absorbs.  With the
+  // row-major layout (row r at r * CPR * 16 bytes) and the chunk swizzle
+  // c ^ swz(r), swz(r) < 8:
+  //  * row operand (row 32rg + slot_perm(L%32), chunk 2c + L/32): the XOR
+  //    only permutes chunks inside groups of 8, so the offset is
+  //    ro[c % 4] + 32 * rg * CPR * 16 + 128 * (c / 4);
+  //  * transposed operand (row 16c + 8h + 4q + (i/4) for lane i of a 16-lane
+  //    group, chunk 4ct + x, x < 4): swz = 2(i/4) + h, so the chunk is
+  //    4 (ct ^ zh) + zl with z = x ^ swz, and the offset is
+  //    to[ct % 2] + 64 (ct - ct % 2) + (16c + 4q) * CPR * 16.
+  int ro[4];
+  int to[2];
 
-  // A operand of a transposed tile: channels 32*ct + L%32, rows of k chunk c
-  // (16 rows).  ds_read_b64_tr_b16: in each 16-lane group, lane i receives
-  // element i%4 of the 8 bytes read by lanes i/4, 4+i/4, 8+i/4, 12+i/4.
-  __device__ __forceinline__ static frag tr_frag(const char* t, int ct, int c) {
+  __device__ __forceinline__ void init_offsets() {
     const int lane = threadIdx.x & 63;
+    const int hl = lane >> 5;
+    const int sp = slot_perm<KPL>(lane & 31);
+#pragma unroll
+    for (int cl = 0; cl < 4; ++cl) ro[cl] = sp * (RT::CPR * 16) + 16 * ((2 * cl + hl) ^ RT::swz(sp));
     const int g = lane >> 4;
     const int sg = lane & 15;
-    const int hl = lane >> 5;
-    const int cb = 32 * ct + 16 * (g & 1) + 4 * (sg & 3);
+    const int rr = sg >> 2;
+    const int x = 2 * (g & 1) + ((sg & 3) >> 1);
+    const int z = x ^ (2 * rr + hl);
+    const int base = (8 * hl + rr) * (RT::CPR * 16) + 16 * (z & 3) + 8 * (sg & 1);
+    to[0] = base + 64 * (z >> 2);
+    to[1] = base + 64 * (1 - (z >> 2));
+  }
+
+  __device__ __forceinline__ frag row_frag(const char* t, int rg, int c) const {
+    return *reinterpret_cast<const frag*>(t + ro[c & 3] + 32 * rg * (RT::CPR * 16) + 128 * (c >> 2));
+  }
+
+  // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of
+  // the 8 bytes read by lanes i/4, 4+i/4, 8+i/4, 12+i/4 (rows k0 .. k0+3).
+  __device__ __forceinline__ frag tr_frag(const char* t, int ct, int c) const {
     typedef short v4s __attribute__((ext_vector_type(4)));
     typedef short v8s __attribute__((ext_vector_type(8)));
     v4s part[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = c * 16 + 8 * hl + 4 * q + (sg >> 2);
-      part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(t + RT::off(row, cb >> 3) + 2 * (cb & 7)));
-    }
+    for (int q = 0; q < 2; ++q)
+      part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(
+          t + to[ct & 1] + 64 * (ct & ~1) + (16 * c + 4 * q) * (RT::CPR * 16)));
     const v8s both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(frag, both);
   }
 
-  // One query tile.  valid(r): this lane's key column is visible to row r.
-  template <class ValidF>
+  // One query tile, 32 rows at a time.  kMasked: valid(r) says whether this
+  // lane's key column is visible to row r (else the tile is fully visible).
+  // Masked entries get exponent -inf, so P = dS = 0 there.
+  template <bool kMasked, class ValidF>
   __device__ __forceinline__ void tile(const KvBuf<D>& B, float sl2, ValidF valid) {
     const int lane = threadIdx.x & 63;
     const int hl = lane >> 5;
-    f32x16 s[2], dp[2];
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
-      s[rg] = f32x16{0};
-      dp[rg] = f32x16{0};
+      f32x16 s = f32x16{0}, dp = f32x16{0};
 #pragma unroll
       for (int c = 0; c < NCD; ++c) {
-        s[rg] = MF::mma(row_frag(B.q, rg, c), kB[c], s[rg]);
-        dp[rg] = MF::mma(row_frag(B.dout, rg, c), vB[c], dp[rg]);
+        s = MF::mma(row_frag(B.q, rg, c), kB[c], s);
+        dp = MF::mma(row_frag(B.dout, rg, c), vB[c], dp);
       }
-    }
-    frag pf[2][2], dsf[2][2];
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
+      // keep the phases of the tile apart: hoisting the LDS reads of later
+      // phases ahead of the products costs more registers than there are
+      __builtin_amdgcn_sched_barrier(0);
+      frag pf[2], dsf[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        // register i = 8c + e holds row 32rg + 16c + 8hl + e
+        // register 8c + e holds row 32rg + 16c + 8hl + e
         const int r0 = 32 * rg + 16 * c + 8 * hl;
-        const f32x4 la = *reinterpret_cast<const f32x4*>(B.lse + r0);
-        const f32x4 lb = *reinterpret_cast<const f32x4*>(B.lse + r0 + 4);
+        const f32x4 la = *reinterpret_cast<const f32x4*>(B.lse2 + r0);
+        const f32x4 lb = *reinterpret_cast<const f32x4*>(B.lse2 + r0 + 4);
         const f32x4 da = *reinterpret_cast<const f32x4*>(B.del + r0);
         const f32x4 db = *reinterpret_cast<const f32x4*>(B.del + r0 + 4);
         float pr[8], ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float lse = e < 4 ? la[e] : lb[e - 4];
+          const float l2 = e < 4 ? la[e] : lb[e - 4];
           const float dl = e < 4 ? da[e] : db[e - 4];
-          const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
-          const float x = valid(r0 + e) ? fast_exp2(__builtin_fmaf(s[rg][8 * c + e], sl2, -l2)) : 0.f;
+          float t = __builtin_fmaf(s[8 * c + e], sl2, -l2);
+          if constexpr (kMasked) t = valid(r0 + e) ? t : -INFINITY;
+          const float x = fast_exp2(t);
           pr[e] = x;
-          ds[e] = x * (dp[rg][8 * c + e] - dl);
+          ds[e] = x * (dp[8 * c + e] - dl);
         }
-        pf[rg][c] = MF::pack(pr);
-        dsf[rg][c] = MF::pack(ds);
+        pf[c] = MF::pack(pr);
+        dsf[c] = MF::pack(ds);
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
+      for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        dv[ct] = MF::mma(tr_frag(B.dout, ct, c), pf[c >> 1][c & 1], dv[ct]);
-        dk[ct] = MF::mma(tr_frag(B.q, ct, c), dsf[c >> 1][c & 1], dk[ct]);
+        for (int c = 0; c < 2; ++c) {
+          dv[ct] = MF::mma(tr_frag(B.dout, ct, 2 * rg + c), pf[c], dv[ct]);
+          dk[ct] = MF::mma(tr_frag(B.q, ct, 2 * rg + c), dsf[c], dk[ct]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -279,6 +304,7 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_slash_bf16_kernel(AttnPa
   const int kin = 32 * kh + l32;
 
   W wk;
+  wk.init_offsets();
   wk.load_keys(p, b, kvh, kpos);
   int count = 0;
   auto tile_of = [&](int t, int* h, int* i, int* fl) {
@@ -287,26 +313,38 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_slash_bf16_kernel(AttnPa
     *i = (v >> 1) & ((1 << 25) - 1);
     *fl = v & 1;
   };
-  auto body = [&](const KvBuf<D>& B, int, int diag) {
-    wk.tile(B, p.sl2, [&](int r) { return !diag || kin <= r; });
-  };
+  // Diagonal tiles (g = 0, causal inside the block) first, in a walk of their
+  // own, so that the main walk has no masking at all.
+  {
+    int i = -1;
+    if (tid < G) {
+      const int list = (b * p.h_q + kvh * G + tid) * p.seg.n_seg + seg;
+      const int sp0 = p.s_ptr[list];
+      if (p.s_ptr[list + 1] > sp0 && p.s_idx[sp0] == 0) i = local_query_block(p, kb_glob);
+    }
+    int tot;
+    const int slot = block_compact<kKvThreads>(i >= 0, L.wsum, &tot);
+    if (i >= 0) L.tiles[slot] = (tid << 26) | (i << 1) | 1;
+    __syncthreads();
+    kv_pipeline<D>(p, L, b, tot, tile_of, [&](const KvBuf<D>& B, int, int) {
+      wk.template tile<true>(B, p.sl2, [&](int r) { return kin <= r; });
+    });
+  }
+  auto body = [&](const KvBuf<D>& B, int, int) { wk.template tile<false>(B, p.sl2, [](int) { return true; }); };
   for (int hh = 0; hh < G; ++hh) {
     const int list = (b * p.h_q + kvh * G + hh) * p.seg.n_seg + seg;
     const int sp0 = p.s_ptr[list];
     const int ns = p.s_ptr[list + 1] - sp0;
     for (int base = 0; base < ns; base += kKvThreads) {
       const int e = base + tid;
-      int i = -1, diag = 0;
+      int i = -1;
       if (e < ns) {
         const int g = p.s_idx[sp0 + e];
-        if (g >= 0 && beta_k + g < nb_seg) {
-          i = local_query_block(p, kb_glob + g);
-          diag = g == 0;
-        }
+        if (g > 0 && beta_k + g < nb_seg) i = local_query_block(p, kb_glob + g);
       }
       int tot;
       const int slot = block_compact<kKvThreads>(i >= 0, L.wsum, &tot);
-      if (i >= 0) L.tiles[count + slot] = (hh << 26) | (i << 1) | diag;
+      if (i >= 0) L.tiles[count + slot] = (hh << 26) | (i << 1);
       count += tot;
       __syncthreads();
       if (count > kKvTiles - kKvThreads) {
@@ -378,6 +416,7 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_cols_bf16_kernel(AttnPar
   __syncthreads();
 
   W wk;
+  wk.init_offsets();
   wk.load_keys(p, b, kvh, kpos);
   auto qglob = [&](int i) { return p.W == 1 ? i : p.q_rank + p.W * i; };
   auto tile_of = [&](int t, int* hh, int* i, int* fl) {
@@ -392,7 +431,8 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_cols_bf16_kernel(AttnPar
     const int off = beta_q - bm;
     const bool lane_ok = col_ok && off >= 0 && ((bits[off >> 5] >> (off & 31)) & 1u) == 0u;
     const int row0 = qbg * kBlock;
-    wk.tile(B, p.sl2, [&](int r) { return lane_ok && m <= row0 + r; });
+    const int mr = lane_ok ? m - row0 : 64;  // first visible row
+    wk.template tile<true>(B, p.sl2, [&](int r) { return mr <= r; });
   };
   kv_pipeline<D>(p, L, b, ntiles, tile_of, body);
   if (col_ok) wk.store(p, b, kvh, kpos, true);

@@ -50,6 +50,23 @@ hipError_t launch_prep_vertical(const AttnParams& p, int n_lists, const int* v_p
   return hipGetLastError();
 }
 
+// lse2 = LSE * log2(e): the backward recomputes P = exp(S - LSE) as
+// exp2(S * scale * log2(e) - lse2).  An empty row (LSE = -inf) maps to +inf,
+// so that P is 0 there whatever the scores.
+__global__ __launch_bounds__(256) void vs_lse_log2_kernel(const float* lse, float* lse2, size_t count) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) {
+    const float l = lse[i];
+    lse2[i] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  }
+}
+
+hipError_t launch_lse_log2(const float* lse, float* lse2, size_t count, hipStream_t st) {
+  if (count == 0) return hipSuccess;
+  VS_TRACED(st, "vs_lse_log2", hipLaunchKernelGGL(vs_lse_log2_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, lse, lse2, count));
+  return hipGetLastError();
+}
+
 // delta[b, h, n] = sum_c dO[b, n, h, c] * O[b, n, h, c]  (MTraining §3.2 Eq. 1:
 // rowsum(dA * A) = rowsum(dO * O)).  D/4 threads per row, 4 channels each.
 template <typename TO, typename TD, int D>

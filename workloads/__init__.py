@@ -79,15 +79,18 @@ class Problem:
 
 
 def rope_rotate_half(x: torch.Tensor, positions: torch.Tensor, base: float = 10000.0,
-                     chunk: int = 8192) -> torch.Tensor:
+                     chunk: int = 8192, dtype: Optional[str] = None) -> torch.Tensor:
     """Rotary embedding (rotate-half pairing of dim i with i + d/2), fp64 math.
 
-    x: [1, N, H, d] float tensor; positions: [N] int64.  Returns fp64 tensor.
+    x: [1, N, H, d] float tensor; positions: [N] int64.  Returns an fp64
+    tensor, or, with ``dtype``, the fp64 result rounded chunk by chunk to that
+    dtype (the same values as rounding the whole fp64 tensor afterwards).
     """
     d = x.shape[-1]
     half = d // 2
     inv = base ** (-2.0 * torch.arange(half, dtype=torch.float64) / d)
-    out = torch.empty(x.shape, dtype=torch.float64)
+    out_dtype = torch.float64 if dtype is None else (torch.float32 if dtype == "f32" else torch.bfloat16)
+    out = torch.empty(x.shape, dtype=out_dtype)
     for s in range(0, x.shape[1], chunk):
         e = min(x.shape[1], s + chunk)
         ang = positions[s:e].to(torch.float64)[:, None] * inv[None, :]      # [c, half]
@@ -95,8 +98,8 @@ def rope_rotate_half(x: torch.Tensor, positions: torch.Tensor, base: float = 100
         sn = torch.sin(ang)[None, :, None, :]
         xs = x[:, s:e].to(torch.float64)
         lo, hi = xs[..., :half], xs[..., half:]
-        out[:, s:e, :, :half] = lo * c - hi * sn
-        out[:, s:e, :, half:] = hi * c + lo * sn
+        r = torch.cat((lo * c - hi * sn, hi * c + lo * sn), dim=-1)
+        out[:, s:e] = r if dtype is None else _round(r, dtype)
     return out
 
 
@@ -155,10 +158,11 @@ def make_problem(wid: int, n: Optional[int] = None, seed: Optional[int] = None,
     if n_out:
         k[:, outliers] *= w["out_factor"]
     pos = torch.arange(n, dtype=torch.int64)
-    q = _round(rope_rotate_half(q, pos), dtype)
-    k = _round(rope_rotate_half(k, pos), dtype)
-    v = _round(v.to(torch.float64), dtype)
-    do = _round(do.to(torch.float64), dtype)
+    q = rope_rotate_half(q, pos, dtype=dtype)
+    k = rope_rotate_half(k, pos, dtype=dtype)
+    # fp32 -> fp64 is exact, so V and dO round straight from fp32
+    v = _round(v, dtype)
+    do = _round(do, dtype)
     sw = stripe_world if stripe_world is not None else w.get("stripe_world", 1)
     return Problem(wid=wid, name=w["name"], dtype=dtype, q=q, k=k, v=v, do=do, h_q=h_q,
                    h_kv=h_kv, d=d, n=n, block=BLOCK, cu_seqlens=cu, v_budget=vb,
