@@ -30,10 +30,11 @@ def flags(arch: str = "gfx950"):
             "-Wno-unused-result", "-munsafe-fp-atomics"]
 
 
-# Per-source extra flags.  The forward keeps its matrix-core accumulators in
-# the VGPR file: the online softmax rescales them with vector ALU
-# instructions, and AGPR residency made the compiler copy the whole output
-# tile back and forth on every iteration.
+# Per-source extra flags.  The attention kernels keep their matrix-core
+# accumulators in the VGPR file: the softmax works on the score tiles with
+# vector ALU instructions right after the products, and with AGPR results the
+# compiler copied whole tiles back and forth on every iteration (measured
+# slower for all three).
 EXTRA = {"vs_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "vs_bwd_kv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "vs_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

@@ -59,7 +59,7 @@ template <int D>
 __device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, int b, int h, int i) {
   typedef RowTile<D> RT;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const unsigned rstride = (unsigned)(p.h_q * D);
   const size_t base = (((size_t)b * p.n_q + (size_t)i * kBlock) * p.h_q + h) * D;
   const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + base;
@@ -74,10 +74,8 @@ __device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, in
     __builtin_amdgcn_global_load_lds((glb_vptr)(db + eoff), (lds_vptr)(B.dout + u * 1024), 16, 0, 0);
   }
   const size_t li = ((size_t)b * p.h_q + h) * p.n_q + (size_t)i * kBlock + lane;
-  if (w == 0)
-    __builtin_amdgcn_global_load_lds((glb_vptr)(p.lse2 + li), (lds_vptr)B.lse2, 4, 0, 0);
-  else
-    __builtin_amdgcn_global_load_lds((glb_vptr)(p.delta + li), (lds_vptr)B.del, 4, 0, 0);
+  const float* src = w == 0 ? p.lse2 : p.delta;
+  __builtin_amdgcn_global_load_lds((glb_vptr)(src + li), (lds_vptr)(w == 0 ? B.lse2 : B.del), 4, 0, 0);
 }
 
 template <int D>
@@ -251,6 +249,17 @@ struct KvLdsB {
 
 // Double-buffered walk over ntiles query tiles: tile_of(t) -> (h, i, flags),
 // body(B, t, flags) computes on the staged tile t.
+// One pipeline step: the next tile's loads go to nxt while body computes on
+// cur.  The two buffers never overlap; saying so (restrict) lets the compiler
+// see that the reads of cur need not wait for the loads into nxt.
+template <int D, class BodyF>
+__device__ __forceinline__ void kv_step(const AttnParams& p, KvBuf<D>* __restrict__ nxt,
+                                        const KvBuf<D>* __restrict__ cur, bool more, int b, int h1,
+                                        int i1, int t, int fl, BodyF& body) {
+  if (more) kv_tile_dma<D>(p, *nxt, b, h1, i1);
+  body(*cur, t, fl);
+}
+
 template <int D, class TileF, class BodyF>
 __device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D>& L, int b, int ntiles,
                                             TileF tile_of, BodyF body) {
@@ -263,13 +272,11 @@ __device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D>& L, i
     // loads visible and frees the other buffer (its tile t-1 compute is over)
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
     __syncthreads();
-    int h1, i1, fl1;
-    if (t + 1 < ntiles) {
-      tile_of(t + 1, &h1, &i1, &fl1);
-      kv_tile_dma<D>(p, L.buf[(t + 1) & 1], b, h1, i1);
-    }
+    int h1 = 0, i1 = 0, fl1;
+    const bool more = t + 1 < ntiles;
+    if (more) tile_of(t + 1, &h1, &i1, &fl1);
     tile_of(t, &h, &i, &fl);
-    body(L.buf[t & 1], t, fl);
+    kv_step<D>(p, &L.buf[(t + 1) & 1], &L.buf[t & 1], more, b, h1, i1, t, fl, body);
   }
   __syncthreads();
 }

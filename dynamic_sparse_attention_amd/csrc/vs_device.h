@@ -89,6 +89,20 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // this wave are outstanding and leaves the other counters alone (gfx9 layout:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// ... and one that waits for every LDS access of this wave (lgkmcnt 0).
+constexpr int lgkmcnt_wait0() { return 15 | (3 << 14) | (7 << 4); }
+
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes land
+// at lds_base + 16 * L (lds_base wave-uniform).  Written as inline assembly so
+// that the compiler does not track it: it would otherwise make every later
+// LDS read of the same array wait for all such loads in flight, which defeats
+// multi-buffering.  The caller waits for completion itself (vmcnt; the loads
+// return in issue order) before reading the data.
+__device__ __forceinline__ void dma_lds16(const void* gptr, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base);
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(m0) : "memory");
+}
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 

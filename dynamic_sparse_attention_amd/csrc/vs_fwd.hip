@@ -30,14 +30,17 @@ struct FwdWorker {
   static constexpr int NCD = D / KC;   // k chunks over head_dim
   static constexpr int NCT = D / 32;   // 32-channel output tiles
   static constexpr int NCK = 32 / KC;  // k chunks over 32 keys
-  // bf16: the 32 V rows of a half-tile go global -> LDS directly
-  // (global_load_lds_dwordx4, 1 KiB per instruction = RPI rows), with the
-  // 16-byte chunks of row r stored at chunk index c ^ 2*(r % 4) so that the
-  // transposed reads (ds_read_b64_tr_b16) of four consecutive rows hit
-  // distinct banks.
+  // bf16: the 32 K rows and the 32 V rows of a half-tile go global -> LDS
+  // directly (global_load_lds_dwordx4, 1 KiB per instruction = RPI rows) into
+  // row-major tiles (row r at r * CPR * 16 bytes) with chunk c of row r at
+  // chunk index c ^ swz(r).  The K operand is read row-wise (rows {0-3, 8-11}
+  // + 4k, eight lanes at a time), the V operand transposed
+  // (ds_read_b64_tr_b16, four consecutive rows by sixteen lanes); swz sends
+  // both to eight distinct 16-byte bank groups.
   static constexpr int CPR = D / 8;                      // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;                   // rows per load instruction
-  static constexpr int NVL = 32 / RPI;                   // V load instructions per half
+  static constexpr int NVL = 32 / RPI;                   // load instructions per 32 rows
+  __device__ static constexpr int swz(int r) { return 2 * (r & 3) + ((r >> 3) & 1); }
   // fp32: V transposed through registers into [channel][key] (pitch VTP).
   static constexpr int VTP = 32 + 4;
   static constexpr int CG = 4;                           // fp32 channels per 16-byte load
@@ -57,6 +60,13 @@ struct FwdWorker {
 
   frag qf[2][NCD];
   f32x16 o[2][NCT];
+  // bf16: this wave's K and V tiles, a ring of two each, every tile in an LDS
+  // array of its own; per-lane offsets of the K (row) and V (transposed)
+  // operand reads, so that the per-read part is an immediate offset.
+  char* kl[2];
+  char* vl[2];
+  int ro[4];
+  int to[2];
   f32x4 vr[kBf16 ? 1 : NVG * KG];   // fp32 path: raw V rows of the next half-tile
   float m[2], l[2];
   const T* kb;   // K of (batch, kv head): row pos at kb + pos * kvs
@@ -66,7 +76,7 @@ struct FwdWorker {
   float sl2;
 
   template <class Set>
-  __device__ __forceinline__ void load_k(const Set& S, int n, Buf& B) const {
+  __device__ __forceinline__ void load_k(const Set& S, int n, frag (&k)[NCD]) const {
     const int lane = threadIdx.x & 63;
     const int hl = lane >> 5;
     const int l32 = lane & 31;
@@ -74,42 +84,69 @@ struct FwdWorker {
     const unsigned key = S.key_pos(n, slot_perm<KPL>(l32));
     const T* krow = kb + key * (unsigned)kvs + hl * KPL;
 #pragma unroll
-    for (int c = 0; c < NCD; ++c) B.k[c] = load_frag<T>(krow + c * KC);
+    for (int c = 0; c < NCD; ++c) k[c] = load_frag<T>(krow + c * KC);
   }
 
-  // bf16: V rows of half n straight into staging buffer dst (asynchronous;
-  // NVL vector-memory instructions).  fp32: into registers.
-  template <class Set>
-  __device__ __forceinline__ void load_v(const Set& S, int n, char* dst) {
+  __device__ __forceinline__ void init_offsets() {
     const int lane = threadIdx.x & 63;
-    if constexpr (kBf16) {
-      const int rr = lane / CPR;
-      const int chunk = (lane % CPR) ^ (2 * (rr & 3));
-      typedef __attribute__((address_space(3))) void* lds_ptr;
-      typedef __attribute__((address_space(1))) void* glb_ptr;
-      if constexpr (Set::kContiguous) {
-        const T* p0 = vb + (unsigned)S.key_pos(n, rr) * (unsigned)kvs + chunk * 8;
+    const int hl = lane >> 5;
+    const int sp = slot_perm<KPL>(lane & 31);
+    // row operand: row sp, chunk 2c + hl; the XOR permutes chunks inside
+    // groups of 8, so the offset is ro[c % 4] + 128 * (c / 4)
 #pragma unroll
-        for (int u = 0; u < NVL; ++u)
-          __builtin_amdgcn_global_load_lds((glb_ptr)(p0 + (unsigned)(u * RPI * kvs)),
-                                           (lds_ptr)(dst + u * 1024), 16, 0, 0);
-      } else {
+    for (int cl = 0; cl < 4; ++cl) ro[cl] = sp * (CPR * 16) + 16 * ((2 * cl + hl) ^ swz(sp));
+    // transposed operand: lane i of a 16-lane group reads row 16c + 8h + 4q +
+    // i/4 at chunk 4ct + x (x < 4); swz = 2(i/4) + h, so the chunk is
+    // 4 (ct ^ zh) + zl with z = x ^ swz
+    const int g = lane >> 4;
+    const int sg = lane & 15;
+    const int rr = sg >> 2;
+    const int x = 2 * (g & 1) + ((sg & 3) >> 1);
+    const int z = x ^ (2 * rr + hl);
+    const int base = (8 * hl + rr) * (CPR * 16) + 16 * (z & 3) + 8 * (sg & 1);
+    to[0] = base + 64 * (z >> 2);
+    to[1] = base + 64 * (1 - (z >> 2));
+  }
+
+  // bf16: the 32 rows (K or V, from src) of half n straight into tile dst
+  // (asynchronous; NVL vector-memory instructions).
+  template <class Set>
+  __device__ __forceinline__ void dma_rows(const Set& S, int n, const T* src, char* dst) const {
+    const int lane = threadIdx.x & 63;
+    const int rr = lane / CPR;
+    if constexpr (Set::kContiguous) {
+      const T* p0 = src + (unsigned)S.key_pos(n, rr) * (unsigned)kvs;
 #pragma unroll
-        for (int u = 0; u < NVL; ++u)
-          __builtin_amdgcn_global_load_lds(
-              (glb_ptr)(vb + (unsigned)S.key_pos(n, rr + u * RPI) * (unsigned)kvs + chunk * 8),
-              (lds_ptr)(dst + u * 1024), 16, 0, 0);
+      for (int u = 0; u < NVL; ++u) {
+        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
+        dma_lds16(p0 + (unsigned)(u * RPI * kvs) + chunk * 8, dst + u * 1024);
       }
     } else {
 #pragma unroll
-      for (int g = 0; g < NVG; ++g) {
-        const int gi = g * 64 + lane;
-        const int kg = gi % NKG;
-        const int cg = gi / NKG;
-#pragma unroll
-        for (int u = 0; u < KG; ++u)
-          vr[g * KG + u] = *reinterpret_cast<const f32x4*>(vb + (unsigned)S.key_pos(n, kg * KG + u) * (unsigned)kvs + cg * CG);
+      for (int u = 0; u < NVL; ++u) {
+        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
+        dma_lds16(src + (unsigned)S.key_pos(n, rr + u * RPI) * (unsigned)kvs + chunk * 8, dst + u * 1024);
       }
+    }
+  }
+
+  // bf16: A operand of S^T = K Q^T from a K tile: key slot_perm(L%32), chunk 2c + L/32.
+  __device__ __forceinline__ frag k_frag(const char* src, int c) const {
+    return *reinterpret_cast<const frag*>(src + ro[c & 3] + 128 * (c >> 2));
+  }
+
+  // fp32: V rows of half n into registers.
+  template <class Set>
+  __device__ __forceinline__ void load_v(const Set& S, int n) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int g = 0; g < NVG; ++g) {
+      const int gi = g * 64 + lane;
+      const int kg = gi % NKG;
+      const int cg = gi / NKG;
+#pragma unroll
+      for (int u = 0; u < KG; ++u)
+        vr[g * KG + u] = *reinterpret_cast<const f32x4*>(vb + (unsigned)S.key_pos(n, kg * KG + u) * (unsigned)kvs + cg * CG);
     }
   }
 
@@ -139,24 +176,15 @@ struct FwdWorker {
     const int lane = threadIdx.x & 63;
     if constexpr (kBf16) {
       // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element
-      // i%4 of the 8 bytes read by lanes i/4, 4+i/4, 8+i/4, 12+i/4.  Lane sigma
-      // reads key row k0 + sigma/4, channels cb + 4*(sigma%4) .. +3, so lane i
-      // gets channel cb + i of keys k0 .. k0+3 (k0 is a multiple of 4).
-      const int g = lane >> 4;
-      const int sg = lane & 15;
-      const int hl = lane >> 5;
-      const int rr = sg >> 2;                               // row within the 4-row group
-      const int cb = 32 * ct + 16 * (g & 1) + 4 * (sg & 3);  // first channel read
+      // i%4 of the 8 bytes read by lanes i/4, 4+i/4, 8+i/4, 12+i/4, i.e.
+      // channel 32ct + 16(g%2) + i of keys 16c + 8h + 4q .. +3.
       typedef short v4s __attribute__((ext_vector_type(4)));
       typedef short v8s __attribute__((ext_vector_type(8)));
       v4s part[2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int row = c * 16 + 8 * hl + 4 * q + rr;
-        const int off = (row / RPI) * 1024 + (row % RPI) * (CPR * 16) +
-                        16 * ((cb >> 3) ^ (2 * (row & 3))) + 2 * (cb & 7);
-        part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(src + off));
-      }
+      for (int q = 0; q < 2; ++q)
+        part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(
+            src + to[ct & 1] + 64 * (ct & ~1) + (16 * c + 4 * q) * (CPR * 16)));
       const v8s both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
       return __builtin_bit_cast(frag, both);
     } else {
@@ -166,19 +194,28 @@ struct FwdWorker {
     }
   }
 
-  __device__ __forceinline__ void scores(Buf& B) const {
+  __device__ __forceinline__ void scores(const frag (&k)[NCD], f32x16 (&s)[2]) const {
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
-      B.s[rg] = f32x16{0};
+      s[rg] = f32x16{0};
 #pragma unroll
-      for (int c = 0; c < NCD; ++c) B.s[rg] = MF::mma(B.k[c], qf[rg][c], B.s[rg]);
+      for (int c = 0; c < NCD; ++c) s[rg] = MF::mma(k[c], qf[rg][c], s[rg]);
+    }
+  }
+
+  __device__ __forceinline__ void scores_lds(const char* ksrc, f32x16 (&s)[2]) const {
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      s[rg] = f32x16{0};
+#pragma unroll
+      for (int c = 0; c < NCD; ++c) s[rg] = MF::mma(k_frag(ksrc, c), qf[rg][c], s[rg]);
     }
   }
 
   // Online softmax, first part: masked row maxima of half-tile n and the
   // (rare) rescale of the running state.  Masks the scores in place.
   template <class Set>
-  __device__ __forceinline__ void softmax_max(const Set& S, int n, Buf& B) {
+  __device__ __forceinline__ void softmax_max(const Set& S, int n, f32x16 (&s)[2]) {
     const int lane = threadIdx.x & 63;
     const int hl = lane >> 5;
     const int l32 = lane & 31;
@@ -188,15 +225,15 @@ struct FwdWorker {
         const int r = 32 * rg + l32;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (!S.valid(n, reg_row<KPL>(i, hl), r)) B.s[rg][i] = -INFINITY;
+          if (!S.valid(n, reg_row<KPL>(i, hl), r)) s[rg][i] = -INFINITY;
       }
     }
     float tm[2];
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
-      float mx = B.s[rg][0];
+      float mx = s[rg][0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, B.s[rg][i]);
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[rg][i]);
       mx = fmaxf(mx, xor32(mx));
       tm[rg] = mx * sl2;
     }
@@ -216,7 +253,7 @@ struct FwdWorker {
 
   // Online softmax, second part: P = exp2(s*scale*log2e - m), row sums, and
   // P^T of both row groups as bf16 (or fp32) B operands.
-  __device__ __forceinline__ void softmax_exp(const Buf& B, frag (&pf)[2][NCK]) {
+  __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2], frag (&pf)[2][NCK]) {
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
       const float mu = (m[rg] == -INFINITY) ? 0.f : m[rg];
@@ -224,7 +261,7 @@ struct FwdWorker {
       float rs = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(__builtin_fmaf(B.s[rg][i], sl2, -mu));
+        p[i] = fast_exp2(__builtin_fmaf(s[rg][i], sl2, -mu));
         rs += p[i];
       }
       rs += xor32(rs);
@@ -246,53 +283,80 @@ struct FwdWorker {
     }
   }
 
-  // Half-tile n with cur = its data; nxt.k holds the K operand of half n+1
-  // and vr the raw V rows of half n+1 (both loaded one step earlier).  The
-  // step is branch-free apart from the rare rescale, so the scheduler can
-  // overlap S(n+1) on the matrix cores with the exponentials of n, and P V(n)
-  // with the loads of n+2.  Past the end the last half is reloaded and
-  // recomputed instead of branching (its results are unused).
-  // Half-tile n: b.s holds S^T(n); staging buffer n&1 holds (or is receiving)
-  // V of half n.  K(n+1) is requested first so that its latency hides behind
-  // the softmax of n; V(n+1) goes to the other buffer while S^T(n+1) runs on
-  // the matrix cores.  Past the end the last half is reloaded and recomputed
-  // instead of branching (results unused).
+  // fp32: half-tile n with S^T(n) in b.s and V(n) staged in buffer n & 1.
+  // K(n+1) is requested first so that its latency hides behind the softmax
+  // of n; V(n+2) is read into registers while S^T(n+1) runs.  Past the end
+  // the last half is reloaded and recomputed instead of branching (results
+  // unused).
   template <class Set>
   __device__ __forceinline__ void step(const Set& S, int n, int N, Buf& b) {
     frag pf[2][NCK];
     const int n1 = n + 1 < N ? n + 1 : N - 1;
-    load_k(S, n1, b);
-    softmax_max(S, n, b);
-    softmax_exp(b, pf);
+    load_k(S, n1, b.k);
+    softmax_max(S, n, b.s);
+    softmax_exp(b.s, pf);
     char* cur = vt + (n & 1) * VBUF;
     char* nxt = vt + ((n + 1) & 1) * VBUF;
-    if constexpr (kBf16) {
-      load_v(S, n1, nxt);
-      scores(b);
-      // everything but the NVL loads of V(n+1) has landed: V(n) is in LDS
-      __builtin_amdgcn_s_waitcnt(vmcnt_wait(NVL));
-    } else {
-      stage(nxt);
-      load_v(S, n + 2 < N ? n + 2 : N - 1, nullptr);
-      scores(b);
-    }
+    stage(nxt);
+    load_v(S, n + 2 < N ? n + 2 : N - 1);
+    scores(b.k, b.s);
     wave_sync();
     pv(cur, pf);
+  }
+
+  // bf16: half-tile n (P = n % 2) with S^T(n) in s, K(n+1) in tile kl[P ^ 1]
+  // and V(n), V(n+1) in tiles vl[P], vl[P ^ 1] (landed or in flight).  K(n+2)
+  // goes out first, into the tile K(n) used (S^T(n) is done), V(n+2) last,
+  // into the tile V(n) used (its products are issued): K gets a step and a
+  // half to land, V two steps.  Loads return in order, so once K(n+1) is in,
+  // V(n) is too.  Past the end the last half is reloaded and recomputed
+  // instead of branching (results unused).
+  template <int P, class Set>
+  __device__ __forceinline__ void step2(const Set& S, int n, int N, f32x16 (&s)[2]) {
+    frag pf[2][NCK];
+    const int n2 = n + 2 < N ? n + 2 : N - 1;
+    dma_rows(S, n2, kb, kl[P]);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_max(S, n, s);
+    softmax_exp(s, pf);
+    // in flight may remain: V(n+1), K(n+2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * NVL));
+    wave_sync();
+    scores_lds(kl[P ^ 1], s);
+    pv(vl[P], pf);
+    // the reads of V(n) are done before V(n+2) may land in their place
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_wait0());
+    dma_rows(S, n2, vb, vl[P]);
   }
 
   template <class Set>
   __device__ __forceinline__ void run(const Set& S) {
     const int N = S.n_halves();
     if (N == 0) return;
-    Buf b;
-    load_v(S, 0, vt);
-    if constexpr (!kBf16) {
+    if constexpr (kBf16) {
+      f32x16 s[2];
+      const int n1 = N > 1 ? 1 : 0;
+      dma_rows(S, 0, kb, kl[0]);
+      dma_rows(S, 0, vb, vl[0]);
+      dma_rows(S, n1, kb, kl[1]);
+      dma_rows(S, n1, vb, vl[1]);
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * NVL));
+      wave_sync();
+      scores_lds(kl[0], s);
+      // a set always has an even number of halves (two per 64-key tile)
+      for (int n = 0; n < N; n += 2) {
+        step2<0>(S, n, N, s);
+        step2<1>(S, n + 1, N, s);
+      }
+    } else {
+      Buf b;
+      load_v(S, 0);
       stage(vt);
-      load_v(S, N > 1 ? 1 : 0, nullptr);
+      load_v(S, N > 1 ? 1 : 0);
+      load_k(S, 0, b.k);
+      scores(b.k, b.s);
+      for (int n = 0; n < N; ++n) step(S, n, N, b);
     }
-    load_k(S, 0, b);
-    scores(b);
-    for (int n = 0; n < N; ++n) step(S, n, N, b);
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
     wave_sync();
   }
@@ -300,10 +364,16 @@ struct FwdWorker {
 
 template <typename T, int D>
 struct FwdLds {
-  static constexpr int VT_BYTES = 4 * 2 * FwdWorker<T, D>::VBUF;
+  static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int OB_PITCH = D + 4;
   static constexpr int OB_BYTES = 64 * OB_PITCH * 4;
-  static constexpr int BUF = VT_BYTES > OB_BYTES ? VT_BYTES : OB_BYTES;
+  // fp32: both V staging buffers of every wave; bf16: the four LDS arrays of
+  // K / V tiles (one tile per wave in each); the first also holds the
+  // output merge afterwards.
+  static constexpr int VT_BYTES = kBf16 ? 0 : 4 * 2 * FwdWorker<T, D>::VBUF;
+  static constexpr int TILE_BYTES = kBf16 ? 4 * 32 * D * 2 : 16;
+  static constexpr int BUF0 = kBf16 ? (TILE_BYTES > OB_BYTES ? TILE_BYTES : OB_BYTES)
+                                    : (VT_BYTES > OB_BYTES ? VT_BYTES : OB_BYTES);
 };
 
 template <typename T, int D>
@@ -311,7 +381,10 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
   typedef FwdWorker<T, D> W;
   typedef FwdLds<T, D> LD;
   __shared__ QMajorLds L;
-  __shared__ __attribute__((aligned(16))) char buf[LD::BUF];
+  __shared__ __attribute__((aligned(16))) char buf[LD::BUF0];
+  __shared__ __attribute__((aligned(16))) char tk1[LD::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char tv0[LD::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char tv1[LD::TILE_BYTES];
   __shared__ float s_m[4][64];
   __shared__ float s_l[4][64];
 
@@ -346,6 +419,11 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
   wk.kb = reinterpret_cast<const T*>(p.k) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
   wk.vb = reinterpret_cast<const T*>(p.v) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
   wk.vt = buf + wave * 2 * W::VBUF;
+  wk.kl[0] = buf + wave * 32 * D * 2;
+  wk.kl[1] = tk1 + wave * 32 * D * 2;
+  wk.vl[0] = tv0 + wave * 32 * D * 2;
+  wk.vl[1] = tv1 + wave * 32 * D * 2;
+  if constexpr (W::kBf16) wk.init_offsets();
   wk.sl2 = p.sl2;
 
   qmajor_drive(p, rb, list, L, wk);

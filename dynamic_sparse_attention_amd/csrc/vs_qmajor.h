@@ -69,7 +69,7 @@ struct QMajorLds {
 };
 
 template <class Worker>
-__device__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list, QMajorLds& L,
+__device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list, QMajorLds& L,
                              Worker& wk) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
