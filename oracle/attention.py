@@ -253,7 +253,7 @@ def bwd_delta(o, do):
 
 
 def bwd_rounding_bounds(q, k, v, do, o, lse, rows_pos, cols_pos, cu_seqlens, index, block=64,
-                        scale=None, u_op=2.0 ** -8, u_o=2.0 ** -8, support=None):
+                        scale=None, u_op=2.0 ** -8, u_o=2.0 ** -8, support=None, row_filter=None):
     """First-order error bounds of a backward whose matrix-core operands P and dS
     are rounded to a format of unit roundoff u_op, with delta formed from an
     output O that was itself computed with P rounded to u_op (O = P V) and
@@ -267,7 +267,8 @@ def bwd_rounding_bounds(q, k, v, do, o, lse, rows_pos, cols_pos, cu_seqlens, ind
       |dV~ - dV| <= u_op P^T |dO|
     (row-wise sums over the support; GQA sums over the group).  Returns
     (bq, bk, bv) shaped like dQ, dK, dV.  ``support`` selects form (ii) when
-    True (default: form (i) for at most 4096 rows).
+    True (default: form (i) for at most 4096 rows).  ``row_filter(seg, beta)``
+    (form (ii) only) keeps the row groups it accepts, as in ``attn_bwd_support``.
     """
     q, k, v, do, o = _f64(q), _f64(k), _f64(v), _f64(do), _f64(o)
     lse = _f64(lse)
@@ -277,6 +278,8 @@ def bwd_rounding_bounds(q, k, v, do, o, lse, rows_pos, cols_pos, cu_seqlens, ind
     hkv = k.shape[1]
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     use_support = (nr > 4096) if support is None else support
+    if row_filter is not None:
+        use_support = True
     D = bwd_delta(o, do)
     bq = np.zeros_like(q)
     bk = np.zeros_like(k)
@@ -301,6 +304,8 @@ def bwd_rounding_bounds(q, k, v, do, o, lse, rows_pos, cols_pos, cu_seqlens, ind
             accumulate(h, g, np.arange(nr), np.arange(cols_pos.size), M)
             continue
         for ri, seg, beta in row_groups(rows_pos, cu_seqlens, block):
+            if row_filter is not None and not row_filter(seg, beta):
+                continue
             ci = support_candidates(seg, beta, rows_pos[ri].max(), cols_pos, cu_seqlens,
                                     index[(h, seg)], block)
             if ci.size == 0:

@@ -1,0 +1,249 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (one call each of the estimator, the forward and the
+backward over the whole sequence; for the striped worker, the 32 ring-step
+calls with the LSE merge and dQ accumulation).
+
+The oracle cannot afford the whole problem, so it checks what it can compute
+one piece at a time:
+  * the estimator: every vertical / slash score and every selected list
+    (the window is only 64 rows per segment);
+  * O, LSE and dQ on sampled whole query blocks (first, second, a seeded
+    middle one, the last two of each segment), all heads;
+  * dK and dV exactly on the last key blocks of each segment: those keys are
+    only seen by the rows of the last blocks, which the oracle computes in
+    full;
+and the rest through identities that hold at any size (MTraining §3.2 Eq. 1:
+rowsum(dA * A) = D makes sum_m dS[n, m] = 0 and, with dQ = scale dS K and
+dK = scale dS^T Q, the GQA group sums <dQ, Q> and <dK, K> agree).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from vs_cases import check_close, index_parity, lists_for_gpu, log, np64
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1200)]
+
+vs = pytest.importorskip("dynamic_sparse_attention_amd")
+
+TAIL = 3  # key blocks per segment whose dK / dV are checked exactly
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _window_q64(prob):
+    """fp64 Q with only the estimator's window rows (last 64 of each segment) filled."""
+    q = np.zeros((prob.n, prob.h_q, prob.d))
+    for s in range(len(prob.cu_seqlens) - 1):
+        e = prob.cu_seqlens[s + 1]
+        a = max(prob.cu_seqlens[s], e - 64)
+        q[a:e] = np64(prob.q[0, a:e])
+    return q
+
+
+def _estimate_and_check(prob, dev, gq, gk, cu):
+    log(f"  oracle estimator (fp64, {prob.h_q} heads, {len(cu) - 1} segments)")
+    oidx, osc = oracle.estimate_index(_window_q64(prob), np64(prob.k[0]), cu, prob.v_budget,
+                                      prob.s_budget, prob.block, 64, return_scores=True)
+    log("  GPU estimator")
+    gidx, vsc, ssc = vs.estimate_index(gq, gk, prob.v_budget, prob.s_budget, cu, return_scores=True)
+    torch.cuda.synchronize()
+    index_parity(prob.name, oidx, osc, [(a.numpy(), b.numpy()) for a, b in gidx.lists()],
+                 vsc[0].cpu().numpy(), ssc[0].cpu().numpy(), prob)
+    return oidx
+
+
+def _sample_blocks(nb, rng):
+    mid = int(rng.integers(2, max(nb - 2, 3)))
+    return sorted({b for b in (0, 1, mid, nb - 2, nb - 1) if 0 <= b < nb})
+
+
+def _rows_of_blocks(starts_blocks):
+    return np.concatenate([np.arange(64 * b, 64 * b + 64) for b in starts_blocks]).astype(np.int64)
+
+
+def _group_identity(name, dq, q, dk, k, h_q, h_kv):
+    """sum_{h in group} <dQ_h, Q_h> == <dK_g, K_g> per KV group (fp64 sums of the GPU tensors).
+
+    Both sides are scale * sum dS[n, m] (q_n . k_m) over the support; the two
+    kernels round their own fp32 dS to bf16 and accumulate in a different
+    order, so they agree to a small fraction of sum |dQ| |Q|.
+    """
+    errs = []
+    for g in range(h_kv):
+        hs = [h for h in range(h_q) if h * h_kv // h_q == g]
+        lhs = sum(float((dq[:, h].double() * q[:, h].double()).sum()) for h in hs)
+        mag = sum(float((dq[:, h].double().abs() * q[:, h].double().abs()).sum()) for h in hs)
+        rhs = float((dk[:, g].double() * k[:, g].double()).sum())
+        rel = abs(lhs - rhs) / max(mag, 1e-30)
+        log(f"  {name} group {g}: <dQ,Q>={lhs:.6e} <dK,K>={rhs:.6e} |diff|/sum|dQ||Q|={rel:.2e}")
+        if rel > 1e-4:
+            errs.append(f"{name} group {g}: identity off by {rel:.2e}")
+    return errs
+
+
+@pytest.mark.parametrize("wid", [2, 3, 5])
+def test_fullsize_contiguous(wid):
+    dev = _dev()
+    log(f"full-size workload {wid}: drawing inputs")
+    prob = workloads.make_problem(wid)
+    cu = prob.cu_seqlens
+    n_seg = len(cu) - 1
+    log(f"  {prob.name}: n={prob.n} hq={prob.h_q} hkv={prob.h_kv} d={prob.d} segments={n_seg}")
+    gq, gk, gv, gdo = (t.to(dev) for t in (prob.q, prob.k, prob.v, prob.do))
+    oidx = _estimate_and_check(prob, dev, gq, gk, cu)
+
+    log("  GPU forward + backward (whole sequence)")
+    idx = vs.index_from_lists(lists_for_gpu(oidx, prob.h_q, n_seg), dev)
+    o, lse = vs.sparse_attn_fwd(gq, gk, gv, idx, cu)
+    dq, dk, dv = vs.sparse_attn_bwd(gq, gk, gv, o, gdo, lse, idx, cu_seqlens=cu)
+    torch.cuda.synchronize()
+
+    k64, v64 = np64(prob.k[0]), np64(prob.v[0])
+    cols = np.arange(prob.n)
+    rng = np.random.default_rng(prob.seed)
+    errs = []
+
+    # sampled query blocks: O, LSE, dQ (with several segments, one block of
+    # each, cycling through first / last / a seeded middle one)
+    blocks = []
+    for s in range(n_seg):
+        a, nb = cu[s] // 64, (cu[s + 1] - cu[s]) // 64
+        pick = _sample_blocks(nb, rng)
+        if n_seg > 1:
+            pick = [(pick[0], pick[-1], pick[len(pick) // 2])[s % 3]]
+        blocks += [a + b for b in pick]
+    rows = _rows_of_blocks(blocks)
+    log(f"  oracle on {len(blocks)} sampled query blocks")
+    q_r, do_r = np64(prob.q[0, rows]), np64(prob.do[0, rows])
+    O, L = oracle.attn_fwd_support(q_r, k64, v64, rows, cols, cu, oidx)
+    D = oracle.bwd_delta(O, do_r)
+    dq_o, _, _ = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, cols, cu, oidx)
+    bq, _, _ = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, oidx, support=True)
+    rt = torch.from_numpy(rows).to(dev)
+    errs += [check_close("O (sampled)", O, np64(o[0, rt]), prob.dtype),
+             check_close("LSE (sampled)", L, np64(lse[0][:, rt]), prob.dtype),
+             check_close("dQ (sampled)", dq_o, np64(dq[0, rt]), prob.dtype, "grad", bq)]
+
+    # the last TAIL key blocks of a segment: only its last TAIL query blocks
+    # see them (first and last segment when there are several)
+    tail_blocks = []
+    for s in sorted({0, n_seg - 1}):
+        b1 = cu[s + 1] // 64
+        tail_blocks += list(range(max(cu[s] // 64, b1 - TAIL), b1))
+    rows = _rows_of_blocks(tail_blocks)
+    log(f"  oracle on the last {TAIL} blocks of each segment ({len(rows)} rows)")
+    q_r, do_r = np64(prob.q[0, rows]), np64(prob.do[0, rows])
+    O, L = oracle.attn_fwd_support(q_r, k64, v64, rows, cols, cu, oidx)
+    D = oracle.bwd_delta(O, do_r)
+    _, dk_o, dv_o = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, cols, cu, oidx)
+    _, bk, bv = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, oidx, support=True)
+    rt = torch.from_numpy(rows).to(dev)
+    errs += [check_close("dK (tail keys)", dk_o[rows], np64(dk[0, rt]), prob.dtype, "grad", bk[rows]),
+             check_close("dV (tail keys)", dv_o[rows], np64(dv[0, rt]), prob.dtype, "grad", bv[rows])]
+
+    errs += _group_identity(prob.name, dq[0], gq[0], dk[0], gk[0], prob.h_q, prob.h_kv)
+    errs = [e for e in errs if e]
+    assert not errs, errs
+
+
+def test_fullsize_striped_worker():
+    """Worker 0 of 32 on the 524288-token sequence: 32 forward calls merged with
+    lse_merge, then 32 backward calls accumulating dQ (Algorithm 2 of the
+    MTraining paper note, run as one worker's share)."""
+    dev = _dev()
+    log("full-size workload 4: drawing inputs")
+    prob = workloads.make_problem(4)
+    W, w = prob.stripe_world, prob.stripe_rank
+    cu = prob.cu_seqlens
+    log(f"  {prob.name}: n={prob.n} world={W} rank={w}")
+    gq_all, gk_all = prob.q.to(dev), prob.k.to(dev)
+    oidx = _estimate_and_check(prob, dev, gq_all, gk_all, cu)
+    del gq_all, gk_all
+    idx = vs.index_from_lists(lists_for_gpu(oidx, prob.h_q, 1), dev)
+
+    rows_all = workloads.stripe_positions(prob.n, W, w).numpy()
+    gq = workloads.stripe_rows(prob.q, W, w).to(dev)
+    gdo = workloads.stripe_rows(prob.do, W, w).to(dev)
+    nq = gq.shape[1]
+    chunks = []
+    for t in range(W):
+        u = (w - t) % W
+        chunks.append((u, workloads.stripe_rows(prob.k, W, u).to(dev),
+                       workloads.stripe_rows(prob.v, W, u).to(dev)))
+    log(f"  GPU: {W} forward calls + merges, {W} backward calls")
+    acc_o = torch.zeros((1, nq, prob.h_q, prob.d), device=dev)
+    acc_l = torch.full((1, prob.h_q, nq), -float("inf"), device=dev)
+    for u, gk, gv in chunks:
+        o, l = vs.sparse_attn_fwd(gq, gk, gv, idx, stripe=(W, w, u), o_f32=True)
+        vs.lse_merge(acc_o, acc_l, o, l)
+    delta = vs.attn_bwd_delta(acc_o, gdo)
+    dq = torch.zeros((1, nq, prob.h_q, prob.d), device=dev)
+    k64, v64 = np64(prob.k[0]), np64(prob.v[0])
+    cols = np.arange(prob.n)
+    nqb = nq // 64
+    # worker rows of its last two local blocks are the only ones that see keys
+    # in global blocks after the worker's third-to-last block
+    tail_local = [nqb - 2, nqb - 1]
+    first_key_blk = rows_all[64 * (nqb - 3)] // 64 + 1
+    dk_tail, dv_tail, key_tail = [], [], []
+    lhs_k = np.zeros(prob.h_kv)
+    for u, gk, gv in chunks:
+        _, dk, dv = vs.sparse_attn_bwd(gq, gk, gv, None, gdo, acc_l, idx, delta=delta, dq=dq,
+                                       stripe=(W, w, u), accumulate=True)
+        kpos = workloads.stripe_positions(prob.n, W, u).numpy()
+        sel = np.nonzero(kpos // 64 >= first_key_blk)[0]
+        st = torch.from_numpy(sel).to(dev)
+        dk_tail.append(np64(dk[0, st]))
+        dv_tail.append(np64(dv[0, st]))
+        key_tail.append(kpos[sel])
+        for g in range(prob.h_kv):
+            lhs_k[g] += float((dk[0, :, g].double() * gk[0, :, g].double()).sum())
+    torch.cuda.synchronize()
+    dk_tail, dv_tail, key_tail = np.concatenate(dk_tail), np.concatenate(dv_tail), np.concatenate(key_tail)
+
+    errs = []
+    rng = np.random.default_rng(prob.seed)
+    lblocks = _sample_blocks(nqb, rng)
+    lrows = _rows_of_blocks(lblocks)
+    rows = rows_all[lrows]
+    log(f"  oracle on worker blocks {lblocks}")
+    q_r, do_r = np64(prob.q[0, rows]), np64(prob.do[0, rows])
+    O, L = oracle.attn_fwd_support(q_r, k64, v64, rows, cols, cu, oidx)
+    D = oracle.bwd_delta(O, do_r)
+    dq_o, _, _ = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, cols, cu, oidx)
+    bq, _, _ = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, oidx,
+                                          u_o=2.0 ** -24, support=True)
+    lt = torch.from_numpy(lrows).to(dev)
+    errs += [check_close("merged O (sampled)", O, np64(acc_o[0, lt]), "bf16"),
+             check_close("merged LSE (sampled)", L, np64(acc_l[0][:, lt]), "bf16"),
+             check_close("accumulated dQ (sampled)", dq_o, np64(dq[0, lt]), "bf16", "grad", bq)]
+
+    lrows = _rows_of_blocks(tail_local)
+    rows = rows_all[lrows]
+    log(f"  oracle on worker blocks {tail_local}: dK / dV of global key blocks >= {first_key_blk}")
+    q_r, do_r = np64(prob.q[0, rows]), np64(prob.do[0, rows])
+    O, L = oracle.attn_fwd_support(q_r, k64, v64, rows, cols, cu, oidx)
+    D = oracle.bwd_delta(O, do_r)
+    _, dk_o, dv_o = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, cols, cu, oidx)
+    _, bk, bv = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, oidx,
+                                           u_o=2.0 ** -24, support=True)
+    errs += [check_close("dK share (tail keys)", dk_o[key_tail], dk_tail, "bf16", "grad", bk[key_tail]),
+             check_close("dV share (tail keys)", dv_o[key_tail], dv_tail, "bf16", "grad", bv[key_tail])]
+
+    for g in range(prob.h_kv):
+        hs = [h for h in range(prob.h_q) if h * prob.h_kv // prob.h_q == g]
+        lhs = sum(float((dq[0, :, h].double() * gq[0, :, h].double()).sum()) for h in hs)
+        mag = sum(float((dq[0, :, h].double().abs() * gq[0, :, h].double().abs()).sum()) for h in hs)
+        rel = abs(lhs - lhs_k[g]) / max(mag, 1e-30)
+        log(f"  ring group {g}: <dQ,Q>={lhs:.6e} sum_u <dK_u,K_u>={lhs_k[g]:.6e} rel={rel:.2e}")
+        if rel > 1e-4:
+            errs.append(f"ring group {g}: identity off by {rel:.2e}")
+    errs = [e for e in errs if e]
+    assert not errs, errs
