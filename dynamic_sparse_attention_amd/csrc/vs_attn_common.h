@@ -45,6 +45,8 @@ struct AttnParams {
   int qranges;        // backward column units: query-block ranges per column tile
   int qrange_len;
   int col_tiles;      // backward column units: column tiles per list
+  int hh_lo, hh_hi;   // backward slash dK/dV: Q heads (within the GQA group) of this launch
+  int kv_accumulate;  // backward slash dK/dV: add to dK/dV instead of storing
   SegTable seg;
 };
 

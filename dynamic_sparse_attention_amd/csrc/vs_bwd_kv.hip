@@ -212,7 +212,8 @@ struct KvWorkerB {
     }
   }
 
-  __device__ __forceinline__ void store(const AttnParams& p, int b, int kvh, int kpos, bool atomic) const {
+  // mode 0: store, 1: add (this thread owns the rows), 2: atomic add
+  __device__ __forceinline__ void store(const AttnParams& p, int b, int kvh, int kpos, int mode) const {
     const int hl = (threadIdx.x & 63) >> 5;
     const size_t off = (((size_t)b * p.n_k + kpos) * p.h_kv + kvh) * D;
 #pragma unroll
@@ -226,12 +227,15 @@ struct KvWorkerB {
           a[u] = dk[ct][4 * i4 + u] * p.scale;
           v[u] = dv[ct][4 * i4 + u];
         }
-        if (atomic) {
+        if (mode == 2) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             atomicAdd(p.dk + off + ch + u, a[u]);
             atomicAdd(p.dv + off + ch + u, v[u]);
           }
+        } else if (mode == 1) {
+          *reinterpret_cast<f32x4*>(p.dk + off + ch) += a;
+          *reinterpret_cast<f32x4*>(p.dv + off + ch) += v;
         } else {
           *reinterpret_cast<f32x4*>(p.dk + off + ch) = a;
           *reinterpret_cast<f32x4*>(p.dv + off + ch) = v;
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_slash_bf16_kernel(AttnPa
   // own, so that the main walk has no masking at all.
   {
     int i = -1;
-    if (tid < G) {
+    if (tid >= p.hh_lo && tid < p.hh_hi) {
       const int list = (b * p.h_q + kvh * G + tid) * p.seg.n_seg + seg;
       const int sp0 = p.s_ptr[list];
       if (p.s_ptr[list + 1] > sp0 && p.s_idx[sp0] == 0) i = local_query_block(p, kb_glob);
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_slash_bf16_kernel(AttnPa
     });
   }
   auto body = [&](const KvBuf<D>& B, int, int) { wk.template tile<false>(B, p.sl2, [](int) { return true; }); };
-  for (int hh = 0; hh < G; ++hh) {
+  for (int hh = p.hh_lo; hh < p.hh_hi; ++hh) {
     const int list = (b * p.h_q + kvh * G + hh) * p.seg.n_seg + seg;
     const int sp0 = p.s_ptr[list];
     const int ns = p.s_ptr[list + 1] - sp0;
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_slash_bf16_kernel(AttnPa
     }
   }
   kv_pipeline<D>(p, L, b, count, tile_of, body);
-  wk.store(p, b, kvh, kpos, false);
+  wk.store(p, b, kvh, kpos, p.kv_accumulate ? 1 : 0);
 }
 
 template <int D>
@@ -442,12 +446,44 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_cols_bf16_kernel(AttnPar
     wk.template tile<true>(B, p.sl2, [&](int r) { return mr <= r; });
   };
   kv_pipeline<D>(p, L, b, ntiles, tile_of, body);
-  if (col_ok) wk.store(p, b, kvh, kpos, true);
+  // Add this wave's dK, dV columns into the gradients: staged through LDS
+  // (the tile buffers are free now) so that each atomic instruction covers
+  // 64 consecutive channels of one key row rather than 32 different rows.
+  float* st = reinterpret_cast<float*>(reinterpret_cast<char*>(&L.buf[0]) + kh * 32 * (D + 4) * 4);
+  const int nvalid = min(max(ncol - 32 * kh, 0), 32);
+  const size_t rstride = (size_t)p.h_kv * D;
+  float* const gdst[2] = {p.dk + ((size_t)b * p.n_k * p.h_kv + kvh) * D,
+                          p.dv + ((size_t)b * p.n_k * p.h_kv + kvh) * D};
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int hl = (tid & 63) >> 5;
+#pragma unroll
+    for (int ct = 0; ct < W::NCT; ++ct)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = t == 0 ? wk.dk[ct][4 * i4 + u] * p.scale : wk.dv[ct][4 * i4 + u];
+        *reinterpret_cast<f32x4*>(st + l32 * (D + 4) + 32 * ct + 8 * i4 + 4 * hl) = v;
+      }
+    wave_sync();
+    for (int r = 0; r < nvalid; ++r) {
+      const int kr = __shfl(kpos, r, 64);
+      float* row = gdst[t] + (size_t)kr * rstride;
+#pragma unroll
+      for (int c0 = 0; c0 < D; c0 += 64) atomicAdd(row + c0 + (tid & 63), st[r * (D + 4) + c0 + (tid & 63)]);
+    }
+    wave_sync();
+  }
 }
 
-hipError_t launch_bwd_kv_bf16(const AttnParams& p, int d, hipStream_t st) {
+hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
+  AttnParams p = p0;
   const dim3 gs((unsigned)(p.batch * p.h_kv * p.nkb));
   const dim3 gc((unsigned)(p.batch * p.h_q * p.seg.n_seg * p.col_tiles * p.qranges));
+  p.hh_lo = 0;
+  p.hh_hi = p.h_q / p.h_kv;
+  p.kv_accumulate = 0;
   if (d == 128) {
     if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128>), gs, dim3(kKvThreads), 0, st, p));
     if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128>), gc, dim3(kKvThreads), 0, st, p));
