@@ -22,20 +22,23 @@
 //     dK, dV of the block are complete at the end and are stored.
 //   * column units: (list, 64 gathered vertical columns, range of query
 //     blocks); added to dK, dV with fp32 atomics after the slash kernel.
+#include <algorithm>
+
 #include "vs_attn_common.h"
 #include "vs_trace.h"
 
 namespace vs {
 
 constexpr int kKvThreads = 128;
-constexpr int kKvTiles = 512;  // tile list capacity per pass
+constexpr int kKvTiles = 512;  // tile list capacity per pass (query blocks)
+constexpr int kTR = 32;        // query rows per staged tile: half a query block
 
 template <int D>
 struct RowTile {
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;       // rows per 1 KiB direct-load instruction
-  static constexpr int BYTES = 64 * D * 2;   // 64 rows
-  static constexpr int NDMA = 64 / RPI;      // direct-load instructions per 64 rows
+  static constexpr int BYTES = kTR * D * 2;  // kTR rows
+  static constexpr int NDMA = kTR / RPI;     // direct-load instructions per tile
   __device__ static __forceinline__ constexpr int swz(int row) { return 2 * (row & 3) + ((row >> 3) & 1); }
   __device__ static __forceinline__ int off(int row, int chunk) {
     return (row / RPI) * 1024 + (row % RPI) * (CPR * 16) + 16 * (chunk ^ swz(row));
@@ -46,22 +49,24 @@ template <int D>
 struct __attribute__((aligned(16))) KvBuf {
   char q[RowTile<D>::BYTES];
   char dout[RowTile<D>::BYTES];
-  float lse2[64];  // LSE * log2(e)
-  float del[64];
+  float lse2[kTR];  // LSE * log2(e)
+  float del[kTR];
 };
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef __attribute__((address_space(1))) void* glb_vptr;
 
-// Direct loads of query tile (local block i, Q head h) into B; each of the two
-// waves issues half of the rows (NDMA instructions) plus one of LSE / delta.
+// Direct loads of query tile (local block i, rows kTR*half .. +kTR, Q head h)
+// into B; each of the two waves issues half of the rows (NDMA / 2
+// instructions) plus one of LSE / delta.
 template <int D>
-__device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, int b, int h, int i) {
+__device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, int b, int h, int i, int half) {
   typedef RowTile<D> RT;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const unsigned rstride = (unsigned)(p.h_q * D);
-  const size_t base = (((size_t)b * p.n_q + (size_t)i * kBlock) * p.h_q + h) * D;
+  const size_t row0 = (size_t)i * kBlock + kTR * half;
+  const size_t base = (((size_t)b * p.n_q + row0) * p.h_q + h) * D;
   const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + base;
   const __bf16* db = reinterpret_cast<const __bf16*>(p.dout) + base;
   const int rsub = lane / RT::CPR;
@@ -73,9 +78,10 @@ __device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, in
     __builtin_amdgcn_global_load_lds((glb_vptr)(qb + eoff), (lds_vptr)(B.q + u * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((glb_vptr)(db + eoff), (lds_vptr)(B.dout + u * 1024), 16, 0, 0);
   }
-  const size_t li = ((size_t)b * p.h_q + h) * p.n_q + (size_t)i * kBlock + lane;
+  const size_t li = ((size_t)b * p.h_q + h) * p.n_q + row0 + lane;
   const float* src = w == 0 ? p.lse2 : p.delta;
-  __builtin_amdgcn_global_load_lds((glb_vptr)(src + li), (lds_vptr)(w == 0 ? B.lse2 : B.del), 4, 0, 0);
+  if (lane < kTR)
+    __builtin_amdgcn_global_load_lds((glb_vptr)(src + li), (lds_vptr)(w == 0 ? B.lse2 : B.del), 4, 0, 0);
 }
 
 template <int D>
@@ -158,57 +164,50 @@ struct KvWorkerB {
     return __builtin_bit_cast(frag, both);
   }
 
-  // One query tile, 32 rows at a time.  kMasked: valid(r) says whether this
-  // lane's key column is visible to row r (else the tile is fully visible).
-  // Masked entries get exponent -inf, so P = dS = 0 there.
+  // One staged query tile of kTR = 32 rows (rows rbase .. rbase + 31 of the
+  // query block).  kMasked: valid(r) says whether this lane's key column is
+  // visible to row r of the block (else the tile is fully visible).  Masked
+  // entries get exponent -inf, so P = dS = 0 there.
   template <bool kMasked, class ValidF>
-  __device__ __forceinline__ void tile(const KvBuf<D>& B, float sl2, ValidF valid) {
+  __device__ __forceinline__ void tile(const KvBuf<D>& B, float sl2, int rbase, ValidF valid) {
     const int lane = threadIdx.x & 63;
     const int hl = lane >> 5;
+    f32x16 s = f32x16{0}, dp = f32x16{0};
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      f32x16 s = f32x16{0}, dp = f32x16{0};
+    for (int c = 0; c < NCD; ++c) {
+      s = MF::mma(row_frag(B.q, 0, c), kB[c], s);
+      dp = MF::mma(row_frag(B.dout, 0, c), vB[c], dp);
+    }
+    frag pf[2], dsf[2];
 #pragma unroll
-      for (int c = 0; c < NCD; ++c) {
-        s = MF::mma(row_frag(B.q, rg, c), kB[c], s);
-        dp = MF::mma(row_frag(B.dout, rg, c), vB[c], dp);
+    for (int c = 0; c < 2; ++c) {
+      // register 8c + e holds tile row 16c + 8hl + e
+      const int r0 = 16 * c + 8 * hl;
+      const f32x4 la = *reinterpret_cast<const f32x4*>(B.lse2 + r0);
+      const f32x4 lb = *reinterpret_cast<const f32x4*>(B.lse2 + r0 + 4);
+      const f32x4 da = *reinterpret_cast<const f32x4*>(B.del + r0);
+      const f32x4 db = *reinterpret_cast<const f32x4*>(B.del + r0 + 4);
+      float pr[8], ds[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float l2 = e < 4 ? la[e] : lb[e - 4];
+        const float dl = e < 4 ? da[e] : db[e - 4];
+        float t = __builtin_fmaf(s[8 * c + e], sl2, -l2);
+        if constexpr (kMasked) t = valid(rbase + r0 + e) ? t : -INFINITY;
+        const float x = fast_exp2(t);
+        pr[e] = x;
+        ds[e] = x * (dp[8 * c + e] - dl);
       }
-      // keep the phases of the tile apart: hoisting the LDS reads of later
-      // phases ahead of the products costs more registers than there are
-      __builtin_amdgcn_sched_barrier(0);
-      frag pf[2], dsf[2];
+      pf[c] = MF::pack(pr);
+      dsf[c] = MF::pack(ds);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        // register 8c + e holds row 32rg + 16c + 8hl + e
-        const int r0 = 32 * rg + 16 * c + 8 * hl;
-        const f32x4 la = *reinterpret_cast<const f32x4*>(B.lse2 + r0);
-        const f32x4 lb = *reinterpret_cast<const f32x4*>(B.lse2 + r0 + 4);
-        const f32x4 da = *reinterpret_cast<const f32x4*>(B.del + r0);
-        const f32x4 db = *reinterpret_cast<const f32x4*>(B.del + r0 + 4);
-        float pr[8], ds[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float l2 = e < 4 ? la[e] : lb[e - 4];
-          const float dl = e < 4 ? da[e] : db[e - 4];
-          float t = __builtin_fmaf(s[8 * c + e], sl2, -l2);
-          if constexpr (kMasked) t = valid(r0 + e) ? t : -INFINITY;
-          const float x = fast_exp2(t);
-          pr[e] = x;
-          ds[e] = x * (dp[8 * c + e] - dl);
-        }
-        pf[c] = MF::pack(pr);
-        dsf[c] = MF::pack(ds);
+        dv[ct] = MF::mma(tr_frag(B.dout, ct, c), pf[c], dv[ct]);
+        dk[ct] = MF::mma(tr_frag(B.q, ct, c), dsf[c], dk[ct]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          dv[ct] = MF::mma(tr_frag(B.dout, ct, 2 * rg + c), pf[c], dv[ct]);
-          dk[ct] = MF::mma(tr_frag(B.q, ct, 2 * rg + c), dsf[c], dk[ct]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -259,34 +258,39 @@ struct KvLdsB {
 template <int D, class BodyF>
 __device__ __forceinline__ void kv_step(const AttnParams& p, KvBuf<D>* __restrict__ nxt,
                                         const KvBuf<D>* __restrict__ cur, bool more, int b, int h1,
-                                        int i1, int t, int fl, BodyF& body) {
-  if (more) kv_tile_dma<D>(p, *nxt, b, h1, i1);
-  body(*cur, t, fl);
+                                        int i1, int half1, int t, int fl, int half, BodyF& body) {
+  if (more) kv_tile_dma<D>(p, *nxt, b, h1, i1, half1);
+  body(*cur, t, fl, half);
 }
 
+// Double-buffered walk over the two halves of ntiles query blocks:
+// tile_of(t) -> (h, i, flags), body(B, t, flags, half) computes on the staged
+// half tile.
 template <int D, class TileF, class BodyF>
 __device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D>& L, int b, int ntiles,
                                             TileF tile_of, BodyF body) {
   if (ntiles == 0) return;
   int h, i, fl;
   tile_of(0, &h, &i, &fl);
-  kv_tile_dma<D>(p, L.buf[0], b, h, i);
-  for (int t = 0; t < ntiles; ++t) {
-    // this wave's loads of tile t are done; the barrier makes every wave's
-    // loads visible and frees the other buffer (its tile t-1 compute is over)
+  kv_tile_dma<D>(p, L.buf[0], b, h, i, 0);
+  const int nu = 2 * ntiles;
+  for (int u = 0; u < nu; ++u) {
+    // this wave's loads of step u are done; the barrier makes every wave's
+    // loads visible and frees the other buffer (its step u-1 compute is over)
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
     __syncthreads();
     int h1 = 0, i1 = 0, fl1;
-    const bool more = t + 1 < ntiles;
-    if (more) tile_of(t + 1, &h1, &i1, &fl1);
-    tile_of(t, &h, &i, &fl);
-    kv_step<D>(p, &L.buf[(t + 1) & 1], &L.buf[t & 1], more, b, h1, i1, t, fl, body);
+    const bool more = u + 1 < nu;
+    if (more) tile_of((u + 1) >> 1, &h1, &i1, &fl1);
+    tile_of(u >> 1, &h, &i, &fl);
+    kv_step<D>(p, &L.buf[(u + 1) & 1], &L.buf[u & 1], more, b, h1, i1, (u + 1) & 1, u >> 1, fl,
+               u & 1, body);
   }
   __syncthreads();
 }
 
 template <int D>
-__global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_slash_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_kv_slash_bf16_kernel(AttnParams p) {
   typedef KvWorkerB<D> W;
   __shared__ KvLdsB<D> L;
   const int tid = threadIdx.x;
@@ -337,11 +341,13 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_slash_bf16_kernel(AttnPa
     const int slot = block_compact<kKvThreads>(i >= 0, L.wsum, &tot);
     if (i >= 0) L.tiles[slot] = (tid << 26) | (i << 1) | 1;
     __syncthreads();
-    kv_pipeline<D>(p, L, b, tot, tile_of, [&](const KvBuf<D>& B, int, int) {
-      wk.template tile<true>(B, p.sl2, [&](int r) { return kin <= r; });
+    kv_pipeline<D>(p, L, b, tot, tile_of, [&](const KvBuf<D>& B, int, int, int half) {
+      wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) { return kin <= r; });
     });
   }
-  auto body = [&](const KvBuf<D>& B, int, int) { wk.template tile<false>(B, p.sl2, [](int) { return true; }); };
+  auto body = [&](const KvBuf<D>& B, int, int, int half) {
+    wk.template tile<false>(B, p.sl2, kTR * half, [](int) { return true; });
+  };
   for (int hh = p.hh_lo; hh < p.hh_hi; ++hh) {
     const int list = (b * p.h_q + kvh * G + hh) * p.seg.n_seg + seg;
     const int sp0 = p.s_ptr[list];
@@ -369,10 +375,10 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_slash_bf16_kernel(AttnPa
 }
 
 template <int D>
-__global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_cols_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_kv_cols_bf16_kernel(AttnParams p) {
   typedef KvWorkerB<D> W;
   __shared__ KvLdsB<D> L;
-  __shared__ uint32_t bits[2048];
+  extern __shared__ uint32_t bits[];  // (nb_seg + 31) / 32 words, sized at launch
   const int tid = threadIdx.x;
   const int kh = tid >> 6;
   const int l32 = tid & 31;
@@ -436,45 +442,41 @@ __global__ __launch_bounds__(kKvThreads) void vs_bwd_kv_cols_bf16_kernel(AttnPar
     *fl = 0;
   };
   const int ntiles = r_hi - r_lo;
-  auto body = [&](const KvBuf<D>& B, int t, int) {
+  auto body = [&](const KvBuf<D>& B, int t, int, int half) {
     const int qbg = qglob(r_lo + t);
     const int beta_q = qbg - a_blk;
     const int off = beta_q - bm;
     const bool lane_ok = col_ok && off >= 0 && ((bits[off >> 5] >> (off & 31)) & 1u) == 0u;
     const int row0 = qbg * kBlock;
     const int mr = lane_ok ? m - row0 : 64;  // first visible row
-    wk.template tile<true>(B, p.sl2, [&](int r) { return mr <= r; });
+    wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) { return mr <= r; });
   };
   kv_pipeline<D>(p, L, b, ntiles, tile_of, body);
-  // Add this wave's dK, dV columns into the gradients: staged through LDS
-  // (the tile buffers are free now) so that each atomic instruction covers
-  // 64 consecutive channels of one key row rather than 32 different rows.
-  float* st = reinterpret_cast<float*>(reinterpret_cast<char*>(&L.buf[0]) + kh * 32 * (D + 4) * 4);
+  // Add this wave's dK, dV columns into the gradients, staged through LDS
+  // (the tile buffers are free now) one 32-channel slice at a time, so that
+  // each atomic instruction covers 32 consecutive channels of two key rows
+  // rather than single channels of 32 different rows.
+  float* st = reinterpret_cast<float*>(reinterpret_cast<char*>(&L.buf[0]) + kh * 32 * 33 * 4);
   const int nvalid = min(max(ncol - 32 * kh, 0), 32);
   const size_t rstride = (size_t)p.h_kv * D;
   float* const gdst[2] = {p.dk + ((size_t)b * p.n_k * p.h_kv + kvh) * D,
                           p.dv + ((size_t)b * p.n_k * p.h_kv + kvh) * D};
+  const int hl = (tid & 63) >> 5;
+  const int c32 = tid & 31;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int hl = (tid & 63) >> 5;
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int ct = 0; ct < W::NCT; ++ct)
+    for (int ct = 0; ct < W::NCT; ++ct) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        f32x4 v;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = t == 0 ? wk.dk[ct][4 * i4 + u] * p.scale : wk.dv[ct][4 * i4 + u];
-        *reinterpret_cast<f32x4*>(st + l32 * (D + 4) + 32 * ct + 8 * i4 + 4 * hl) = v;
+      for (int i = 0; i < 16; ++i)
+        st[l32 * 33 + c_row(i, hl)] = t == 0 ? wk.dk[ct][i] * p.scale : wk.dv[ct][i];
+      wave_sync();
+      for (int r = hl; r < nvalid; r += 2) {
+        const int kr = __shfl(kpos, r, 64);
+        atomicAdd(gdst[t] + (size_t)kr * rstride + 32 * ct + c32, st[r * 33 + c32]);
       }
-    wave_sync();
-    for (int r = 0; r < nvalid; ++r) {
-      const int kr = __shfl(kpos, r, 64);
-      float* row = gdst[t] + (size_t)kr * rstride;
-#pragma unroll
-      for (int c0 = 0; c0 < D; c0 += 64) atomicAdd(row + c0 + (tid & 63), st[r * (D + 4) + c0 + (tid & 63)]);
+      wave_sync();
     }
-    wave_sync();
-  }
 }
 
 hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
@@ -484,12 +486,17 @@ hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
   p.hh_lo = 0;
   p.hh_hi = p.h_q / p.h_kv;
   p.kv_accumulate = 0;
+  // bitmap of the selected block-diagonals: one bit per block of the longest segment
+  int nb_max = p.W == 1 ? 0 : p.n_global / kBlock;
+  for (int sgi = 0; p.W == 1 && sgi < p.seg.n_seg; ++sgi)
+    nb_max = std::max(nb_max, p.seg.start_blk[sgi + 1] - p.seg.start_blk[sgi]);
+  const size_t bits_bytes = (size_t)((nb_max + 31) / 32) * 4 + 4;
   if (d == 128) {
     if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128>), gs, dim3(kKvThreads), 0, st, p));
-    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128>), gc, dim3(kKvThreads), 0, st, p));
+    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128>), gc, dim3(kKvThreads), bits_bytes, st, p));
   } else {
     if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64>), gs, dim3(kKvThreads), 0, st, p));
-    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64>), gc, dim3(kKvThreads), 0, st, p));
+    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64>), gc, dim3(kKvThreads), bits_bytes, st, p));
   }
   return hipGetLastError();
 }
