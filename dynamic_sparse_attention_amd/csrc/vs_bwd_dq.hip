@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kQThreads) void vs_bwd_dq_bf16_kernel(AttnParams p)
   constexpr int OB_PITCH = D + 4;
   constexpr int OB_BYTES = 64 * OB_PITCH * 4;
   constexpr int BUF = KT_BYTES > OB_BYTES ? KT_BYTES : OB_BYTES;
-  __shared__ QMajorLds L;
+  __shared__ QMajorLds<> L;
   __shared__ __attribute__((aligned(16))) char buf[BUF];
 
   int hb, i_local;

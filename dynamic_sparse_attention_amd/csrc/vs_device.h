@@ -104,7 +104,24 @@ __device__ __forceinline__ void dma_lds16(const void* gptr, const void* lds_base
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(m0) : "memory");
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine every lane's value with lane i ^ 32's (the two halves of a wave):
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second, so with both operands x the pair holds x[i] and
+// x[i ^ 32] in every lane, without a round trip through LDS.  (Written as
+// inline assembly: the compiler builtin returns the first register twice.)
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float half_max(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
+}
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

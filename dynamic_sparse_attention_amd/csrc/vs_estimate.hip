@@ -85,13 +85,13 @@ __global__ __launch_bounds__(256) void vs_est_pass1_kernel(AttnParams p, TilePre
           tt[i] = (key < k1 && key <= row) ? sc[i] * p.sl2 : -INFINITY;
           mx = fmaxf(mx, tt[i]);
         }
-        mx = fmaxf(mx, xor32(mx));
+        mx = half_max(mx);
         const float mn = fmaxf(m[rg], mx);
         const float mu = mn == -INFINITY ? 0.f : mn;
         float rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) rs += fast_exp2(tt[i] - mu);
-        rs += xor32(rs);
+        rs = half_sum(rs);
         l[rg] = l[rg] * fast_exp2(m[rg] - mu) + rs;
         m[rg] = mn;
       }
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePre
           col += (key < k1 && key <= row) ? fast_exp2(sc[i] * p.sl2 - s_lse[wave][rr]) : 0.f;
         }
       }
-      col += xor32(col);
+      col = half_sum(col);
       if (hl == 0 && key < k1) v_score[((size_t)b * p.h_q + h) * p.n_global + key] = col;
       float bs = hl == 0 ? col : 0.f;
 #pragma unroll

@@ -234,7 +234,7 @@ struct FwdWorker {
       float mx = s[rg][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[rg][i]);
-      mx = fmaxf(mx, xor32(mx));
+      mx = half_max(mx);
       tm[rg] = mx * sl2;
     }
     const bool grow = tm[0] > m[0] + kRescale || tm[1] > m[1] + kRescale;
@@ -264,7 +264,7 @@ struct FwdWorker {
         p[i] = fast_exp2(__builtin_fmaf(s[rg][i], sl2, -mu));
         rs += p[i];
       }
-      rs += xor32(rs);
+      rs = half_sum(rs);
       l[rg] += rs;
 #pragma unroll
       for (int c = 0; c < NCK; ++c) pf[rg][c] = MF::pack(&p[c * KPL]);
@@ -380,7 +380,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
   typedef FwdWorker<T, D> W;
   typedef FwdLds<T, D> LD;
-  __shared__ QMajorLds L;
+  __shared__ QMajorLds<> L;
   __shared__ __attribute__((aligned(16))) char buf[LD::BUF0];
   __shared__ __attribute__((aligned(16))) char tk1[LD::TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char tv0[LD::TILE_BYTES];

@@ -27,6 +27,7 @@ struct SlashSet {
   int tot;
   int wave;
   __device__ __forceinline__ int n_halves() const { return tot > wave ? 2 * ((tot - wave + 3) >> 2) : 0; }
+  __device__ __forceinline__ int n_halves_max() const { return tot > 0 ? 2 * ((tot + 3) >> 2) : 0; }
   __device__ __forceinline__ int tv(int n) const { return tiles[wave + 4 * (n >> 1)]; }
   __device__ __forceinline__ int key_pos(int n, int r) const { return (tv(n) >> 1) * kBlock + 32 * (n & 1) + r; }
   __device__ __forceinline__ bool full(int n) const { return (tv(n) & 1) == 0; }
@@ -41,6 +42,7 @@ struct ColSet {
   int nt;            // 64-column tiles in the list
   int wave;
   __device__ __forceinline__ int n_halves() const { return nt > wave ? 2 * ((nt - wave + 3) >> 2) : 0; }
+  __device__ __forceinline__ int n_halves_max() const { return nt > 0 ? 2 * ((nt + 3) >> 2) : 0; }
   __device__ __forceinline__ int base(int n) const { return 64 * (wave + 4 * (n >> 1)) + 32 * (n & 1); }
   __device__ __forceinline__ int key_pos(int n, int r) const {
     const int i = base(n) + r;
@@ -60,34 +62,37 @@ struct ColSet {
   }
 };
 
+template <int NT = kQThreads>
 struct QMajorLds {
   uint32_t bits[kMaxBitWords];
-  int tiles[kQThreads];
-  int cols[2 * kQThreads];
-  int coff[2 * kQThreads];
-  int wsum[kQThreads / 64];
+  int tiles[NT];
+  int cols[2 * NT];
+  int coff[2 * NT];
+  int wsum[NT / 64];
 };
 
-template <class Worker>
-__device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list, QMajorLds& L,
-                             Worker& wk) {
+// NT threads; wave w consumes the tiles of key stream w % 4 (with 8 waves,
+// waves w and w + 4 share a stream and split its rows).
+template <int NT, class Worker>
+__device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list,
+                                             QMajorLds<NT>& L, Worker& wk) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = (tid >> 6) & 3;
   const int sp0 = p.s_ptr[list];
   const int ns = p.s_ptr[list + 1] - sp0;
 
   // Bitmap of the selected block-diagonals, for the "already covered" test.
   const int nwords = (rb.nb_seg + 31) >> 5;
-  for (int w = tid; w < nwords; w += kQThreads) L.bits[w] = 0u;
+  for (int w = tid; w < nwords; w += NT) L.bits[w] = 0u;
   __syncthreads();
-  for (int e = tid; e < ns; e += kQThreads) {
+  for (int e = tid; e < ns; e += NT) {
     const int g = p.s_idx[sp0 + e];
     if (g >= 0 && g < rb.nb_seg) atomicOr(&L.bits[g >> 5], 1u << (g & 31));
   }
   __syncthreads();
 
   // Slash tiles: key block beta - g for every selected g <= beta.
-  for (int base = 0; base < ns; base += kQThreads) {
+  for (int base = 0; base < ns; base += NT) {
     const int e = base + tid;
     int j = -1, diag = 0;
     if (e < ns) {
@@ -98,7 +103,7 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
       }
     }
     int tot;
-    const int slot = block_compact<kQThreads>(j >= 0, L.wsum, &tot);
+    const int slot = block_compact<NT>(j >= 0, L.wsum, &tot);
     if (j >= 0) L.tiles[slot] = 2 * j + diag;
     __syncthreads();
     wk.run(SlashSet{L.tiles, tot, wave});
@@ -117,7 +122,7 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
   const int vlimit = lo;
   int count = 0, e0 = 0;
   while (true) {
-    while (count < kQThreads && e0 < vlimit) {
+    while (count < NT && e0 < vlimit) {
       const int e = e0 + tid;
       bool keep = false;
       int m = 0, bm = 0;
@@ -128,13 +133,13 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
         keep = ((L.bits[off >> 5] >> (off & 31)) & 1u) == 0u;
       }
       int tot;
-      const int slot = block_compact<kQThreads>(keep, L.wsum, &tot);
+      const int slot = block_compact<NT>(keep, L.wsum, &tot);
       if (keep) {
         L.cols[count + slot] = local_key_pos(p, m);
         L.coff[count + slot] = (bm == rb.beta) ? (m - rb.qb_glob * kBlock) : -1;
       }
       count += tot;
-      e0 += kQThreads;
+      e0 += NT;
       __syncthreads();
     }
     const bool last = e0 >= vlimit;
