@@ -380,7 +380,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
   typedef FwdWorker<T, D> W;
   typedef FwdLds<T, D> LD;
-  __shared__ QMajorLds<> L;
+  // fp32 needs most of the LDS for its staging buffers: smaller column batches
+  __shared__ QMajorLds<kQThreads, sizeof(T) == 2 ? kColBatch : 2 * kQThreads> L;
   __shared__ __attribute__((aligned(16))) char buf[LD::BUF0];
   __shared__ __attribute__((aligned(16))) char tk1[LD::TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char tv0[LD::TILE_BYTES];

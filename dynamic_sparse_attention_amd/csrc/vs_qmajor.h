@@ -62,20 +62,26 @@ struct ColSet {
   }
 };
 
-template <int NT = kQThreads>
+// Selected vertical columns are gathered in batches of up to kColBatch
+// (16 tiles of 64 columns, four per wave with 256 threads), so that each
+// pipelined walk over a batch has several tiles per wave to overlap.
+constexpr int kColBatch = 1024;
+
+template <int NT = kQThreads, int NCOL = kColBatch>
 struct QMajorLds {
+  static constexpr int kCols = NCOL;
   uint32_t bits[kMaxBitWords];
   int tiles[NT];
-  int cols[2 * NT];
-  int coff[2 * NT];
+  int cols[NCOL];
+  int coff[NCOL];
   int wsum[NT / 64];
 };
 
 // NT threads; wave w consumes the tiles of key stream w % 4 (with 8 waves,
 // waves w and w + 4 share a stream and split its rows).
-template <int NT, class Worker>
+template <int NT, int NCOL, class Worker>
 __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list,
-                                             QMajorLds<NT>& L, Worker& wk) {
+                                             QMajorLds<NT, NCOL>& L, Worker& wk) {
   const int tid = threadIdx.x;
   const int wave = (tid >> 6) & 3;
   const int sp0 = p.s_ptr[list];
@@ -122,7 +128,7 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
   const int vlimit = lo;
   int count = 0, e0 = 0;
   while (true) {
-    while (count < NT && e0 < vlimit) {
+    while (count <= NCOL - NT && e0 < vlimit) {
       const int e = e0 + tid;
       bool keep = false;
       int m = 0, bm = 0;
