@@ -104,6 +104,19 @@ __device__ __forceinline__ void dma_lds16(const void* gptr, const void* lds_base
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(m0) : "memory");
 }
 
+// Same, addressed as a wave-uniform 64-bit base plus a per-lane 32-bit byte
+// offset (no 64-bit address arithmetic per lane), into LDS at byte address
+// m0 (wave-uniform, from lds_addr()).
+__device__ __forceinline__ void dma_lds16_so(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array, wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+
 // Combine every lane's value with lane i ^ 32's (the two halves of a wave):
 // v_permlane32_swap exchanges the upper half of its first operand with the
 // lower half of its second, so with both operands x the pair holds x[i] and

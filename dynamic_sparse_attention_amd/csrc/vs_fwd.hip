@@ -65,6 +65,7 @@ struct FwdWorker {
   // operand reads, so that the per-read part is an immediate offset.
   char* kl[2];
   char* vl[2];
+  uint32_t kla[2], vla[2];  // their LDS byte addresses (wave-uniform)
   int ro[4];
   int to[2];
   f32x4 vr[kBf16 ? 1 : NVG * KG];   // fp32 path: raw V rows of the next half-tile
@@ -111,24 +112,26 @@ struct FwdWorker {
   // bf16: the 32 rows (K or V, from src) of half n straight into tile dst
   // (asynchronous; NVL vector-memory instructions).
   template <class Set>
-  __device__ __forceinline__ void dma_rows(const Set& S, int n, const T* src, char* dst) const {
+  __device__ __forceinline__ void dma_rows(const Set& S, int n, const T* src, uint32_t dst) const {
     const int lane = threadIdx.x & 63;
     const int rr = lane / CPR;
     if constexpr (Set::kContiguous) {
-      const T* p0 = src + (unsigned)S.key_pos(n, rr) * (unsigned)kvs;
+      const uint32_t o0 = (uint32_t)S.key_pos(n, rr) * (uint32_t)(kvs * sizeof(T));
 #pragma unroll
       for (int u = 0; u < NVL; ++u) {
         const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
-        dma_lds16(p0 + (unsigned)(u * RPI * kvs) + chunk * 8, dst + u * 1024);
+        dma_lds16_so(src, o0 + (uint32_t)(u * RPI * kvs * sizeof(T)) + chunk * 16, dst + u * 1024);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < NVL; ++u) {
         const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
-        dma_lds16(src + (unsigned)S.key_pos(n, rr + u * RPI) * (unsigned)kvs + chunk * 8, dst + u * 1024);
+        dma_lds16_so(src, (uint32_t)S.key_pos(n, rr + u * RPI) * (uint32_t)(kvs * sizeof(T)) + chunk * 16,
+                     dst + u * 1024);
       }
     }
   }
+
 
   // bf16: A operand of S^T = K Q^T from a K tile: key slot_perm(L%32), chunk 2c + L/32.
   __device__ __forceinline__ frag k_frag(const char* src, int c) const {
@@ -315,7 +318,7 @@ struct FwdWorker {
   __device__ __forceinline__ void step2(const Set& S, int n, int N, f32x16 (&s)[2]) {
     frag pf[2][NCK];
     const int n2 = n + 2 < N ? n + 2 : N - 1;
-    dma_rows(S, n2, kb, kl[P]);
+    dma_rows(S, n2, kb, kla[P]);
     __builtin_amdgcn_sched_barrier(0);
     softmax_max(S, n, s);
     softmax_exp(s, pf);
@@ -326,7 +329,7 @@ struct FwdWorker {
     pv(vl[P], pf);
     // the reads of V(n) are done before V(n+2) may land in their place
     __builtin_amdgcn_s_waitcnt(lgkmcnt_wait0());
-    dma_rows(S, n2, vb, vl[P]);
+    dma_rows(S, n2, vb, vla[P]);
   }
 
   template <class Set>
@@ -336,10 +339,10 @@ struct FwdWorker {
     if constexpr (kBf16) {
       f32x16 s[2];
       const int n1 = N > 1 ? 1 : 0;
-      dma_rows(S, 0, kb, kl[0]);
-      dma_rows(S, 0, vb, vl[0]);
-      dma_rows(S, n1, kb, kl[1]);
-      dma_rows(S, n1, vb, vl[1]);
+      dma_rows(S, 0, kb, kla[0]);
+      dma_rows(S, 0, vb, vla[0]);
+      dma_rows(S, n1, kb, kla[1]);
+      dma_rows(S, n1, vb, vla[1]);
       __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * NVL));
       wave_sync();
       scores_lds(kl[0], s);
@@ -424,7 +427,13 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
   wk.kl[1] = tk1 + wave * 32 * D * 2;
   wk.vl[0] = tv0 + wave * 32 * D * 2;
   wk.vl[1] = tv1 + wave * 32 * D * 2;
-  if constexpr (W::kBf16) wk.init_offsets();
+  if constexpr (W::kBf16) {
+    wk.init_offsets();
+    for (int i = 0; i < 2; ++i) {
+      wk.kla[i] = lds_addr(wk.kl[i]);
+      wk.vla[i] = lds_addr(wk.vl[i]);
+    }
+  }
   wk.sl2 = p.sl2;
 
   qmajor_drive(p, rb, list, L, wk);

@@ -97,6 +97,44 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
   }
   __syncthreads();
 
+  // Vertical list: its length below the causal limit and its first chunks
+  // are fetched before the slash walk, so that their latency hides behind it.
+  const int vc = p.vcnt[list];
+  const int* vs = p.vsel + (size_t)list * p.vsel_stride;
+  const int lim_pos = (rb.qb_glob + 1) * kBlock;
+  // vlimit = number of entries < lim_pos (the list is ascending), found by an
+  // NT-ary search: every round samples NT evenly spaced entries of [lo, hi)
+  // at once, so two rounds of loads cover lists of up to NT^2 entries.
+  int lo = 0, hi = vc;  // entries below lo are < lim_pos, from hi on >= lim_pos
+  while (lo < hi) {
+    const int S = (hi - lo + NT - 1) / NT;
+    const int e = lo + tid * S;
+    const bool lt = e < hi && vs[e] < lim_pos;
+    int k;
+    block_compact<NT>(lt, L.wsum, &k);  // the true flags form a prefix
+    __syncthreads();                    // L.wsum is reused by the next round
+    if (k == 0) {
+      hi = lo;
+    } else {
+      const int nlo = lo + (k - 1) * S + 1;
+      hi = min(lo + k * S, hi);
+      lo = nlo;
+    }
+  }
+  const int vlimit = lo;
+  // R chunks of NT candidates per batch: at most R*NT + 63 gathered columns
+  constexpr int R = NCOL / NT - 1;
+  static_assert(R >= 1, "column batch too small");
+  int mv[R];
+  auto fetch = [&](int e0) {
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      const int e = e0 + c * NT + tid;
+      mv[c] = e < vlimit ? vs[e] : 0;
+    }
+  };
+  fetch(0);
+
   // Slash tiles: key block beta - g for every selected g <= beta.
   for (int base = 0; base < ns; base += NT) {
     const int e = base + tid;
@@ -116,25 +154,19 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
     __syncthreads();
   }
 
-  // Column tiles: verticals m < 64*(qb+1) not covered by a selected block.
-  const int vc = p.vcnt[list];
-  const int* vs = p.vsel + (size_t)list * p.vsel_stride;
-  const int lim_pos = (rb.qb_glob + 1) * kBlock;
-  int lo = 0, hi = vc;  // first entry >= lim_pos
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (vs[mid] < lim_pos) lo = mid + 1; else hi = mid;
-  }
-  const int vlimit = lo;
+  // Column tiles: verticals m < 64*(qb+1) not covered by a selected block,
+  // gathered R chunks at a time; the next R chunks are fetched while the
+  // current batch is walked.
   int count = 0, e0 = 0;
-  while (true) {
-    while (count <= NCOL - NT && e0 < vlimit) {
-      const int e = e0 + tid;
+  while (e0 < vlimit) {
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      if (e0 + c * NT >= vlimit) break;  // uniform
+      const int e = e0 + c * NT + tid;
       bool keep = false;
-      int m = 0, bm = 0;
+      const int m = mv[c];
+      const int bm = m / kBlock - rb.a_blk;
       if (e < vlimit) {
-        m = vs[e];
-        bm = m / kBlock - rb.a_blk;
         const int off = rb.beta - bm;
         keep = ((L.bits[off >> 5] >> (off & 31)) & 1u) == 0u;
       }
@@ -145,10 +177,11 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
         L.coff[count + slot] = (bm == rb.beta) ? (m - rb.qb_glob * kBlock) : -1;
       }
       count += tot;
-      e0 += NT;
       __syncthreads();
     }
+    e0 += R * NT;
     const bool last = e0 >= vlimit;
+    if (!last) fetch(e0);
     const int nt = last ? (count + 63) / 64 : count / 64;
     wk.run(ColSet{L.cols, L.coff, last ? count : 64 * nt, nt, wave});
     if (last) break;
