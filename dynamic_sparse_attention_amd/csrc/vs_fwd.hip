@@ -15,6 +15,8 @@
 // product from registers (slot_perm).  Softmax state is fp32; P is rounded
 // to bf16 for the matrix cores when the inputs are bf16.  The four waves'
 // (max, sum, O) merge through LDS at the end.
+#include <algorithm>
+
 #include "vs_qmajor.h"
 #include "vs_trace.h"
 
@@ -513,10 +515,359 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
   }
 }
 
+// bf16 forward with the rows split over waves: a workgroup of 2*NS waves
+// serves NS key streams; waves w and w + NS take stream w % NS for query
+// rows 32 (w / NS) .. +31, so the two waves of a stream share every K and V
+// tile and each issues half of its direct loads.  One workgroup barrier per
+// half-tile publishes both halves of the loads and frees the other buffer of
+// the ring of two.  Each wave keeps Q^T of its 32 rows in registers (about
+// 250 registers in all, so two waves fit on a SIMD); per half-tile
+// S^T = K Q^T reads K row-wise from LDS, the online softmax runs on the 16
+// scores per lane, and O^T += V^T P^T reads V transposed (ds_read_b64_tr_b16)
+// with P^T taken from registers (slot_perm).  With NS = 2 a workgroup needs
+// under 80 KB of LDS, so two independent workgroups share a CU: one's index
+// expansion, waits and output merge overlap the other's products.
+
+template <int D>
+struct FwdRowsWorker {
+  typedef Mfma<__bf16> MF;
+  typedef MF::frag frag;
+  static constexpr int KPL = MF::KPL;
+  static constexpr int KC = 2 * KPL;
+  static constexpr int NCD = D / KC;   // k chunks over head_dim
+  static constexpr int NCT = D / 32;   // 32-channel output tiles
+  static constexpr int NCK = 32 / KC;  // k chunks over 32 keys
+  static constexpr int CPR = D / 8;    // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR; // rows per 1 KiB direct load
+  static constexpr int NVL = 32 / RPI; // direct loads per 32-row tile
+  static constexpr int NVH = NVL / 2;  // ... issued by each wave of a stream
+  static constexpr int TB = 32 * D * 2;
+  static constexpr float kRescale = 8.f;
+  __device__ static constexpr int swz(int r) { return 2 * (r & 3) + ((r >> 3) & 1); }
+
+  frag qf[NCD];   // Q^T of this wave's 32 rows
+  f32x16 o[NCT];  // O^T [channel][row]
+  float m, l;     // this lane's row: running max (exp2 domain) and sum
+  int ro[4];
+  int to[2];
+  const char* kt[2];      // this stream's K tiles (ring of two)
+  const char* vt[2];
+  uint32_t kta[2], vta[2];
+  const __bf16* kb;
+  const __bf16* vb;
+  int kvs;
+  int rh;                 // row half of this wave
+  float sl2;
+
+  __device__ __forceinline__ void init_offsets() {
+    const int lane = threadIdx.x & 63;
+    const int hl = lane >> 5;
+    const int sp = slot_perm<KPL>(lane & 31);
+#pragma unroll
+    for (int cl = 0; cl < 4; ++cl) ro[cl] = sp * (CPR * 16) + 16 * ((2 * cl + hl) ^ swz(sp));
+    const int g = lane >> 4;
+    const int sg = lane & 15;
+    const int rr = sg >> 2;
+    const int x = 2 * (g & 1) + ((sg & 3) >> 1);
+    const int z = x ^ (2 * rr + hl);
+    const int base = (8 * hl + rr) * (CPR * 16) + 16 * (z & 3) + 8 * (sg & 1);
+    to[0] = base + 64 * (z >> 2);
+    to[1] = base + 64 * (1 - (z >> 2));
+  }
+
+  // This wave's half of the direct loads of the 32 rows (K or V, from src) of
+  // half n into the tile at LDS address dst.
+  template <class Set>
+  __device__ __forceinline__ void dma_half(const Set& S, int n, const __bf16* src, uint32_t dst) const {
+    const int lane = threadIdx.x & 63;
+    const int rr = lane / CPR;
+    const uint32_t rb = (uint32_t)(kvs * 2);
+    if constexpr (Set::kContiguous) {
+      const uint32_t o0 = (uint32_t)S.key_pos(n, rh * NVH * RPI + rr) * rb;
+#pragma unroll
+      for (int u0 = 0; u0 < NVH; ++u0) {
+        const int u = rh * NVH + u0;
+        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
+        dma_lds16_so(src, o0 + (uint32_t)(u0 * RPI) * rb + chunk * 16, dst + u * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int u0 = 0; u0 < NVH; ++u0) {
+        const int u = rh * NVH + u0;
+        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
+        dma_lds16_so(src, (uint32_t)S.key_pos(n, u * RPI + rr) * rb + chunk * 16, dst + u * 1024);
+      }
+    }
+  }
+
+  __device__ __forceinline__ frag k_frag(const char* src, int c) const {
+    return *reinterpret_cast<const frag*>(src + ro[c & 3] + 128 * (c >> 2));
+  }
+
+  // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of
+  // the 8 bytes read by lanes i/4, 4+i/4, 8+i/4, 12+i/4, i.e. channel
+  // 32ct + 16(g%2) + i of keys 16c + 8h + 4q .. +3.
+  __device__ __forceinline__ frag vt_frag(const char* src, int ct, int c) const {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    v4s part[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(
+          src + to[ct & 1] + 64 * (ct & ~1) + (16 * c + 4 * q) * (CPR * 16)));
+    const v8s both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(frag, both);
+  }
+
+  __device__ __forceinline__ void scores(const char* ksrc, f32x16& s) const {
+    s = f32x16{0};
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) s = MF::mma(k_frag(ksrc, c), qf[c], s);
+  }
+
+  // Half n of this stream, with S^T(n) in s: masks, online softmax and P V
+  // from tile vt[P]; S^T(n+1) goes into sn from tile kt[P ^ 1] meanwhile (the
+  // exponentials and these products are independent, so the matrix cores run
+  // while the softmax does).
+  template <int P, class Set>
+  __device__ __forceinline__ void compute(const Set& S, int n, f32x16& s, f32x16& sn) {
+    const int lane = threadIdx.x & 63;
+    const int hl = lane >> 5;
+    const int r = 32 * rh + (lane & 31);
+    if (!S.full(n)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!S.valid(n, reg_row<KPL>(i, hl), r)) s[i] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    const float tm = half_max(mx) * sl2;
+    if (__any(tm > m + kRescale)) {
+      const float mn = fmaxf(m, tm);
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) o[ct] *= alpha;
+      m = mn;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    // Written in issue order, fenced against reordering: each product of
+    // S^T(n+1) is followed by a share of the exponentials of half n and one
+    // LDS read four products ahead (K rows, then V for the P V products).
+    constexpr int NVF = NCT * NCK;
+    constexpr int NRD = NCD + NVF;
+    constexpr int AHEAD = 4;
+    constexpr int EPM = 16 / NCD;
+    frag kf[NCD];
+    frag vf[NVF];
+    auto issue = [&](int i) {
+      if (i < NCD) kf[i] = k_frag(kt[P ^ 1], i);
+      else if (i < NRD) vf[i - NCD] = vt_frag(vt[P], (i - NCD) % NCT, (i - NCD) / NCT);
+    };
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) issue(i);
+    float pr[16];
+    float rs = 0.f;
+    sn = f32x16{0};
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) {
+      sn = MF::mma(kf[c], qf[c], sn);
+#pragma unroll
+      for (int e = 0; e < EPM; ++e) {
+        const int i = c * EPM + e;
+        pr[i] = fast_exp2(__builtin_fmaf(s[i], sl2, -mu));
+        rs += pr[i];
+      }
+      issue(c + AHEAD);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += half_sum(rs);
+    frag pf[NCK];
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) pf[c] = MF::pack(&pr[c * KPL]);
+#pragma unroll
+    for (int j = 0; j < NVF; ++j) {
+      o[j % NCT] = MF::mma(vf[j], pf[j / NCT], o[j % NCT]);
+      issue(NCD + j + AHEAD);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Step n (P = n % 2).  K(m) and V(m) live in ring slot m % 2.  Entering,
+  // S^T(n) is in s and this wave's loads of K(n+1) and V(n) are in flight;
+  // once they have landed the barrier publishes the partner's halves too and
+  // tells that every wave is done with K(n) and V(n-1), whose slots take
+  // K(n+2) and V(n+1).  Past the end of the stream S^T of the last slot is
+  // recomputed instead of branching (results unused).
+  template <int P, class Set>
+  __device__ __forceinline__ void step(const Set& S, int n, int N, f32x16 (&s)[2]) {
+    // this wave's loads have landed and its LDS reads of the previous step
+    // have returned before the other waves may overwrite those tiles
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & lgkmcnt_wait0());
+    __syncthreads();
+    if (n + 2 < N) dma_half(S, n + 2, kb, kta[P]);
+    if (n + 1 < N) dma_half(S, n + 1, vb, vta[P ^ 1]);
+    if (n < N) compute<P>(S, n, s[P], s[P ^ 1]);
+  }
+
+  // All waves take the same number of steps (the longest stream's), so that
+  // every barrier is reached by everyone; a stream with fewer halves idles
+  // through its last steps.
+  template <class Set>
+  __device__ __forceinline__ void run(const Set& S) {
+    const int NA = S.n_halves_max();
+    if (NA == 0) return;
+    const int N = S.n_halves();
+    f32x16 s[2];
+    if (N > 0) {
+      dma_half(S, 0, kb, kta[0]);
+      dma_half(S, 0, vb, vta[0]);
+      dma_half(S, 1, kb, kta[1]);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(NVH));
+    __syncthreads();
+    if (N > 0) scores(kt[0], s[0]);
+    // sets have an even number of halves (two per 64-key tile)
+    for (int n = 0; n < NA; n += 2) {
+      step<0>(S, n, N, s);
+      step<1>(S, n + 1, N, s);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  }
+};
+
+// Bitmap words of the two-stream kernel: segments of up to 32768 blocks
+// (longer ones take the four-wave kernel).
+constexpr int kRowsBitWords = 1024;
+
+template <int D, int NS>
+__global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) void vs_fwd_rows_kernel(AttnParams p) {
+  typedef FwdRowsWorker<D> W;
+  constexpr int NT = 128 * NS;
+  constexpr int OB_PITCH = D + 4;
+  constexpr int OB_BYTES = 64 * OB_PITCH * 4;
+  // [ring slot][K, V][stream] tiles
+  constexpr int TILES = 2 * 2 * NS * W::TB;
+  __shared__ QMajorLds<NT, kColBatch, NS == 2 ? kRowsBitWords : kMaxBitWords> L;
+  __shared__ __attribute__((aligned(16))) char tiles[TILES > OB_BYTES ? TILES : OB_BYTES];
+  __shared__ float s_m[NS][64];
+  __shared__ float s_l[NS][64];
+  __shared__ float s_inv[64];
+
+  int hb, i_local;
+  qmajor_item(p, blockIdx.x, &hb, &i_local);
+  const int b = hb / p.h_q;
+  const int h = hb % p.h_q;
+  const int kvh = h * p.h_kv / p.h_q;
+  const RowBlock rb = row_block(p, i_local);
+  const int list = (b * p.h_q + h) * p.seg.n_seg + rb.seg;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int ks = wave % NS;
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  W wk;
+  wk.rh = wave / NS;
+  const __bf16* q = reinterpret_cast<const __bf16*>(p.q);
+  const size_t qrow0 = (size_t)b * p.n_q + (size_t)i_local * kBlock;
+  const int r = 32 * wk.rh + l32;  // this lane's row of the block
+  {
+    const __bf16* qr = q + ((qrow0 + r) * p.h_q + h) * D;
+#pragma unroll
+    for (int c = 0; c < W::NCD; ++c) wk.qf[c] = load_frag<__bf16>(qr + c * W::KC + hl * W::KPL);
+  }
+#pragma unroll
+  for (int ct = 0; ct < W::NCT; ++ct) wk.o[ct] = f32x16{0};
+  wk.m = -INFINITY;
+  wk.l = 0.f;
+  wk.kvs = p.h_kv * D;
+  wk.kb = reinterpret_cast<const __bf16*>(p.k) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
+  wk.vb = reinterpret_cast<const __bf16*>(p.v) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    wk.kt[i] = tiles + ((i * 2 + 0) * NS + ks) * W::TB;
+    wk.vt[i] = tiles + ((i * 2 + 1) * NS + ks) * W::TB;
+    wk.kta[i] = lds_addr(wk.kt[i]);
+    wk.vta[i] = lds_addr(wk.vt[i]);
+  }
+  wk.sl2 = p.sl2;
+  wk.init_offsets();
+
+  qmajor_drive<NS>(p, rb, list, L, wk);
+
+  // Combine the streams' states of every row.
+  if (hl == 0) {
+    s_m[ks][r] = wk.m;
+    s_l[ks][r] = wk.l;
+  }
+  __syncthreads();
+  float mg = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NS; ++w) mg = fmaxf(mg, s_m[w][r]);
+  const float f = fast_exp2(wk.m - ((mg == -INFINITY) ? 0.f : mg));
+  float* ob = reinterpret_cast<float*>(tiles);
+  for (int w = 0; w < NS; ++w) {
+    if (ks == w) {
+#pragma unroll
+      for (int ct = 0; ct < W::NCT; ++ct)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          float* dst = ob + r * OB_PITCH + 32 * ct + 8 * i4 + 4 * hl;
+          f32x4 v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = wk.o[ct][4 * i4 + u] * f;
+          if (w == 0) *reinterpret_cast<f32x4*>(dst) = v;
+          else *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
+        }
+    }
+    __syncthreads();
+  }
+  // Normalise and write O (row-major, coalesced) and LSE (natural log).
+  if (tid < 64) {
+    float mt = -INFINITY;
+    for (int w = 0; w < NS; ++w) mt = fmaxf(mt, s_m[w][tid]);
+    const float mu = (mt == -INFINITY) ? 0.f : mt;
+    float lg = 0.f;
+    for (int w = 0; w < NS; ++w) lg += s_l[w][tid] * fast_exp2(s_m[w][tid] - mu);
+    s_inv[tid] = lg > 0.f ? 1.f / lg : 0.f;
+    p.lse[((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + tid] =
+        lg > 0.f ? (mt + __log2f(lg)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  for (int x = tid; x < 64 * D / 4; x += NT) {
+    const int rr = x / (D / 4);
+    const int c4 = (x % (D / 4)) * 4;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(ob + rr * OB_PITCH + c4) * s_inv[rr];
+    const size_t off = ((qrow0 + rr) * p.h_q + h) * D + c4;
+    if (p.o_f32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o_out) + off) = v;
+    } else {
+      bf16x4 w4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w4[u] = (__bf16)v[u];
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.o_out) + off) = w4;
+    }
+  }
+}
+
+
 hipError_t launch_fwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st) {
   const dim3 grid((unsigned)(p.batch * p.h_q * p.nqb));
   if (grid.x == 0) return hipSuccess;
-  if (dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<__bf16, 128>), grid, dim3(kQThreads), 0, st, p));
+  // the two-stream kernel's bitmap covers segments of up to 32 * kRowsBitWords blocks
+  int nb_max = p.n_global / kBlock;
+  if (p.W == 1) {
+    nb_max = 0;
+    for (int s = 0; s < p.seg.n_seg; ++s) nb_max = std::max(nb_max, p.seg.start_blk[s + 1] - p.seg.start_blk[s]);
+  }
+  const bool rows = nb_max <= 32 * kRowsBitWords;
+  if (dtype_bf16 && d == 128 && rows) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<128, 2>), grid, dim3(256), 0, st, p));
+  else if (dtype_bf16 && d == 64 && rows) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<64, 2>), grid, dim3(256), 0, st, p));
+  else if (dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<__bf16, 128>), grid, dim3(kQThreads), 0, st, p));
   else if (dtype_bf16 && d == 64) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<__bf16, 64>), grid, dim3(kQThreads), 0, st, p));
   else if (!dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<float, 128>), grid, dim3(kQThreads), 0, st, p));
   else VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<float, 64>), grid, dim3(kQThreads), 0, st, p));

@@ -17,36 +17,38 @@ namespace vs {
 constexpr int kQThreads = 256;
 constexpr int kMaxBitWords = 2048;  // block offsets < 65536 (segments up to 4M tokens)
 
-// The half-tiles (32 keys) one wave consumes from the current tile list: tiles
-// wave, wave + 4, ... (round-robin over the 4 waves), two halves each.
-// key_pos(n, r): local key position of key r (0..31) of half-tile n;
+// The half-tiles (32 keys) one key stream consumes from the current tile
+// list: tiles wave, wave + NS, ... (round-robin over NS streams), two halves
+// each.  key_pos(n, r): local key position of key r (0..31) of half-tile n;
 // full(n): no masking needed; valid(n, e, r): key e of the half for row r.
-struct SlashSet {
+template <int NS>
+struct SlashSetT {
   static constexpr bool kContiguous = true;  // the 32 keys of a half are consecutive
   const int* tiles;  // 2 * local key block + (g == 0)
   int tot;
-  int wave;
-  __device__ __forceinline__ int n_halves() const { return tot > wave ? 2 * ((tot - wave + 3) >> 2) : 0; }
-  __device__ __forceinline__ int n_halves_max() const { return tot > 0 ? 2 * ((tot + 3) >> 2) : 0; }
-  __device__ __forceinline__ int tv(int n) const { return tiles[wave + 4 * (n >> 1)]; }
+  int wave;          // key stream
+  __device__ __forceinline__ int n_halves() const { return tot > wave ? 2 * ((tot - wave + NS - 1) / NS) : 0; }
+  __device__ __forceinline__ int n_halves_max() const { return tot > 0 ? 2 * ((tot + NS - 1) / NS) : 0; }
+  __device__ __forceinline__ int tv(int n) const { return tiles[wave + NS * (n >> 1)]; }
   __device__ __forceinline__ int key_pos(int n, int r) const { return (tv(n) >> 1) * kBlock + 32 * (n & 1) + r; }
   __device__ __forceinline__ bool full(int n) const { return (tv(n) & 1) == 0; }
   __device__ __forceinline__ bool valid(int n, int e, int r) const { return 32 * (n & 1) + e <= r; }
 };
 
-struct ColSet {
+template <int NS>
+struct ColSetT {
   static constexpr bool kContiguous = false;
   const int* cols;   // local key positions of the gathered columns
   const int* coff;   // -1, or the first row (0..63) that may see the column
   int count;         // columns in the list
   int nt;            // 64-column tiles in the list
-  int wave;
-  __device__ __forceinline__ int n_halves() const { return nt > wave ? 2 * ((nt - wave + 3) >> 2) : 0; }
-  __device__ __forceinline__ int n_halves_max() const { return nt > 0 ? 2 * ((nt + 3) >> 2) : 0; }
-  __device__ __forceinline__ int base(int n) const { return 64 * (wave + 4 * (n >> 1)) + 32 * (n & 1); }
+  int wave;          // key stream
+  __device__ __forceinline__ int n_halves() const { return nt > wave ? 2 * ((nt - wave + NS - 1) / NS) : 0; }
+  __device__ __forceinline__ int n_halves_max() const { return nt > 0 ? 2 * ((nt + NS - 1) / NS) : 0; }
+  __device__ __forceinline__ int base(int n) const { return 64 * (wave + NS * (n >> 1)) + 32 * (n & 1); }
   __device__ __forceinline__ int key_pos(int n, int r) const {
     const int i = base(n) + r;
-    return cols[i < count ? i : 64 * (wave + 4 * (n >> 1))];
+    return cols[i < count ? i : 64 * (wave + NS * (n >> 1))];
   }
   // Columns are in ascending position, so those with a per-row limit (inside
   // the query block) come last: a half is unmasked if its last column has none.
@@ -67,23 +69,28 @@ struct ColSet {
 // pipelined walk over a batch has several tiles per wave to overlap.
 constexpr int kColBatch = 1024;
 
-template <int NT = kQThreads, int NCOL = kColBatch>
+typedef SlashSetT<4> SlashSet;
+typedef ColSetT<4> ColSet;
+
+// NBITS words of block-diagonal bitmap: segments of up to 32 * NBITS blocks.
+template <int NT = kQThreads, int NCOL = kColBatch, int NBITS = kMaxBitWords>
 struct QMajorLds {
   static constexpr int kCols = NCOL;
-  uint32_t bits[kMaxBitWords];
+  static constexpr int kBitWords = NBITS;
+  uint32_t bits[NBITS];
   int tiles[NT];
   int cols[NCOL];
   int coff[NCOL];
   int wsum[NT / 64];
 };
 
-// NT threads; wave w consumes the tiles of key stream w % 4 (with 8 waves,
-// waves w and w + 4 share a stream and split its rows).
-template <int NT, int NCOL, class Worker>
+// NT threads; wave w consumes the tiles of key stream w % NS (with more
+// waves than streams, the waves of a stream split its rows).
+template <int NS = 4, int NT, int NCOL, int NBITS, class Worker>
 __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list,
-                                             QMajorLds<NT, NCOL>& L, Worker& wk) {
+                                             QMajorLds<NT, NCOL, NBITS>& L, Worker& wk) {
   const int tid = threadIdx.x;
-  const int wave = (tid >> 6) & 3;
+  const int wave = (tid >> 6) % NS;
   const int sp0 = p.s_ptr[list];
   const int ns = p.s_ptr[list + 1] - sp0;
 
@@ -150,7 +157,7 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
     const int slot = block_compact<NT>(j >= 0, L.wsum, &tot);
     if (j >= 0) L.tiles[slot] = 2 * j + diag;
     __syncthreads();
-    wk.run(SlashSet{L.tiles, tot, wave});
+    wk.run(SlashSetT<NS>{L.tiles, tot, wave});
     __syncthreads();
   }
 
@@ -183,7 +190,7 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
     const bool last = e0 >= vlimit;
     if (!last) fetch(e0);
     const int nt = last ? (count + 63) / 64 : count / 64;
-    wk.run(ColSet{L.cols, L.coff, last ? count : 64 * nt, nt, wave});
+    wk.run(ColSetT<NS>{L.cols, L.coff, last ? count : 64 * nt, nt, wave});
     if (last) break;
     __syncthreads();
     const int rem = count - 64 * nt;
