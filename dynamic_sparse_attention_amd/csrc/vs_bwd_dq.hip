@@ -12,7 +12,7 @@
 // goes straight to registers as the A operand of dP^T = V dO^T.  The loads
 // of half n+1 are issued at the start of step n, and S^T, dP^T of n+1 are
 // computed after the dQ products of n.
-#include "vs_qmajor.h"
+#include "vs_rows.h"
 #include "vs_trace.h"
 
 namespace vs {
@@ -268,10 +268,219 @@ __global__ __launch_bounds__(kQThreads) void vs_bwd_dq_bf16_kernel(AttnParams p)
   }
 }
 
+// Row-split dQ: a workgroup of 2*NS waves serves NS key streams, the two
+// waves of a stream own rows 0-31 and 32-63 and share its K and V tiles in
+// LDS (both read row-wise for S^T = K Q^T and dP^T = V dO^T, K also
+// transposed for dQ^T += K^T dS^T).  Each wave holds Q^T, dO^T and dQ^T of
+// its 32 rows (about 220 registers), so with NS = 2 (80 KB of LDS) two
+// independent workgroups share a CU.
+template <int D>
+struct DqRowsWorker : RowsTiles<D> {
+  typedef RowsTiles<D> T;
+  typedef typename T::MF MF;
+  typedef typename T::frag frag;
+  using T::KPL;
+  using T::NCD;
+  using T::NCT;
+  using T::NCK;
+  using T::NVH;
+  using T::kb;
+  using T::vb;
+  using T::rh;
+  using T::k_frag;
+  using T::t_frag;
+  using T::dma_half;
+
+  frag qf[NCD];     // Q^T of this wave's 32 rows
+  frag dof[NCD];    // dO^T
+  f32x16 dq[NCT];   // dQ^T [channel][row]
+  f32x16 s, dp;     // S^T, dP^T of the current half
+  float lse2;       // this lane's row: LSE * log2(e), +inf for an empty row
+  float dl;         // delta
+  const char* kt[2];  // this stream's tiles (rings of two)
+  const char* vt[2];
+  uint32_t kta[2], vta[2];
+  float sl2;
+
+  __device__ __forceinline__ void scores(const char* ksrc, const char* vsrc) {
+    s = f32x16{0};
+    dp = f32x16{0};
+#pragma unroll
+    for (int c = 0; c < NCD; ++c) {
+      s = MF::mma(k_frag(ksrc, c), qf[c], s);
+      dp = MF::mma(k_frag(vsrc, c), dof[c], dp);
+    }
+  }
+
+  // dS^T of half n as bf16 B operands: P = exp2(S log2(e) scale - LSE log2(e)),
+  // dS = P (dP - delta); masked and empty-row entries give P = 0.
+  template <class Set>
+  __device__ __forceinline__ void dscores(const Set& S, int n, frag (&dsf)[NCK]) {
+    const int lane = threadIdx.x & 63;
+    const int hl = lane >> 5;
+    const int r = 32 * rh + (lane & 31);
+    if (!S.full(n)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!S.valid(n, reg_row<KPL>(i, hl), r)) s[i] = -INFINITY;
+    }
+    float ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pr = fast_exp2(__builtin_fmaf(s[i], sl2, -lse2));
+      ds[i] = pr * (dp[i] - dl);
+    }
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) dsf[c] = MF::pack(&ds[c * KPL]);
+  }
+
+  // Step n (P = n % 2).  K(m) and V(m) live in ring slot m % 2.  Entering,
+  // S^T(n), dP^T(n) are in s, dp and this wave's loads of K(n+1), V(n+1) are
+  // in flight.  dS(n) and the dQ products of half n (K(n) transposed) come
+  // first; the barrier then publishes K(n+1), V(n+1) and tells that every
+  // wave is done with K(n) and V(n), whose slots take K(n+2), V(n+2); S^T and
+  // dP^T of n+1 follow.
+  template <int P, class Set>
+  __device__ __forceinline__ void step(const Set& S, int n, int N) {
+    if (n < N) {
+      frag dsf[NCK];
+      dscores(S, n, dsf);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int c = 0; c < NCK; ++c) dq[ct] = MF::mma(t_frag(kt[P], ct, c), dsf[c], dq[ct]);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & lgkmcnt_wait0());
+    __syncthreads();
+    if (n + 2 < N) {
+      dma_half(S, n + 2, kb, kta[P]);
+      dma_half(S, n + 2, vb, vta[P]);
+    }
+    if (n + 1 < N) scores(kt[P ^ 1], vt[P ^ 1]);
+  }
+
+  // All waves take the same number of steps (the longest stream's), so that
+  // every barrier is reached by everyone.
+  template <class Set>
+  __device__ __forceinline__ void run(const Set& S) {
+    const int NA = S.n_halves_max();
+    if (NA == 0) return;
+    const int N = S.n_halves();
+    if (N > 0) {
+      dma_half(S, 0, kb, kta[0]);
+      dma_half(S, 0, vb, vta[0]);
+      dma_half(S, 1, kb, kta[1]);
+      dma_half(S, 1, vb, vta[1]);
+    }
+    // this wave's loads of K(0), V(0) have landed (K(1), V(1) may not have)
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * NVH));
+    __syncthreads();
+    if (N > 0) scores(kt[0], vt[0]);
+    // sets have an even number of halves (two per 64-key tile)
+    for (int n = 0; n < NA; n += 2) {
+      step<0>(S, n, N);
+      step<1>(S, n + 1, N);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  }
+};
+
+template <int D, int NS>
+__global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_dq_rows_kernel(AttnParams p) {
+  typedef DqRowsWorker<D> W;
+  constexpr int NT = 128 * NS;
+  constexpr int OB_PITCH = D + 4;
+  constexpr int OB_BYTES = 64 * OB_PITCH * 4;
+  // [ring slot][K, V][stream] tiles
+  constexpr int TILES = 2 * 2 * NS * W::TB;
+  __shared__ QMajorLds<NT, kColBatch, kRowsBitWords> L;
+  __shared__ __attribute__((aligned(16))) char tiles[TILES > OB_BYTES ? TILES : OB_BYTES];
+
+  int hb, i_local;
+  qmajor_item(p, blockIdx.x, &hb, &i_local);
+  const int b = hb / p.h_q;
+  const int h = hb % p.h_q;
+  const int kvh = h * p.h_kv / p.h_q;
+  const RowBlock rb = row_block(p, i_local);
+  const int list = (b * p.h_q + h) * p.seg.n_seg + rb.seg;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int ks = wave % NS;
+  const int lane = tid & 63;
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  W wk;
+  wk.rh = wave / NS;
+  const int r = 32 * wk.rh + l32;  // this lane's row of the block
+  const __bf16* q = reinterpret_cast<const __bf16*>(p.q);
+  const __bf16* dout = reinterpret_cast<const __bf16*>(p.dout);
+  const size_t row0 = (size_t)b * p.n_q + (size_t)i_local * kBlock;
+  {
+    const size_t roff = ((row0 + r) * p.h_q + h) * D + hl * W::KPL;
+#pragma unroll
+    for (int c = 0; c < W::NCD; ++c) {
+      wk.qf[c] = load_frag<__bf16>(q + roff + c * W::KC);
+      wk.dof[c] = load_frag<__bf16>(dout + roff + c * W::KC);
+    }
+    const size_t li = ((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + r;
+    const float lse = p.lse[li];
+    wk.lse2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+    wk.dl = p.delta[li];
+  }
+#pragma unroll
+  for (int ct = 0; ct < W::NCT; ++ct) wk.dq[ct] = f32x16{0};
+  wk.kvs = p.h_kv * D;
+  wk.kb = reinterpret_cast<const __bf16*>(p.k) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
+  wk.vb = reinterpret_cast<const __bf16*>(p.v) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    wk.kt[i] = tiles + ((i * 2 + 0) * NS + ks) * W::TB;
+    wk.vt[i] = tiles + ((i * 2 + 1) * NS + ks) * W::TB;
+    wk.kta[i] = lds_addr(wk.kt[i]);
+    wk.vta[i] = lds_addr(wk.vt[i]);
+  }
+  wk.sl2 = p.sl2;
+  wk.init_offsets();
+
+  qmajor_drive<NS>(p, rb, list, L, wk);
+
+  // Sum the streams' dQ^T of every row, then scale and store (or add).
+  float* ob = reinterpret_cast<float*>(tiles);
+  for (int w = 0; w < NS; ++w) {
+    if (ks == w) {
+#pragma unroll
+      for (int ct = 0; ct < W::NCT; ++ct)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          float* dst = ob + r * OB_PITCH + 32 * ct + 8 * i4 + 4 * hl;
+          f32x4 v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = wk.dq[ct][4 * i4 + u];
+          if (w == 0) *reinterpret_cast<f32x4*>(dst) = v;
+          else *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
+        }
+    }
+    __syncthreads();
+  }
+  for (int x = tid; x < 64 * D / 4; x += NT) {
+    const int rr = x / (D / 4);
+    const int c4 = (x % (D / 4)) * 4;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(ob + rr * OB_PITCH + c4) * p.scale;
+    float* dst = p.dq + ((row0 + rr) * p.h_q + h) * D + c4;
+    if (p.dq_accumulate) *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
+    else *reinterpret_cast<f32x4*>(dst) = v;
+  }
+}
+
 hipError_t launch_bwd_dq_bf16(const AttnParams& p, int d, hipStream_t st) {
   const dim3 gq((unsigned)(p.batch * p.h_q * p.nqb));
   if (gq.x == 0) return hipSuccess;
-  if (d == 128) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_bf16_kernel<128>), gq, dim3(kQThreads), 0, st, p));
+  // the row-split kernel's bitmap covers segments of up to 32 * kRowsBitWords blocks
+  const bool rows = max_segment_blocks(p) <= 32 * kRowsBitWords;
+  if (d == 128 && rows) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_rows_kernel<128, 2>), gq, dim3(256), 0, st, p));
+  else if (d == 64 && rows) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_rows_kernel<64, 2>), gq, dim3(256), 0, st, p));
+  else if (d == 128) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_bf16_kernel<128>), gq, dim3(kQThreads), 0, st, p));
   else VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_bf16_kernel<64>), gq, dim3(kQThreads), 0, st, p));
   return hipGetLastError();
 }

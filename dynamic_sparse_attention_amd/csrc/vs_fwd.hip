@@ -15,9 +15,7 @@
 // product from registers (slot_perm).  Softmax state is fp32; P is rounded
 // to bf16 for the matrix cores when the inputs are bf16.  The four waves'
 // (max, sum, O) merge through LDS at the end.
-#include <algorithm>
-
-#include "vs_qmajor.h"
+#include "vs_rows.h"
 #include "vs_trace.h"
 
 namespace vs {
@@ -529,95 +527,31 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
 // expansion, waits and output merge overlap the other's products.
 
 template <int D>
-struct FwdRowsWorker {
-  typedef Mfma<__bf16> MF;
-  typedef MF::frag frag;
-  static constexpr int KPL = MF::KPL;
-  static constexpr int KC = 2 * KPL;
-  static constexpr int NCD = D / KC;   // k chunks over head_dim
-  static constexpr int NCT = D / 32;   // 32-channel output tiles
-  static constexpr int NCK = 32 / KC;  // k chunks over 32 keys
-  static constexpr int CPR = D / 8;    // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR; // rows per 1 KiB direct load
-  static constexpr int NVL = 32 / RPI; // direct loads per 32-row tile
-  static constexpr int NVH = NVL / 2;  // ... issued by each wave of a stream
-  static constexpr int TB = 32 * D * 2;
+struct FwdRowsWorker : RowsTiles<D> {
+  typedef RowsTiles<D> T;
+  typedef typename T::MF MF;
+  typedef typename T::frag frag;
+  using T::KPL;
+  using T::NCD;
+  using T::NCT;
+  using T::NCK;
+  using T::NVH;
+  using T::kb;
+  using T::vb;
+  using T::rh;
+  using T::k_frag;
+  using T::dma_half;
   static constexpr float kRescale = 8.f;
-  __device__ static constexpr int swz(int r) { return 2 * (r & 3) + ((r >> 3) & 1); }
 
   frag qf[NCD];   // Q^T of this wave's 32 rows
   f32x16 o[NCT];  // O^T [channel][row]
   float m, l;     // this lane's row: running max (exp2 domain) and sum
-  int ro[4];
-  int to[2];
   const char* kt[2];      // this stream's K tiles (ring of two)
   const char* vt[2];
   uint32_t kta[2], vta[2];
-  const __bf16* kb;
-  const __bf16* vb;
-  int kvs;
-  int rh;                 // row half of this wave
   float sl2;
 
-  __device__ __forceinline__ void init_offsets() {
-    const int lane = threadIdx.x & 63;
-    const int hl = lane >> 5;
-    const int sp = slot_perm<KPL>(lane & 31);
-#pragma unroll
-    for (int cl = 0; cl < 4; ++cl) ro[cl] = sp * (CPR * 16) + 16 * ((2 * cl + hl) ^ swz(sp));
-    const int g = lane >> 4;
-    const int sg = lane & 15;
-    const int rr = sg >> 2;
-    const int x = 2 * (g & 1) + ((sg & 3) >> 1);
-    const int z = x ^ (2 * rr + hl);
-    const int base = (8 * hl + rr) * (CPR * 16) + 16 * (z & 3) + 8 * (sg & 1);
-    to[0] = base + 64 * (z >> 2);
-    to[1] = base + 64 * (1 - (z >> 2));
-  }
-
-  // This wave's half of the direct loads of the 32 rows (K or V, from src) of
-  // half n into the tile at LDS address dst.
-  template <class Set>
-  __device__ __forceinline__ void dma_half(const Set& S, int n, const __bf16* src, uint32_t dst) const {
-    const int lane = threadIdx.x & 63;
-    const int rr = lane / CPR;
-    const uint32_t rb = (uint32_t)(kvs * 2);
-    if constexpr (Set::kContiguous) {
-      const uint32_t o0 = (uint32_t)S.key_pos(n, rh * NVH * RPI + rr) * rb;
-#pragma unroll
-      for (int u0 = 0; u0 < NVH; ++u0) {
-        const int u = rh * NVH + u0;
-        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
-        dma_lds16_so(src, o0 + (uint32_t)(u0 * RPI) * rb + chunk * 16, dst + u * 1024);
-      }
-    } else {
-#pragma unroll
-      for (int u0 = 0; u0 < NVH; ++u0) {
-        const int u = rh * NVH + u0;
-        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
-        dma_lds16_so(src, (uint32_t)S.key_pos(n, u * RPI + rr) * rb + chunk * 16, dst + u * 1024);
-      }
-    }
-  }
-
-  __device__ __forceinline__ frag k_frag(const char* src, int c) const {
-    return *reinterpret_cast<const frag*>(src + ro[c & 3] + 128 * (c >> 2));
-  }
-
-  // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of
-  // the 8 bytes read by lanes i/4, 4+i/4, 8+i/4, 12+i/4, i.e. channel
-  // 32ct + 16(g%2) + i of keys 16c + 8h + 4q .. +3.
-  __device__ __forceinline__ frag vt_frag(const char* src, int ct, int c) const {
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    typedef short v8s __attribute__((ext_vector_type(8)));
-    v4s part[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(
-          src + to[ct & 1] + 64 * (ct & ~1) + (16 * c + 4 * q) * (CPR * 16)));
-    const v8s both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(frag, both);
-  }
+  __device__ __forceinline__ frag vt_frag(const char* src, int ct, int c) const { return this->t_frag(src, ct, c); }
 
   __device__ __forceinline__ void scores(const char* ksrc, f32x16& s) const {
     s = f32x16{0};
@@ -737,10 +671,6 @@ struct FwdRowsWorker {
   }
 };
 
-// Bitmap words of the two-stream kernel: segments of up to 32768 blocks
-// (longer ones take the four-wave kernel).
-constexpr int kRowsBitWords = 1024;
-
 template <int D, int NS>
 __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) void vs_fwd_rows_kernel(AttnParams p) {
   typedef FwdRowsWorker<D> W;
@@ -859,12 +789,7 @@ hipError_t launch_fwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st
   const dim3 grid((unsigned)(p.batch * p.h_q * p.nqb));
   if (grid.x == 0) return hipSuccess;
   // the two-stream kernel's bitmap covers segments of up to 32 * kRowsBitWords blocks
-  int nb_max = p.n_global / kBlock;
-  if (p.W == 1) {
-    nb_max = 0;
-    for (int s = 0; s < p.seg.n_seg; ++s) nb_max = std::max(nb_max, p.seg.start_blk[s + 1] - p.seg.start_blk[s]);
-  }
-  const bool rows = nb_max <= 32 * kRowsBitWords;
+  const bool rows = max_segment_blocks(p) <= 32 * kRowsBitWords;
   if (dtype_bf16 && d == 128 && rows) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<128, 2>), grid, dim3(256), 0, st, p));
   else if (dtype_bf16 && d == 64 && rows) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<64, 2>), grid, dim3(256), 0, st, p));
   else if (dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<__bf16, 128>), grid, dim3(kQThreads), 0, st, p));
