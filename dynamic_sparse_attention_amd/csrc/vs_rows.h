@@ -4,18 +4,27 @@
 // own query rows 0-31 and 32-63 of the block and share every 32-key tile of
 // the stream: each issues half of the tile's direct global -> LDS loads
 // (1 KiB per instruction, no registers), a workgroup barrier publishes both
-// halves.  A tile is row-major (row r at r * D * 2 bytes) with the 16-byte
-// chunk c of row r at chunk index c ^ swz(r), swz(r) = 2 (r mod 4) +
-// floor(r / 8) mod 2, so that both kinds of operand read hit eight distinct
-// bank groups:
-//   * row reads (k_frag): the A operand of a product with the tile's rows as
-//     output rows (S^T = K Q^T, dP^T = V dO^T), rows permuted by slot_perm so
-//     that the result registers are the k slots of the next product's B
-//     operand;
+// halves.  Operands are read from the tile in two ways:
+//   * row reads (k_frag, ds_read_b128): the A operand of a product with the
+//     tile's rows as output rows (S^T = K Q^T, dP^T = V dO^T), rows permuted
+//     by slot_perm so that the result registers are the k slots of the next
+//     product's B operand;
 //   * transposed reads (t_frag, ds_read_b64_tr_b16): the A operand of a
 //     product contracting over the tile's keys (O^T += V^T P^T,
 //     dQ^T += K^T dS^T).
-// Per-lane offsets are computed once; the per-read part is an immediate.
+// gfx950's LDS serves 256 bytes per cycle: sixteen lanes of a 16-byte read or
+// 32 lanes of an 8-byte read, so each such group must touch sixteen distinct
+// 16-byte bank groups.  The layout that achieves it for both kinds of read:
+// the rows of one direct load (RPI = 4 rows of 256 bytes for d = 128, 8 of
+// 128 bytes for d = 64) are contiguous, each such 1 KiB group is followed by
+// 16 bytes of padding (so successive groups start one bank group further
+// on), and inside the group the 16-byte chunk c of row b sits at chunk index
+// c ^ swz(b).  For d = 128, swz(b) = 4b puts the four rows of a group in four
+// different quarters of the bank window (transposed reads take four
+// consecutive rows) while the padding spreads the sixteen rows of a row read
+// over the window; d = 64 uses swz(b) = 4 bit1(b) + 2 bit2(b) with two rows
+// per window.  Per-lane offsets are computed once; the per-read part is an
+// immediate.
 #pragma once
 
 #include "vs_qmajor.h"
@@ -35,11 +44,15 @@ struct RowsTiles {
   static constexpr int RPI = 64 / CPR; // rows per 1 KiB direct load
   static constexpr int NVL = 32 / RPI; // direct loads per 32-row tile
   static constexpr int NVH = NVL / 2;  // ... issued by each wave of a stream
-  static constexpr int TB = 32 * D * 2;
-  __device__ static constexpr int swz(int r) { return 2 * (r & 3) + ((r >> 3) & 1); }
+  static constexpr int GROUP = 1024 + 16;      // bytes per direct-load group, padded
+  static constexpr int TB = NVL * GROUP;       // bytes per 32-row tile
+  // chunk index XOR of row b (0 .. RPI-1) of a group
+  __device__ static constexpr int swz(int b) {
+    return D == 128 ? 4 * (b & 3) : 4 * ((b >> 1) & 1) + 2 * ((b >> 2) & 1);
+  }
 
   int ro[4];
-  int to[2];
+  int to[4];
   const __bf16* kb;   // K of (batch, kv head): row pos at kb + pos * kvs
   const __bf16* vb;
   int kvs;
@@ -48,52 +61,62 @@ struct RowsTiles {
   __device__ __forceinline__ void init_offsets() {
     const int lane = threadIdx.x & 63;
     const int hl = lane >> 5;
-    // row operand: row sp, chunk 2c + hl; the XOR permutes chunks inside
-    // groups of 8, so the offset is ro[c % 4] + 128 * (c / 4)
+    // row operand: row sp, chunk 2c + hl
     const int sp = slot_perm<KPL>(lane & 31);
+    const int a = sp / RPI, b = sp % RPI;
 #pragma unroll
-    for (int cl = 0; cl < 4; ++cl) ro[cl] = sp * (CPR * 16) + 16 * ((2 * cl + hl) ^ swz(sp));
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (D == 128) ro[j] = a * GROUP + b * 256 + 16 * hl + 64 * (j ^ b);  // j = c / 2
+      else ro[j] = a * GROUP + b * 128 + 16 * hl + 32 * (j ^ (swz(b) >> 1));         // j = c
+    }
     // transposed operand: lane i of a 16-lane group reads row 16c + 8h + 4q +
-    // i/4 at chunk 4ct + x (x < 4); swz = 2(i/4) + h, so the chunk is
-    // 4 (ct ^ zh) + zl with z = x ^ swz
+    // i/4 at chunk 4ct + x (x < 4), bytes 8 (i % 2) .. +7
     const int g = lane >> 4;
     const int sg = lane & 15;
     const int rr = sg >> 2;
     const int x = 2 * (g & 1) + ((sg & 3) >> 1);
-    const int z = x ^ (2 * rr + hl);
-    const int base = (8 * hl + rr) * (CPR * 16) + 16 * (z & 3) + 8 * (sg & 1);
-    to[0] = base + 64 * (z >> 2);
-    to[1] = base + 64 * (1 - (z >> 2));
+    const int half = 8 * (sg & 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (D == 128) {
+        to[j] = 2 * hl * GROUP + rr * 256 + 64 * (j ^ rr) + 16 * x + half;  // j = ct
+      } else {
+        const int ct = j >> 1, q = j & 1;                                   // j = 2 ct + q
+        to[j] = hl * GROUP + (4 * q + rr) * 128 + 64 * (ct ^ ((rr >> 1) & 1)) + 16 * (x ^ (2 * q)) + half;
+      }
+    }
   }
 
   // This wave's half of the direct loads of the 32 rows (K or V, from src) of
-  // half n into the tile at LDS address dst.
+  // half n into the tile at LDS address dst: load u lands in group u, lane L
+  // at byte 16 L of it, i.e. row u * RPI + L / CPR, chunk slot L % CPR, which
+  // holds chunk (L % CPR) ^ swz(L / CPR) of that row.
   template <class Set>
   __device__ __forceinline__ void dma_half(const Set& S, int n, const __bf16* src, uint32_t dst) const {
     const int lane = threadIdx.x & 63;
     const int rr = lane / CPR;
+    const int chunk = (lane % CPR) ^ swz(rr);
     const uint32_t rb = (uint32_t)(kvs * 2);
     if constexpr (Set::kContiguous) {
-      const uint32_t o0 = (uint32_t)S.key_pos(n, rh * NVH * RPI + rr) * rb;
+      const uint32_t o0 = (uint32_t)S.key_pos(n, rh * NVH * RPI + rr) * rb + chunk * 16;
 #pragma unroll
       for (int u0 = 0; u0 < NVH; ++u0) {
         const int u = rh * NVH + u0;
-        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
-        dma_lds16_so(src, o0 + (uint32_t)(u0 * RPI) * rb + chunk * 16, dst + u * 1024);
+        dma_lds16_so(src, o0 + (uint32_t)(u0 * RPI) * rb, dst + u * GROUP);
       }
     } else {
 #pragma unroll
       for (int u0 = 0; u0 < NVH; ++u0) {
         const int u = rh * NVH + u0;
-        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
-        dma_lds16_so(src, (uint32_t)S.key_pos(n, u * RPI + rr) * rb + chunk * 16, dst + u * 1024);
+        dma_lds16_so(src, (uint32_t)S.key_pos(n, u * RPI + rr) * rb + chunk * 16, dst + u * GROUP);
       }
     }
   }
 
   // Row operand: tile row slot_perm(L % 32), channels of k chunk c.
   __device__ __forceinline__ frag k_frag(const char* src, int c) const {
-    return *reinterpret_cast<const frag*>(src + ro[c & 3] + 128 * (c >> 2));
+    if constexpr (D == 128) return *reinterpret_cast<const frag*>(src + ro[c >> 1] + 32 * (c & 1));
+    else return *reinterpret_cast<const frag*>(src + ro[c]);
   }
 
   // Transposed operand: channels 32ct + L % 32, keys of k chunk c.
@@ -105,9 +128,10 @@ struct RowsTiles {
     typedef short v8s __attribute__((ext_vector_type(8)));
     v4s part[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(
-          src + to[ct & 1] + 64 * (ct & ~1) + (16 * c + 4 * q) * (CPR * 16)));
+    for (int q = 0; q < 2; ++q) {
+      const char* a = D == 128 ? src + to[ct] + (4 * c + q) * GROUP : src + to[2 * ct + q] + 2 * c * GROUP;
+      part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)a);
+    }
     const v8s both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(frag, both);
   }
