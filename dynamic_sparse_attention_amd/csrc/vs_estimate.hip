@@ -18,9 +18,10 @@
 //           over a 64-key block is the slash score of its block-diagonal;
 //   top-k:  one workgroup per (list, kind): 4-pass radix select on the fp32
 //           score bits (scores are >= 0, so the bits order like the values),
-//           then an ordered compaction that writes the chosen indices
-//           ascending, taking the lowest indices among scores equal to the
-//           threshold.
+//           with wave-aggregated histogram increments, then an ordered
+//           compaction over contiguous per-wave ranges that writes the chosen
+//           indices ascending, taking the lowest indices among scores equal
+//           to the threshold.
 #include "vs_attn_common.h"
 #include "vs_trace.h"
 
@@ -104,22 +105,41 @@ __global__ __launch_bounds__(256) void vs_est_pass1_kernel(AttnParams p, TilePre
   }
 }
 
-__global__ __launch_bounds__(64) void vs_est_combine_kernel(AttnParams p, TilePrefix tp, int tiles_total,
+// Per (list, window row): merge the per-tile (max, sum of exp) partials into
+// the row's LSE (log2 domain).  1024 threads per list: thread (group, row)
+// merges the tiles t = group, group + 16, ... of its row, then the 16 group
+// states of each row merge through LDS.
+constexpr int kCombineGroups = 16;
+
+__global__ __launch_bounds__(64 * kCombineGroups) void vs_est_combine_kernel(AttnParams p, TilePrefix tp, int tiles_total,
                                                             const float2* part, float* lse2) {
+  __shared__ float2 st[kCombineGroups][64];
   const int list = blockIdx.x;
   const int s = list % p.seg.n_seg;
   const int bh = list / p.seg.n_seg;
-  const int r = threadIdx.x;
+  const int r = threadIdx.x & 63;
+  const int grp = threadIdx.x >> 6;
   const float2* pp = part + (size_t)bh * tiles_total * 64;
-  float M = -INFINITY;
-  for (int t = tp.v[s]; t < tp.v[s + 1]; ++t) M = fmaxf(M, pp[(size_t)t * 64 + r].x);
-  const float mu = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
-  for (int t = tp.v[s]; t < tp.v[s + 1]; ++t) {
+  float M = -INFINITY, L = 0.f;
+  for (int t = tp.v[s] + grp; t < tp.v[s + 1]; t += kCombineGroups) {
     const float2 v = pp[(size_t)t * 64 + r];
-    L += v.y * fast_exp2(v.x - mu);
+    const float mn = fmaxf(M, v.x);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    L = L * fast_exp2(M - mu) + v.y * fast_exp2(v.x - mu);
+    M = mn;
   }
-  lse2[(size_t)list * 64 + r] = L > 0.f ? M + __log2f(L) : INFINITY;
+  st[grp][r] = make_float2(M, L);
+  __syncthreads();
+  if (grp == 0) {
+    float Mg = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < kCombineGroups; ++g) Mg = fmaxf(Mg, st[g][r].x);
+    const float mu = Mg == -INFINITY ? 0.f : Mg;
+    float Lg = 0.f;
+#pragma unroll
+    for (int g = 0; g < kCombineGroups; ++g) Lg += st[g][r].y * fast_exp2(st[g][r].x - mu);
+    lse2[(size_t)list * 64 + r] = Lg > 0.f ? Mg + __log2f(Lg) : INFINITY;
+  }
 }
 
 template <typename T, int D>
@@ -196,9 +216,25 @@ __global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePre
 }
 
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkUnroll = 8;  // candidate loads per thread in flight
 
-__device__ __forceinline__ int block_excl_scan_count(bool flag, int* wsum, int* total) {
-  return block_compact<kTopkThreads>(flag, wsum, total);
+// Histogram increment of the active lanes' bins, aggregated per wave: the
+// scores of a list cluster in a few bins of the leading digits, and lanes
+// adding to one LDS word serialise.  Up to four distinct bins of the wave
+// are added with one atomic each; the remaining lanes add their own.
+__device__ __forceinline__ void wave_hist_add(int* hist, int bin, bool active) {
+  const int lane = threadIdx.x & 63;
+  uint64_t rem = __ballot(active);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    if (rem == 0) break;  // uniform
+    const int leader = __ffsll((unsigned long long)rem) - 1;
+    const int lb = __shfl(bin, leader, 64);
+    const uint64_t same = __ballot(active && bin == lb) & rem;
+    if (lane == leader) atomicAdd(&hist[lb], __popcll(same));
+    rem &= ~same;
+  }
+  if ((rem >> lane) & 1ull) atomicAdd(&hist[bin], 1);
 }
 
 __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p, const float* v_score,
@@ -206,7 +242,7 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
                                                                    int* v_idx, const int* s_ptr,
                                                                    int* s_idx) {
   __shared__ int hist[256];
-  __shared__ int wsum[kTopkThreads / 64];
+  __shared__ int wsum[2][kTopkThreads / 64];
   __shared__ int sel[2];
   const int kind = blockIdx.x & 1;
   const int list = blockIdx.x >> 1;
@@ -232,6 +268,8 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
     add = 0;
   }
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   if (k >= L) {
     for (int x = tid; x < k; x += kTopkThreads) out[x] = x < L ? x + add : -1;
     return;
@@ -244,9 +282,19 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
     const int shift = 24 - 8 * pass;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int x = tid; x < L; x += kTopkThreads) {
-      const uint32_t v = u[x];
-      if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & 255], 1);
+    // eight candidates per thread in flight at a time; uniform trip count
+    for (int base = 0; base < L; base += kTopkUnroll * kTopkThreads) {
+      uint32_t v[kTopkUnroll];
+#pragma unroll
+      for (int j = 0; j < kTopkUnroll; ++j) {
+        const int x = base + j * kTopkThreads + tid;
+        v[j] = x < L ? u[x] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kTopkUnroll; ++j) {
+        const int x = base + j * kTopkThreads + tid;
+        wave_hist_add(hist, (int)((v[j] >> shift) & 255), x < L && (v[j] & pmask) == prefix);
+      }
     }
     __syncthreads();
     if (tid == 0) {
@@ -265,23 +313,68 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
     __syncthreads();
   }
   // prefix is the k-th largest value; take everything above it and the kr
-  // lowest-index entries equal to it, in index order.
-  int count = 0, eq_seen = 0;
-  for (int base = 0; base < L; base += kTopkThreads) {
-    const int x = base + tid;
-    const uint32_t v = x < L ? u[x] : 0u;
-    const bool gt = x < L && v > prefix;
-    const bool eq = x < L && v == prefix;
-    int eq_tot;
-    const int eq_before = block_excl_scan_count(eq, wsum, &eq_tot);
-    __syncthreads();
-    const bool take = gt || (eq && eq_seen + eq_before < kr);
-    int tot;
-    const int slot = block_compact<kTopkThreads>(take, wsum, &tot);
-    if (take) out[count + slot] = x + add;
-    count += tot;
-    eq_seen += eq_tot;
-    __syncthreads();
+  // lowest-index entries equal to it, in index order.  Wave w owns the
+  // contiguous range [w C, (w + 1) C) of the candidates: it counts them,
+  // one workgroup scan gives every wave its output offset and its number of
+  // equal entries before it, and a second walk writes the chosen indices
+  // (ballot prefixes order the lanes of each 64-entry step).
+  const int C = ((L + kTopkThreads / 64 - 1) / (kTopkThreads / 64) + 63) & ~63;
+  const int x0 = wave * C;
+  const int x1 = min(x0 + C, L);
+  int n_gt = 0, n_eq = 0;
+  for (int xb = x0; xb < x1; xb += kTopkUnroll * 64) {
+    uint32_t v[kTopkUnroll];
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int x = xb + 64 * j + lane;
+      v[j] = x < x1 ? u[x] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int x = xb + 64 * j + lane;
+      n_gt += x < x1 && v[j] > prefix;
+      n_eq += x < x1 && v[j] == prefix;
+    }
+  }
+  // wave totals
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    n_gt += __shfl_xor(n_gt, o, 64);
+    n_eq += __shfl_xor(n_eq, o, 64);
+  }
+  if (lane == 0) {
+    wsum[0][wave] = n_gt;
+    wsum[1][wave] = n_eq;
+  }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += wsum[0][w];
+    eq_before += wsum[1][w];
+  }
+  int pos = gt_before + min(eq_before, kr);  // taken entries before this wave's range
+  int eq_seen = eq_before;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int xb0 = x0; xb0 < x1; xb0 += kTopkUnroll * 64) {  // wave-uniform trip count
+    uint32_t vv[kTopkUnroll];
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int x = xb0 + 64 * j + lane;
+      vv[j] = x < x1 ? u[x] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int x = xb0 + 64 * j + lane;
+      const uint32_t v = vv[j];
+      const bool gt = x < x1 && v > prefix;
+      const bool eq = x < x1 && v == prefix;
+      const uint64_t meq = __ballot(eq);
+      const bool take = gt || (eq && eq_seen + __popcll(meq & below) < kr);
+      const uint64_t mt = __ballot(take);
+      if (take) out[pos + __popcll(mt & below)] = x + add;
+      pos += __popcll(mt);
+      eq_seen += __popcll(meq);
+    }
   }
 }
 
@@ -296,7 +389,7 @@ hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int
 #define VS_EST(T, DD)                                                                                   \
   do {                                                                                                  \
     VS_TRACED(st, "vs_est_pass1", hipLaunchKernelGGL((vs_est_pass1_kernel<T, DD>), g1, dim3(256), 0, st, p, tp, tiles_total, partials)); \
-    VS_TRACED(st, "vs_est_combine", hipLaunchKernelGGL(vs_est_combine_kernel, dim3(n_lists), dim3(64), 0, st, p, tp, tiles_total,        \
+    VS_TRACED(st, "vs_est_combine", hipLaunchKernelGGL(vs_est_combine_kernel, dim3(n_lists), dim3(64 * kCombineGroups), 0, st, p, tp, tiles_total,        \
                        (const float2*)partials, lse2));                                                 \
     VS_TRACED(st, "vs_est_pass2", hipLaunchKernelGGL((vs_est_pass2_kernel<T, DD>), g1, dim3(256), 0, st, p, tp, tiles_total,          \
                        (const float*)lse2, v_score, s_score));                                           \
