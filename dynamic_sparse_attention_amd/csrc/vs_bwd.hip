@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kQThreads) void vs_bwd_dq_kernel(AttnParams p) {
   constexpr int OB_PITCH = D + 4;
   constexpr int OB_BYTES = 64 * OB_PITCH * 4;
   constexpr int BUF = KT_BYTES > OB_BYTES ? KT_BYTES : OB_BYTES;
-  __shared__ QMajorLds L;
+  __shared__ QMajorLds<> L;
   __shared__ __attribute__((aligned(16))) char buf[BUF];
 
   int hb, i_local;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kQThreads) void vs_bwd_dq_kernel(AttnParams p) {
   wk.kt = reinterpret_cast<T*>(buf) + wave * D * W::KTP;
   wk.sl2 = p.sl2;
 
-  qmajor_drive(p, rb, list, L, wk);
+  qmajor_drive(p, rb, list, L, qm_bits, wk);
 
   float* ob = reinterpret_cast<float*>(buf);
   for (int w = 0; w < 4; ++w) {
@@ -425,7 +425,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kKThreads) void vs_bwd_dkdv_cols_kernel(AttnParams p) {
   typedef KvWorker<T, D> W;
   __shared__ KvLds<T, D> L;
-  __shared__ uint32_t bits[kMaxBitWords];
+  uint32_t* bits = qm_bits;  // (nb_seg + 31) / 32 words of dynamic LDS
   const int tid = threadIdx.x;
   const int kh = tid >> 6;
   const int lane = tid & 63;
@@ -515,11 +515,12 @@ hipError_t launch_bwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st
   const dim3 gq((unsigned)(p.batch * p.h_q * p.nqb));
   const dim3 gs((unsigned)(p.batch * p.h_kv * p.nkb));
   const dim3 gc((unsigned)(p.batch * p.h_q * p.seg.n_seg * p.col_tiles * p.qranges));
+  const size_t dyn = qmajor_bits_bytes(p);
 #define VS_BWD(T, DD)                                                                           \
   do {                                                                                          \
     if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_dkdv_slash_kernel<T, DD>), gs, dim3(kKThreads), 0, st, p)); \
-    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_dkdv_cols_kernel<T, DD>), gc, dim3(kKThreads), 0, st, p));   \
-    if (gq.x) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_kernel<T, DD>), gq, dim3(kQThreads), 0, st, p));                 \
+    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_dkdv_cols_kernel<T, DD>), gc, dim3(kKThreads), dyn, st, p)); \
+    if (gq.x) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_kernel<T, DD>), gq, dim3(kQThreads), dyn, st, p));               \
   } while (0)
   if (d == 128) VS_BWD(float, 128);
   else VS_BWD(float, 64);

@@ -6,50 +6,40 @@
 // a running sum ("Ring Attention Paper Analysis", "The Blockwise
 // Partitioning Strategy").
 //
-// gfx950 design: one workgroup (4 waves) per (batch, Q head, 64-row query
-// block).  Every wave holds Q^T for all 64 rows in registers and consumes
-// whole 64-key tiles on its own (split over keys, not rows), so a K or V row
-// is read by exactly one wave: K goes straight from global memory into the
-// A operand of S^T = K Q^T, V is transposed through the wave's own LDS
-// region for the A operand of O^T += V^T P^T, and P^T feeds the second
-// product from registers (slot_perm).  Softmax state is fp32; P is rounded
-// to bf16 for the matrix cores when the inputs are bf16.  The four waves'
-// (max, sum, O) merge through LDS at the end.
+// gfx950 design.  bf16 inputs: the row-split kernel below (K and V tiles
+// staged in LDS by direct loads, shared by the two waves that own a query
+// block's 64 rows).  fp32 inputs (vs_fwd_f32_kernel): one workgroup (4 waves)
+// per (batch, Q head, 64-row query block); every wave holds Q^T for all 64
+// rows in registers and consumes whole 64-key tiles on its own (split over
+// keys, not rows), so a K or V row is read by exactly one wave: K goes
+// straight from global memory into the A operand of S^T = K Q^T, V is
+// transposed through the wave's own LDS region for the A operand of
+// O^T += V^T P^T, and P^T feeds the second product from registers
+// (slot_perm).  Softmax state is fp32.  The four waves' (max, sum, O) merge
+// through LDS at the end.
 #include "vs_rows.h"
 #include "vs_trace.h"
 
 namespace vs {
 
-template <typename T, int D>
-struct FwdWorker {
-  typedef Mfma<T> MF;
+template <int D>
+struct FwdWorkerF32 {
+  typedef Mfma<float> MF;
   typedef typename MF::frag frag;
-  static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int KPL = MF::KPL;
   static constexpr int KC = 2 * KPL;
   static constexpr int NCD = D / KC;   // k chunks over head_dim
   static constexpr int NCT = D / 32;   // 32-channel output tiles
   static constexpr int NCK = 32 / KC;  // k chunks over 32 keys
-  // bf16: the 32 K rows and the 32 V rows of a half-tile go global -> LDS
-  // directly (global_load_lds_dwordx4, 1 KiB per instruction = RPI rows) into
-  // row-major tiles (row r at r * CPR * 16 bytes) with chunk c of row r at
-  // chunk index c ^ swz(r).  The K operand is read row-wise (rows {0-3, 8-11}
-  // + 4k, eight lanes at a time), the V operand transposed
-  // (ds_read_b64_tr_b16, four consecutive rows by sixteen lanes); swz sends
-  // both to eight distinct 16-byte bank groups.
-  static constexpr int CPR = D / 8;                      // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;                   // rows per load instruction
-  static constexpr int NVL = 32 / RPI;                   // load instructions per 32 rows
-  __device__ static constexpr int swz(int r) { return 2 * (r & 3) + ((r >> 3) & 1); }
-  // fp32: V transposed through registers into [channel][key] (pitch VTP).
+  // V transposed through registers into [channel][key] (pitch VTP).
   static constexpr int VTP = 32 + 4;
-  static constexpr int CG = 4;                           // fp32 channels per 16-byte load
-  static constexpr int KG = 2;                           // fp32 keys per 8-byte store
+  static constexpr int CG = 4;         // channels per 16-byte load
+  static constexpr int KG = 2;         // keys per 8-byte store
   static constexpr int NKG = 32 / KG;
-  static constexpr int NVG = kBf16 ? 1 : NKG * (D / CG) / 64;
-  static constexpr int VBUF = kBf16 ? 32 * D * 2 : D * VTP * 4;  // bytes per staging buffer
+  static constexpr int NVG = NKG * (D / CG) / 64;
+  static constexpr int VBUF = D * VTP * 4;  // bytes per staging buffer
   // Rescale the output only when a row max grows by more than 2^8 (in the
-  // exp2 domain): exp2(t - m) then stays below 256, exact enough in bf16/fp32.
+  // exp2 domain): exp2(t - m) then stays below 256.
   static constexpr float kRescale = 8.f;
 
   // The half-tile in flight: K operand and S^T.
@@ -60,20 +50,12 @@ struct FwdWorker {
 
   frag qf[2][NCD];
   f32x16 o[2][NCT];
-  // bf16: this wave's K and V tiles, a ring of two each, every tile in an LDS
-  // array of its own; per-lane offsets of the K (row) and V (transposed)
-  // operand reads, so that the per-read part is an immediate offset.
-  char* kl[2];
-  char* vl[2];
-  uint32_t kla[2], vla[2];  // their LDS byte addresses (wave-uniform)
-  int ro[4];
-  int to[2];
-  f32x4 vr[kBf16 ? 1 : NVG * KG];   // fp32 path: raw V rows of the next half-tile
+  f32x4 vr[NVG * KG];   // raw V rows of the next half-tile
   float m[2], l[2];
-  const T* kb;   // K of (batch, kv head): row pos at kb + pos * kvs
-  const T* vb;
+  const float* kb;      // K of (batch, kv head): row pos at kb + pos * kvs
+  const float* vb;
   int kvs;
-  char* vt;      // this wave's two staging buffers [2][VBUF]
+  char* vt;             // this wave's two staging buffers [2][VBUF]
   float sl2;
 
   template <class Set>
@@ -83,62 +65,12 @@ struct FwdWorker {
     const int l32 = lane & 31;
     // A operand of S^T = K Q^T: slot l32 loads key slot_perm(l32) of the half.
     const unsigned key = S.key_pos(n, slot_perm<KPL>(l32));
-    const T* krow = kb + key * (unsigned)kvs + hl * KPL;
+    const float* krow = kb + key * (unsigned)kvs + hl * KPL;
 #pragma unroll
-    for (int c = 0; c < NCD; ++c) k[c] = load_frag<T>(krow + c * KC);
+    for (int c = 0; c < NCD; ++c) k[c] = load_frag<float>(krow + c * KC);
   }
 
-  __device__ __forceinline__ void init_offsets() {
-    const int lane = threadIdx.x & 63;
-    const int hl = lane >> 5;
-    const int sp = slot_perm<KPL>(lane & 31);
-    // row operand: row sp, chunk 2c + hl; the XOR permutes chunks inside
-    // groups of 8, so the offset is ro[c % 4] + 128 * (c / 4)
-#pragma unroll
-    for (int cl = 0; cl < 4; ++cl) ro[cl] = sp * (CPR * 16) + 16 * ((2 * cl + hl) ^ swz(sp));
-    // transposed operand: lane i of a 16-lane group reads row 16c + 8h + 4q +
-    // i/4 at chunk 4ct + x (x < 4); swz = 2(i/4) + h, so the chunk is
-    // 4 (ct ^ zh) + zl with z = x ^ swz
-    const int g = lane >> 4;
-    const int sg = lane & 15;
-    const int rr = sg >> 2;
-    const int x = 2 * (g & 1) + ((sg & 3) >> 1);
-    const int z = x ^ (2 * rr + hl);
-    const int base = (8 * hl + rr) * (CPR * 16) + 16 * (z & 3) + 8 * (sg & 1);
-    to[0] = base + 64 * (z >> 2);
-    to[1] = base + 64 * (1 - (z >> 2));
-  }
-
-  // bf16: the 32 rows (K or V, from src) of half n straight into tile dst
-  // (asynchronous; NVL vector-memory instructions).
-  template <class Set>
-  __device__ __forceinline__ void dma_rows(const Set& S, int n, const T* src, uint32_t dst) const {
-    const int lane = threadIdx.x & 63;
-    const int rr = lane / CPR;
-    if constexpr (Set::kContiguous) {
-      const uint32_t o0 = (uint32_t)S.key_pos(n, rr) * (uint32_t)(kvs * sizeof(T));
-#pragma unroll
-      for (int u = 0; u < NVL; ++u) {
-        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
-        dma_lds16_so(src, o0 + (uint32_t)(u * RPI * kvs * sizeof(T)) + chunk * 16, dst + u * 1024);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < NVL; ++u) {
-        const int chunk = (lane % CPR) ^ swz(u * RPI + rr);
-        dma_lds16_so(src, (uint32_t)S.key_pos(n, rr + u * RPI) * (uint32_t)(kvs * sizeof(T)) + chunk * 16,
-                     dst + u * 1024);
-      }
-    }
-  }
-
-
-  // bf16: A operand of S^T = K Q^T from a K tile: key slot_perm(L%32), chunk 2c + L/32.
-  __device__ __forceinline__ frag k_frag(const char* src, int c) const {
-    return *reinterpret_cast<const frag*>(src + ro[c & 3] + 128 * (c >> 2));
-  }
-
-  // fp32: V rows of half n into registers.
+  // V rows of half n into registers.
   template <class Set>
   __device__ __forceinline__ void load_v(const Set& S, int n) {
     const int lane = threadIdx.x & 63;
@@ -153,23 +85,21 @@ struct FwdWorker {
     }
   }
 
-  // fp32 path: raw V rows transposed into dst[channel][key].
+  // Raw V rows transposed into dst[channel][key].
   __device__ __forceinline__ void stage(char* dst) const {
-    if constexpr (!kBf16) {
-      const int lane = threadIdx.x & 63;
-      float* df = reinterpret_cast<float*>(dst);
+    const int lane = threadIdx.x & 63;
+    float* df = reinterpret_cast<float*>(dst);
 #pragma unroll
-      for (int g = 0; g < NVG; ++g) {
-        const int gi = g * 64 + lane;
-        const int kg = gi % NKG;
-        const int cg = gi / NKG;
+    for (int g = 0; g < NVG; ++g) {
+      const int gi = g * 64 + lane;
+      const int kg = gi % NKG;
+      const int cg = gi / NKG;
 #pragma unroll
-        for (int c = 0; c < CG; ++c) {
-          f32x2 pk;
-          pk[0] = vr[g * KG][c];
-          pk[1] = vr[g * KG + 1][c];
-          *reinterpret_cast<f32x2*>(df + (cg * CG + c) * VTP + kg * KG) = pk;
-        }
+      for (int c = 0; c < CG; ++c) {
+        f32x2 pk;
+        pk[0] = vr[g * KG][c];
+        pk[1] = vr[g * KG + 1][c];
+        *reinterpret_cast<f32x2*>(df + (cg * CG + c) * VTP + kg * KG) = pk;
       }
     }
   }
@@ -177,24 +107,9 @@ struct FwdWorker {
   // A operand of O^T += V^T P^T: channels 32ct + L%32, keys of k chunk c.
   __device__ __forceinline__ frag vt_frag(const char* src, int ct, int c) const {
     const int lane = threadIdx.x & 63;
-    if constexpr (kBf16) {
-      // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element
-      // i%4 of the 8 bytes read by lanes i/4, 4+i/4, 8+i/4, 12+i/4, i.e.
-      // channel 32ct + 16(g%2) + i of keys 16c + 8h + 4q .. +3.
-      typedef short v4s __attribute__((ext_vector_type(4)));
-      typedef short v8s __attribute__((ext_vector_type(8)));
-      v4s part[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(
-            src + to[ct & 1] + 64 * (ct & ~1) + (16 * c + 4 * q) * (CPR * 16)));
-      const v8s both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      return __builtin_bit_cast(frag, both);
-    } else {
-      const int hl = lane >> 5;
-      const int l32 = lane & 31;
-      return reinterpret_cast<const float*>(src)[(32 * ct + l32) * VTP + c * KC + hl * KPL];
-    }
+    const int hl = lane >> 5;
+    const int l32 = lane & 31;
+    return reinterpret_cast<const float*>(src)[(32 * ct + l32) * VTP + c * KC + hl * KPL];
   }
 
   __device__ __forceinline__ void scores(const frag (&k)[NCD], f32x16 (&s)[2]) const {
@@ -203,15 +118,6 @@ struct FwdWorker {
       s[rg] = f32x16{0};
 #pragma unroll
       for (int c = 0; c < NCD; ++c) s[rg] = MF::mma(k[c], qf[rg][c], s[rg]);
-    }
-  }
-
-  __device__ __forceinline__ void scores_lds(const char* ksrc, f32x16 (&s)[2]) const {
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      s[rg] = f32x16{0};
-#pragma unroll
-      for (int c = 0; c < NCD; ++c) s[rg] = MF::mma(k_frag(ksrc, c), qf[rg][c], s[rg]);
     }
   }
 
@@ -255,7 +161,7 @@ struct FwdWorker {
   }
 
   // Online softmax, second part: P = exp2(s*scale*log2e - m), row sums, and
-  // P^T of both row groups as bf16 (or fp32) B operands.
+  // P^T of both row groups as B operands.
   __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[2], frag (&pf)[2][NCK]) {
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
@@ -286,7 +192,7 @@ struct FwdWorker {
     }
   }
 
-  // fp32: half-tile n with S^T(n) in b.s and V(n) staged in buffer n & 1.
+  // Half-tile n with S^T(n) in b.s and V(n) staged in buffer n & 1.
   // K(n+1) is requested first so that its latency hides behind the softmax
   // of n; V(n+2) is read into registers while S^T(n+1) runs.  Past the end
   // the last half is reloaded and recomputed instead of branching (results
@@ -307,88 +213,33 @@ struct FwdWorker {
     pv(cur, pf);
   }
 
-  // bf16: half-tile n (P = n % 2) with S^T(n) in s, K(n+1) in tile kl[P ^ 1]
-  // and V(n), V(n+1) in tiles vl[P], vl[P ^ 1] (landed or in flight).  K(n+2)
-  // goes out first, into the tile K(n) used (S^T(n) is done), V(n+2) last,
-  // into the tile V(n) used (its products are issued): K gets a step and a
-  // half to land, V two steps.  Loads return in order, so once K(n+1) is in,
-  // V(n) is too.  Past the end the last half is reloaded and recomputed
-  // instead of branching (results unused).
-  template <int P, class Set>
-  __device__ __forceinline__ void step2(const Set& S, int n, int N, f32x16 (&s)[2]) {
-    frag pf[2][NCK];
-    const int n2 = n + 2 < N ? n + 2 : N - 1;
-    dma_rows(S, n2, kb, kla[P]);
-    __builtin_amdgcn_sched_barrier(0);
-    softmax_max(S, n, s);
-    softmax_exp(s, pf);
-    // in flight may remain: V(n+1), K(n+2)
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * NVL));
-    wave_sync();
-    scores_lds(kl[P ^ 1], s);
-    pv(vl[P], pf);
-    // the reads of V(n) are done before V(n+2) may land in their place
-    __builtin_amdgcn_s_waitcnt(lgkmcnt_wait0());
-    dma_rows(S, n2, vb, vla[P]);
-  }
-
   template <class Set>
   __device__ __forceinline__ void run(const Set& S) {
     const int N = S.n_halves();
     if (N == 0) return;
-    if constexpr (kBf16) {
-      f32x16 s[2];
-      const int n1 = N > 1 ? 1 : 0;
-      dma_rows(S, 0, kb, kla[0]);
-      dma_rows(S, 0, vb, vla[0]);
-      dma_rows(S, n1, kb, kla[1]);
-      dma_rows(S, n1, vb, vla[1]);
-      __builtin_amdgcn_s_waitcnt(vmcnt_wait(3 * NVL));
-      wave_sync();
-      scores_lds(kl[0], s);
-      // a set always has an even number of halves (two per 64-key tile)
-      for (int n = 0; n < N; n += 2) {
-        step2<0>(S, n, N, s);
-        step2<1>(S, n + 1, N, s);
-      }
-    } else {
-      Buf b;
-      load_v(S, 0);
-      stage(vt);
-      load_v(S, N > 1 ? 1 : 0);
-      load_k(S, 0, b.k);
-      scores(b.k, b.s);
-      for (int n = 0; n < N; ++n) step(S, n, N, b);
-    }
+    Buf b;
+    load_v(S, 0);
+    stage(vt);
+    load_v(S, N > 1 ? 1 : 0);
+    load_k(S, 0, b.k);
+    scores(b.k, b.s);
+    for (int n = 0; n < N; ++n) step(S, n, N, b);
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
     wave_sync();
   }
 };
 
-template <typename T, int D>
-struct FwdLds {
-  static constexpr bool kBf16 = sizeof(T) == 2;
-  static constexpr int OB_PITCH = D + 4;
-  static constexpr int OB_BYTES = 64 * OB_PITCH * 4;
-  // fp32: both V staging buffers of every wave; bf16: the four LDS arrays of
-  // K / V tiles (one tile per wave in each); the first also holds the
-  // output merge afterwards.
-  static constexpr int VT_BYTES = kBf16 ? 0 : 4 * 2 * FwdWorker<T, D>::VBUF;
-  static constexpr int TILE_BYTES = kBf16 ? 4 * 32 * D * 2 : 16;
-  static constexpr int BUF0 = kBf16 ? (TILE_BYTES > OB_BYTES ? TILE_BYTES : OB_BYTES)
-                                    : (VT_BYTES > OB_BYTES ? VT_BYTES : OB_BYTES);
-};
-
-template <typename T, int D>
-__global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
-  typedef FwdWorker<T, D> W;
-  typedef FwdLds<T, D> LD;
-  // fp32 needs most of the LDS for its staging buffers: smaller column batches
-  __shared__ QMajorLds<kQThreads, sizeof(T) == 2 ? kColBatch : 2 * kQThreads> L;
-  __shared__ __attribute__((aligned(16))) char buf[LD::BUF0];
-  __shared__ __attribute__((aligned(16))) char tk1[LD::TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char tv0[LD::TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char tv1[LD::TILE_BYTES];
+template <int D>
+__global__ __launch_bounds__(kQThreads) void vs_fwd_f32_kernel(AttnParams p) {
+  typedef FwdWorkerF32<D> W;
+  constexpr int OB_PITCH = D + 4;
+  constexpr int OB_BYTES = 64 * OB_PITCH * 4;
+  // both V staging buffers of every wave; the output merge afterwards
+  constexpr int VT_BYTES = 4 * 2 * W::VBUF;
+  constexpr int BUF0 = VT_BYTES > OB_BYTES ? VT_BYTES : OB_BYTES;
+  // most of the LDS holds the staging buffers: smaller column batches
+  __shared__ QMajorLds<kQThreads, 2 * kQThreads> L;
+  __shared__ __attribute__((aligned(16))) char buf[BUF0];
   __shared__ float s_m[4][64];
   __shared__ float s_l[4][64];
 
@@ -407,36 +258,25 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
   const int l32 = lane & 31;
 
   W wk;
-  const T* q = reinterpret_cast<const T*>(p.q);
+  const float* q = reinterpret_cast<const float*>(p.q);
   const size_t qrow0 = (size_t)b * p.n_q + (size_t)i_local * kBlock;
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
-    const T* qr = q + ((qrow0 + 32 * rg + l32) * p.h_q + h) * D;
+    const float* qr = q + ((qrow0 + 32 * rg + l32) * p.h_q + h) * D;
 #pragma unroll
-    for (int c = 0; c < W::NCD; ++c) wk.qf[rg][c] = load_frag<T>(qr + c * W::KC + hl * W::KPL);
+    for (int c = 0; c < W::NCD; ++c) wk.qf[rg][c] = load_frag<float>(qr + c * W::KC + hl * W::KPL);
 #pragma unroll
     for (int ct = 0; ct < W::NCT; ++ct) wk.o[rg][ct] = f32x16{0};
     wk.m[rg] = -INFINITY;
     wk.l[rg] = 0.f;
   }
   wk.kvs = p.h_kv * D;
-  wk.kb = reinterpret_cast<const T*>(p.k) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
-  wk.vb = reinterpret_cast<const T*>(p.v) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
+  wk.kb = reinterpret_cast<const float*>(p.k) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
+  wk.vb = reinterpret_cast<const float*>(p.v) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
   wk.vt = buf + wave * 2 * W::VBUF;
-  wk.kl[0] = buf + wave * 32 * D * 2;
-  wk.kl[1] = tk1 + wave * 32 * D * 2;
-  wk.vl[0] = tv0 + wave * 32 * D * 2;
-  wk.vl[1] = tv1 + wave * 32 * D * 2;
-  if constexpr (W::kBf16) {
-    wk.init_offsets();
-    for (int i = 0; i < 2; ++i) {
-      wk.kla[i] = lds_addr(wk.kl[i]);
-      wk.vla[i] = lds_addr(wk.vl[i]);
-    }
-  }
   wk.sl2 = p.sl2;
 
-  qmajor_drive(p, rb, list, L, wk);
+  qmajor_drive(p, rb, list, L, qm_bits, wk);
 
   // Combine the four waves' states: global max, rescaled sums and outputs.
   if (hl == 0) {
@@ -466,7 +306,7 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
             const int ch = 32 * ct + 8 * i4 + 4 * hl;
-            float* dst = ob + (32 * rg + l32) * LD::OB_PITCH + ch;
+            float* dst = ob + (32 * rg + l32) * OB_PITCH + ch;
             f32x4 v;
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = wk.o[rg][ct][4 * i4 + u] * f[rg];
@@ -498,18 +338,9 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
   for (int x = tid; x < 64 * D / 4; x += kQThreads) {
     const int r = x / (D / 4);
     const int c4 = (x % (D / 4)) * 4;
-    f32x4 v = *reinterpret_cast<const f32x4*>(ob + r * LD::OB_PITCH + c4) * s_inv[r];
+    f32x4 v = *reinterpret_cast<const f32x4*>(ob + r * OB_PITCH + c4) * s_inv[r];
     const size_t off = ((qrow0 + r) * p.h_q + h) * D + c4;
-    if (p.o_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o_out) + off) = v;
-    } else if (sizeof(T) == 2) {
-      bf16x4 w4;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) w4[u] = (__bf16)v[u];
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.o_out) + off) = w4;
-    } else {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o_out) + off) = v;
-    }
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o_out) + off) = v;
   }
 }
 
@@ -522,9 +353,10 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_kernel(AttnParams p) {
 // 250 registers in all, so two waves fit on a SIMD); per half-tile
 // S^T = K Q^T reads K row-wise from LDS, the online softmax runs on the 16
 // scores per lane, and O^T += V^T P^T reads V transposed (ds_read_b64_tr_b16)
-// with P^T taken from registers (slot_perm).  With NS = 2 a workgroup needs
-// under 80 KB of LDS, so two independent workgroups share a CU: one's index
-// expansion, waits and output merge overlap the other's products.
+// with P^T taken from registers (slot_perm).  With NS = 1 (the launched
+// form) a workgroup is two waves and needs under 40 KB of LDS, so four
+// independent workgroups share a CU: one's index expansion, waits and output
+// merge overlap the others' products.
 
 template <int D>
 struct FwdRowsWorker : RowsTiles<D> {
@@ -679,7 +511,7 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int OB_BYTES = 64 * OB_PITCH * 4;
   // [ring slot][K, V][stream] tiles
   constexpr int TILES = 2 * 2 * NS * W::TB;
-  __shared__ QMajorLds<NT, kColBatch, NS == 2 ? kRowsBitWords : kMaxBitWords> L;
+  __shared__ QMajorLds<NT, RowsLdsCfg<NS>::kCols> L;
   __shared__ __attribute__((aligned(16))) char tiles[TILES > OB_BYTES ? TILES : OB_BYTES];
   __shared__ float s_m[NS][64];
   __shared__ float s_l[NS][64];
@@ -727,7 +559,7 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   wk.sl2 = p.sl2;
   wk.init_offsets();
 
-  qmajor_drive<NS>(p, rb, list, L, wk);
+  qmajor_drive<NS>(p, rb, list, L, qm_bits, wk);
 
   // Combine the streams' states of every row.
   if (hl == 0) {
@@ -788,14 +620,11 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
 hipError_t launch_fwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st) {
   const dim3 grid((unsigned)(p.batch * p.h_q * p.nqb));
   if (grid.x == 0) return hipSuccess;
-  // the two-stream kernel's bitmap covers segments of up to 32 * kRowsBitWords blocks
-  const bool rows = max_segment_blocks(p) <= 32 * kRowsBitWords;
-  if (dtype_bf16 && d == 128 && rows) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<128, 2>), grid, dim3(256), 0, st, p));
-  else if (dtype_bf16 && d == 64 && rows) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<64, 2>), grid, dim3(256), 0, st, p));
-  else if (dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<__bf16, 128>), grid, dim3(kQThreads), 0, st, p));
-  else if (dtype_bf16 && d == 64) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<__bf16, 64>), grid, dim3(kQThreads), 0, st, p));
-  else if (!dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<float, 128>), grid, dim3(kQThreads), 0, st, p));
-  else VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_kernel<float, 64>), grid, dim3(kQThreads), 0, st, p));
+  const size_t dyn = qmajor_bits_bytes(p);
+  if (dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<128, 1>), grid, dim3(128), dyn, st, p));
+  else if (dtype_bf16) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<64, 1>), grid, dim3(128), dyn, st, p));
+  else if (d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_f32_kernel<128>), grid, dim3(kQThreads), dyn, st, p));
+  else VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_f32_kernel<64>), grid, dim3(kQThreads), dyn, st, p));
   return hipGetLastError();
 }
 

@@ -15,7 +15,6 @@
 namespace vs {
 
 constexpr int kQThreads = 256;
-constexpr int kMaxBitWords = 2048;  // block offsets < 65536 (segments up to 4M tokens)
 
 // The half-tiles (32 keys) one key stream consumes from the current tile
 // list: tiles wave, wave + NS, ... (round-robin over NS streams), two halves
@@ -72,12 +71,9 @@ constexpr int kColBatch = 1024;
 typedef SlashSetT<4> SlashSet;
 typedef ColSetT<4> ColSet;
 
-// NBITS words of block-diagonal bitmap: segments of up to 32 * NBITS blocks.
-template <int NT = kQThreads, int NCOL = kColBatch, int NBITS = kMaxBitWords>
+template <int NT = kQThreads, int NCOL = kColBatch>
 struct QMajorLds {
   static constexpr int kCols = NCOL;
-  static constexpr int kBitWords = NBITS;
-  uint32_t bits[NBITS];
   int tiles[NT];
   int cols[NCOL];
   int coff[NCOL];
@@ -86,9 +82,11 @@ struct QMajorLds {
 
 // NT threads; wave w consumes the tiles of key stream w % NS (with more
 // waves than streams, the waves of a stream split its rows).
-template <int NS = 4, int NT, int NCOL, int NBITS, class Worker>
+// bits: the block-diagonal bitmap, (longest segment's blocks + 31) / 32 words
+// of dynamic LDS (qmajor_bits_bytes).
+template <int NS = 4, int NT, int NCOL, class Worker>
 __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list,
-                                             QMajorLds<NT, NCOL, NBITS>& L, Worker& wk) {
+                                             QMajorLds<NT, NCOL>& L, uint32_t* bits, Worker& wk) {
   const int tid = threadIdx.x;
   const int wave = (tid >> 6) % NS;
   const int sp0 = p.s_ptr[list];
@@ -96,11 +94,11 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
 
   // Bitmap of the selected block-diagonals, for the "already covered" test.
   const int nwords = (rb.nb_seg + 31) >> 5;
-  for (int w = tid; w < nwords; w += NT) L.bits[w] = 0u;
+  for (int w = tid; w < nwords; w += NT) bits[w] = 0u;
   __syncthreads();
   for (int e = tid; e < ns; e += NT) {
     const int g = p.s_idx[sp0 + e];
-    if (g >= 0 && g < rb.nb_seg) atomicOr(&L.bits[g >> 5], 1u << (g & 31));
+    if (g >= 0 && g < rb.nb_seg) atomicOr(&bits[g >> 5], 1u << (g & 31));
   }
   __syncthreads();
 
@@ -175,7 +173,7 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
       const int bm = m / kBlock - rb.a_blk;
       if (e < vlimit) {
         const int off = rb.beta - bm;
-        keep = ((L.bits[off >> 5] >> (off & 31)) & 1u) == 0u;
+        keep = ((bits[off >> 5] >> (off & 31)) & 1u) == 0u;
       }
       int tot;
       const int slot = block_compact<NT>(keep, L.wsum, &tot);
@@ -224,5 +222,23 @@ __device__ __forceinline__ void qmajor_item(const AttnParams& p, int wg, int* hb
   }
   *i_local = p.nqb - 1 - ir;
 }
+
+// Longest segment of a call, in blocks (the whole index grid when striped).
+inline int max_segment_blocks(const AttnParams& p) {
+  if (p.W != 1) return p.n_global / kBlock;
+  int nb = 0;
+  for (int s = 0; s < p.seg.n_seg; ++s) {
+    const int l = p.seg.start_blk[s + 1] - p.seg.start_blk[s];
+    nb = l > nb ? l : nb;
+  }
+  return nb;
+}
+
+// Dynamic LDS of the query-major kernels: the block-diagonal bitmap.
+inline size_t qmajor_bits_bytes(const AttnParams& p) {
+  return (size_t)((max_segment_blocks(p) + 31) / 32) * 4 + 4;
+}
+
+extern __shared__ uint32_t qm_bits[];
 
 }  // namespace vs

@@ -137,19 +137,14 @@ struct RowsTiles {
   }
 };
 
-// Bitmap words of the row-split kernels: segments of up to 32768 blocks
-// (longer ones take the four-wave kernels).
-constexpr int kRowsBitWords = 1024;
-
-// Longest segment of a call, in blocks (the whole index grid when striped).
-inline int max_segment_blocks(const AttnParams& p) {
-  if (p.W != 1) return p.n_global / kBlock;
-  int nb = 0;
-  for (int s = 0; s < p.seg.n_seg; ++s) {
-    const int l = p.seg.start_blk[s + 1] - p.seg.start_blk[s];
-    nb = l > nb ? l : nb;
-  }
-  return nb;
-}
+// Index-expansion LDS for NS key streams: with one stream a workgroup (two
+// waves) must fit in a quarter of the CU's LDS, so its column batches are
+// smaller.
+template <int NS> struct RowsLdsCfg {
+  static constexpr int kCols = kColBatch;
+};
+template <> struct RowsLdsCfg<1> {
+  static constexpr int kCols = 256;
+};
 
 }  // namespace vs
