@@ -427,8 +427,18 @@ vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, 
   a.dv = dv;
   a.dq_accumulate = dq_accumulate != 0;
   a.col_tiles = (idx->v_cap_max + 63) / 64;
-  a.qrange_len = 128;
+  // Column units of about 48 query blocks.  Consecutive units of a column
+  // tile differ in the query range and go round-robin to the 8 XCDs; with a
+  // range count that is a multiple of 8 every XCD would always get the same
+  // ranges, and the early ranges carry little work (few columns start that
+  // early), which left one XCD with over twice the work of another.  An odd
+  // count spreads every column tile's ranges over all XCDs.
+  a.qrange_len = 48;
   a.qranges = (c.nqb + a.qrange_len - 1) / a.qrange_len;
+  while (a.qranges > 1 && a.qranges % 2 == 0) {
+    ++a.qrange_len;
+    a.qranges = (c.nqb + a.qrange_len - 1) / a.qrange_len;
+  }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (!delta) {
