@@ -441,14 +441,27 @@ vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, 
   }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (!delta) {
-    float* dws = reinterpret_cast<float*>(base + w.delta);
-    e = vs::launch_delta(o, o_f32 != 0, c.bf16, dout, dws, c.batch, c.n_q, c.h_q, c.d, s);
-    delta = dws;
+  float* l2 = reinterpret_cast<float*>(base + w.lse2);
+  a.o = o;
+  a.o_f32 = o_f32 != 0;
+  if (c.bf16) {
+    // The dQ kernel runs first and writes delta (when none is given) and
+    // LSE * log2(e) of its rows for the dK/dV kernels.
+    if (!delta) {
+      float* dws = reinterpret_cast<float*>(base + w.delta);
+      a.delta_out = dws;
+      delta = dws;
+    }
+    a.lse2_out = l2;
+  } else {
+    if (!delta) {
+      float* dws = reinterpret_cast<float*>(base + w.delta);
+      e = vs::launch_delta(o, o_f32 != 0, c.bf16, dout, dws, c.batch, c.n_q, c.h_q, c.d, s);
+      delta = dws;
+    }
+    if (e == hipSuccess) e = vs::launch_lse_log2(lse, l2, (size_t)c.batch * c.h_q * c.n_q, s);
   }
   a.delta = delta;
-  float* l2 = reinterpret_cast<float*>(base + w.lse2);
-  if (e == hipSuccess) e = vs::launch_lse_log2(lse, l2, (size_t)c.batch * c.h_q * c.n_q, s);
   a.lse2 = l2;
   if (e == hipSuccess) e = vs::launch_prep_vertical(a, c.n_lists(), idx->v_ptr, idx->v_idx, s);
   if (e == hipSuccess) e = vs::launch_bwd(a, c.bf16, c.d, s);

@@ -32,6 +32,8 @@ struct AttnParams {
   float* lse;         // forward: written; backward: read
   const float* delta; // backward only
   const float* lse2;  // backward only: LSE * log2(e), +inf for an empty row
+  float* delta_out;   // backward, bf16 dQ kernel: compute delta of its rows from o, dout and store it here
+  float* lse2_out;    // backward, bf16 dQ kernel: store LSE * log2(e) of its rows here
   float* dq;
   float* dk;
   float* dv;

@@ -508,9 +508,11 @@ hipError_t launch_bwd_dq_bf16(const AttnParams& p, int d, hipStream_t st);
 // fp32 inputs the kernels of this file.
 hipError_t launch_bwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st) {
   if (dtype_bf16) {
-    hipError_t e = launch_bwd_kv_bf16(p, d, st);
+    // dQ first: with delta_out / lse2_out set it writes the row terms the
+    // dK/dV kernels read.
+    hipError_t e = launch_bwd_dq_bf16(p, d, st);
     if (e != hipSuccess) return e;
-    return launch_bwd_dq_bf16(p, d, st);
+    return launch_bwd_kv_bf16(p, d, st);
   }
   const dim3 gq((unsigned)(p.batch * p.h_q * p.nqb));
   const dim3 gs((unsigned)(p.batch * p.h_kv * p.nkb));

@@ -171,7 +171,39 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
     const size_t li = ((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + r;
     const float lse = p.lse[li];
     wk.lse2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
-    wk.dl = p.delta[li];
+    if (p.delta_out) {
+      // delta = rowsum(dO * O) of this lane's row (Eq. 1), from the dO^T
+      // fragments already in registers; lanes L and L + 32 hold the two
+      // halves of every channel chunk of one row.
+      float acc = 0.f;
+      if (p.o_f32) {
+        const float* o = reinterpret_cast<const float*>(p.o) + roff;
+#pragma unroll
+        for (int c = 0; c < W::NCD; ++c) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(o + c * W::KC);
+          const f32x4 a2 = *reinterpret_cast<const f32x4*>(o + c * W::KC + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc = __builtin_fmaf(a[j], (float)wk.dof[c][j], acc);
+            acc = __builtin_fmaf(a2[j], (float)wk.dof[c][4 + j], acc);
+          }
+        }
+      } else {
+        const __bf16* o = reinterpret_cast<const __bf16*>(p.o) + roff;
+#pragma unroll
+        for (int c = 0; c < W::NCD; ++c) {
+          const bf16x8 a = load_frag<__bf16>(o + c * W::KC);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc = __builtin_fmaf((float)a[j], (float)wk.dof[c][j], acc);
+        }
+      }
+      acc += __shfl_xor(acc, 32, 64);
+      wk.dl = acc;
+      if (hl == 0) p.delta_out[li] = acc;
+    } else {
+      wk.dl = p.delta[li];
+    }
+    if (p.lse2_out && hl == 0) p.lse2_out[li] = wk.lse2;
   }
 #pragma unroll
   for (int ct = 0; ct < W::NCT; ++ct) wk.dq[ct] = f32x16{0};
