@@ -110,6 +110,11 @@ vs_status check_problem(const vs_problem* p, Prob* c) {
   }
   if ((long long)p->batch * p->n_q > (1ll << 31) / 64 || (long long)p->batch * p->n_k > (1ll << 31) / 64)
     return fail(VS_ERR_UNSUPPORTED, "batch * tokens too large");
+  // The bf16 attention kernels address K and V rows of one (batch, KV head)
+  // with 32-bit byte offsets.
+  if (p->dtype == VS_BF16 && (long long)p->n_k * p->h_kv * p->head_dim * 2 >= (1ll << 32))
+    return fail(VS_ERR_UNSUPPORTED, "n_k * h_kv * head_dim * 2 = %lld bytes of K per sequence exceeds 4 GiB",
+                (long long)p->n_k * p->h_kv * p->head_dim * 2);
   c->batch = p->batch;
   c->h_q = p->h_q;
   c->h_kv = p->h_kv;

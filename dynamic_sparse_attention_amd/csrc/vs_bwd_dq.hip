@@ -64,11 +64,7 @@ struct DqRowsWorker : RowsTiles<D> {
     const int lane = threadIdx.x & 63;
     const int hl = lane >> 5;
     const int r = 32 * rh + (lane & 31);
-    if (!S.full(n)) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (!S.valid(n, reg_row<KPL>(i, hl), r)) s[i] = -INFINITY;
-    }
+    if (!S.full(n)) S.template mask<KPL>(n, hl, r, s);
     float ds[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -156,7 +152,7 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   const int l32 = lane & 31;
 
   W wk;
-  wk.rh = wave / NS;
+  wk.rh = __builtin_amdgcn_readfirstlane(wave / NS);
   const int r = 32 * wk.rh + l32;  // this lane's row of the block
   const __bf16* q = reinterpret_cast<const __bf16*>(p.q);
   const __bf16* dout = reinterpret_cast<const __bf16*>(p.dout);

@@ -32,34 +32,46 @@ struct SlashSetT {
   __device__ __forceinline__ int key_pos(int n, int r) const { return (tv(n) >> 1) * kBlock + 32 * (n & 1) + r; }
   __device__ __forceinline__ bool full(int n) const { return (tv(n) & 1) == 0; }
   __device__ __forceinline__ bool valid(int n, int e, int r) const { return 32 * (n & 1) + e <= r; }
+  // -inf where key reg_row(i, hl) of half n is not visible from row r
+  template <int KPL>
+  __device__ __forceinline__ void mask(int n, int hl, int r, f32x16& s) const {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!valid(n, reg_row<KPL>(i, hl), r)) s[i] = -INFINITY;
+  }
 };
 
 template <int NS>
 struct ColSetT {
   static constexpr bool kContiguous = false;
   const int* cols;   // local key positions of the gathered columns
-  const int* coff;   // -1, or the first row (0..63) that may see the column
+  const int* coff;   // -1, or the first row (0..63) that may see the column (kBlock: none)
   int count;         // columns in the list
   int nt;            // 64-column tiles in the list
   int wave;          // key stream
   __device__ __forceinline__ int n_halves() const { return nt > wave ? 2 * ((nt - wave + NS - 1) / NS) : 0; }
   __device__ __forceinline__ int n_halves_max() const { return nt > 0 ? 2 * ((nt + NS - 1) / NS) : 0; }
   __device__ __forceinline__ int base(int n) const { return 64 * (wave + NS * (n >> 1)) + 32 * (n & 1); }
-  __device__ __forceinline__ int key_pos(int n, int r) const {
-    const int i = base(n) + r;
-    return cols[i < count ? i : 64 * (wave + NS * (n >> 1))];
-  }
+  // Entries past count up to the end of the last tile repeat a listed
+  // column (qmajor_drive fills them), so every read is of a valid position.
+  __device__ __forceinline__ int key_pos(int n, int r) const { return cols[base(n) + r]; }
   // Columns are in ascending position, so those with a per-row limit (inside
-  // the query block) come last: a half is unmasked if its last column has none.
-  __device__ __forceinline__ bool full(int n) const {
-    const int i = base(n) + 31;
-    return i < count && coff[i] < 0;
-  }
-  __device__ __forceinline__ bool valid(int n, int e, int r) const {
-    const int i = base(n) + e;
-    if (i >= count) return false;
-    const int c = coff[i];
-    return c < 0 || c <= r;
+  // the query block) come last, then the padding (limit kBlock, seen by no
+  // row): a half is unmasked if its last column has no limit.
+  __device__ __forceinline__ bool full(int n) const { return coff[base(n) + 31] < 0; }
+  __device__ __forceinline__ bool valid(int n, int e, int r) const { return coff[base(n) + e] <= r; }
+  // -inf where key reg_row(i, hl) of half n is not visible from row r; the
+  // limits of a lane's 16 keys are two runs of KPL = 8, read as four 16-byte
+  // loads.
+  template <int KPL>
+  __device__ __forceinline__ void mask(int n, int hl, int r, f32x16& s) const {
+    static_assert(KPL == 8, "bf16 operand layout");
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4* c = reinterpret_cast<const i32x4*>(coff + base(n) + hl * KPL);
+    const i32x4 q[4] = {c[0], c[1], c[4], c[5]};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (q[i / 4][i % 4] > r) s[i] = -INFINITY;
   }
 };
 
@@ -75,8 +87,8 @@ template <int NT = kQThreads, int NCOL = kColBatch>
 struct QMajorLds {
   static constexpr int kCols = NCOL;
   int tiles[NT];
-  int cols[NCOL];
-  int coff[NCOL];
+  alignas(16) int cols[NCOL];
+  alignas(16) int coff[NCOL];
   int wsum[NT / 64];
 };
 
@@ -88,7 +100,7 @@ template <int NS = 4, int NT, int NCOL, class Worker>
 __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list,
                                              QMajorLds<NT, NCOL>& L, uint32_t* bits, Worker& wk) {
   const int tid = threadIdx.x;
-  const int wave = (tid >> 6) % NS;
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) % NS);
   const int sp0 = p.s_ptr[list];
   const int ns = p.s_ptr[list + 1] - sp0;
 
@@ -188,6 +200,14 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
     const bool last = e0 >= vlimit;
     if (!last) fetch(e0);
     const int nt = last ? (count + 63) / 64 : count / 64;
+    if (last && (count & 63) != 0) {
+      // pad the last tile with a listed column that no row sees
+      for (int t = count + tid; t < 64 * nt; t += NT) {
+        L.cols[t] = L.cols[0];
+        L.coff[t] = kBlock;
+      }
+      __syncthreads();
+    }
     wk.run(ColSetT<NS>{L.cols, L.coff, last ? count : 64 * nt, nt, wave});
     if (last) break;
     __syncthreads();

@@ -80,7 +80,8 @@ typedef struct vs_problem {
   int32_t h_kv;         /* key/value heads; Q head h reads KV head h*h_kv/h_q      */
   int32_t head_dim;     /* 64 or 128                                              */
   int32_t n_q;          /* rows per batch row held by this call                   */
-  int32_t n_k;          /* keys per batch row held by this call                   */
+  int32_t n_k;          /* keys per batch row held by this call; for bf16,         
+                           n_k*h_kv*head_dim*2 < 2^32 (else VS_ERR_UNSUPPORTED)   */
   int32_t block;        /* B, 64 (the slash granularity of MTraining §4.1 (ii))    */
   int32_t dtype;        /* vs_dtype of Q, K, V, dO (and O unless o_f32)            */
   float scale;          /* score scale; <= 0 selects 1/sqrt(head_dim)             */
