@@ -102,6 +102,14 @@ def test_problem_validation(abi):
     assert status_of(abi, prob(abi, scale=float("nan"))) == abi.VS_ERR_SHAPE
     many = list(range(0, 64 * 130, 64))
     assert status_of(abi, prob(abi, cu=many)) == abi.VS_ERR_UNSUPPORTED
+    # bf16 K rows of one sequence are addressed with 32-bit byte offsets:
+    # 2^24 tokens x 2 KV heads x 128 x 2 bytes = 8 GiB is refused, fp32 (other
+    # kernels) and 2^23 tokens with one KV head (exactly 2^31 bytes) are not
+    big = [0, 1 << 22, 2 << 22, 3 << 22, 4 << 22]
+    assert status_of(abi, prob(abi, cu=big)) == abi.VS_ERR_UNSUPPORTED
+    assert "4 GiB" in L.vs_last_error().decode()
+    assert status_of(abi, prob(abi, cu=big, dtype=abi.VS_F32)) == abi.VS_OK
+    assert status_of(abi, prob(abi, cu=big[:3], h_q=1, h_kv=1)) == abi.VS_OK
     # block striping
     assert status_of(abi, prob(abi, cu=[0, 8192], n_q=1024, n_k=1024, stripe_world=8, q_rank=1,
                                k_rank=7)) == abi.VS_OK
