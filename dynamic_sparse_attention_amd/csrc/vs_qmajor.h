@@ -223,20 +223,33 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
 }
 
 // Work-item mapping of a query-major grid of batch*h_q*nqb workgroups.  The
-// dispatcher deals consecutive workgroup ids round-robin to the 8 XCDs; the
-// mapping gives each XCD a fixed set of heads (adjacent heads share a KV
-// head) and walks its query blocks from the last (most keys) to the first, so
-// blocks that share key blocks run close together on one L2.
+// dispatcher deals consecutive workgroup ids round-robin to the 8 XCDs, each
+// with its own L2.  The Q heads of one (batch, KV head) group read the same
+// K / V rows, and where their index lists overlap (shared block-diagonals or
+// columns) the same tiles: the mapping puts every head of a group on the same
+// XCD, the heads of one query block in consecutive slots, so that they run
+// together and share those tiles in L2.  With fewer groups than XCDs a group
+// spreads over 8 / groups XCDs, which take its query blocks in turn (block r
+// goes to the group's XCD r % (8 / groups), which balances the longer late
+// blocks); with more, each XCD takes whole groups.  Query blocks are walked
+// from the last (most keys) to the first.
 __device__ __forceinline__ void qmajor_item(const AttnParams& p, int wg, int* hb, int* i_local) {
-  const int HB = p.batch * p.h_q;
+  const int NG = p.batch * p.h_kv;
+  const int GS = p.h_q / p.h_kv;
+  const int xcd = wg & 7;
+  const int slot = wg >> 3;
   int ir;
-  if (HB % 8 == 0) {
-    const int per = HB / 8;
-    const int xcd = wg & 7;
-    const int slot = wg >> 3;
-    *hb = xcd * per + slot % per;
-    ir = slot / per;
+  if (8 % NG == 0 && p.nqb % (8 / NG) == 0) {
+    const int xpg = 8 / NG;            // XCDs per group
+    *hb = (xcd / xpg) * GS + slot % GS;  // group * GS + head = b * h_q + h
+    ir = (slot / GS) * xpg + xcd % xpg;
+  } else if (NG % 8 == 0) {
+    const int per = NG / 8;            // groups per XCD
+    const int u = slot % (per * GS);
+    *hb = (xcd * per + u / GS) * GS + u % GS;
+    ir = slot / (per * GS);
   } else {
+    const int HB = p.batch * p.h_q;
     *hb = wg % HB;
     ir = wg / HB;
   }
