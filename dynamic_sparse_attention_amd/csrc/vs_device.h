@@ -175,7 +175,7 @@ __device__ __forceinline__ int block_compact(bool flag, int* wsum, int* total) {
     before += (w < wave) ? c : 0;
     tot += c;
   }
-  *total = tot;
+  *total = __builtin_amdgcn_readfirstlane(tot);  // uniform: keep it (and what derives from it) scalar
   return before + inwave;
 }
 

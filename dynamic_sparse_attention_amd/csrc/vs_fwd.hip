@@ -392,11 +392,12 @@ struct FwdRowsWorker : RowsTiles<D> {
   }
 
   // Half n of this stream, with S^T(n) in s: masks, online softmax and P V
-  // from tile vt[P]; S^T(n+1) goes into sn from tile kt[P ^ 1] meanwhile (the
+  // from V tile vc; S^T(n+1) goes into sn from K tile kn meanwhile (the
   // exponentials and these products are independent, so the matrix cores run
   // while the softmax does).
-  template <int P, class Set>
-  __device__ __forceinline__ void compute(const Set& S, int n, f32x16& s, f32x16& sn) {
+  template <class Set>
+  __device__ __forceinline__ void compute(const Set& S, int n, f32x16& s, f32x16& sn, const char* kn,
+                                          const char* vc) {
     const int lane = threadIdx.x & 63;
     const int hl = lane >> 5;
     const int r = 32 * rh + (lane & 31);
@@ -424,8 +425,8 @@ struct FwdRowsWorker : RowsTiles<D> {
     frag kf[NCD];
     frag vf[NVF];
     auto issue = [&](int i) {
-      if (i < NCD) kf[i] = k_frag(kt[P ^ 1], i);
-      else if (i < NRD) vf[i - NCD] = vt_frag(vt[P], (i - NCD) % NCT, (i - NCD) / NCT);
+      if (i < NCD) kf[i] = k_frag(kn, i);
+      else if (i < NRD) vf[i - NCD] = vt_frag(vc, (i - NCD) % NCT, (i - NCD) / NCT);
     };
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) issue(i);
@@ -470,7 +471,7 @@ struct FwdRowsWorker : RowsTiles<D> {
     __syncthreads();
     if (n + 2 < N) dma_half(S, n + 2, kb, kta[P]);
     if (n + 1 < N) dma_half(S, n + 1, vb, vta[P ^ 1]);
-    if (n < N) compute<P>(S, n, s[P], s[P ^ 1]);
+    if (n < N) compute(S, n, s[P], s[P ^ 1], kt[P ^ 1], vt[P]);
   }
 
   // All waves take the same number of steps (the longest stream's), so that

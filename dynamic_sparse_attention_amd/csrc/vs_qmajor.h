@@ -233,27 +233,33 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
 // goes to the group's XCD r % (8 / groups), which balances the longer late
 // blocks); with more, each XCD takes whole groups.  Query blocks are walked
 // from the last (most keys) to the first.
-__device__ __forceinline__ void qmajor_item(const AttnParams& p, int wg, int* hb, int* i_local) {
+// upg work units per group (its Q heads, or pairs of them); *unit = group *
+// upg + unit in the group.
+__device__ __forceinline__ void qmajor_item_units(const AttnParams& p, int wg, int upg, int* unit, int* i_local) {
   const int NG = p.batch * p.h_kv;
-  const int GS = p.h_q / p.h_kv;
   const int xcd = wg & 7;
   const int slot = wg >> 3;
   int ir;
   if (8 % NG == 0 && p.nqb % (8 / NG) == 0) {
     const int xpg = 8 / NG;            // XCDs per group
-    *hb = (xcd / xpg) * GS + slot % GS;  // group * GS + head = b * h_q + h
-    ir = (slot / GS) * xpg + xcd % xpg;
+    *unit = (xcd / xpg) * upg + slot % upg;
+    ir = (slot / upg) * xpg + xcd % xpg;
   } else if (NG % 8 == 0) {
     const int per = NG / 8;            // groups per XCD
-    const int u = slot % (per * GS);
-    *hb = (xcd * per + u / GS) * GS + u % GS;
-    ir = slot / (per * GS);
+    const int u = slot % (per * upg);
+    *unit = (xcd * per + u / upg) * upg + u % upg;
+    ir = slot / (per * upg);
   } else {
-    const int HB = p.batch * p.h_q;
-    *hb = wg % HB;
+    const int HB = NG * upg;
+    *unit = wg % HB;
     ir = wg / HB;
   }
   *i_local = p.nqb - 1 - ir;
+}
+
+// One Q head per workgroup: *hb = b * h_q + h.
+__device__ __forceinline__ void qmajor_item(const AttnParams& p, int wg, int* hb, int* i_local) {
+  qmajor_item_units(p, wg, p.h_q / p.h_kv, hb, i_local);
 }
 
 // Longest segment of a call, in blocks (the whole index grid when striped).
