@@ -23,6 +23,7 @@ Every function names the passage it follows.  Readings of silent or garbled
 steps are listed in the repository's design notes.
 """
 from .index import (capacities, window_probs, window_scores, select_topk, estimate_index,
+                    topp_count, estimate_index_topp,
                     dense_mask)
 from .attention import (attn_fwd_dense, attn_bwd_dense, attn_fwd_support, attn_bwd_support,
                         lse_merge, row_groups, support_candidates, bwd_delta,
@@ -31,7 +32,7 @@ from .accounting import mask_area_bruteforce, mask_area_formula, dense_causal_ar
 
 __all__ = [
     "capacities", "window_probs", "window_scores", "select_topk", "estimate_index",
-    "dense_mask", "attn_fwd_dense", "attn_bwd_dense", "attn_fwd_support", "attn_bwd_support",
+    "topp_count", "estimate_index_topp", "dense_mask", "attn_fwd_dense", "attn_bwd_dense", "attn_fwd_support", "attn_bwd_support",
     "lse_merge", "row_groups", "support_candidates", "bwd_delta", "bwd_rounding_bounds",
     "mask_area_bruteforce",
     "mask_area_formula", "dense_causal_area",

@@ -85,6 +85,58 @@ def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[:k])
 
 
+def topp_count(scores: np.ndarray, p: float) -> int:
+    """``topp`` (Algorithm 1, budget lines): the fewest top scores that hold a
+    fraction p of the total mass.
+
+    With the scores sorted descending (ties to the lowest index, the order of
+    ``argtopk``) and c their running sum, k = min{k : c[k-1] >= p * c[-1]};
+    p <= 0 or an all-zero list gives 0.  c[-1] is the total, so p >= 1 gives
+    the number of positive scores.  Reading of the pages (they define ``topp``
+    only by name): the "minimal number of lines that recall a target
+    proportion of the attention mass" of MTraining §4.1 (i).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    if s.size == 0 or p <= 0:
+        return 0
+    order = np.lexsort((np.arange(s.size), -s))
+    c = np.cumsum(s[order])
+    total = c[-1]
+    if total <= 0:
+        return 0
+    return int(np.argmax(c >= min(p, 1.0) * total)) + 1
+
+
+def estimate_index_topp(q, k, cu_seqlens, v_cap, s_cap, p_v, p_s, block=64, last_q=64, scale=None,
+                        return_scores=False):
+    """Vertical-Slash index with top-p budgets (Algorithm 1: k_v = topp(sum_v, p_v),
+    k_s = topp(pooled sum_s, p_s)), each capped by the fixed-budget capacity of
+    ``capacities(v_cap[h], s_cap[h], ...)``.
+
+    Returns {(h, seg): (iv, is_)} like ``estimate_index`` (lists of k_v <= cap
+    and k_s <= cap entries) and, with return_scores, also the scores and the
+    counts {(h, seg): (k_v, k_s)}.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    out, scores, counts = {}, {}, {}
+    for h in range(hq):
+        g = h * hkv // hq
+        for s in range(len(cu_seqlens) - 1):
+            a, e = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+            cv, cg = capacities(v_cap[h], s_cap[h], e - a, n, block)
+            v, sigma = window_scores(q[:, h], k[:, g], a, e, scale, block, last_q)
+            kv = min(topp_count(v, p_v[h]), cv)
+            kg = min(topp_count(sigma, p_s[h]), cg)
+            out[(h, s)] = (select_topk(v, kv) + a, select_topk(sigma, kg))
+            scores[(h, s)] = (v, sigma)
+            counts[(h, s)] = (kv, kg)
+    return (out, scores, counts) if return_scores else out
+
+
 def estimate_index(q, k, cu_seqlens, v_budget, s_budget, block=64, last_q=64, scale=None,
                    return_scores=False):
     """Vertical-Slash index for every (Q head, segment) of one batch row.

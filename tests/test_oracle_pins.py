@@ -291,6 +291,74 @@ def test_p6_topk_matches_stable_sort():
         assert oracle.select_topk(x, kk).tolist() == ref
 
 
+# ---------------------------------------------------------------- top-p budgets (Algorithm 1 topp)
+def test_topp_brute_force_over_subsets():
+    """topp(x, p) is the size of the smallest subset whose mass reaches p of the
+    total (MTraining §4.1 (i): the minimal number of lines that recall a target
+    proportion of the mass) — found here by enumerating every subset."""
+    import itertools
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        n = int(rng.integers(1, 8))
+        x = rng.integers(0, 5, size=n).astype(float) * rng.choice([1.0, 0.37])
+        p = float(rng.choice([0.0, 0.1, 0.33, 0.5, 0.8, 0.95, 1.0, rng.random()]))
+        total = x.sum()
+        best = 0
+        if p > 0 and total > 0:
+            best = min(len(c) for r in range(1, n + 1) for c in itertools.combinations(range(n), r)
+                       if sum(x[list(c)]) >= p * total)
+        assert oracle.topp_count(x, p) == best, (x, p)
+
+
+def test_topp_closed_forms():
+    """Uniform masses need ceil(p n) entries; geometric masses r^i need
+    ceil(log(1 - p (1 - r^n)) / log r) (partial sums of a geometric series);
+    p <= 0 or zero mass gives 0, p >= 1 every positive entry."""
+    rng = np.random.default_rng(22)
+    for n in (1, 7, 64, 1000):
+        for p in (0.01, 0.25, 0.5, 0.9, 0.999):
+            assert oracle.topp_count(np.full(n, 0.125), p) == math.ceil(p * n - 1e-12)
+    for r in (0.5, 0.9, 0.99):
+        n = 300
+        x = r ** np.arange(n)
+        perm = rng.permutation(n)  # positions do not matter, only the masses
+        for p in (0.1, 0.37, 0.6, 0.9, 0.99):
+            t = math.log(1 - p * (1 - r ** n)) / math.log(r)
+            if abs(t - round(t)) < 1e-6:
+                continue
+            assert oracle.topp_count(x[perm], p) == math.ceil(t), (r, p)
+    x = np.array([0.0, 3.0, 0.0, 1.0, 2.0])
+    assert oracle.topp_count(x, 0.0) == 0 and oracle.topp_count(x, -1.0) == 0
+    assert oracle.topp_count(x, 1.0) == 3 and oracle.topp_count(x, 2.0) == 3
+    assert oracle.topp_count(np.zeros(9), 0.5) == 0
+
+
+def test_topp_index_reduces_to_fixed_budgets():
+    """With p = 1 and budgets at or below the number of positive scores, the
+    top-p index is the fixed-budget index (argtopk with those budgets); with
+    p = 1 and unbounded budgets every positive-mass candidate is selected."""
+    rng = np.random.default_rng(23)
+    n, hq, hkv, d, B = 640, 2, 1, 16, 64
+    q = rng.standard_normal((n, hq, d))
+    k = rng.standard_normal((n, hkv, d))
+    cu = [0, 256, n]
+    vb, sb = [70, 40], [200, 130]
+    fixed = oracle.estimate_index(q, k, cu, vb, sb, B, 64)
+    topp, sc, cnt = oracle.estimate_index_topp(q, k, cu, vb, sb, [1.0, 1.0], [1.0, 1.0], B, 64,
+                                               return_scores=True)
+    for key in fixed:
+        assert np.array_equal(fixed[key][0], topp[key][0]) and np.array_equal(fixed[key][1], topp[key][1])
+    big, sc, cnt = oracle.estimate_index_topp(q, k, cu, [n] * hq, [n] * hq, [1.0] * hq, [1.0] * hq, B, 64,
+                                              return_scores=True)
+    for (h, s), (iv, is_) in big.items():
+        v, sigma = sc[(h, s)]
+        assert iv.size == int(np.count_nonzero(v > 0)) and is_.size == int(np.count_nonzero(sigma > 0))
+        # and a smaller p keeps a prefix of the same ranking
+        part = oracle.estimate_index_topp(q, k, cu, [n] * hq, [n] * hq, [0.5] * hq, [0.5] * hq, B, 64)
+        assert set(part[(h, s)][0]) <= set(iv) and set(part[(h, s)][1]) <= set(is_)
+        assert v[part[(h, s)][0] - cu[s]].sum() >= 0.5 * v.sum()
+
+
 # ---------------------------------------------------------------- P7 RoPE / Theorem 3.1
 def test_p7_rope_shift_invariance():
     rng = np.random.default_rng(11)
