@@ -8,6 +8,7 @@ library is not built, the calls raise.
 Entry points (same names as the C ABI):
   * ``estimate_index``   — online Vertical-Slash index (MTraining paper note,
     Algorithm 1; MTraining arXiv 2510.18830 §4.1);
+  * ``estimate_index_topp`` — the same with top-p budgets (Algorithm 1 topp);
   * ``sparse_attn_fwd``  — sparse attention forward with LSE;
   * ``sparse_attn_bwd``  — dQ, dK, dV over the same support;
   * ``lse_merge``        — merge_out_and_lse of Algorithm 2;
@@ -25,7 +26,8 @@ from . import _abi
 from ._abi import VsError
 
 BLOCK = 64
-__all__ = ["VsIndexT", "index_capacity", "estimate_index", "sparse_attn_fwd", "sparse_attn_bwd",
+__all__ = ["VsIndexT", "index_capacity", "estimate_index", "estimate_index_topp", "sparse_attn_fwd",
+           "sparse_attn_bwd",
            "attn_bwd_delta", "lse_merge", "VsError", "BLOCK"]
 
 
@@ -150,6 +152,48 @@ def estimate_index(q: torch.Tensor, k: torch.Tensor, v_budget: Sequence[int],
                                    _stream(dev)))
     idx = VsIndexT(v_ptr, v_idx, s_ptr, s_idx, vm, sm)
     return (idx, v_score, s_score) if return_scores else idx
+
+
+def estimate_index_topp(q: torch.Tensor, k: torch.Tensor, v_cap: Sequence[int], s_cap: Sequence[int],
+                        p_v: Sequence[float], p_s: Sequence[float], cu_seqlens=None,
+                        return_scores: bool = False):
+    """Online Vertical-Slash index with top-p budgets: per (Q head, segment) the
+    fewest top verticals / block-diagonals holding a share p_v[h] / p_s[h] of the
+    window mass, at most the capacities of the token budgets v_cap / s_cap.
+
+    Returns (VsIndexT, counts [B*Hq*n_seg, 2] int32 = (k_v, k_s) per list) and,
+    with return_scores, also the vertical and slash scores.  Unused capacity is
+    padded with -1.
+    """
+    dev = q.device
+    _need(q, "q", dev=dev)
+    _need(k, "k", q.dtype, dev)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if len(p_v) != Hq or len(p_s) != Hq:
+        raise ValueError(f"p_v and p_s need {Hq} entries")
+    dc = _dtype_code(q)
+    vp, sp, vm, sm = index_capacity(B, Hq, Hkv, d, N, v_cap, s_cap, cu_seqlens, dc)
+    P = _Problem(B, Hq, Hkv, d, N, N, dc, cu_seqlens, None, None)
+    v_ptr = torch.tensor(vp, dtype=torch.int32, device=dev)
+    s_ptr = torch.tensor(sp, dtype=torch.int32, device=dev)
+    v_idx = torch.empty(max(vp[-1], 1), dtype=torch.int32, device=dev)
+    s_idx = torch.empty(max(sp[-1], 1), dtype=torch.int32, device=dev)
+    pv = torch.tensor([float(x) for x in p_v], dtype=torch.float32, device=dev)
+    ps = torch.tensor([float(x) for x in p_s], dtype=torch.float32, device=dev)
+    counts = torch.empty((len(vp) - 1, 2), dtype=torch.int32, device=dev)
+    v_score = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if return_scores else None
+    s_score = torch.empty((B, Hq, N // BLOCK), dtype=torch.float32, device=dev) if return_scores else None
+    L = _abi.lib()
+    nb = ctypes.c_size_t()
+    _abi.check(L.vs_workspace_size(P.ref, 0, None, ctypes.byref(nb)))
+    ws = _workspace(dev, nb.value)
+    _abi.check(L.vs_estimate_index_topp(P.ref, _ptr(q), _ptr(k), 0, _ptr(pv), _ptr(ps), _ptr(v_ptr),
+                                        _ptr(v_idx), _ptr(s_ptr), _ptr(s_idx), _ptr(counts),
+                                        _ptr(v_score), _ptr(s_score), _ptr(ws), ws.numel(),
+                                        _stream(dev)))
+    idx = VsIndexT(v_ptr, v_idx, s_ptr, s_idx, vm, sm)
+    return (idx, counts, v_score, s_score) if return_scores else (idx, counts)
 
 
 def index_from_lists(lists: List[Tuple[Sequence[int], Sequence[int]]], device) -> VsIndexT:

@@ -42,6 +42,7 @@ SIGNATURES = {
     "vs_index_capacity": (i32, [PP, i32p, i32p, i32p, i32p, i32p, i32p]),
     "vs_workspace_size": (i32, [PP, i32, IP, ctypes.POINTER(sz)]),
     "vs_estimate_index": (i32, [PP, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+    "vs_estimate_index_topp": (i32, [PP, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     "vs_sparse_attn_fwd": (i32, [PP, vp, vp, vp, IP, vp, i32, vp, vp, sz, vp]),
     "vs_attn_bwd_delta": (i32, [PP, vp, i32, vp, vp, vp]),
     "vs_sparse_attn_bwd": (i32, [PP, vp, vp, vp, vp, i32, vp, vp, vp, IP, vp, i32, vp, vp, vp, sz, vp]),

@@ -31,7 +31,7 @@ struct EstParams;
 hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int* v_ptr, int* v_idx,
                            const int* s_ptr, int* s_idx, float* v_score, float* s_score,
                            float2* partials, float* lse2, int tiles_total, const int* tile_prefix,
-                           hipStream_t st);
+                           const float* p_v, const float* p_s, int* kcount, hipStream_t st);
 constexpr int kEstKeyTile = 256;
 }  // namespace vs
 
@@ -191,7 +191,7 @@ AttnWs attn_ws(const Prob& c, int v_cap_max, bool backward) {
 }
 
 struct EstWs {
-  size_t part, lse2, vscore, sscore, tprefix, total;
+  size_t part, lse2, vscore, sscore, kcount, tprefix, total;
   int tiles_total;
   std::vector<int> tile_prefix;
 };
@@ -211,6 +211,8 @@ EstWs est_ws(const Prob& c) {
   off += align256((size_t)c.batch * c.h_q * c.n_global * 4);
   w.sscore = off;
   off += align256((size_t)c.batch * c.h_q * (c.n_global / c.block) * 4);
+  w.kcount = off;  // top-p: entries per (list, kind)
+  off += align256((size_t)c.n_lists() * 2 * 4);
   w.tprefix = off;
   w.total = off;
   return w;
@@ -328,10 +330,11 @@ vs_status vs_workspace_size(const vs_problem* p, int32_t op, const vs_index* idx
   return ok();
 }
 
-vs_status vs_estimate_index(const vs_problem* p, const void* q, const void* k, int32_t last_q,
-                            const int32_t* v_ptr, int32_t* v_idx, const int32_t* s_ptr,
-                            int32_t* s_idx, float* v_score, float* s_score, void* ws,
-                            size_t ws_bytes, vs_stream_t stream) {
+namespace {
+vs_status estimate(const char* what, const vs_problem* p, const void* q, const void* k, int32_t last_q,
+                   const float* p_v, const float* p_s, const int32_t* v_ptr, int32_t* v_idx,
+                   const int32_t* s_ptr, int32_t* s_idx, int32_t* counts, float* v_score,
+                   float* s_score, void* ws, size_t ws_bytes, vs_stream_t stream) {
   Prob c;
   vs_status st = check_problem(p, &c);
   if (st) return st;
@@ -350,11 +353,31 @@ vs_status vs_estimate_index(const vs_problem* p, const void* q, const void* k, i
   char* base = static_cast<char*>(ws);
   float* vsc = v_score ? v_score : reinterpret_cast<float*>(base + w.vscore);
   float* ssc = s_score ? s_score : reinterpret_cast<float*>(base + w.sscore);
+  int* kc = counts ? counts : reinterpret_cast<int*>(base + w.kcount);
   return hip_status(vs::launch_estimate(a, c.bf16, c.d, v_ptr, v_idx, s_ptr, s_idx, vsc, ssc,
                                         reinterpret_cast<float2*>(base + w.part),
                                         reinterpret_cast<float*>(base + w.lse2), w.tiles_total,
-                                        w.tile_prefix.data(), (hipStream_t)stream),
-                    "vs_estimate_index");
+                                        w.tile_prefix.data(), p_v, p_s, kc, (hipStream_t)stream),
+                    what);
+}
+}  // namespace
+
+vs_status vs_estimate_index(const vs_problem* p, const void* q, const void* k, int32_t last_q,
+                            const int32_t* v_ptr, int32_t* v_idx, const int32_t* s_ptr,
+                            int32_t* s_idx, float* v_score, float* s_score, void* ws,
+                            size_t ws_bytes, vs_stream_t stream) {
+  return estimate("vs_estimate_index", p, q, k, last_q, nullptr, nullptr, v_ptr, v_idx, s_ptr, s_idx,
+                  nullptr, v_score, s_score, ws, ws_bytes, stream);
+}
+
+vs_status vs_estimate_index_topp(const vs_problem* p, const void* q, const void* k, int32_t last_q,
+                                 const float* p_v, const float* p_s, const int32_t* v_ptr,
+                                 int32_t* v_idx, const int32_t* s_ptr, int32_t* s_idx,
+                                 int32_t* counts, float* v_score, float* s_score, void* ws,
+                                 size_t ws_bytes, vs_stream_t stream) {
+  if (!p_v || !p_s) return fail(VS_ERR_NULL, "p_v or p_s is NULL");
+  return estimate("vs_estimate_index_topp", p, q, k, last_q, p_v, p_s, v_ptr, v_idx, s_ptr, s_idx,
+                  counts, v_score, s_score, ws, ws_bytes, stream);
 }
 
 vs_status vs_sparse_attn_fwd(const vs_problem* p, const void* q, const void* k, const void* v,

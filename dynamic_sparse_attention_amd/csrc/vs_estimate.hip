@@ -237,10 +237,12 @@ __device__ __forceinline__ void wave_hist_add(int* hist, int bin, bool active) {
   if ((rem >> lane) & 1ull) atomicAdd(&hist[bin], 1);
 }
 
+// kcount (optional): the number of entries to select per (list, kind), at
+// most the list's capacity; the rest of the list is padded with -1.
 __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p, const float* v_score,
                                                                    const float* s_score, const int* v_ptr,
                                                                    int* v_idx, const int* s_ptr,
-                                                                   int* s_idx) {
+                                                                   int* s_idx, const int* kcount) {
   __shared__ int hist[256];
   __shared__ int wsum[2][kTopkThreads / 64];
   __shared__ int sel[2];
@@ -270,11 +272,17 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int cap = k;
+  if (kcount) k = min(kcount[blockIdx.x], cap);
   if (k >= L) {
-    for (int x = tid; x < k; x += kTopkThreads) out[x] = x < L ? x + add : -1;
+    for (int x = tid; x < cap; x += kTopkThreads) out[x] = x < L ? x + add : -1;
     return;
   }
-  if (k <= 0) return;
+  if (k <= 0) {
+    for (int x = tid; x < cap; x += kTopkThreads) out[x] = -1;
+    return;
+  }
+  for (int x = k + tid; x < cap; x += kTopkThreads) out[x] = -1;
   const uint32_t* u = reinterpret_cast<const uint32_t*>(sc);
   uint32_t prefix = 0, pmask = 0;
   int kr = k;
@@ -378,10 +386,233 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
   }
 }
 
+// Top-p budgets (Algorithm 1, topp): per (list, kind) the fewest top scores,
+// in (score desc, index asc) order, that hold a fraction p of the list's
+// mass.  The decision is taken in integers, so it is exact and the same in
+// every run: score s (fp32, >= 0) has mass m = rint(s * 2^54) (an observation
+// window of at most 64 rows holds a mass of at most 64, so sums stay below
+// 2^61); the target is T = ceil(t * total / 2^24) with t = rint(p * 2^24), p
+// clamped to [0, 1]; k = the fewest entries whose masses reach T (0 when
+// T = 0), capped by the list's capacity.  k is found by the four 8-bit radix
+// passes of the top-k select with a mass histogram beside the count
+// histogram (the crossing digit of each pass), over the entries at or above
+// the cap-th largest score only, then the run of equal scores at the
+// crossing.
+__device__ __forceinline__ unsigned long long score_mass(uint32_t bits) {
+  return (unsigned long long)__builtin_rint((double)__uint_as_float(bits) * 0x1p54);
+}
+
+// Count and mass histogram increments of the active lanes, aggregated per
+// wave like wave_hist_add.
+__device__ __forceinline__ void wave_mass_add(int* hc, unsigned long long* hm, int bin, bool active,
+                                              unsigned long long m) {
+  const int lane = threadIdx.x & 63;
+  uint64_t rem = __ballot(active);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    if (rem == 0) break;  // uniform
+    const int leader = __ffsll((unsigned long long)rem) - 1;
+    const int lb = __shfl(bin, leader, 64);
+    const uint64_t same = __ballot(active && bin == lb) & rem;
+    unsigned long long v = ((same >> lane) & 1ull) ? m : 0ull;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == leader) {
+      atomicAdd(&hc[lb], __popcll(same));
+      atomicAdd(&hm[lb], v);
+    }
+    rem &= ~same;
+  }
+  if ((rem >> lane) & 1ull) {
+    atomicAdd(&hc[bin], 1);
+    atomicAdd(&hm[bin], m);
+  }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void vs_est_topp_kernel(AttnParams p, const float* v_score,
+                                                                   const float* s_score, const int* v_ptr,
+                                                                   const int* s_ptr, const float* p_v,
+                                                                   const float* p_s, int* kcount) {
+  __shared__ int hc[256];
+  __shared__ unsigned long long hm[256];
+  __shared__ unsigned long long red[kTopkThreads / 64];
+  __shared__ unsigned long long red2[kTopkThreads / 64];
+  __shared__ unsigned long long sel_need;
+  __shared__ int sel_d, sel_above;
+  const int kind = blockIdx.x & 1;
+  const int list = blockIdx.x >> 1;
+  const int s = list % p.seg.n_seg;
+  const int bh = list / p.seg.n_seg;
+  const int h = bh % p.h_q;
+  const int a_blk = p.seg.start_blk[s];
+  const int nb_s = p.seg.start_blk[s + 1] - a_blk;
+  const int nbt = p.n_global / kBlock;
+  const float* sc;
+  int L, cap;
+  float thr;
+  if (kind == 0) {
+    sc = v_score + (size_t)bh * p.n_global + (size_t)a_blk * kBlock;
+    L = nb_s * kBlock;
+    cap = v_ptr[list + 1] - v_ptr[list];
+    thr = p_v[h];
+  } else {
+    sc = s_score + (size_t)bh * nbt + a_blk;
+    L = nb_s;
+    cap = s_ptr[list + 1] - s_ptr[list];
+    thr = p_s[h];
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const float pc = thr > 0.f ? fminf(thr, 1.f) : 0.f;  // NaN counts as 0
+  const unsigned long long t = (unsigned long long)__builtin_rintf(pc * 16777216.f);
+  if (cap <= 0 || t == 0 || L <= 0) {
+    if (tid == 0) kcount[blockIdx.x] = 0;
+    return;
+  }
+  const uint32_t* u = reinterpret_cast<const uint32_t*>(sc);
+  // k never exceeds the capacity, so only entries at or above the cap-th
+  // largest score kc can be selected: a count-only radix select (as in the
+  // top-k select) finds kc, and the mass passes below look at those entries
+  // only.
+  uint32_t kc = 0;
+  if (cap < L) {
+    uint32_t pre = 0, pm = 0;
+    int kr = cap;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      if (tid < 256) hc[tid] = 0;
+      __syncthreads();
+      for (int base = 0; base < L; base += kTopkUnroll * kTopkThreads) {
+        uint32_t v[kTopkUnroll];
+#pragma unroll
+        for (int j = 0; j < kTopkUnroll; ++j) {
+          const int x = base + j * kTopkThreads + tid;
+          v[j] = x < L ? u[x] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kTopkUnroll; ++j) {
+          const int x = base + j * kTopkThreads + tid;
+          wave_hist_add(hc, (int)((v[j] >> shift) & 255), x < L && (v[j] & pm) == pre);
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int cum = 0, d = 255;
+        for (; d >= 0; --d) {
+          if (cum + hc[d] >= kr) break;
+          cum += hc[d];
+        }
+        sel_d = d;
+        sel_above = kr - cum;
+      }
+      __syncthreads();
+      pre |= (uint32_t)sel_d << shift;
+      pm |= 255u << shift;
+      kr = sel_above;
+      __syncthreads();
+    }
+    kc = pre;
+  }
+  // total mass, and the mass of the entries >= kc (integer sums: exact in
+  // any order)
+  unsigned long long acc = 0, acc_ge = 0;
+  for (int x = tid; x < L; x += kTopkThreads) {
+    const uint32_t b = u[x];
+    const unsigned long long m = score_mass(b);
+    acc += m;
+    acc_ge += b >= kc ? m : 0ull;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    acc += __shfl_xor(acc, o, 64);
+    acc_ge += __shfl_xor(acc_ge, o, 64);
+  }
+  if (lane == 0) {
+    red[wave] = acc;
+    red2[wave] = acc_ge;
+  }
+  __syncthreads();
+  unsigned long long total = 0, total_ge = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    total += red[w];
+    total_ge += red2[w];
+  }
+  if (total == 0) {
+    if (tid == 0) kcount[blockIdx.x] = 0;
+    return;
+  }
+  // T = ceil(t * total / 2^24) with total = hi 2^30 + lo (no product above 2^61)
+  const unsigned long long hi = total >> 30, lo = total & ((1ull << 30) - 1);
+  unsigned long long need = t * hi * 64ull + (t * lo + (1ull << 24) - 1) / (1ull << 24);
+  if (need > total_ge) {
+    // even every entry >= kc (at least cap of them) does not reach T
+    if (tid == 0) kcount[blockIdx.x] = cap;
+    return;
+  }
+  // Invariant: need <= the mass of the entries >= kc that match the prefix;
+  // each pass picks the digit at which the mass of the larger entries
+  // reaches it.
+  uint32_t prefix = 0, pmask = 0;
+  int above = 0, count_eq = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) {
+      hc[tid] = 0;
+      hm[tid] = 0ull;
+    }
+    __syncthreads();
+    for (int base = 0; base < L; base += kTopkUnroll * kTopkThreads) {
+      uint32_t v[kTopkUnroll];
+#pragma unroll
+      for (int j = 0; j < kTopkUnroll; ++j) {
+        const int x = base + j * kTopkThreads + tid;
+        v[j] = x < L ? u[x] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kTopkUnroll; ++j) {
+        const int x = base + j * kTopkThreads + tid;
+        const bool act = x < L && v[j] >= kc && (v[j] & pmask) == prefix;
+        if (__ballot(act) == 0ull) continue;  // uniform
+        wave_mass_add(hc, hm, (int)((v[j] >> shift) & 255), act, act ? score_mass(v[j]) : 0ull);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long cm = 0;
+      int cc = 0, d = 255;
+      for (; d > 0; --d) {
+        if (cm + hm[d] >= need) break;
+        cm += hm[d];
+        cc += hc[d];
+      }
+      sel_d = d;
+      sel_above = cc;
+      sel_need = need - cm;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sel_d << shift;
+    pmask |= 255u << shift;
+    above += sel_above;
+    need = sel_need;
+    count_eq = hc[sel_d];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    // entries equal to the crossing score, in index order, each of mass ms
+    const unsigned long long ms = score_mass(prefix);
+    long long e = ms > 0 ? (long long)((need + ms - 1) / ms) : (long long)count_eq;
+    e = e > count_eq ? count_eq : (e < 1 ? 1 : e);
+    const long long k = (long long)above + e;
+    kcount[blockIdx.x] = (int)(k < cap ? k : cap);
+  }
+}
+
 hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int* v_ptr, int* v_idx,
                            const int* s_ptr, int* s_idx, float* v_score, float* s_score,
                            float2* partials, float* lse2, int tiles_total, const int* tile_prefix,
-                           hipStream_t st) {
+                           const float* p_v, const float* p_s, int* kcount, hipStream_t st) {
   TilePrefix tp;
   for (int s = 0; s <= p.seg.n_seg; ++s) tp.v[s] = tile_prefix[s];
   const int n_lists = p.batch * p.h_q * p.seg.n_seg;
@@ -400,8 +631,13 @@ hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int
   else if (!dtype_bf16 && d == 128) VS_EST(float, 128);
   else VS_EST(float, 64);
 #undef VS_EST
+  if (p_v) {
+    VS_TRACED(st, "vs_est_topp", hipLaunchKernelGGL(vs_est_topp_kernel, dim3(2 * n_lists), dim3(kTopkThreads), 0, st, p,
+                       (const float*)v_score, (const float*)s_score, v_ptr, s_ptr, p_v, p_s, kcount));
+  }
   VS_TRACED(st, "vs_est_topk", hipLaunchKernelGGL(vs_est_topk_kernel, dim3(2 * n_lists), dim3(kTopkThreads), 0, st, p,
-                     (const float*)v_score, (const float*)s_score, v_ptr, v_idx, s_ptr, s_idx));
+                     (const float*)v_score, (const float*)s_score, v_ptr, v_idx, s_ptr, s_idx,
+                     p_v ? (const int*)kcount : (const int*)nullptr));
   return hipGetLastError();
 }
 

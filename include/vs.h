@@ -128,7 +128,8 @@ vs_status vs_index_capacity(const vs_problem* p, const int32_t* v_budget,
                             int32_t* s_ptr_host, int32_t* v_cap_max,
                             int32_t* s_cap_max);
 
-/* Workspace bytes an entry point needs: op 0 = vs_estimate_index,
+/* Workspace bytes an entry point needs: op 0 = vs_estimate_index (and
+ * vs_estimate_index_topp),
  * 1 = vs_sparse_attn_fwd, 2 = vs_sparse_attn_bwd.  idx may be NULL for op 0;
  * for ops 1 and 2 it supplies the capacity bounds.  The workspace is DEVICE
  * memory, 256-byte aligned, owned by the caller, and may be reused across
@@ -159,6 +160,29 @@ vs_status vs_estimate_index(const vs_problem* p, const void* q, const void* k,
                             const int32_t* s_ptr, int32_t* s_idx, float* v_score,
                             float* s_score, void* ws, size_t ws_bytes,
                             vs_stream_t stream);
+
+/* Online index estimation with top-p budgets (MTraining paper note,
+ * Algorithm 1: k_v = topp(sum_v(A_hat), p_v), k_s = topp(pooled sum_s(A_hat),
+ * p_s); MTraining §4.1 (i): the fewest lines that recall a target share of
+ * the window's attention mass).  Scores as in vs_estimate_index; then for
+ * every (b, h, s) and kind, k = the fewest highest scores (ties to the lowest
+ * index) whose mass reaches the fraction p_v[h] (verticals) or p_s[h]
+ * (block-diagonals) of the list's total, capped by the list's capacity
+ * (v_ptr / s_ptr from vs_index_capacity, whose budgets act as upper bounds).
+ * The k selected entries are written ascending at the start of the list and
+ * the rest of its capacity is padded with -1.  The comparison is exact: a
+ * score s has integer mass rint(s * 2^54), the target is
+ * ceil(rint(p * 2^24) * total / 2^24), p clamped to [0, 1] (NaN as 0).
+ * p_v, p_s: DEVICE fp32, h_q entries each.  counts (DEVICE, nullable):
+ * receives k per list and kind at [2*l + 0] (verticals) and [2*l + 1]
+ * (block-diagonals).  Workspace: op 0 of vs_workspace_size.  Other arguments
+ * and errors as vs_estimate_index. */
+vs_status vs_estimate_index_topp(const vs_problem* p, const void* q, const void* k,
+                                 int32_t last_q, const float* p_v, const float* p_s,
+                                 const int32_t* v_ptr, int32_t* v_idx, const int32_t* s_ptr,
+                                 int32_t* s_idx, int32_t* counts, float* v_score,
+                                 float* s_score, void* ws, size_t ws_bytes,
+                                 vs_stream_t stream);
 
 /* Sparse attention forward (MTraining paper note, Algorithm 1 last step and
  * Algorithm 2 block_bar_sparse_attention_forward; online softmax as in

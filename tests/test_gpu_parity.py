@@ -165,3 +165,117 @@ def test_striped_ring_share():
             check_close("ring dV", dvw, dv_all, "bf16", "grad", bv)]
     errs = [e for e in errs if e]
     assert not errs, errs
+
+
+def _topp_count_int(scores_f32, p):
+    """The top-p count in the kernel's integer arithmetic (the decision the
+    device takes, recomputed exactly from the device's own fp32 scores):
+    masses rint(s * 2^54), target ceil(rint(p * 2^24) * total / 2^24)."""
+    pc = np.float32(p)
+    pc = np.float32(min(pc, np.float32(1.0))) if pc > 0 else np.float32(0.0)
+    t = int(np.rint(np.float64(pc) * 2.0 ** 24))
+    m = np.rint(np.asarray(scores_f32, np.float32).astype(np.float64) * 2.0 ** 54).astype(np.uint64)
+    total = int(m.sum(dtype=np.uint64))
+    if t == 0 or total == 0:
+        return 0
+    need = -(-(t * total) // (1 << 24))
+    order = np.lexsort((np.arange(m.size), -np.asarray(scores_f32, np.float64)))
+    c = np.cumsum([int(x) for x in m[order]], dtype=object)
+    return int(np.argmax(np.array([x >= need for x in c]))) + 1
+
+
+TOPP_CASES = {
+    # name: (make_problem kwargs, caps v, caps s)
+    "w2-n4096": (dict(wid=2, n=4096), [4096] * 8 + [60] * 8, [4096] * 8 + [640] * 8),
+    "w5-n8192-docs": (dict(wid=5, n=8192, n_docs=4), [8192] * 16, [8192] * 16),
+}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", list(TOPP_CASES))
+def test_topp_index(name):
+    """Top-p budgets (Algorithm 1 topp): device counts equal the integer
+    definition on the device's scores; each list is the top-k of those scores
+    padded with -1; counts and sets match the fp64 oracle or differ only within
+    the certified bound; and attention on the padded index matches the oracle."""
+    dev = _dev()
+    kw, vcap, scap = TOPP_CASES[name]
+    kw = dict(kw)
+    prob = workloads.make_problem(kw.pop("wid"), **kw)
+    hq, n_seg = prob.h_q, len(prob.cu_seqlens) - 1
+    grid = [0.0, 0.05, 0.3, 0.5, 0.7, 0.9, 0.99, 1.0]
+    p_v = [grid[h % 8] for h in range(hq)]
+    p_s = [grid[(3 * h + 1) % 8] for h in range(hq)]
+    log(f"case topp {name}: n={prob.n} hq={hq} docs={n_seg}")
+    q, k = np64(prob.q[0]), np64(prob.k[0])
+    oidx, osc, ocnt = oracle.estimate_index_topp(q, k, prob.cu_seqlens, vcap, scap, p_v, p_s, prob.block,
+                                                 64, return_scores=True)
+    gq, gk = prob.q.to(dev), prob.k.to(dev)
+    gidx, gcnt, vsc, ssc = vs.estimate_index_topp(gq, gk, vcap, scap, p_v, p_s, prob.cu_seqlens,
+                                                  return_scores=True)
+    torch.cuda.synchronize()
+    gl = [(a.numpy(), b.numpy()) for a, b in gidx.lists()]
+    gcnt = gcnt.cpu().numpy()
+    vsc, ssc = vsc[0].cpu().numpy(), ssc[0].cpu().numpy()
+    flips = swaps = 0
+    for h in range(hq):
+        for s in range(n_seg):
+            a, e = prob.cu_seqlens[s], prob.cu_seqlens[s + 1]
+            l = h * n_seg + s
+            cv, cg = oracle.capacities(vcap[h], scap[h], e - a, prob.n, prob.block)
+            for kind, pp, cap, gsc, osc_k, off in (
+                    (0, p_v[h], cv, vsc[h, a:e], osc[(h, s)][0], a),
+                    (1, p_s[h], cg, ssc[h, a // 64:e // 64], osc[(h, s)][1], 0)):
+                kg = int(gcnt[l, kind])
+                # 1. the device's decision, exactly
+                assert kg == min(_topp_count_int(gsc, pp), cap), (name, h, s, kind, kg)
+                # 2. the list: top-kg of the device's scores, ascending, then -1
+                lst = gl[l][kind]
+                assert lst.size == cap and np.all(lst[kg:] == -1), (name, h, s, kind)
+                order = np.lexsort((np.arange(gsc.size), -np.asarray(gsc, np.float64)))
+                assert np.array_equal(lst[:kg], np.sort(order[:kg]) + off), (name, h, s, kind)
+                # 3. against the fp64 oracle
+                ko = ocnt[(h, s)][kind]
+                o64 = np.asarray(osc_k, np.float64)
+                if kg != ko:
+                    so = np.sort(o64)[::-1]
+                    cum = np.concatenate(([0.0], np.cumsum(so)))
+                    tot = cum[-1]
+                    delta = 2 * np.abs(np.asarray(gsc, np.float64) - o64).sum() + 2.0 ** -24 * tot + 1e-12
+                    pc = min(pp, 1.0)
+                    # the device's uncapped count reaches the target at kg (unless
+                    # capped) and not before it, up to the score differences
+                    assert kg == cap or cum[kg] >= pc * tot - delta, (name, h, s, kind, kg, ko)
+                    assert kg == 0 or cum[kg - 1] < pc * tot + delta, (name, h, s, kind, kg, ko)
+                    flips += 1
+                ref = oracle.select_topk(o64, kg) + off
+                if not np.array_equal(np.sort(ref), lst[:kg]):
+                    kth = np.sort(o64)[::-1][kg - 1]
+                    extra = np.setdiff1d(lst[:kg], ref) - off
+                    miss = np.setdiff1d(ref, lst[:kg]) - off
+                    tol = 1e-4 * max(kth, 1e-30)
+                    assert np.all(np.abs(o64[extra] - kth) <= tol) and np.all(np.abs(o64[miss] - kth) <= tol), \
+                        (name, h, s, kind, "non-tie mismatch")
+                    swaps += extra.size
+    log(f"  topp {name}: counts match (certified boundary flips={flips}), near-tie swaps={swaps}")
+    # attention on the padded device index against the oracle on the same lists
+    lists = {(h, s): (gl[h * n_seg + s][0][gl[h * n_seg + s][0] >= 0].astype(np.int64),
+                      gl[h * n_seg + s][1][gl[h * n_seg + s][1] >= 0].astype(np.int64))
+             for h in range(hq) for s in range(n_seg)}
+    v_, do_ = np64(prob.v[0]), np64(prob.do[0])
+    pos = np.arange(prob.n)
+    O, L = oracle.attn_fwd_support(q, k, v_, pos, pos, prob.cu_seqlens, lists)
+    D = oracle.bwd_delta(O, do_)
+    dq, dk, dv = oracle.attn_bwd_support(q, k, v_, do_, L, D, pos, pos, prob.cu_seqlens, lists)
+    gv, gdo = prob.v.to(dev), prob.do.to(dev)
+    o, lse = vs.sparse_attn_fwd(gq, gk, gv, gidx, prob.cu_seqlens)
+    gdq, gdk, gdv = vs.sparse_attn_bwd(gq, gk, gv, o, gdo, lse, gidx, cu_seqlens=prob.cu_seqlens)
+    torch.cuda.synchronize()
+    bq, bk, bv = oracle.bwd_rounding_bounds(q, k, v_, do_, O, L, pos, pos, prob.cu_seqlens, lists)
+    errs = [check_close(f"topp {name} O", O, np64(o[0]), prob.dtype),
+            check_close(f"topp {name} LSE", L, lse[0].cpu().numpy().astype(np.float64), prob.dtype),
+            check_close(f"topp {name} dQ", dq, np64(gdq[0]), prob.dtype, "grad", bq),
+            check_close(f"topp {name} dK", dk, np64(gdk[0]), prob.dtype, "grad", bk),
+            check_close(f"topp {name} dV", dv, np64(gdv[0]), prob.dtype, "grad", bv)]
+    errs = [e for e in errs if e]
+    assert not errs, errs
