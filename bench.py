@@ -86,7 +86,7 @@ def trace_read(vs):
     return out
 
 
-def cpu_baseline(prob, lists, target_s):
+def cpu_baseline(prob, lists, target_s, topp=None):
     """The CPU oracle, as it stands, on a bounded sample of the same workload.
 
     Sample: the estimator for one Q head (window scoring over all keys) and the
@@ -110,10 +110,15 @@ def cpu_baseline(prob, lists, target_s):
     do = prob.do[0].to(dtype=__import__("torch").float64).numpy()
     n = prob.n
     t0 = time.perf_counter()
-    oracle.estimate_index(q[:, h:h + 1], k[:, g:g + 1], prob.cu_seqlens, prob.v_budget[:1],
-                          prob.s_budget[:1])
+    if topp is None:
+        oracle.estimate_index(q[:, h:h + 1], k[:, g:g + 1], prob.cu_seqlens, prob.v_budget[:1],
+                              prob.s_budget[:1])
+    else:
+        oracle.estimate_index_topp(q[:, h:h + 1], k[:, g:g + 1], prob.cu_seqlens, prob.v_budget[:1],
+                                   prob.s_budget[:1], [topp[0]], [topp[1]])
     t_est = time.perf_counter() - t0
-    index = {(0, 0): (np.asarray(lists[h][0]), np.asarray(lists[h][1]))}
+    iv, is_ = np.asarray(lists[h][0]), np.asarray(lists[h][1])
+    index = {(0, 0): (iv[iv >= 0], is_[is_ >= 0])}
     nb = n // 64
     order = np.concatenate([np.arange(s, nb, 64) for s in range(64)])  # spread over the sequence
     pos = np.arange(n)
@@ -150,6 +155,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="workload id (3 = N=131072)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--topp", default=None, metavar="P_V,P_S",
+                    help="estimate with top-p budgets (vs_estimate_index_topp) at these mass "
+                         "fractions, the workload's budgets as caps")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -181,7 +189,19 @@ def main():
     dk = torch.empty((B, N, prob.h_kv, d), dtype=torch.float32, device=dev)
     dv = torch.empty_like(dk)
 
-    idx = vs.estimate_index(q, k, prob.v_budget, prob.s_budget, cu)
+    topp = None
+    if args.topp:
+        topp = tuple(float(x) for x in args.topp.split(","))
+        if len(topp) != 2:
+            raise SystemExit("--topp takes P_V,P_S")
+
+    def estimate():
+        if topp is None:
+            return vs.estimate_index(q, k, prob.v_budget, prob.s_budget, cu)
+        return vs.estimate_index_topp(q, k, prob.v_budget, prob.s_budget, [topp[0]] * Hq,
+                                      [topp[1]] * Hq, cu)[0]
+
+    idx = estimate()
     lists = [(a.numpy(), b.numpy()) for a, b in idx.lists()]
     ent_heads = accounting.executed_area(lists, cu, Hq)
     ent = int(ent_heads.sum())
@@ -193,7 +213,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        ix = vs.estimate_index(q, k, prob.v_budget, prob.s_budget, cu)
+        ix = estimate()
         if ev is not None:
             ev[1].record(stream)
         vs.sparse_attn_fwd(q, k, v, ix, cu, out=o, lse=lse)
@@ -256,7 +276,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         t1 = time.time()
-        cpu = cpu_baseline(prob, lists, args.cpu_seconds)
+        cpu = cpu_baseline(prob, lists, args.cpu_seconds, topp)
         log(f"cpu baseline {cpu['value']} TFLOP/s in {time.time() - t1:.1f} s")
 
     out = {
@@ -268,7 +288,10 @@ def main():
         "pct_bf16_peak_executed": round(100 * exec_tf / PEAK_BF16_TFLOPS, 3),
         "config": {"workload": prob.name, "batch": 1, "seq_len": N, "h_q": Hq, "h_kv": prob.h_kv,
                    "head_dim": d, "block": 64, "v_budget": prob.v_budget[0],
-                   "s_budget": prob.s_budget[0], "executed_entries": ent, "causal_entries": dense,
+                   "s_budget": prob.s_budget[0],
+                   "estimator": "fixed budgets" if topp is None else
+                   f"top-p p_v={topp[0]} p_s={topp[1]} (budgets as caps)",
+                   "executed_entries": ent, "causal_entries": dense,
                    "density": round(ent / dense, 5), "phases_ms": {k_: round(v_, 4) for k_, v_ in phases.items()},
                    "kernels_avg_ms": per_kernel, "kernels_ms_per_step": per_step,
                    "parallelism": "none"},
