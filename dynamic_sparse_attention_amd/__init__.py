@@ -212,11 +212,18 @@ def index_from_lists(lists: List[Tuple[Sequence[int], Sequence[int]]], device) -
 
 def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: VsIndexT,
                     cu_seqlens=None, stripe=None, o_f32: bool = False, scale=None,
-                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    merge: bool = False):
     """Sparse attention forward.  Returns (o [B, Nq, Hq, d], lse [B, Hq, Nq] fp32).
 
     stripe = (world, q_rank, k_rank) for a block-striped call (one ring step).
+    merge: out (fp32) and lse hold a running result (zeros / -inf to start);
+    this call's result is merged into them in place (fused lse_merge).
     """
+    if merge:
+        if out is None or lse is None:
+            raise ValueError("merge needs out (fp32) and lse holding the running result")
+        o_f32 = True
     dev = q.device
     _need(q, "q", dev=dev)
     _need(k, "k", q.dtype, dev)
@@ -235,7 +242,8 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Vs
     _abi.check(L.vs_workspace_size(P.ref, 1, ctypes.byref(ix), ctypes.byref(nb)))
     ws = _workspace(dev, nb.value)
     _abi.check(L.vs_sparse_attn_fwd(P.ref, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(ix), _ptr(o),
-                                    int(o_f32), _ptr(l), _ptr(ws), ws.numel(), _stream(dev)))
+                                    2 if merge else int(o_f32), _ptr(l), _ptr(ws), ws.numel(),
+                                    _stream(dev)))
     return o, l
 
 

@@ -402,8 +402,10 @@ vs_status vs_sparse_attn_fwd(const vs_problem* p, const void* q, const void* k, 
   a.vsel = reinterpret_cast<int*>(base + w.vsel);
   a.vcnt = reinterpret_cast<int*>(base + w.vcnt);
   a.vsel_stride = std::max(idx->v_cap_max, 1);
+  if (o_f32 < 0 || o_f32 > 2) return fail(VS_ERR_SHAPE, "o_f32 %d is not 0, 1 or 2", o_f32);
   a.o_out = o;
   a.o_f32 = o_f32 != 0;
+  a.o_merge = o_f32 == 2;
   a.lse = lse;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = vs::launch_prep_vertical(a, c.n_lists(), idx->v_ptr, idx->v_idx, s);

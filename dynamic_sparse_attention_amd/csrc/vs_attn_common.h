@@ -38,6 +38,7 @@ struct AttnParams {
   float* dk;
   float* dv;
   int o_f32;
+  int o_merge;        // forward: o_out (fp32) and lse hold a running result; merge this call's into them
   int dq_accumulate;
   int batch, h_q, h_kv, n_q, n_k, nqb, nkb;
   float scale;

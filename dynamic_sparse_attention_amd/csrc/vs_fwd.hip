@@ -22,6 +22,28 @@
 
 namespace vs {
 
+// merge_out_and_lse (MTraining paper note, Algorithm 2) of one row's result
+// of this call (LSE lc, output O / lg) into a running fp32 result (LSE la,
+// output O_acc), as lse_merge does: with mx = max(la, lc), w1 = e^(la - mx),
+// w2 = e^(lc - mx), the merged output is (w1 O_acc + w2 O / lg) / (w1 + w2)
+// and the merged LSE mx + ln(w1 + w2); two empty results give O = 0 and
+// LSE = -inf.  Returns the merged LSE, the weight *a of O_acc and the weight
+// *bo of the unnormalised O.
+__device__ __forceinline__ float merge_row(float la, float lc, float inv_lg, float* a, float* bo) {
+  const float mx = fmaxf(la, lc);
+  if (mx == -INFINITY) {
+    *a = 0.f;
+    *bo = 0.f;
+    return -INFINITY;
+  }
+  const float w1 = expf(la - mx);
+  const float w2 = expf(lc - mx);
+  const float tot = w1 + w2;
+  *a = w1 / tot;
+  *bo = w2 / tot * inv_lg;
+  return mx + logf(tot);
+}
+
 template <int D>
 struct FwdWorkerF32 {
   typedef Mfma<float> MF;
@@ -322,17 +344,28 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_f32_kernel(AttnParams p) {
     }
     __syncthreads();
   }
-  // Normalise and write O (row-major, coalesced) and LSE.
+  // Normalise and write O (row-major, coalesced) and LSE, or merge them
+  // into the running result.
   __shared__ float s_inv[64];
+  __shared__ float s_acc[64];
   if (tid < 64) {
     float mg = -INFINITY;
     for (int w = 0; w < 4; ++w) mg = fmaxf(mg, s_m[w][tid]);
     const float mu = (mg == -INFINITY) ? 0.f : mg;
     float lg = 0.f;
     for (int w = 0; w < 4; ++w) lg += s_l[w][tid] * fast_exp2(s_m[w][tid] - mu);
-    s_inv[tid] = lg > 0.f ? 1.f / lg : 0.f;
+    const float inv = lg > 0.f ? 1.f / lg : 0.f;
     const float lse = lg > 0.f ? (mg + __log2f(lg)) * kLn2 : -INFINITY;
-    p.lse[((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + tid] = lse;
+    float* lp = p.lse + ((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + tid;
+    if (p.o_merge) {
+      float a, bo;
+      *lp = merge_row(*lp, lse, inv, &a, &bo);
+      s_acc[tid] = a;
+      s_inv[tid] = bo;
+    } else {
+      *lp = lse;
+      s_inv[tid] = inv;
+    }
   }
   __syncthreads();
   for (int x = tid; x < 64 * D / 4; x += kQThreads) {
@@ -340,7 +373,9 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_f32_kernel(AttnParams p) {
     const int c4 = (x % (D / 4)) * 4;
     f32x4 v = *reinterpret_cast<const f32x4*>(ob + r * OB_PITCH + c4) * s_inv[r];
     const size_t off = ((qrow0 + r) * p.h_q + h) * D + c4;
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o_out) + off) = v;
+    float* dst = reinterpret_cast<float*>(p.o_out) + off;
+    if (p.o_merge) v += *reinterpret_cast<const f32x4*>(dst) * s_acc[r];
+    *reinterpret_cast<f32x4*>(dst) = v;
   }
 }
 
@@ -513,6 +548,7 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ float s_m[NS][64];
   __shared__ float s_l[NS][64];
   __shared__ float s_inv[64];
+  __shared__ float s_acc[64];
 
   int hb, i_local;
   qmajor_item(p, blockIdx.x, &hb, &i_local);
@@ -585,25 +621,37 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     __syncthreads();
   }
-  // Normalise and write O (row-major, coalesced) and LSE (natural log).
+  // Normalise and write O (row-major, coalesced) and LSE (natural log), or
+  // merge them into the running result.
   if (tid < 64) {
     float mt = -INFINITY;
     for (int w = 0; w < NS; ++w) mt = fmaxf(mt, s_m[w][tid]);
     const float mu = (mt == -INFINITY) ? 0.f : mt;
     float lg = 0.f;
     for (int w = 0; w < NS; ++w) lg += s_l[w][tid] * fast_exp2(s_m[w][tid] - mu);
-    s_inv[tid] = lg > 0.f ? 1.f / lg : 0.f;
-    p.lse[((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + tid] =
-        lg > 0.f ? (mt + __log2f(lg)) * kLn2 : -INFINITY;
+    const float inv = lg > 0.f ? 1.f / lg : 0.f;
+    const float lse = lg > 0.f ? (mt + __log2f(lg)) * kLn2 : -INFINITY;
+    float* lp = p.lse + ((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + tid;
+    if (p.o_merge) {
+      float a, bo;
+      *lp = merge_row(*lp, lse, inv, &a, &bo);
+      s_acc[tid] = a;
+      s_inv[tid] = bo;
+    } else {
+      *lp = lse;
+      s_inv[tid] = inv;
+    }
   }
   __syncthreads();
   for (int x = tid; x < 64 * D / 4; x += NT) {
     const int rr = x / (D / 4);
     const int c4 = (x % (D / 4)) * 4;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(ob + rr * OB_PITCH + c4) * s_inv[rr];
+    f32x4 v = *reinterpret_cast<const f32x4*>(ob + rr * OB_PITCH + c4) * s_inv[rr];
     const size_t off = ((qrow0 + rr) * p.h_q + h) * D + c4;
     if (p.o_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o_out) + off) = v;
+      float* dst = reinterpret_cast<float*>(p.o_out) + off;
+      if (p.o_merge) v += *reinterpret_cast<const f32x4*>(dst) * s_acc[rr];
+      *reinterpret_cast<f32x4*>(dst) = v;
     } else {
       bf16x4 w4;
 #pragma unroll

@@ -191,7 +191,12 @@ vs_status vs_estimate_index_topp(const vs_problem* p, const void* q, const void*
  * selected vertical or beta(n) - beta(m) a selected block-diagonal of the
  * row's (b, h, s) list.  q [batch, n_q, h_q, d], k/v [batch, n_k, h_kv, d]
  * (DEVICE, dtype).  o [batch, n_q, h_q, d] (fp32 if o_f32 else dtype),
- * lse [batch, h_q, n_q] fp32.  Rows are fully overwritten.
+ * lse [batch, h_q, n_q] fp32.  Rows are fully overwritten, except with
+ * o_f32 = 2: then o (fp32) and lse hold a running result (O = 0, LSE = -inf
+ * for nothing yet) and this call's result is merged into them in place, as
+ * lse_merge does (merge_out_and_lse of Algorithm 2, fused: one ring step of a
+ * striped worker without a partial buffer).  o_f32 other than 0, 1, 2 is
+ * VS_ERR_SHAPE.
  * Errors: VS_ERR_NULL, VS_ERR_SHAPE, VS_ERR_UNSUPPORTED, VS_ERR_INDEX,
  * VS_ERR_WORKSPACE, VS_ERR_HIP. */
 vs_status vs_sparse_attn_fwd(const vs_problem* p, const void* q, const void* k,

@@ -147,9 +147,21 @@ def test_entry_points_reject_before_launch(abi):
     st = L.vs_estimate_index(ctypes.byref(ps), FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
                              1 << 40, None)
     assert st == abi.VS_ERR_UNSUPPORTED
+    # estimate with top-p budgets
+    st = L.vs_estimate_index_topp(P, FAKE, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                  FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_NULL
+    st = L.vs_estimate_index_topp(P, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                  FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_UNSUPPORTED
+    st = L.vs_estimate_index_topp(P, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                  FAKE, 16, None)
+    assert st == abi.VS_ERR_WORKSPACE
     # forward
     st = L.vs_sparse_attn_fwd(P, FAKE, FAKE, FAKE, ctypes.byref(ix), FAKE, 0, FAKE, FAKE, 16, None)
     assert st == abi.VS_ERR_WORKSPACE
+    st = L.vs_sparse_attn_fwd(P, FAKE, FAKE, FAKE, ctypes.byref(ix), FAKE, 3, FAKE, FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_SHAPE  # o_f32 is 0, 1 or 2 (merge into the running result)
     st = L.vs_sparse_attn_fwd(P, FAKE, FAKE, None, ctypes.byref(ix), FAKE, 0, FAKE, FAKE, 1 << 40, None)
     assert st == abi.VS_ERR_NULL
     bad = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 5000, 4)

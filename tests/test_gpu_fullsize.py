@@ -154,9 +154,10 @@ def test_fullsize_contiguous(wid):
 
 
 def test_fullsize_striped_worker():
-    """Worker 0 of 32 on the 524288-token sequence: 32 forward calls merged with
-    lse_merge, then 32 backward calls accumulating dQ (Algorithm 2 of the
-    MTraining paper note, run as one worker's share)."""
+    """Worker 0 of 32 on the 524288-token sequence: 32 forward calls merging
+    into the running result (fused; the same with lse_merge must agree), then
+    32 backward calls accumulating dQ (Algorithm 2 of the MTraining paper note,
+    run as one worker's share)."""
     dev = _dev()
     log("full-size workload 4: drawing inputs")
     prob = workloads.make_problem(4)
@@ -177,12 +178,23 @@ def test_fullsize_striped_worker():
         u = (w - t) % W
         chunks.append((u, workloads.stripe_rows(prob.k, W, u).to(dev),
                        workloads.stripe_rows(prob.v, W, u).to(dev)))
-    log(f"  GPU: {W} forward calls + merges, {W} backward calls")
+    log(f"  GPU: {W} forward calls with the merge fused, {W} forward calls + lse_merge, {W} backward calls")
     acc_o = torch.zeros((1, nq, prob.h_q, prob.d), device=dev)
     acc_l = torch.full((1, prob.h_q, nq), -float("inf"), device=dev)
     for u, gk, gv in chunks:
+        vs.sparse_attn_fwd(gq, gk, gv, idx, stripe=(W, w, u), out=acc_o, lse=acc_l, merge=True)
+    sep_o = torch.zeros_like(acc_o)
+    sep_l = torch.full_like(acc_l, -float("inf"))
+    for u, gk, gv in chunks:
         o, l = vs.sparse_attn_fwd(gq, gk, gv, idx, stripe=(W, w, u), o_f32=True)
-        vs.lse_merge(acc_o, acc_l, o, l)
+        vs.lse_merge(sep_o, sep_l, o, l)
+    del o, l
+    torch.cuda.synchronize()
+    # the fused and the separate merge do the same fp32 arithmetic up to one rounding
+    assert torch.allclose(acc_o, sep_o, rtol=1e-5, atol=1e-6)
+    fin = torch.isfinite(sep_l)
+    assert torch.equal(fin, torch.isfinite(acc_l)) and torch.allclose(acc_l[fin], sep_l[fin], rtol=1e-6, atol=1e-5)
+    del sep_o, sep_l
     delta = vs.attn_bwd_delta(acc_o, gdo)
     dq = torch.zeros((1, nq, prob.h_q, prob.d), device=dev)
     k64, v64 = np64(prob.k[0]), np64(prob.v[0])

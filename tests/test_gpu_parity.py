@@ -110,7 +110,8 @@ def test_delta_and_merge_kernels():
 
 
 def test_striped_ring_share():
-    """One worker's striped ring share: chunk calls + lse_merge = global rows (W=8)."""
+    """One worker's striped ring share: chunk calls + lse_merge = global rows (W=8),
+    and the same with the merge fused into each chunk's forward."""
     dev = _dev()
     W, w = 8, 3
     prob = workloads.make_problem(4, n=8192, v_budget=512, s_budget=1536, stripe_world=W)
@@ -127,6 +128,9 @@ def test_striped_ring_share():
     nq = gq.shape[1]
     acc_o = torch.zeros((1, nq, prob.h_q, prob.d), device=dev)
     acc_l = torch.full((1, prob.h_q, nq), -float("inf"), device=dev)
+    # the same ring share with the merge fused into the forward (o_f32 = 2)
+    fused_o = torch.zeros_like(acc_o)
+    fused_l = torch.full_like(acc_l, -float("inf"))
     chunks = []
     for t in range(W):
         u = (w - t) % W
@@ -141,9 +145,17 @@ def test_striped_ring_share():
             assert_close("chunk O", Oc, o[0].cpu().numpy(), "bf16")
             assert_close("chunk LSE", Lc, l[0].cpu().numpy().astype(np.float64), "bf16")
         vs.lse_merge(acc_o, acc_l, o, l)
+        vs.sparse_attn_fwd(gq, gk, gv, idx, stripe=(W, w, u), out=fused_o, lse=fused_l, merge=True)
     torch.cuda.synchronize()
     assert_close("merged O", Og[rows], acc_o[0].cpu().numpy(), "bf16")
     assert_close("merged LSE", Lg[:, rows], acc_l[0].cpu().numpy().astype(np.float64), "bf16")
+    assert_close("fused-merge O", Og[rows], fused_o[0].cpu().numpy(), "bf16")
+    assert_close("fused-merge LSE", Lg[:, rows], fused_l[0].cpu().numpy().astype(np.float64), "bf16")
+    # fused and separate merges do the same fp32 arithmetic up to one rounding
+    assert torch.allclose(fused_o, acc_o, rtol=1e-5, atol=1e-6)
+    assert torch.equal(torch.isinf(fused_l), torch.isinf(acc_l))
+    fin = torch.isfinite(acc_l)
+    assert torch.allclose(fused_l[fin], acc_l[fin], rtol=1e-6, atol=1e-5)
     delta = vs.attn_bwd_delta(acc_o, gdo)
     dq = torch.zeros((1, nq, prob.h_q, prob.d), device=dev)
     dk_all = np.zeros_like(dkg)
