@@ -1,13 +1,15 @@
 // vs_qmajor.h — query-major walk over the Vertical-Slash support of one
 // query block, shared by the forward kernel and the dQ backward kernel.
 //
-// A workgroup of 4 waves owns one (batch, Q head, query block).  It expands
-// the index of the block on the fly (MTraining paper note, Algorithm 1
-// sparseformat and Algorithm 2 convert_index): first the selected
-// block-diagonals become key-block tiles, then the selected vertical columns
-// that are not inside a selected block become 64-column tiles.  The tiles are
-// dealt round-robin to the waves; each wave keeps its own running state for
-// all 64 rows and the workgroup combines the four states at the end.
+// A workgroup owns one (batch, Q head, query block) and expands the index of
+// the block on the fly (MTraining paper note, Algorithm 1 sparseformat and
+// Algorithm 2 convert_index): first the selected block-diagonals become
+// key-block tiles, then the selected vertical columns that are not inside a
+// selected block become 64-column tiles.  The tiles are dealt round-robin to
+// NS key streams.  The bf16 kernels run one stream of two waves (rows 0-31
+// and 32-63, sharing every tile); the fp32 kernels run four streams of one
+// wave each, every wave keeping a running state for all 64 rows, combined at
+// the end.
 #pragma once
 
 #include "vs_attn_common.h"

@@ -1,10 +1,9 @@
 // vs_rows.h — K / V tiles of the row-split query-major kernels (bf16).
 //
-// A workgroup of four waves serves two key streams; the two waves of a stream
-// own query rows 0-31 and 32-63 of the block and share every 32-key tile of
-// the stream: each issues half of the tile's direct global -> LDS loads
-// (1 KiB per instruction, no registers), a workgroup barrier publishes both
-// halves.  Operands are read from the tile in two ways:
+// The two waves of a key stream own query rows 0-31 and 32-63 of the block
+// and share every 32-key tile of the stream: each issues half of the tile's
+// direct global -> LDS loads (1 KiB per instruction, no registers), a
+// workgroup barrier publishes both halves.  Operands are read from the tile in two ways:
 //   * row reads (k_frag, ds_read_b128): the A operand of a product with the
 //     tile's rows as output rows (S^T = K Q^T, dP^T = V dO^T), rows permuted
 //     by slot_perm so that the result registers are the k slots of the next
