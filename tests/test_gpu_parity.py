@@ -291,3 +291,38 @@ def test_topp_index(name):
             check_close(f"topp {name} dV", dv, np64(gdv[0]), prob.dtype, "grad", bv)]
     errs = [e for e in errs if e]
     assert not errs, errs
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("wid,dtype,d", [(1, "f32", 64), (2, "bf16", 64)])
+def test_fused_merge_other_kernels(wid, dtype, d):
+    """The merge fused into the forward (o_f32 = 2) in the fp32 kernel and the
+    d = 64 bf16 kernel: two striped KV chunks merged in the epilogue equal the
+    same chunks merged by lse_merge, and the oracle's global rows."""
+    dev = _dev()
+    W, w = 2, 1
+    prob = workloads.make_problem(wid, n=2048, h_q=2, h_kv=1, d=d, dtype=dtype, v_budget=150,
+                                  s_budget=400, stripe_world=W)
+    oidx, _ = oracle_index(prob)
+    q, k, v = (np64(t[0]) for t in (prob.q, prob.k, prob.v))
+    pos = np.arange(prob.n)
+    Og, Lg = oracle.attn_fwd_support(q, k, v, pos, pos, prob.cu_seqlens, oidx)
+    rows = workloads.stripe_positions(prob.n, W, w).numpy()
+    idx = vs.index_from_lists(lists_for_gpu(oidx, prob.h_q, 1), dev)
+    gq = workloads.stripe_rows(prob.q, W, w).to(dev)
+    nq = gq.shape[1]
+    sep_o = torch.zeros((1, nq, prob.h_q, prob.d), device=dev)
+    sep_l = torch.full((1, prob.h_q, nq), -float("inf"), device=dev)
+    fused_o, fused_l = torch.zeros_like(sep_o), torch.full_like(sep_l, -float("inf"))
+    for u in range(W):
+        gk = workloads.stripe_rows(prob.k, W, u).to(dev)
+        gv = workloads.stripe_rows(prob.v, W, u).to(dev)
+        o, l = vs.sparse_attn_fwd(gq, gk, gv, idx, stripe=(W, w, u), o_f32=True)
+        vs.lse_merge(sep_o, sep_l, o, l)
+        vs.sparse_attn_fwd(gq, gk, gv, idx, stripe=(W, w, u), out=fused_o, lse=fused_l, merge=True)
+    torch.cuda.synchronize()
+    assert torch.allclose(fused_o, sep_o, rtol=1e-5, atol=1e-6)
+    fin = torch.isfinite(sep_l)
+    assert torch.equal(fin, torch.isfinite(fused_l)) and torch.allclose(fused_l[fin], sep_l[fin], rtol=1e-6, atol=1e-5)
+    assert_close("fused-merge O", Og[rows], fused_o[0].cpu().numpy(), prob.dtype)
+    assert_close("fused-merge LSE", Lg[:, rows], fused_l[0].cpu().numpy().astype(np.float64), prob.dtype)
