@@ -170,7 +170,7 @@ void fill_params(const Prob& c, vs::AttnParams* a) {
 
 // Workspace layouts.
 struct AttnWs {
-  size_t vsel, vcnt, delta, lse2, total;
+  size_t vsel, vcnt, share, delta, lse2, total;
 };
 // Forward: prepared vertical lists.  Backward: also delta (when the caller
 // gives none) and LSE * log2(e), one fp32 per (batch, Q head, row) each.
@@ -181,6 +181,8 @@ AttnWs attn_ws(const Prob& c, int v_cap_max, bool backward) {
   off += align256((size_t)c.n_lists() * std::max(v_cap_max, 1) * 4);
   w.vcnt = off;
   off += align256((size_t)c.n_lists() * 4);
+  w.share = off;  // the work-mapping flag of the query-major kernels
+  off += 256;
   const size_t rows = align256((size_t)c.batch * c.h_q * c.n_q * 4);
   w.delta = off;
   if (backward) off += rows;
@@ -401,6 +403,7 @@ vs_status vs_sparse_attn_fwd(const vs_problem* p, const void* q, const void* k, 
   char* base = static_cast<char*>(ws);
   a.vsel = reinterpret_cast<int*>(base + w.vsel);
   a.vcnt = reinterpret_cast<int*>(base + w.vcnt);
+  a.map_group = reinterpret_cast<int*>(base + w.share);
   a.vsel_stride = std::max(idx->v_cap_max, 1);
   if (o_f32 < 0 || o_f32 > 2) return fail(VS_ERR_SHAPE, "o_f32 %d is not 0, 1 or 2", o_f32);
   a.o_out = o;
@@ -450,6 +453,7 @@ vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, 
   char* base = static_cast<char*>(ws);
   a.vsel = reinterpret_cast<int*>(base + w.vsel);
   a.vcnt = reinterpret_cast<int*>(base + w.vcnt);
+  a.map_group = reinterpret_cast<int*>(base + w.share);
   a.vsel_stride = std::max(idx->v_cap_max, 1);
   a.lse = const_cast<float*>(lse);
   a.dq = dq;

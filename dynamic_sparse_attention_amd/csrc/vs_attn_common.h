@@ -39,6 +39,8 @@ struct AttnParams {
   float* dv;
   int o_f32;
   int o_merge;        // forward: o_out (fp32) and lse hold a running result; merge this call's into them
+  int* map_group;     // query-major grids: set on the device to 1 when the Q heads of a group share
+                      // most of their block-diagonals (the group-wise work mapping), else 0; may be null
   int dq_accumulate;
   int batch, h_q, h_kv, n_q, n_k, nqb, nkb;
   float scale;

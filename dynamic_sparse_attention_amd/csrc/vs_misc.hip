@@ -43,10 +43,61 @@ __global__ __launch_bounds__(256) void vs_prep_vertical_kernel(AttnParams p, con
   if (threadIdx.x == 0) const_cast<int*>(p.vcnt)[l] = count < p.vsel_stride ? count : p.vsel_stride;
 }
 
+// Whether the Q heads of each (batch, KV head) group share their selected
+// block-diagonals: over up to 1024 evenly spread lists of non-leading heads,
+// the fraction of their entries that the group's first head (same batch and
+// segment) also selected.  *share = 1 when it is at least one half; this
+// picks the work mapping of the query-major kernels (qmajor_item).  One
+// workgroup; lists are ascending, with -1 padding at the end.
+__global__ __launch_bounds__(256) void vs_group_share_kernel(AttnParams p, int* share) {
+  __shared__ long long red[2][4];
+  const int GS = p.h_q / p.h_kv;
+  const int n_lists = p.batch * p.h_q * p.seg.n_seg;
+  const int stride = n_lists > 1024 ? n_lists / 1024 : 1;
+  long long common = 0, total = 0;
+  for (int t = threadIdx.x; t * stride < n_lists && t < 1024; t += 256) {
+    const int l = t * stride;
+    const int seg = l % p.seg.n_seg;
+    const int bh = l / p.seg.n_seg;
+    const int h = bh % p.h_q;
+    const int b = bh / p.h_q;
+    const int h0 = (h / GS) * GS;
+    if (h == h0) continue;
+    const int l0 = (b * p.h_q + h0) * p.seg.n_seg + seg;
+    int ia = p.s_ptr[l], ib = p.s_ptr[l0];
+    const int ea = p.s_ptr[l + 1], eb = p.s_ptr[l0 + 1];
+    while (ia < ea && p.s_idx[ia] >= 0) {
+      const int x = p.s_idx[ia];
+      while (ib < eb && p.s_idx[ib] >= 0 && p.s_idx[ib] < x) ++ib;
+      if (ib < eb && p.s_idx[ib] == x) ++common;
+      ++total;
+      ++ia;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    common += __shfl_xor(common, o, 64);
+    total += __shfl_xor(total, o, 64);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wave] = common;
+    red[1][wave] = total;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const long long c = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    const long long n = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    *share = (n > 0 && 2 * c >= n) ? 1 : 0;
+  }
+}
+
 hipError_t launch_prep_vertical(const AttnParams& p, int n_lists, const int* v_ptr, const int* v_idx,
                                 hipStream_t st) {
   if (n_lists == 0) return hipSuccess;
   VS_TRACED(st, "vs_prep_vertical", hipLaunchKernelGGL(vs_prep_vertical_kernel, dim3(n_lists), dim3(256), 0, st, p, v_ptr, v_idx));
+  if (p.map_group)
+    VS_TRACED(st, "vs_group_share", hipLaunchKernelGGL(vs_group_share_kernel, dim3(1), dim3(256), 0, st, p, p.map_group));
   return hipGetLastError();
 }
 

@@ -226,15 +226,19 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
 
 // Work-item mapping of a query-major grid of batch*h_q*nqb workgroups.  The
 // dispatcher deals consecutive workgroup ids round-robin to the 8 XCDs, each
-// with its own L2.  The Q heads of one (batch, KV head) group read the same
-// K / V rows, and where their index lists overlap (shared block-diagonals or
-// columns) the same tiles: the mapping puts every head of a group on the same
-// XCD, the heads of one query block in consecutive slots, so that they run
-// together and share those tiles in L2.  With fewer groups than XCDs a group
-// spreads over 8 / groups XCDs, which take its query blocks in turn (block r
-// goes to the group's XCD r % (8 / groups), which balances the longer late
-// blocks); with more, each XCD takes whole groups.  Query blocks are walked
-// from the last (most keys) to the first.
+// with its own L2, and the mapping decides which tiles meet in an L2:
+//   * by head (the default): each XCD takes batch*h_q/8 heads and walks all
+//     their query blocks from the last (most keys) to the first, so
+//     consecutive query blocks of a head run together and share its column
+//     tiles and the tiles of nearby block-diagonals;
+//   * by group (qmajor_item_units, when the index says the Q heads of a
+//     (batch, KV head) group share most of their block-diagonals): every head
+//     of a group on the same XCD, the heads of one query block in
+//     consecutive slots, so they share the tiles of common diagonals; with
+//     fewer groups than XCDs a group spreads over 8 / groups XCDs, which take
+//     its query blocks in turn (block r goes to the group's XCD
+//     r % (8 / groups), balancing the longer late blocks); with more, each
+//     XCD takes whole groups.
 // upg work units per group (its Q heads, or pairs of them); *unit = group *
 // upg + unit in the group.
 __device__ __forceinline__ void qmajor_item_units(const AttnParams& p, int wg, int upg, int* unit, int* i_local) {
@@ -261,7 +265,23 @@ __device__ __forceinline__ void qmajor_item_units(const AttnParams& p, int wg, i
 
 // One Q head per workgroup: *hb = b * h_q + h.
 __device__ __forceinline__ void qmajor_item(const AttnParams& p, int wg, int* hb, int* i_local) {
-  qmajor_item_units(p, wg, p.h_q / p.h_kv, hb, i_local);
+  if (p.map_group && *p.map_group) {
+    qmajor_item_units(p, wg, p.h_q / p.h_kv, hb, i_local);
+    return;
+  }
+  const int HB = p.batch * p.h_q;
+  int ir;
+  if (HB % 8 == 0) {
+    const int per = HB / 8;
+    const int xcd = wg & 7;
+    const int slot = wg >> 3;
+    *hb = xcd * per + slot % per;
+    ir = slot / per;
+  } else {
+    *hb = wg % HB;
+    ir = wg / HB;
+  }
+  *i_local = p.nqb - 1 - ir;
 }
 
 // Longest segment of a call, in blocks (the whole index grid when striped).
