@@ -46,16 +46,24 @@ __global__ __launch_bounds__(256) void vs_prep_vertical_kernel(AttnParams p, con
 // Whether the Q heads of each (batch, KV head) group share their selected
 // block-diagonals: over up to 1024 evenly spread lists of non-leading heads,
 // the fraction of their entries that the group's first head (same batch and
-// segment) also selected.  *share = 1 when it is at least one half; this
+// segment) also selected (the first kShareCap entries of each list, a
+// sample for longer ones).  *share = 1 when it is at least one half; this
 // picks the work mapping of the query-major kernels (qmajor_item).  One
-// workgroup; lists are ascending, with -1 padding at the end.
+// workgroup: each wave stages the leading head's list in LDS and its lanes
+// binary-search their own entries in it.  Lists are ascending, with -1
+// padding at the end (ordered as +inf).
+constexpr int kShareCap = 2048;
+
 __global__ __launch_bounds__(256) void vs_group_share_kernel(AttnParams p, int* share) {
+  __shared__ int lead[4][kShareCap];
   __shared__ long long red[2][4];
   const int GS = p.h_q / p.h_kv;
   const int n_lists = p.batch * p.h_q * p.seg.n_seg;
   const int stride = n_lists > 1024 ? n_lists / 1024 : 1;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   long long common = 0, total = 0;
-  for (int t = threadIdx.x; t * stride < n_lists && t < 1024; t += 256) {
+  for (int t = wave; t * stride < n_lists && t < 1024; t += 4) {  // wave-uniform
     const int l = t * stride;
     const int seg = l % p.seg.n_seg;
     const int bh = l / p.seg.n_seg;
@@ -64,23 +72,33 @@ __global__ __launch_bounds__(256) void vs_group_share_kernel(AttnParams p, int* 
     const int h0 = (h / GS) * GS;
     if (h == h0) continue;
     const int l0 = (b * p.h_q + h0) * p.seg.n_seg + seg;
-    int ia = p.s_ptr[l], ib = p.s_ptr[l0];
-    const int ea = p.s_ptr[l + 1], eb = p.s_ptr[l0 + 1];
-    while (ia < ea && p.s_idx[ia] >= 0) {
-      const int x = p.s_idx[ia];
-      while (ib < eb && p.s_idx[ib] >= 0 && p.s_idx[ib] < x) ++ib;
-      if (ib < eb && p.s_idx[ib] == x) ++common;
+    const int* A = p.s_idx + p.s_ptr[l];
+    const int* B = p.s_idx + p.s_ptr[l0];
+    const int na = min(p.s_ptr[l + 1] - p.s_ptr[l], kShareCap);
+    const int nb = min(p.s_ptr[l0 + 1] - p.s_ptr[l0], kShareCap);
+    for (int i = lane; i < nb; i += 64) lead[wave][i] = B[i];
+    wave_sync();
+    for (int i = lane; i < na; i += 64) {
+      const int x = A[i];
+      if (x < 0) continue;
       ++total;
-      ++ia;
+      int lo = 0, hi = nb;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const int v = lead[wave][mid];
+        if (v >= 0 && v < x) lo = mid + 1;
+        else hi = mid;
+      }
+      common += lo < nb && lead[wave][lo] == x;
     }
+    wave_sync();  // every lane is done with lead[wave] before the next list
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     common += __shfl_xor(common, o, 64);
     total += __shfl_xor(total, o, 64);
   }
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  if (lane == 0) {
     red[0][wave] = common;
     red[1][wave] = total;
   }
