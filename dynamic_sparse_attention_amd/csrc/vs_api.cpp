@@ -439,6 +439,11 @@ vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, 
   if (!q || !k || !v || !dout || !lse || !dq || !dk || !dv)
     return fail(VS_ERR_NULL, "q, k, v, dout, lse, dq, dk or dv is NULL");
   if (!delta && !o) return fail(VS_ERR_NULL, "o is NULL and no delta was given");
+  // The bf16 dK/dV kernels tag each staged query tile with the Q head's
+  // index inside its GQA group in the top bits of a 32-bit word (0 .. 31).
+  if (c.bf16 && c.h_q / c.h_kv > 32)
+    return fail(VS_ERR_UNSUPPORTED, "bf16 backward takes at most 32 Q heads per KV head (got %d)",
+                c.h_q / c.h_kv);
   const AttnWs w = attn_ws(c, idx->v_cap_max, true);
   if (!ws || ws_bytes < w.total)
     return fail(VS_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);

@@ -218,7 +218,8 @@ vs_status vs_attn_bwd_delta(const vs_problem* p, const void* o, int32_t o_f32,
  * NULL, then it is computed from o and dout into the workspace (o and dout
  * are read only in that case).  dq [batch, n_q, h_q, d] fp32 is overwritten,
  * or accumulated into when dq_accumulate != 0; dk, dv [batch, n_k, h_kv, d]
- * fp32 are overwritten.
+ * fp32 are overwritten.  With bf16 inputs a GQA group holds at most 32 Q
+ * heads (h_q / h_kv <= 32), else VS_ERR_UNSUPPORTED.
  * Errors: VS_ERR_NULL, VS_ERR_SHAPE, VS_ERR_UNSUPPORTED, VS_ERR_INDEX,
  * VS_ERR_WORKSPACE, VS_ERR_HIP. */
 vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k,

@@ -180,6 +180,10 @@ def test_entry_points_reject_before_launch(abi):
     st = L.vs_sparse_attn_bwd(P, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, ctypes.byref(ix), FAKE, 0,
                               FAKE, FAKE, FAKE, fwd_ws, None)
     assert st == abi.VS_ERR_WORKSPACE
+    wide = prob(abi, h_q=33, h_kv=1)  # a GQA group of 33 Q heads: beyond the bf16 dK/dV tile tags
+    st = L.vs_sparse_attn_bwd(ctypes.byref(wide), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None,
+                              ctypes.byref(ix), FAKE, 0, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == abi.VS_ERR_UNSUPPORTED and "32 Q heads" in L.vs_last_error().decode()
     st = L.vs_attn_bwd_delta(P, None, 0, FAKE, FAKE, None)
     assert st == abi.VS_ERR_NULL
     # merge
