@@ -237,6 +237,45 @@ __device__ __forceinline__ void wave_hist_add(int* hist, int bin, bool active) {
   if ((rem >> lane) & 1ull) atomicAdd(&hist[bin], 1);
 }
 
+// Run by the 64 lanes of one wave: the digit d of the kr-th largest active
+// entry (counting from the top bin down, hist[d] the count of digit d) and
+// the rank kr - (entries in bins above d) inside that bin, into sel[0..1].
+// Lane l sums bins 255-4l .. 252-4l; a prefix over the lanes finds the lane
+// whose bins reach kr, which then walks its four.  (d = -1 if the bins hold
+// fewer than kr entries.)
+__device__ __forceinline__ void select_digit(const int* hist, int kr, int* sel) {
+  const int lane = threadIdx.x & 63;
+  int c[4], own = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c[q] = hist[255 - 4 * lane - q];
+    own += c[q];
+  }
+  int incl = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  const uint64_t hit = __ballot(incl >= kr);
+  if (hit == 0) {
+    if (lane == 63) {
+      sel[0] = -1;
+      sel[1] = kr - incl;
+    }
+    return;
+  }
+  if (lane == __ffsll((unsigned long long)hit) - 1) {
+    int cum = incl - own, q = 0;
+    for (; q < 3; ++q) {
+      if (cum + c[q] >= kr) break;
+      cum += c[q];
+    }
+    sel[0] = 255 - 4 * lane - q;
+    sel[1] = kr - cum;
+  }
+}
+
 // kcount (optional): the number of entries to select per (list, kind), at
 // most the list's capacity; the rest of the list is padded with -1.
 __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p, const float* v_score,
@@ -305,15 +344,7 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
       }
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, d = 255;
-      for (; d >= 0; --d) {
-        if (cum + hist[d] >= kr) break;
-        cum += hist[d];
-      }
-      sel[0] = d;
-      sel[1] = kr - cum;
-    }
+    if (tid < 64) select_digit(hist, kr, sel);
     __syncthreads();
     prefix |= (uint32_t)sel[0] << shift;
     pmask |= 255u << shift;
