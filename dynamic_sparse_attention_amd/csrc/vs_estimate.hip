@@ -39,6 +39,15 @@ __device__ __forceinline__ int tile_seg(const TilePrefix& tp, int n_seg, int t) 
   return s;
 }
 
+// This lane's part (channels hl * KPL + c * KC ..) of K row key_l.
+template <typename T, int NCD, int KC, int KPL>
+__device__ __forceinline__ void est_load_k(const T* kb, int kvs, int key_l, int hl,
+                                           typename Mfma<T>::frag (&kf)[NCD]) {
+  const T* kr = kb + (size_t)key_l * kvs;
+#pragma unroll
+  for (int c = 0; c < NCD; ++c) kf[c] = load_frag<T>(kr + c * KC + hl * KPL);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void vs_est_pass1_kernel(AttnParams p, TilePrefix tp, int tiles_total,
                                                            float2* part) {
@@ -67,12 +76,7 @@ __global__ __launch_bounds__(256) void vs_est_pass1_kernel(AttnParams p, TilePre
       for (int c = 0; c < NCD; ++c) qf[rg][c] = load_frag<T>(qr + c * KC + hl * KPL);
     }
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-    for (int kc = k0; kc < k1; kc += 32) {
-      const int key_l = min(kc + l32, k1 - 1);
-      const T* kr = kb + (size_t)key_l * kvs;
-      frag kf[NCD];
-#pragma unroll
-      for (int c = 0; c < NCD; ++c) kf[c] = load_frag<T>(kr + c * KC + hl * KPL);
+    auto chunk = [&](int kc, const frag (&kf)[NCD]) {
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg) {
         f32x16 sc = f32x16{0};
@@ -96,6 +100,16 @@ __global__ __launch_bounds__(256) void vs_est_pass1_kernel(AttnParams p, TilePre
         l[rg] = l[rg] * fast_exp2(m[rg] - mu) + rs;
         m[rg] = mn;
       }
+    };
+    // Chunks of 32 keys in pairs (a tile spans whole 64-key blocks), each
+    // chunk's K rows loaded while the previous chunk computes.
+    frag ka[NCD], kn[NCD];
+    est_load_k<T, NCD, KC, KPL>(kb, kvs, min(k0 + l32, k1 - 1), hl, ka);
+    for (int kc = k0; kc < k1; kc += 64) {
+      est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 32 + l32, k1 - 1), hl, kn);
+      chunk(kc, ka);
+      if (kc + 64 < k1) est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 64 + l32, k1 - 1), hl, ka);
+      chunk(kc + 32, kn);
     }
     if (hl == 0) {
 #pragma unroll
@@ -178,12 +192,8 @@ __global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePre
       for (int c = 0; c < NCD; ++c) qa[rg][c] = load_frag<T>(qr + c * KC + hl * KPL);
     }
     float blk_acc = 0.f;
-    for (int kc = k0; kc < k1; kc += 32) {
+    auto chunk = [&](int kc, const frag (&kf)[NCD]) {
       const int key = kc + l32;
-      const T* kr = kb + (size_t)min(key, k1 - 1) * kvs;
-      frag kf[NCD];
-#pragma unroll
-      for (int c = 0; c < NCD; ++c) kf[c] = load_frag<T>(kr + c * KC + hl * KPL);
       float col = 0.f;
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg) {
@@ -210,6 +220,15 @@ __global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePre
         }
         blk_acc = 0.f;
       }
+    };
+    // as in pass 1: chunk pairs, the next chunk's K rows loaded meanwhile
+    frag ka[NCD], kn[NCD];
+    est_load_k<T, NCD, KC, KPL>(kb, kvs, min(k0 + l32, k1 - 1), hl, ka);
+    for (int kc = k0; kc < k1; kc += 64) {
+      est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 32 + l32, k1 - 1), hl, kn);
+      chunk(kc, ka);
+      if (kc + 64 < k1) est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 64 + l32, k1 - 1), hl, ka);
+      chunk(kc + 32, kn);
     }
     wave_sync();
   }
