@@ -35,6 +35,9 @@ CASES = {
     "w1-fp32-d128-gqa": dict(wid=1, n=2048, h_q=4, h_kv=2, d=128, v_budget=200, s_budget=256),
     # three Q heads per KV head: the bf16 kernels that serve one head per workgroup
     "w2-gqa3-odd": dict(wid=2, n=3072, h_q=3, h_kv=1, v_budget=250, s_budget=700),
+    # 32 Q heads on one KV head: the largest group the bf16 backward takes
+    # (the dK/dV kernels tag staged tiles with the head index 0 .. 31)
+    "w2-gqa32": dict(wid=2, n=1024, h_q=32, h_kv=1, v_budget=100, s_budget=256),
 }
 
 
