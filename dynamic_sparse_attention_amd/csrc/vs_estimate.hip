@@ -489,6 +489,7 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topp_kernel(AttnParams p,
   __shared__ unsigned long long red2[kTopkThreads / 64];
   __shared__ unsigned long long sel_need;
   __shared__ int sel_d, sel_above;
+  __shared__ int sel2[2];
   const int kind = blockIdx.x & 1;
   const int list = blockIdx.x >> 1;
   const int s = list % p.seg.n_seg;
@@ -547,19 +548,11 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topp_kernel(AttnParams p,
         }
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, d = 255;
-        for (; d >= 0; --d) {
-          if (cum + hc[d] >= kr) break;
-          cum += hc[d];
-        }
-        sel_d = d;
-        sel_above = kr - cum;
-      }
+      if (tid < 64) select_digit(hc, kr, sel2);
       __syncthreads();
-      pre |= (uint32_t)sel_d << shift;
+      pre |= (uint32_t)sel2[0] << shift;
       pm |= 255u << shift;
-      kr = sel_above;
+      kr = sel2[1];
       __syncthreads();
     }
     kc = pre;
