@@ -47,10 +47,16 @@ def _stream(dev: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, dev=None):
+def _need(t: torch.Tensor, name: str, dtype=None, dev=None, strided=False):
+    """Checks a tensor argument.  strided: a [batch, token, head, d] view whose
+    last dimension is contiguous is accepted (its strides go to the library);
+    otherwise the tensor must be contiguous."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
+    if strided:
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be [batch, token, head, d] with d contiguous")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
@@ -58,17 +64,29 @@ def _need(t: torch.Tensor, name: str, dtype=None, dev=None):
         raise ValueError(f"{name} is on {t.device}, expected {dev}")
 
 
-class _Problem:
-    """A vs_problem plus the host arrays it points to (kept alive)."""
+def _strides(t: Optional[torch.Tensor]):
+    return (0, 0, 0) if t is None else tuple(int(x) for x in t.stride()[:3])
 
-    def __init__(self, batch, h_q, h_kv, d, n_q, n_k, dtype_code, cu_seqlens, stripe, scale):
+
+class _Problem:
+    """A vs_problem plus the host arrays it points to (kept alive).
+
+    stripe = (W, q_rank, k_rank) with k_rank an int or "all" (K/V hold every
+    rank's chunk, chunk u after chunk u-1).  Strides are taken from the
+    tensors given (q, k, v, o, do); absent ones are contiguous."""
+
+    def __init__(self, batch, h_q, h_kv, d, n_q, n_k, dtype_code, cu_seqlens, stripe, scale,
+                 q=None, k=None, v=None, o=None, do=None):
         W, qr, kr = stripe if stripe is not None else (1, 0, 0)
+        if kr == "all":
+            kr = _abi.VS_ALL_CHUNKS
         n_global = n_q * W
         cu = list(cu_seqlens) if cu_seqlens is not None else [0, n_global]
         self.cu = (ctypes.c_int32 * len(cu))(*[int(x) for x in cu])
+        st = [_abi.i64x3(*_strides(t)) for t in (q, k, v, o, do)]
         self.s = _abi.VsProblem(batch, h_q, h_kv, d, n_q, n_k, BLOCK, dtype_code,
                                 float(scale) if scale else 0.0, len(cu) - 1,
-                                ctypes.cast(self.cu, _abi.i32p), int(W), int(qr), int(kr))
+                                ctypes.cast(self.cu, _abi.i32p), int(W), int(qr), int(kr), *st)
         self.n_seg = len(cu) - 1
 
     @property
@@ -130,13 +148,13 @@ def estimate_index(q: torch.Tensor, k: torch.Tensor, v_budget: Sequence[int],
     return_scores, the vertical scores [B, Hq, N] and slash scores [B, Hq, N/64]).
     """
     dev = q.device
-    _need(q, "q", dev=dev)
-    _need(k, "k", q.dtype, dev)
+    _need(q, "q", dev=dev, strided=True)
+    _need(k, "k", q.dtype, dev, strided=True)
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     dc = _dtype_code(q)
     vp, sp, vm, sm = index_capacity(B, Hq, Hkv, d, N, v_budget, s_budget, cu_seqlens, dc)
-    P = _Problem(B, Hq, Hkv, d, N, N, dc, cu_seqlens, None, None)
+    P = _Problem(B, Hq, Hkv, d, N, N, dc, cu_seqlens, None, None, q=q, k=k)
     v_ptr = torch.tensor(vp, dtype=torch.int32, device=dev)
     s_ptr = torch.tensor(sp, dtype=torch.int32, device=dev)
     v_idx = torch.empty(max(vp[-1], 1), dtype=torch.int32, device=dev)
@@ -166,15 +184,15 @@ def estimate_index_topp(q: torch.Tensor, k: torch.Tensor, v_cap: Sequence[int], 
     padded with -1.
     """
     dev = q.device
-    _need(q, "q", dev=dev)
-    _need(k, "k", q.dtype, dev)
+    _need(q, "q", dev=dev, strided=True)
+    _need(k, "k", q.dtype, dev, strided=True)
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     if len(p_v) != Hq or len(p_s) != Hq:
         raise ValueError(f"p_v and p_s need {Hq} entries")
     dc = _dtype_code(q)
     vp, sp, vm, sm = index_capacity(B, Hq, Hkv, d, N, v_cap, s_cap, cu_seqlens, dc)
-    P = _Problem(B, Hq, Hkv, d, N, N, dc, cu_seqlens, None, None)
+    P = _Problem(B, Hq, Hkv, d, N, N, dc, cu_seqlens, None, None, q=q, k=k)
     v_ptr = torch.tensor(vp, dtype=torch.int32, device=dev)
     s_ptr = torch.tensor(sp, dtype=torch.int32, device=dev)
     v_idx = torch.empty(max(vp[-1], 1), dtype=torch.int32, device=dev)
@@ -216,7 +234,9 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Vs
                     merge: bool = False):
     """Sparse attention forward.  Returns (o [B, Nq, Hq, d], lse [B, Hq, Nq] fp32).
 
-    stripe = (world, q_rank, k_rank) for a block-striped call (one ring step).
+    stripe = (world, q_rank, k_rank) for a block-striped call (one ring step);
+    k_rank = "all": k / v hold every rank's chunk, one after the other
+    (the whole ring of worker q_rank in one call).
     merge: out (fp32) and lse hold a running result (zeros / -inf to start);
     this call's result is merged into them in place (fused lse_merge).
     """
@@ -225,17 +245,17 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Vs
             raise ValueError("merge needs out (fp32) and lse holding the running result")
         o_f32 = True
     dev = q.device
-    _need(q, "q", dev=dev)
-    _need(k, "k", q.dtype, dev)
-    _need(v, "v", q.dtype, dev)
+    _need(q, "q", dev=dev, strided=True)
+    _need(k, "k", q.dtype, dev, strided=True)
+    _need(v, "v", q.dtype, dev, strided=True)
     B, Nq, Hq, d = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
-    P = _Problem(B, Hq, Hkv, d, Nq, Nk, _dtype_code(q), cu_seqlens, stripe, scale)
     odt = torch.float32 if o_f32 else q.dtype
     o = out if out is not None else torch.empty((B, Nq, Hq, d), dtype=odt, device=dev)
     l = lse if lse is not None else torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
-    _need(o, "out", odt, dev)
+    _need(o, "out", odt, dev, strided=True)
     _need(l, "lse", torch.float32, dev)
+    P = _Problem(B, Hq, Hkv, d, Nq, Nk, _dtype_code(q), cu_seqlens, stripe, scale, q=q, k=k, v=v, o=o)
     ix = index.struct()
     L = _abi.lib()
     nb = ctypes.c_size_t()
@@ -250,10 +270,10 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Vs
 def attn_bwd_delta(o: torch.Tensor, do: torch.Tensor, out: Optional[torch.Tensor] = None):
     """delta [B, Hq, N] = rowsum(dO * O) (fp32)."""
     dev = do.device
-    _need(o, "o", dev=dev)
-    _need(do, "do", dev=dev)
+    _need(o, "o", dev=dev, strided=True)
+    _need(do, "do", dev=dev, strided=True)
     B, N, Hq, d = do.shape
-    P = _Problem(B, Hq, Hq, d, N, N, _dtype_code(do), None, None, None)
+    P = _Problem(B, Hq, Hq, d, N, N, _dtype_code(do), None, None, None, o=o, do=do)
     delta = out if out is not None else torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     _abi.check(_abi.lib().vs_attn_bwd_delta(P.ref, _ptr(o), int(o.dtype == torch.float32),
                                             _ptr(do), _ptr(delta), _stream(dev)))
@@ -271,11 +291,11 @@ def sparse_attn_bwd(q, k, v, o, do, lse, index: VsIndexT, delta=None, dq=None,
     """
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (do, "do")):
-        _need(t, n, q.dtype, dev)
+        _need(t, n, q.dtype, dev, strided=True)
     _need(lse, "lse", torch.float32, dev)
     B, Nq, Hq, d = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
-    P = _Problem(B, Hq, Hkv, d, Nq, Nk, _dtype_code(q), cu_seqlens, stripe, scale)
+    P = _Problem(B, Hq, Hkv, d, Nq, Nk, _dtype_code(q), cu_seqlens, stripe, scale, q=q, k=k, v=v, o=o, do=do)
     acc = bool(accumulate)
     if acc and dq is None:
         raise ValueError("accumulate=True needs dq")
@@ -287,7 +307,7 @@ def sparse_attn_bwd(q, k, v, o, do, lse, index: VsIndexT, delta=None, dq=None,
         _need(t, n, torch.float32, dev)
     o_f32 = 0
     if o is not None:
-        _need(o, "o", dev=dev)
+        _need(o, "o", dev=dev, strided=True)
         o_f32 = int(o.dtype == torch.float32)
     if delta is not None:
         _need(delta, "delta", torch.float32, dev)

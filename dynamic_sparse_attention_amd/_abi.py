@@ -24,10 +24,16 @@ i32, f32, vp, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_siz
 i32p = ctypes.POINTER(ctypes.c_int32)
 
 
+VS_ALL_CHUNKS = -1
+i64x3 = ctypes.c_int64 * 3
+
+
 class VsProblem(ctypes.Structure):
     _fields_ = [("batch", i32), ("h_q", i32), ("h_kv", i32), ("head_dim", i32), ("n_q", i32),
                 ("n_k", i32), ("block", i32), ("dtype", i32), ("scale", f32), ("n_seg", i32),
-                ("cu_seqlens", i32p), ("stripe_world", i32), ("q_rank", i32), ("k_rank", i32)]
+                ("cu_seqlens", i32p), ("stripe_world", i32), ("q_rank", i32), ("k_rank", i32),
+                ("q_stride", i64x3), ("k_stride", i64x3), ("v_stride", i64x3), ("o_stride", i64x3),
+                ("do_stride", i64x3)]
 
 
 class VsIndex(ctypes.Structure):

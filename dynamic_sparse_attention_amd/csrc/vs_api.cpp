@@ -21,8 +21,8 @@ namespace vs {
 hipError_t launch_fwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st);
 hipError_t launch_prep_vertical(const AttnParams& p, int n_lists, const int* v_ptr, const int* v_idx,
                                 hipStream_t st);
-hipError_t launch_delta(const void* o, int o_f32, int bf16, const void* dout, float* delta, int batch,
-                        int n, int h, int d, hipStream_t st);
+hipError_t launch_delta(const void* o, Stride3 so, int o_f32, int bf16, const void* dout, Stride3 sdo,
+                        float* delta, int batch, int n, int h, int d, hipStream_t st);
 hipError_t launch_lse_log2(const float* lse, float* lse2, size_t count, hipStream_t st);
 hipError_t launch_lse_merge(int batch, int n, int heads, int d, float* o_acc, float* lse_acc,
                             const float* o_part, const float* lse_part, hipStream_t st);
@@ -57,11 +57,32 @@ vs_status ok() {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Prob {
-  int batch, h_q, h_kv, d, n_q, n_k, block, bf16, n_seg, W, q_rank, k_rank, n_global, nqb, nkb;
+  int batch, h_q, h_kv, d, n_q, n_k, block, bf16, n_seg, W, q_rank, k_rank, k_all, n_global, nqb, nkb;
   float scale;
   std::vector<int> cu;
+  vs::Stride3 sq, sk, sv, so, sdo;
   int n_lists() const { return batch * h_q * n_seg; }
 };
+
+// Element strides of one tensor: all zero selects the contiguous layout
+// [batch, n, heads, d]; otherwise each must be >= 0 and a multiple of 8
+// elements (16-byte loads of bf16 rows).
+vs_status stride_of(const int64_t* in, long long n, long long heads, long long d, const char* name,
+                    vs::Stride3* out) {
+  if (in[0] == 0 && in[1] == 0 && in[2] == 0) {
+    *out = {n * heads * d, heads * d, d};
+    return VS_OK;
+  }
+  static const char* dim[3] = {"batch", "token", "head"};
+  for (int i = 0; i < 3; ++i) {
+    if (in[i] < 0) return fail(VS_ERR_SHAPE, "%s %s stride %lld is negative", name, dim[i], (long long)in[i]);
+    if (in[i] % 8 != 0)
+      return fail(VS_ERR_UNSUPPORTED, "%s %s stride %lld is not a multiple of 8 elements", name, dim[i],
+                  (long long)in[i]);
+  }
+  *out = {in[0], in[1], in[2]};
+  return VS_OK;
+}
 
 vs_status check_problem(const vs_problem* p, Prob* c) {
   if (!p) return fail(VS_ERR_NULL, "problem is NULL");
@@ -94,6 +115,7 @@ vs_status check_problem(const vs_problem* p, Prob* c) {
   }
   c->n_global = c->cu[p->n_seg];
   c->W = p->stripe_world;
+  c->k_all = 0;
   if (c->W < 1) return fail(VS_ERR_SHAPE, "stripe_world must be >= 1");
   if (c->W == 1) {
     if (p->n_q != c->n_global || p->n_k != c->n_global)
@@ -103,18 +125,31 @@ vs_status check_problem(const vs_problem* p, Prob* c) {
     if (p->n_seg != 1) return fail(VS_ERR_UNSUPPORTED, "striped calls take one segment");
     if (c->n_global % (p->block * c->W) != 0)
       return fail(VS_ERR_SHAPE, "n_global %d not a multiple of block*stripe_world", c->n_global);
-    if (p->n_q != c->n_global / c->W || p->n_k != c->n_global / c->W)
-      return fail(VS_ERR_SHAPE, "striped call needs n_q == n_k == n_global/stripe_world");
-    if (p->q_rank < 0 || p->q_rank >= c->W || p->k_rank < 0 || p->k_rank >= c->W)
-      return fail(VS_ERR_SHAPE, "q_rank/k_rank outside [0, stripe_world)");
+    c->k_all = p->k_rank == VS_ALL_CHUNKS;
+    const int nk_want = c->k_all ? c->n_global : c->n_global / c->W;
+    if (p->n_q != c->n_global / c->W || p->n_k != nk_want)
+      return fail(VS_ERR_SHAPE, "striped call needs n_q == n_global/stripe_world and n_k == %s",
+                  c->k_all ? "n_global (all chunks)" : "n_global/stripe_world");
+    if (p->q_rank < 0 || p->q_rank >= c->W || (!c->k_all && (p->k_rank < 0 || p->k_rank >= c->W)))
+      return fail(VS_ERR_SHAPE, "q_rank/k_rank outside [0, stripe_world) (k_rank may be VS_ALL_CHUNKS)");
   }
   if ((long long)p->batch * p->n_q > (1ll << 31) / 64 || (long long)p->batch * p->n_k > (1ll << 31) / 64)
     return fail(VS_ERR_UNSUPPORTED, "batch * tokens too large");
-  // The bf16 attention kernels address K and V rows of one (batch, KV head)
-  // with 32-bit byte offsets.
-  if (p->dtype == VS_BF16 && (long long)p->n_k * p->h_kv * p->head_dim * 2 >= (1ll << 32))
-    return fail(VS_ERR_UNSUPPORTED, "n_k * h_kv * head_dim * 2 = %lld bytes of K per sequence exceeds 4 GiB",
-                (long long)p->n_k * p->h_kv * p->head_dim * 2);
+  vs_status st;
+  if ((st = stride_of(p->q_stride, p->n_q, p->h_q, p->head_dim, "q", &c->sq))) return st;
+  if ((st = stride_of(p->k_stride, p->n_k, p->h_kv, p->head_dim, "k", &c->sk))) return st;
+  if ((st = stride_of(p->v_stride, p->n_k, p->h_kv, p->head_dim, "v", &c->sv))) return st;
+  if ((st = stride_of(p->o_stride, p->n_q, p->h_q, p->head_dim, "o", &c->so))) return st;
+  if ((st = stride_of(p->do_stride, p->n_q, p->h_q, p->head_dim, "do", &c->sdo))) return st;
+  // The bf16 attention kernels address the K and V rows of one (batch, KV
+  // head) with 32-bit byte offsets from a per-(batch, head) base.
+  if (p->dtype == VS_BF16 && p->n_k > 0) {
+    const long long kmax = (long long)(p->n_k - 1) * c->sk.t * 2 + 256;
+    const long long vmax = (long long)(p->n_k - 1) * c->sv.t * 2 + 256;
+    if (kmax >= (1ll << 32) || vmax >= (1ll << 32))
+      return fail(VS_ERR_UNSUPPORTED,
+                  "K/V rows of one head span %lld / %lld bytes, beyond the kernels' 4 GiB offsets", kmax, vmax);
+  }
   c->batch = p->batch;
   c->h_q = p->h_q;
   c->h_kv = p->h_kv;
@@ -163,7 +198,13 @@ void fill_params(const Prob& c, vs::AttnParams* a) {
   a->W = c.W;
   a->q_rank = c.q_rank;
   a->k_rank = c.k_rank;
+  a->k_all = c.k_all;
   a->n_global = c.n_global;
+  a->sq = c.sq;
+  a->sk = c.sk;
+  a->sv = c.sv;
+  a->so = c.so;
+  a->sdo = c.sdo;
   a->seg.n_seg = c.n_seg;
   for (int s = 0; s <= c.n_seg; ++s) a->seg.start_blk[s] = c.cu[s] / c.block;
 }
@@ -422,8 +463,8 @@ vs_status vs_attn_bwd_delta(const vs_problem* p, const void* o, int32_t o_f32, c
   vs_status st = check_problem(p, &c);
   if (st) return st;
   if (!o || !dout || !delta) return fail(VS_ERR_NULL, "o, dout or delta is NULL");
-  return hip_status(vs::launch_delta(o, o_f32 != 0, c.bf16, dout, delta, c.batch, c.n_q, c.h_q, c.d,
-                                     (hipStream_t)stream),
+  return hip_status(vs::launch_delta(o, c.so, o_f32 != 0, c.bf16, dout, c.sdo, delta, c.batch, c.n_q,
+                                     c.h_q, c.d, (hipStream_t)stream),
                     "vs_attn_bwd_delta");
 }
 
@@ -495,7 +536,7 @@ vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, 
   } else {
     if (!delta) {
       float* dws = reinterpret_cast<float*>(base + w.delta);
-      e = vs::launch_delta(o, o_f32 != 0, c.bf16, dout, dws, c.batch, c.n_q, c.h_q, c.d, s);
+      e = vs::launch_delta(o, c.so, o_f32 != 0, c.bf16, dout, c.sdo, dws, c.batch, c.n_q, c.h_q, c.d, s);
       delta = dws;
     }
     if (e == hipSuccess) e = vs::launch_lse_log2(lse, l2, (size_t)c.batch * c.h_q * c.n_q, s);

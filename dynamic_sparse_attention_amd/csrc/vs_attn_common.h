@@ -10,12 +10,23 @@
 //     whose block offset beta - beta(m) is not selected (those entries are
 //     already inside a slash tile), 64 columns per tile, causal per row.
 // Positions in the index are global (index coordinates); a block-striped
-// call relabels global key block k_rank + W*j to local block j.
+// call relabels global key block k_rank + W*j to local block j, or, holding
+// every rank's chunk one after the other, global block u + W*j to local
+// block u*(nkb/W) + j.
 #pragma once
 
 #include "vs_device.h"
 
 namespace vs {
+
+// Element strides of one [batch, token, head, channel] tensor (channels
+// contiguous).
+struct Stride3 {
+  long long b, t, h;
+  __host__ __device__ __forceinline__ long long at(long long bb, long long tt, long long hh) const {
+    return bb * b + tt * t + hh * h;
+  }
+};
 
 struct AttnParams {
   const void* q;
@@ -46,7 +57,9 @@ struct AttnParams {
   float scale;
   float sl2;          // scale * log2(e)
   int W, q_rank, k_rank;
+  int k_all;          // striped: K/V hold every rank's chunk (k_rank unused)
   int n_global;
+  Stride3 sq, sk, sv, so, sdo;  // element strides of Q, K, V, O (its own type), dO
   int qranges;        // backward column units: query-block ranges per column tile
   int qrange_len;
   int col_tiles;      // backward column units: column tiles per list
@@ -86,10 +99,26 @@ __device__ __forceinline__ RowBlock row_block(const AttnParams& p, int i_local) 
 // Local key block of global key block kb_glob, or -1 if this call does not hold it.
 __device__ __forceinline__ int local_key_block(const AttnParams& p, int kb_glob) {
   if (p.W == 1) return (kb_glob >= 0 && kb_glob < p.nkb) ? kb_glob : -1;
+  if (kb_glob < 0) return -1;
+  if (p.k_all) {
+    const int nc = p.nkb / p.W;  // key blocks per chunk
+    const int j = kb_glob / p.W;
+    return j < nc ? (kb_glob % p.W) * nc + j : -1;
+  }
   const int d = kb_glob - p.k_rank;
   if (d < 0 || d % p.W != 0) return -1;
   const int j = d / p.W;
   return j < p.nkb ? j : -1;
+}
+
+// Global key block of local key block j (0 <= j < nkb).
+__device__ __forceinline__ int global_key_block(const AttnParams& p, int j) {
+  if (p.W == 1) return j;
+  if (p.k_all) {
+    const int nc = p.nkb / p.W;
+    return j / nc + p.W * (j % nc);
+  }
+  return p.k_rank + p.W * j;
 }
 
 // Local query block of global block qb_glob, or -1 if this call does not hold it.
@@ -104,8 +133,7 @@ __device__ __forceinline__ int local_query_block(const AttnParams& p, int qb_glo
 // Local key position of a global position held by this call.
 __device__ __forceinline__ int local_key_pos(const AttnParams& p, int m_glob) {
   if (p.W == 1) return m_glob;
-  const int kb = m_glob / kBlock;
-  return ((kb - p.k_rank) / p.W) * kBlock + (m_glob % kBlock);
+  return local_key_block(p, m_glob / kBlock) * kBlock + (m_glob % kBlock);
 }
 
 }  // namespace vs

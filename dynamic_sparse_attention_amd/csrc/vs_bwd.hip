@@ -45,7 +45,7 @@ struct DqWorker {
   float dl[2];     // delta
   const T* kb;
   const T* vb;
-  int kvs;
+  int kvs, vvs;    // K and V row strides (elements)
   T* kt;           // this wave's K^T staging area [D][KTP]
   float sl2;
 
@@ -56,7 +56,7 @@ struct DqWorker {
     const int l32 = lane & 31;
     const int kpos = S.key_pos(n, slot_perm<KPL>(l32));
     const T* krow = kb + (size_t)kpos * kvs;
-    const T* vrow = vb + (size_t)kpos * kvs;
+    const T* vrow = vb + (size_t)kpos * vvs;
     frag kf[NCD], vf[NCD];
 #pragma unroll
     for (int c = 0; c < NCD; ++c) {
@@ -137,14 +137,15 @@ __global__ __launch_bounds__(kQThreads) void vs_bwd_dq_kernel(AttnParams p) {
   W wk;
   const T* q = reinterpret_cast<const T*>(p.q);
   const T* dout = reinterpret_cast<const T*>(p.dout);
-  const size_t row0 = (size_t)b * p.n_q + (size_t)i_local * kBlock;
+  const int row0 = i_local * kBlock;  // first row of the block in this batch row
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
-    const size_t roff = ((row0 + 32 * rg + l32) * p.h_q + h) * D;
+    const size_t qoff = p.sq.at(b, row0 + 32 * rg + l32, h);
+    const size_t doff = p.sdo.at(b, row0 + 32 * rg + l32, h);
 #pragma unroll
     for (int c = 0; c < W::NCD; ++c) {
-      wk.qf[rg][c] = load_frag<T>(q + roff + c * W::KC + hl * W::KPL);
-      wk.dof[rg][c] = load_frag<T>(dout + roff + c * W::KC + hl * W::KPL);
+      wk.qf[rg][c] = load_frag<T>(q + qoff + c * W::KC + hl * W::KPL);
+      wk.dof[rg][c] = load_frag<T>(dout + doff + c * W::KC + hl * W::KPL);
     }
 #pragma unroll
     for (int ct = 0; ct < W::NCT; ++ct) wk.dq[rg][ct] = f32x16{0};
@@ -153,9 +154,10 @@ __global__ __launch_bounds__(kQThreads) void vs_bwd_dq_kernel(AttnParams p) {
     wk.lse2[rg] = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
     wk.dl[rg] = p.delta[li];
   }
-  wk.kvs = p.h_kv * D;
-  wk.kb = reinterpret_cast<const T*>(p.k) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
-  wk.vb = reinterpret_cast<const T*>(p.v) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
+  wk.kvs = (int)p.sk.t;
+  wk.vvs = (int)p.sv.t;
+  wk.kb = reinterpret_cast<const T*>(p.k) + p.sk.at(b, 0, kvh);
+  wk.vb = reinterpret_cast<const T*>(p.v) + p.sv.at(b, 0, kvh);
   wk.kt = reinterpret_cast<T*>(buf) + wave * D * W::KTP;
   wk.sl2 = p.sl2;
 
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(kQThreads) void vs_bwd_dq_kernel(AttnParams p) {
     const int r = x / (D / 4);
     const int c4 = (x % (D / 4)) * 4;
     const f32x4 v = *reinterpret_cast<const f32x4*>(ob + r * OB_PITCH + c4) * p.scale;
-    float* dst = p.dq + ((row0 + r) * p.h_q + h) * D + c4;
+    float* dst = p.dq + (((size_t)b * p.n_q + row0 + r) * p.h_q + h) * D + c4;
     if (p.dq_accumulate) *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
     else *reinterpret_cast<f32x4*>(dst) = v;
   }
@@ -215,8 +217,8 @@ struct KvWorker {
   // One query tile of 64 rows (LDS: Q^T, dO^T, lse2, delta already staged).
   // valid(r) for this lane's key column and row r.
   template <class ValidF>
-  __device__ __forceinline__ void tile(const T* qrows, const T* dorows, size_t rstride, const T* qt,
-                                       const T* dot, const float* s_lse2, const float* s_del,
+  __device__ __forceinline__ void tile(const T* qrows, const T* dorows, size_t qstride, size_t dostride,
+                                       const T* qt, const T* dot, const float* s_lse2, const float* s_del,
                                        float sl2, ValidF valid) {
     const int lane = threadIdx.x & 63;
     const int hl = lane >> 5;
@@ -224,13 +226,13 @@ struct KvWorker {
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
-      const size_t roff = (size_t)(32 * rg + slot_perm<KPL>(l32)) * rstride;
+      const size_t rr = (size_t)(32 * rg + slot_perm<KPL>(l32));
       s[rg] = f32x16{0};
       dp[rg] = f32x16{0};
 #pragma unroll
       for (int c = 0; c < NCD; ++c) {
-        const frag qa = load_frag<T>(qrows + roff + c * KC + hl * KPL);
-        const frag da = load_frag<T>(dorows + roff + c * KC + hl * KPL);
+        const frag qa = load_frag<T>(qrows + rr * qstride + c * KC + hl * KPL);
+        const frag da = load_frag<T>(dorows + rr * dostride + c * KC + hl * KPL);
         s[rg] = MF::mma(qa, kB[c], s[rg]);
         dp[rg] = MF::mma(da, vB[c], dp[rg]);
       }
@@ -282,12 +284,10 @@ struct KvLds {
 template <typename T, int D>
 __device__ __forceinline__ void kv_stage(const AttnParams& p, KvLds<T, D>& L, int b, int h, int i) {
   const int tid = threadIdx.x;
-  const size_t rstride = (size_t)p.h_q * D;
-  const T* qb = reinterpret_cast<const T*>(p.q) + ((size_t)b * p.n_q + (size_t)i * kBlock) * rstride + (size_t)h * D;
-  const T* db = reinterpret_cast<const T*>(p.dout) + ((size_t)b * p.n_q + (size_t)i * kBlock) * rstride + (size_t)h * D;
-  auto pos = [&](int r) { return (size_t)r * rstride; };
-  stage_transposed<T, D, 64, KvWorker<T, D>::RTP, kKThreads>(L.qt, qb, pos, tid);
-  stage_transposed<T, D, 64, KvWorker<T, D>::RTP, kKThreads>(L.dot, db, pos, tid);
+  const T* qb = reinterpret_cast<const T*>(p.q) + p.sq.at(b, i * kBlock, h);
+  const T* db = reinterpret_cast<const T*>(p.dout) + p.sdo.at(b, i * kBlock, h);
+  stage_transposed<T, D, 64, KvWorker<T, D>::RTP, kKThreads>(L.qt, qb, [&](int r) { return (size_t)r * p.sq.t; }, tid);
+  stage_transposed<T, D, 64, KvWorker<T, D>::RTP, kKThreads>(L.dot, db, [&](int r) { return (size_t)r * p.sdo.t; }, tid);
   const size_t li = ((size_t)b * p.h_q + h) * p.n_q + (size_t)i * kBlock;
   if (tid < 64) {
     const float lse = p.lse[li + tid];
@@ -303,9 +303,8 @@ __device__ __forceinline__ void kv_load_keys(KvWorker<T, D>& wk, const AttnParam
   typedef KvWorker<T, D> W;
   const int lane = threadIdx.x & 63;
   const int hl = lane >> 5;
-  const size_t off = (((size_t)b * p.n_k + kpos) * p.h_kv + kvh) * D;
-  const T* kr = reinterpret_cast<const T*>(p.k) + off;
-  const T* vr = reinterpret_cast<const T*>(p.v) + off;
+  const T* kr = reinterpret_cast<const T*>(p.k) + p.sk.at(b, kpos, kvh);
+  const T* vr = reinterpret_cast<const T*>(p.v) + p.sv.at(b, kpos, kvh);
 #pragma unroll
   for (int c = 0; c < W::NCD; ++c) {
     wk.kB[c] = load_frag<T>(kr + c * W::KC + hl * W::KPL);
@@ -372,7 +371,7 @@ __global__ __launch_bounds__(kKThreads) void vs_bwd_dkdv_slash_kernel(AttnParams
     a_blk = p.seg.start_blk[seg];
     nb_seg = p.seg.start_blk[seg + 1] - a_blk;
   } else {
-    kb_glob = p.k_rank + p.W * j;
+    kb_glob = global_key_block(p, j);
     seg = 0;
     a_blk = 0;
     nb_seg = p.n_global / kBlock;
@@ -383,7 +382,6 @@ __global__ __launch_bounds__(kKThreads) void vs_bwd_dkdv_slash_kernel(AttnParams
 
   W wk;
   kv_load_keys<T, D>(wk, p, b, kvh, kpos);
-  const size_t rstride = (size_t)p.h_q * D;
   for (int hh = 0; hh < G; ++hh) {
     const int h = kvh * G + hh;
     const int list = (b * p.h_q + h) * p.seg.n_seg + seg;
@@ -409,9 +407,9 @@ __global__ __launch_bounds__(kKThreads) void vs_bwd_dkdv_slash_kernel(AttnParams
         const bool dg = (v & 1) != 0;
         kv_stage<T, D>(p, L, b, h, qi);
         __syncthreads();
-        const T* qrows = reinterpret_cast<const T*>(p.q) + ((size_t)b * p.n_q + (size_t)qi * kBlock) * rstride + (size_t)h * D;
-        const T* drows = reinterpret_cast<const T*>(p.dout) + ((size_t)b * p.n_q + (size_t)qi * kBlock) * rstride + (size_t)h * D;
-        wk.tile(qrows, drows, rstride, L.qt, L.dot, L.lse2, L.del, p.sl2,
+        const T* qrows = reinterpret_cast<const T*>(p.q) + p.sq.at(b, qi * kBlock, h);
+        const T* drows = reinterpret_cast<const T*>(p.dout) + p.sdo.at(b, qi * kBlock, h);
+        wk.tile(qrows, drows, p.sq.t, p.sdo.t, L.qt, L.dot, L.lse2, L.del, p.sl2,
                 [&](int r) { return !dg || kin <= r; });
         __syncthreads();
       }
@@ -482,7 +480,6 @@ __global__ __launch_bounds__(kKThreads) void vs_bwd_dkdv_cols_kernel(AttnParams 
 
   W wk;
   kv_load_keys<T, D>(wk, p, b, kvh, kpos);
-  const size_t rstride = (size_t)p.h_q * D;
   for (int i = r_lo; i < r_hi; ++i) {
     const int qbg = qglob(i);
     if (qbg < first_blk) continue;  // uniform across the workgroup
@@ -491,10 +488,10 @@ __global__ __launch_bounds__(kKThreads) void vs_bwd_dkdv_cols_kernel(AttnParams 
     const bool lane_ok = col_ok && off >= 0 && ((bits[off >> 5] >> (off & 31)) & 1u) == 0u;
     kv_stage<T, D>(p, L, b, h, i);
     __syncthreads();
-    const T* qrows = reinterpret_cast<const T*>(p.q) + ((size_t)b * p.n_q + (size_t)i * kBlock) * rstride + (size_t)h * D;
-    const T* drows = reinterpret_cast<const T*>(p.dout) + ((size_t)b * p.n_q + (size_t)i * kBlock) * rstride + (size_t)h * D;
+    const T* qrows = reinterpret_cast<const T*>(p.q) + p.sq.at(b, i * kBlock, h);
+    const T* drows = reinterpret_cast<const T*>(p.dout) + p.sdo.at(b, i * kBlock, h);
     const int row0 = qbg * kBlock;
-    wk.tile(qrows, drows, rstride, L.qt, L.dot, L.lse2, L.del, p.sl2,
+    wk.tile(qrows, drows, p.sq.t, p.sdo.t, L.qt, L.dot, L.lse2, L.del, p.sl2,
             [&](int r) { return lane_ok && m <= row0 + r; });
     __syncthreads();
   }

@@ -94,8 +94,8 @@ struct DqRowsWorker : RowsTiles<D> {
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & lgkmcnt_wait0());
     __syncthreads();
     if (n + 2 < N) {
-      dma_half(S, n + 2, kb, kta[P]);
-      dma_half(S, n + 2, vb, vta[P]);
+      dma_half(S, n + 2, kb, this->krb, kta[P]);
+      dma_half(S, n + 2, vb, this->vrb, vta[P]);
     }
     if (n + 1 < N) scores(kt[P ^ 1], vt[P ^ 1]);
   }
@@ -108,10 +108,10 @@ struct DqRowsWorker : RowsTiles<D> {
     if (NA == 0) return;
     const int N = S.n_halves();
     if (N > 0) {
-      dma_half(S, 0, kb, kta[0]);
-      dma_half(S, 0, vb, vta[0]);
-      dma_half(S, 1, kb, kta[1]);
-      dma_half(S, 1, vb, vta[1]);
+      dma_half(S, 0, kb, this->krb, kta[0]);
+      dma_half(S, 0, vb, this->vrb, vta[0]);
+      dma_half(S, 1, kb, this->krb, kta[1]);
+      dma_half(S, 1, vb, this->vrb, vta[1]);
     }
     // this wave's loads of K(0), V(0) have landed (K(1), V(1) may not have)
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * NVH));
@@ -156,13 +156,15 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   const int r = 32 * wk.rh + l32;  // this lane's row of the block
   const __bf16* q = reinterpret_cast<const __bf16*>(p.q);
   const __bf16* dout = reinterpret_cast<const __bf16*>(p.dout);
-  const size_t row0 = (size_t)b * p.n_q + (size_t)i_local * kBlock;
+  const int row0 = i_local * kBlock;  // first row of the block in this batch row
   {
-    const size_t roff = ((row0 + r) * p.h_q + h) * D + hl * W::KPL;
+    const size_t qoff = p.sq.at(b, row0 + r, h) + hl * W::KPL;
+    const size_t doff = p.sdo.at(b, row0 + r, h) + hl * W::KPL;
+    const size_t roff = p.so.at(b, row0 + r, h) + hl * W::KPL;  // O, for delta
 #pragma unroll
     for (int c = 0; c < W::NCD; ++c) {
-      wk.qf[c] = load_frag<__bf16>(q + roff + c * W::KC);
-      wk.dof[c] = load_frag<__bf16>(dout + roff + c * W::KC);
+      wk.qf[c] = load_frag<__bf16>(q + qoff + c * W::KC);
+      wk.dof[c] = load_frag<__bf16>(dout + doff + c * W::KC);
     }
     const size_t li = ((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + r;
     const float lse = p.lse[li];
@@ -203,9 +205,10 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 #pragma unroll
   for (int ct = 0; ct < W::NCT; ++ct) wk.dq[ct] = f32x16{0};
-  wk.kvs = p.h_kv * D;
-  wk.kb = reinterpret_cast<const __bf16*>(p.k) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
-  wk.vb = reinterpret_cast<const __bf16*>(p.v) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
+  wk.krb = (uint32_t)(p.sk.t * 2);
+  wk.vrb = (uint32_t)(p.sv.t * 2);
+  wk.kb = reinterpret_cast<const __bf16*>(p.k) + p.sk.at(b, 0, kvh);
+  wk.vb = reinterpret_cast<const __bf16*>(p.v) + p.sv.at(b, 0, kvh);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     wk.kt[i] = tiles + ((i * 2 + 0) * NS + ks) * W::TB;
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
     const int rr = x / (D / 4);
     const int c4 = (x % (D / 4)) * 4;
     const f32x4 v = *reinterpret_cast<const f32x4*>(ob + rr * OB_PITCH + c4) * p.scale;
-    float* dst = p.dq + ((row0 + rr) * p.h_q + h) * D + c4;
+    float* dst = p.dq + (((size_t)b * p.n_q + row0 + rr) * p.h_q + h) * D + c4;
     if (p.dq_accumulate) *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
     else *reinterpret_cast<f32x4*>(dst) = v;
   }

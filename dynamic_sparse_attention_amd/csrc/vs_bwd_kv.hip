@@ -64,19 +64,17 @@ __device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, in
   typedef RowTile<D> RT;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const unsigned rstride = (unsigned)(p.h_q * D);
-  const size_t row0 = (size_t)i * kBlock + kTR * half;
-  const size_t base = (((size_t)b * p.n_q + row0) * p.h_q + h) * D;
-  const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + base;
-  const __bf16* db = reinterpret_cast<const __bf16*>(p.dout) + base;
+  const int row0 = i * kBlock + kTR * half;  // first row of the tile in this batch row
+  const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + p.sq.at(b, row0, h);
+  const __bf16* db = reinterpret_cast<const __bf16*>(p.dout) + p.sdo.at(b, row0, h);
   const int rsub = lane / RT::CPR;
 #pragma unroll
   for (int u0 = 0; u0 < RT::NDMA / 2; ++u0) {
     const int u = w * (RT::NDMA / 2) + u0;
     const int chunk = (lane % RT::CPR) ^ RT::swz(u * RT::RPI + rsub);
-    const unsigned eoff = (unsigned)(u * RT::RPI + rsub) * rstride + chunk * 8;
-    __builtin_amdgcn_global_load_lds((glb_vptr)(qb + eoff), (lds_vptr)(B.q + u * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_vptr)(db + eoff), (lds_vptr)(B.dout + u * 1024), 16, 0, 0);
+    const int rr = u * RT::RPI + rsub;  // row of the tile, < kTR
+    __builtin_amdgcn_global_load_lds((glb_vptr)(qb + rr * p.sq.t + chunk * 8), (lds_vptr)(B.q + u * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_vptr)(db + rr * p.sdo.t + chunk * 8), (lds_vptr)(B.dout + u * 1024), 16, 0, 0);
   }
   const size_t li = ((size_t)b * p.h_q + h) * p.n_q + row0 + lane;
   const float* src = w == 0 ? p.lse2 : p.delta;
@@ -101,9 +99,8 @@ struct KvWorkerB {
 
   __device__ __forceinline__ void load_keys(const AttnParams& p, int b, int kvh, int kpos) {
     const int hl = (threadIdx.x & 63) >> 5;
-    const size_t off = (((size_t)b * p.n_k + kpos) * p.h_kv + kvh) * D + hl * KPL;
-    const __bf16* kr = reinterpret_cast<const __bf16*>(p.k) + off;
-    const __bf16* vr = reinterpret_cast<const __bf16*>(p.v) + off;
+    const __bf16* kr = reinterpret_cast<const __bf16*>(p.k) + p.sk.at(b, kpos, kvh) + hl * KPL;
+    const __bf16* vr = reinterpret_cast<const __bf16*>(p.v) + p.sv.at(b, kpos, kvh) + hl * KPL;
 #pragma unroll
     for (int c = 0; c < NCD; ++c) {
       kB[c] = load_frag<__bf16>(kr + c * KC);
@@ -309,7 +306,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     a_blk = p.seg.start_blk[seg];
     nb_seg = p.seg.start_blk[seg + 1] - a_blk;
   } else {
-    kb_glob = p.k_rank + p.W * j;
+    kb_glob = global_key_block(p, j);
     seg = 0;
     a_blk = 0;
     nb_seg = p.n_global / kBlock;

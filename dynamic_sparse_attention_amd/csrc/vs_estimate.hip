@@ -63,15 +63,15 @@ __global__ __launch_bounds__(256) void vs_est_pass1_kernel(AttnParams p, TilePre
   const int k0 = a + (tg - tp.v[s]) * kEstKeyTile;
   const int k1 = min(k0 + kEstKeyTile, e);
   const int G = p.h_q / p.h_kv;
-  const int kvs = p.h_kv * D;
-  const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)b * p.n_k * kvs + (size_t)kvh * D;
+  const int kvs = (int)p.sk.t;
+  const T* kb = reinterpret_cast<const T*>(p.k) + p.sk.at(b, 0, kvh);
   const T* q = reinterpret_cast<const T*>(p.q);
   for (int hg = wave; hg < G; hg += 4) {
     const int h = kvh * G + hg;
     frag qf[2][NCD];
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
-      const T* qr = q + (((size_t)b * p.n_q + (e - 64 + 32 * rg + l32)) * p.h_q + h) * D;
+      const T* qr = q + p.sq.at(b, e - 64 + 32 * rg + l32, h);
 #pragma unroll
       for (int c = 0; c < NCD; ++c) qf[rg][c] = load_frag<T>(qr + c * KC + hl * KPL);
     }
@@ -174,9 +174,9 @@ __global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePre
   const int k0 = a + (tg - tp.v[s]) * kEstKeyTile;
   const int k1 = min(k0 + kEstKeyTile, e);
   const int G = p.h_q / p.h_kv;
-  const int kvs = p.h_kv * D;
+  const int kvs = (int)p.sk.t;
   const int nbt = p.n_global / kBlock;
-  const T* kb = reinterpret_cast<const T*>(p.k) + (size_t)b * p.n_k * kvs + (size_t)kvh * D;
+  const T* kb = reinterpret_cast<const T*>(p.k) + p.sk.at(b, 0, kvh);
   const T* q = reinterpret_cast<const T*>(p.q);
   for (int hg = wave; hg < G; hg += 4) {
     const int h = kvh * G + hg;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePre
     frag qa[2][NCD];
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg) {
-      const T* qr = q + (((size_t)b * p.n_q + (e - 64 + 32 * rg + l32)) * p.h_q + h) * D;
+      const T* qr = q + p.sq.at(b, e - 64 + 32 * rg + l32, h);
 #pragma unroll
       for (int c = 0; c < NCD; ++c) qa[rg][c] = load_frag<T>(qr + c * KC + hl * KPL);
     }

@@ -75,8 +75,8 @@ struct FwdWorkerF32 {
   f32x4 vr[NVG * KG];   // raw V rows of the next half-tile
   float m[2], l[2];
   const float* kb;      // K of (batch, kv head): row pos at kb + pos * kvs
-  const float* vb;
-  int kvs;
+  const float* vb;      // V of (batch, kv head): row pos at vb + pos * vvs
+  int kvs, vvs;
   char* vt;             // this wave's two staging buffers [2][VBUF]
   float sl2;
 
@@ -87,7 +87,7 @@ struct FwdWorkerF32 {
     const int l32 = lane & 31;
     // A operand of S^T = K Q^T: slot l32 loads key slot_perm(l32) of the half.
     const unsigned key = S.key_pos(n, slot_perm<KPL>(l32));
-    const float* krow = kb + key * (unsigned)kvs + hl * KPL;
+    const float* krow = kb + (size_t)key * (size_t)kvs + hl * KPL;
 #pragma unroll
     for (int c = 0; c < NCD; ++c) k[c] = load_frag<float>(krow + c * KC);
   }
@@ -103,7 +103,7 @@ struct FwdWorkerF32 {
       const int cg = gi / NKG;
 #pragma unroll
       for (int u = 0; u < KG; ++u)
-        vr[g * KG + u] = *reinterpret_cast<const f32x4*>(vb + (unsigned)S.key_pos(n, kg * KG + u) * (unsigned)kvs + cg * CG);
+        vr[g * KG + u] = *reinterpret_cast<const f32x4*>(vb + (size_t)S.key_pos(n, kg * KG + u) * (size_t)vvs + cg * CG);
     }
   }
 
@@ -281,10 +281,10 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_f32_kernel(AttnParams p) {
 
   W wk;
   const float* q = reinterpret_cast<const float*>(p.q);
-  const size_t qrow0 = (size_t)b * p.n_q + (size_t)i_local * kBlock;
+  const int row0 = i_local * kBlock;  // first row of the block in this batch row
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
-    const float* qr = q + ((qrow0 + 32 * rg + l32) * p.h_q + h) * D;
+    const float* qr = q + p.sq.at(b, row0 + 32 * rg + l32, h);
 #pragma unroll
     for (int c = 0; c < W::NCD; ++c) wk.qf[rg][c] = load_frag<float>(qr + c * W::KC + hl * W::KPL);
 #pragma unroll
@@ -292,9 +292,10 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_f32_kernel(AttnParams p) {
     wk.m[rg] = -INFINITY;
     wk.l[rg] = 0.f;
   }
-  wk.kvs = p.h_kv * D;
-  wk.kb = reinterpret_cast<const float*>(p.k) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
-  wk.vb = reinterpret_cast<const float*>(p.v) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
+  wk.kvs = (int)p.sk.t;
+  wk.vvs = (int)p.sv.t;
+  wk.kb = reinterpret_cast<const float*>(p.k) + p.sk.at(b, 0, kvh);
+  wk.vb = reinterpret_cast<const float*>(p.v) + p.sv.at(b, 0, kvh);
   wk.vt = buf + wave * 2 * W::VBUF;
   wk.sl2 = p.sl2;
 
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_f32_kernel(AttnParams p) {
     const int r = x / (D / 4);
     const int c4 = (x % (D / 4)) * 4;
     f32x4 v = *reinterpret_cast<const f32x4*>(ob + r * OB_PITCH + c4) * s_inv[r];
-    const size_t off = ((qrow0 + r) * p.h_q + h) * D + c4;
+    const size_t off = p.so.at(b, row0 + r, h) + c4;
     float* dst = reinterpret_cast<float*>(p.o_out) + off;
     if (p.o_merge) v += *reinterpret_cast<const f32x4*>(dst) * s_acc[r];
     *reinterpret_cast<f32x4*>(dst) = v;
@@ -504,8 +505,8 @@ struct FwdRowsWorker : RowsTiles<D> {
     // have returned before the other waves may overwrite those tiles
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & lgkmcnt_wait0());
     __syncthreads();
-    if (n + 2 < N) dma_half(S, n + 2, kb, kta[P]);
-    if (n + 1 < N) dma_half(S, n + 1, vb, vta[P ^ 1]);
+    if (n + 2 < N) dma_half(S, n + 2, kb, this->krb, kta[P]);
+    if (n + 1 < N) dma_half(S, n + 1, vb, this->vrb, vta[P ^ 1]);
     if (n < N) compute(S, n, s[P], s[P ^ 1], kt[P ^ 1], vt[P]);
   }
 
@@ -519,9 +520,9 @@ struct FwdRowsWorker : RowsTiles<D> {
     const int N = S.n_halves();
     f32x16 s[2];
     if (N > 0) {
-      dma_half(S, 0, kb, kta[0]);
-      dma_half(S, 0, vb, vta[0]);
-      dma_half(S, 1, kb, kta[1]);
+      dma_half(S, 0, kb, this->krb, kta[0]);
+      dma_half(S, 0, vb, this->vrb, vta[0]);
+      dma_half(S, 1, kb, this->krb, kta[1]);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(NVH));
     __syncthreads();
@@ -568,10 +569,10 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   W wk;
   wk.rh = __builtin_amdgcn_readfirstlane(wave / NS);
   const __bf16* q = reinterpret_cast<const __bf16*>(p.q);
-  const size_t qrow0 = (size_t)b * p.n_q + (size_t)i_local * kBlock;
-  const int r = 32 * wk.rh + l32;  // this lane's row of the block
+  const int row0 = i_local * kBlock;  // first row of the block in this batch row
+  const int r = 32 * wk.rh + l32;     // this lane's row of the block
   {
-    const __bf16* qr = q + ((qrow0 + r) * p.h_q + h) * D;
+    const __bf16* qr = q + p.sq.at(b, row0 + r, h);
 #pragma unroll
     for (int c = 0; c < W::NCD; ++c) wk.qf[c] = load_frag<__bf16>(qr + c * W::KC + hl * W::KPL);
   }
@@ -579,9 +580,10 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int ct = 0; ct < W::NCT; ++ct) wk.o[ct] = f32x16{0};
   wk.m = -INFINITY;
   wk.l = 0.f;
-  wk.kvs = p.h_kv * D;
-  wk.kb = reinterpret_cast<const __bf16*>(p.k) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
-  wk.vb = reinterpret_cast<const __bf16*>(p.v) + (size_t)b * p.n_k * wk.kvs + (size_t)kvh * D;
+  wk.krb = (uint32_t)(p.sk.t * 2);
+  wk.vrb = (uint32_t)(p.sv.t * 2);
+  wk.kb = reinterpret_cast<const __bf16*>(p.k) + p.sk.at(b, 0, kvh);
+  wk.vb = reinterpret_cast<const __bf16*>(p.v) + p.sv.at(b, 0, kvh);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     wk.kt[i] = tiles + ((i * 2 + 0) * NS + ks) * W::TB;
@@ -647,7 +649,7 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
     const int rr = x / (D / 4);
     const int c4 = (x % (D / 4)) * 4;
     f32x4 v = *reinterpret_cast<const f32x4*>(ob + rr * OB_PITCH + c4) * s_inv[rr];
-    const size_t off = ((qrow0 + rr) * p.h_q + h) * D + c4;
+    const size_t off = p.so.at(b, row0 + rr, h) + c4;
     if (p.o_f32) {
       float* dst = reinterpret_cast<float*>(p.o_out) + off;
       if (p.o_merge) v += *reinterpret_cast<const f32x4*>(dst) * s_acc[rr];

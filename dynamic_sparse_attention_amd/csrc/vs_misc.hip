@@ -137,40 +137,41 @@ hipError_t launch_lse_log2(const float* lse, float* lse2, size_t count, hipStrea
 }
 
 // delta[b, h, n] = sum_c dO[b, n, h, c] * O[b, n, h, c]  (MTraining §3.2 Eq. 1:
-// rowsum(dA * A) = rowsum(dO * O)).  D/4 threads per row, 4 channels each.
+// rowsum(dA * A) = rowsum(dO * O)).  D/4 threads per row, 4 channels each;
+// O and dO are addressed through their strides.
 template <typename TO, typename TD, int D>
-__global__ __launch_bounds__(256) void vs_delta_kernel(const TO* o, const TD* dout, float* delta,
-                                                       int batch, int n, int h, size_t rows) {
+__global__ __launch_bounds__(256) void vs_delta_kernel(const TO* o, Stride3 so, const TD* dout, Stride3 sdo,
+                                                       float* delta, int batch, int n, int h, size_t rows) {
   constexpr int TPR = D / 4;
   const size_t gt = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t row = gt / TPR;
   const int c4 = (int)(gt % TPR) * 4;
+  // row = (b * n + pos) * h + head  ->  delta[(b * h + head) * n + pos]
+  const size_t head = row % h;
+  const size_t bp = row / h;
+  const size_t pos = bp % n;
+  const size_t b = bp / n;
   float acc = 0.f;
   if (row < rows) {
+    const TO* orow = o + so.at(b, pos, head) + c4;
+    const TD* drow = dout + sdo.at(b, pos, head) + c4;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc += to_f32(o[row * D + c4 + u]) * to_f32(dout[row * D + c4 + u]);
+    for (int u = 0; u < 4; ++u) acc += to_f32(orow[u]) * to_f32(drow[u]);
   }
 #pragma unroll
   for (int w = TPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, 64);
-  if (row < rows && (gt % TPR) == 0) {
-    // row = (b * n + pos) * h + head  ->  delta[(b * h + head) * n + pos]
-    const size_t head = row % h;
-    const size_t bp = row / h;
-    const size_t pos = bp % n;
-    const size_t b = bp / n;
-    delta[(b * h + head) * n + pos] = acc;
-  }
+  if (row < rows && (gt % TPR) == 0) delta[(b * h + head) * n + pos] = acc;
 }
 
-hipError_t launch_delta(const void* o, int o_f32, int bf16, const void* dout, float* delta, int batch,
-                        int n, int h, int d, hipStream_t st) {
+hipError_t launch_delta(const void* o, Stride3 so, int o_f32, int bf16, const void* dout, Stride3 sdo,
+                        float* delta, int batch, int n, int h, int d, hipStream_t st) {
   const size_t rows = (size_t)batch * n * h;
   if (rows == 0) return hipSuccess;
   const size_t threads = rows * (d / 4);
   const dim3 grid((unsigned)((threads + 255) / 256));
 #define VS_DELTA(TO, TD, DD)                                                                        \
   VS_TRACED(st, "vs_delta", hipLaunchKernelGGL((vs_delta_kernel<TO, TD, DD>), grid, dim3(256), 0, st, (const TO*)o, \
-                     (const TD*)dout, delta, batch, n, h, rows))
+                     so, (const TD*)dout, sdo, delta, batch, n, h, rows))
   if (d == 128) {
     if (o_f32 && bf16) VS_DELTA(float, __bf16, 128);
     else if (o_f32) VS_DELTA(float, float, 128);

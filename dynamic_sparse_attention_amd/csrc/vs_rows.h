@@ -52,9 +52,9 @@ struct RowsTiles {
 
   int ro[4];
   int to[4];
-  const __bf16* kb;   // K of (batch, kv head): row pos at kb + pos * kvs
-  const __bf16* vb;
-  int kvs;
+  const __bf16* kb;   // K of (batch, kv head): key row pos at byte pos * krb
+  const __bf16* vb;   // V of (batch, kv head): key row pos at byte pos * vrb
+  uint32_t krb, vrb;  // row strides in bytes
   int rh;             // row half of this wave
 
   __device__ __forceinline__ void init_offsets() {
@@ -91,22 +91,21 @@ struct RowsTiles {
   // u lands in group u, lane L at byte 16 L of it, i.e. row u * RPI + L / CPR,
   // chunk slot L % CPR, which holds chunk (L % CPR) ^ swz(L / CPR) of that
   // row.  dst is wave-uniform, so the LDS destinations stay in scalar
-  // registers.  Byte offsets are 32-bit: the caller guarantees
-  // n_k * kvs * 2 < 2^32 (which also keeps row positions below 2^24 for the
-  // 24-bit multiply).
+  // registers.  Byte offsets are 32-bit: the caller guarantees that
+  // (n_k - 1) * rb + 256 < 2^32 for row stride rb (bytes).
   template <int NP, class Set>
-  __device__ __forceinline__ void dma_part(const Set& S, int n, const __bf16* src, uint32_t dst, int part) const {
+  __device__ __forceinline__ void dma_part(const Set& S, int n, const __bf16* src, uint32_t rb, uint32_t dst,
+                                           int part) const {
     constexpr int NU = NVL / NP;
     static_assert(NU >= 1 && NVL % NP == 0, "loads per part");
     const int lane = threadIdx.x & 63;
     const int rr = lane / CPR;
     const uint32_t cbyte = (uint32_t)(((lane % CPR) ^ swz(rr)) * 16);
-    const uint32_t rb = (uint32_t)(kvs * 2);
     if constexpr (Set::kContiguous) {
       // consecutive rows: a wave-uniform base per load, the lane part fixed
       const int key0 = __builtin_amdgcn_readfirstlane(S.key_pos(n, part * NU * RPI));
       const char* g = reinterpret_cast<const char*>(src) + (size_t)key0 * rb;
-      const uint32_t loff = __umul24((uint32_t)rr, rb) + cbyte;
+      const uint32_t loff = (uint32_t)rr * rb + cbyte;
 #pragma unroll
       for (int u0 = 0; u0 < NU; ++u0)
         dma_lds16_so(g + (size_t)(u0 * RPI) * rb, loff, dst + (part * NU + u0) * GROUP);
@@ -118,14 +117,14 @@ struct RowsTiles {
       for (int u0 = 0; u0 < NU; ++u0) pos[u0] = (uint32_t)S.key_pos(n, (part * NU + u0) * RPI + rr);
 #pragma unroll
       for (int u0 = 0; u0 < NU; ++u0)
-        dma_lds16_so(src, __umul24(pos[u0], rb) + cbyte, dst + (part * NU + u0) * GROUP);
+        dma_lds16_so(src, pos[u0] * rb + cbyte, dst + (part * NU + u0) * GROUP);
     }
   }
 
   // This wave's half of the loads when the two waves of a row pair share them.
   template <class Set>
-  __device__ __forceinline__ void dma_half(const Set& S, int n, const __bf16* src, uint32_t dst) const {
-    dma_part<2>(S, n, src, dst, rh);
+  __device__ __forceinline__ void dma_half(const Set& S, int n, const __bf16* src, uint32_t rb, uint32_t dst) const {
+    dma_part<2>(S, n, src, rb, dst, rh);
   }
 
   // Row operand: tile row slot_perm(L % 32), channels of k chunk c.

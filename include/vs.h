@@ -20,10 +20,13 @@
  * - Device buffers are caller-owned and must stay valid until the enqueued
  *   work completes.  Host arrays (vs_problem.cu_seqlens, budgets) are read
  *   only during the call.
- * - Tensor layout is contiguous [batch, token, head, head_dim] ("BSHD") for
- *   Q, K, V, O, dO, dQ, dK, dV and contiguous [batch, head, token] for LSE and
- *   delta.  Element types: Q, K, V, dO in vs_problem.dtype; O in that dtype or
- *   fp32 (o_f32); LSE, delta, dQ, dK, dV are fp32.
+ * - Tensor layout is [batch, token, head, head_dim] ("BSHD") for Q, K, V,
+ *   O, dO, dQ, dK, dV and contiguous [batch, head, token] for LSE and delta.
+ *   Q, K, V, O and dO take element strides for (batch, token, head) in
+ *   vs_problem (head_dim contiguous), so that for instance slices of a fused
+ *   QKV projection are passed without a copy; dQ, dK, dV, LSE and delta are
+ *   contiguous.  Element types: Q, K, V, dO in vs_problem.dtype; O in that
+ *   dtype or fp32 (o_f32); LSE, delta, dQ, dK, dV are fp32.
  * - LSE is the natural-log log-sum-exp of the scaled scores of a row over its
  *   support.  A row with an empty support has O = 0 and LSE = -inf and
  *   contributes no gradient.
@@ -73,6 +76,23 @@ typedef enum { VS_F32 = 0, VS_BF16 = 1 } vs_dtype;
  * n_global == W*n_q == W*n_k.  A striped call computes the global mask
  * restricted to its rows and keys; one worker's ring step on KV chunk u is
  * the call with q_rank = worker, k_rank = u.
+ * All chunks at once (k_rank = VS_ALL_CHUNKS): K and V hold the W chunks one
+ * after the other, chunk u (the keys of rank u) at rows u*n_global/W ..
+ * (u+1)*n_global/W - 1, so n_k == n_global; local key block u*(n_k/W) + j is
+ * global block u + W*j.  The call is the whole ring of one worker (every step
+ * of Algorithm 2's inner loop) in one pass: the rows' softmax runs over all
+ * chunks at once, so no partial result is merged, and dK / dV come out for
+ * every chunk, in the same chunk-after-chunk layout.
+ *
+ * Strides: x_stride[0..2] are the element strides of batch, token and head
+ * (head_dim is contiguous).  All three zero selects the contiguous layout
+ * ([batch, n, heads, head_dim] with n = n_q for Q, O, dO and n_k for K, V).
+ * Otherwise each must be >= 0 and a multiple of 8 elements, and the tensor's
+ * base pointer 16-byte aligned; rows of the output O must not overlap.
+ * o_stride is in elements of O's type (fp32 when o_f32).  For bf16 inputs
+ * the kernels address the rows of one (batch, KV head) of K and V with
+ * 32-bit byte offsets: (n_k - 1) * token stride * 2 + 256 must stay below
+ * 2^32 (else VS_ERR_UNSUPPORTED).
  */
 typedef struct vs_problem {
   int32_t batch;        /* >= 1                                                   */
@@ -80,8 +100,8 @@ typedef struct vs_problem {
   int32_t h_kv;         /* key/value heads; Q head h reads KV head h*h_kv/h_q      */
   int32_t head_dim;     /* 64 or 128                                              */
   int32_t n_q;          /* rows per batch row held by this call                   */
-  int32_t n_k;          /* keys per batch row held by this call; for bf16,         
-                           n_k*h_kv*head_dim*2 < 2^32 (else VS_ERR_UNSUPPORTED)   */
+  int32_t n_k;          /* keys per batch row held by this call (bf16: see the
+                           32-bit offset limit under Strides above)               */
   int32_t block;        /* B, 64 (the slash granularity of MTraining §4.1 (ii))    */
   int32_t dtype;        /* vs_dtype of Q, K, V, dO (and O unless o_f32)            */
   float scale;          /* score scale; <= 0 selects 1/sqrt(head_dim)             */
@@ -90,10 +110,17 @@ typedef struct vs_problem {
                                 every segment length a multiple of block (>0) */
   int32_t stripe_world; /* 1 = contiguous, W > 1 = block-striped                   */
   int32_t q_rank;       /* striped: rank whose row blocks this call holds          */
-  int32_t k_rank;       /* striped: rank whose key blocks this call holds          */
+  int32_t k_rank;       /* striped: rank whose key blocks this call holds, or
+                           VS_ALL_CHUNKS: K/V hold every rank's chunk              */
+  int64_t q_stride[3];  /* element strides (batch, token, head); all 0 = contiguous */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];  /* of O, in O's element type                              */
+  int64_t do_stride[3]; /* of dO                                                  */
 } vs_problem;
 
 #define VS_MAX_SEGMENTS 128
+#define VS_ALL_CHUNKS (-1)
 
 /* The Vertical-Slash index, one list pair per (batch b, Q head h, segment s),
  * list number l = (b*h_q + h)*n_seg + s.  All four arrays are DEVICE memory.
@@ -147,8 +174,8 @@ vs_status vs_workspace_size(const vs_problem* p, int32_t op, const vs_index* idx
  * ascending into v_idx / s_idx (padding -1 when a capacity exceeds the
  * candidates).  Scores are computed from bf16/fp32 inputs with fp32
  * accumulation.
- * q: [batch, n, h_q, d]; k: [batch, n, h_kv, d] (DEVICE, contiguous layout
- * only: stripe_world must be 1).  v_ptr, s_ptr: DEVICE offsets from
+ * q: [batch, n, h_q, d]; k: [batch, n, h_kv, d] (DEVICE, strides from the
+ * problem; the estimation sees the whole sequence: stripe_world must be 1).  v_ptr, s_ptr: DEVICE offsets from
  * vs_index_capacity.  v_score [batch, h_q, n] and s_score
  * [batch, h_q, n/block] (fp32, DEVICE, nullable) receive the scores; s_score
  * entry of segment s, offset g, is at [b, h, cu_seqlens[s]/block + g].

@@ -81,6 +81,22 @@ def test_capacity_matches_oracle(abi, cu, vb, sb):
     assert sm == max(sp[i + 1] - sp[i] for i in range(len(sp) - 1))
 
 
+def test_capacity_golden(abi):
+    """vs_index_capacity against the hand-derived per-document shares of
+    tests/golden/segment_capacities.json (not against the oracle's function)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "segment_capacities.json")) as f:
+        fx = json.load(f)
+    cu = fx["cu_seqlens"]
+    for case in fx["cases"]:
+        p = prob(abi, cu=cu, h_q=1, h_kv=1)
+        st, vp, sp, _, _ = capacity(abi, p, [case["v_budget"]], [case["s_budget"]])
+        assert st == abi.VS_OK
+        got = [[vp[s + 1] - vp[s], sp[s + 1] - sp[s]] for s in range(len(cu) - 1)]
+        assert got == case["expected"], (case, got)
+
+
 def status_of(abi, p, vb=None, sb=None):
     return capacity(abi, p, vb or [1] * p.h_q, sb or [1] * p.h_q)[0]
 
@@ -118,6 +134,44 @@ def test_problem_validation(abi):
     assert status_of(abi, prob(abi, cu=[0, 4096, 8192], n_q=1024, n_k=1024, stripe_world=8)) == \
         abi.VS_ERR_UNSUPPORTED
     assert status_of(abi, prob(abi, cu=[0, 8192], n_q=2048, n_k=1024, stripe_world=8)) == abi.VS_ERR_SHAPE
+
+
+def test_stride_validation(abi):
+    """Strides (batch, token, head) per tensor: all zero = contiguous; negative
+    ones are shape errors, ones that break 16-byte rows are unsupported; for
+    bf16 the K / V rows of one head must stay within 32-bit byte offsets."""
+    L = abi.lib()
+    n = 4096
+    fused = ((16 + 2 * 2) * 128 * n, (16 + 2 * 2) * 128, 128)  # slices of a fused QKV projection
+    ok = prob(abi, q_stride=fused, k_stride=fused, v_stride=fused, o_stride=(0, 0, 0),
+              do_stride=(n * 16 * 256, 16 * 256, 256))
+    assert status_of(abi, ok) == abi.VS_OK
+    assert status_of(abi, prob(abi, k_stride=(0, -256, 128))) == abi.VS_ERR_SHAPE
+    assert "negative" in L.vs_last_error().decode()
+    assert status_of(abi, prob(abi, q_stride=(0, 2052, 128))) == abi.VS_ERR_UNSUPPORTED
+    assert "multiple of 8" in L.vs_last_error().decode()
+    assert status_of(abi, prob(abi, o_stride=(0, 2048, 132))) == abi.VS_ERR_UNSUPPORTED
+    assert status_of(abi, prob(abi, do_stride=(4, 0, 0))) == abi.VS_ERR_UNSUPPORTED
+    # K rows 2^20 tokens apart at a stride of 4096 elements: (2^20 - 1) * 8 KiB
+    # exceeds 4 GiB of byte offsets in bf16, not in fp32 (other kernels)
+    cu = [0, 1 << 20]
+    wide = (0, 4096, 128)
+    assert status_of(abi, prob(abi, cu=cu, k_stride=wide)) == abi.VS_ERR_UNSUPPORTED
+    assert "4 GiB" in L.vs_last_error().decode()
+    assert status_of(abi, prob(abi, cu=cu, v_stride=wide)) == abi.VS_ERR_UNSUPPORTED
+    assert status_of(abi, prob(abi, cu=cu, k_stride=wide, dtype=abi.VS_F32)) == abi.VS_OK
+    assert status_of(abi, prob(abi, cu=cu, q_stride=wide)) == abi.VS_OK  # Q rows use 64-bit offsets
+
+
+def test_all_chunks_validation(abi):
+    """k_rank = VS_ALL_CHUNKS: K / V hold every rank's chunk, so n_k = n_global."""
+    W = 8
+    kw = dict(cu=[0, 8192], n_q=1024, stripe_world=W, q_rank=3, k_rank=abi.VS_ALL_CHUNKS)
+    assert status_of(abi, prob(abi, n_k=8192, **kw)) == abi.VS_OK
+    assert status_of(abi, prob(abi, n_k=1024, **kw)) == abi.VS_ERR_SHAPE
+    assert status_of(abi, prob(abi, n_k=8192, **dict(kw, k_rank=-2))) == abi.VS_ERR_SHAPE
+    # without striping the field is ignored (one contiguous sequence)
+    assert status_of(abi, prob(abi, k_rank=abi.VS_ALL_CHUNKS)) == abi.VS_OK
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first

@@ -68,6 +68,147 @@ def _rows_of_blocks(starts_blocks):
     return np.concatenate([np.arange(64 * b, 64 * b + 64) for b in starts_blocks]).astype(np.int64)
 
 
+def _mid_key_blocks(oidx, cu, heads, rng, per_seg=2):
+    """Per segment, per_seg key blocks from the middle half of the segment in
+    which no Q head of `heads` selected a vertical column: their keys are read
+    only through selected block-diagonals, by the query blocks j + g, so the
+    oracle gets their complete dK / dV from those rows alone."""
+    out = []
+    for s in range(len(cu) - 1):
+        a, e = cu[s] // 64, cu[s + 1] // 64
+        nb = e - a
+        vert = set()
+        for h in heads:
+            vert.update((np.asarray(oidx[(h, s)][0]) // 64).tolist())
+        cand = [b for b in range(a + nb // 4, a + (3 * nb) // 4) if b not in vert]
+        if len(cand) < per_seg:
+            cand = [b for b in range(a, e) if b not in vert]
+        assert len(cand) >= per_seg, ("no key block free of verticals in segment", s)
+        out.append(sorted(int(x) for x in rng.choice(cand, size=per_seg, replace=False)))
+    return out
+
+
+def _query_blocks_reading(oidx, cu, heads, seg, key_blocks):
+    """Global query blocks j + g (g a selected block-diagonal of any head in
+    `heads`) that read the given global key blocks of segment seg."""
+    a, e = cu[seg] // 64, cu[seg + 1] // 64
+    qb = set()
+    for h in heads:
+        for g in np.asarray(oidx[(h, seg)][1]).tolist():
+            for j in key_blocks:
+                if j + g < e:
+                    qb.add(j + g)
+    return sorted(qb)
+
+
+def _group_index(oidx, heads, n_seg):
+    """The index of the Q heads `heads` (one KV group), renumbered 0..len-1."""
+    return {(i, s): oidx[(h, s)] for i, h in enumerate(heads) for s in range(n_seg)}
+
+
+def _check_mid_key_blocks(name, prob, oidx, rows_of, dk, dv, key_pos, grp, rng, per_seg=2):
+    """Element-wise dK / dV of mid-sequence key blocks of KV group grp against
+    the oracle, computed from every row that reads them.
+
+    The key blocks hold no vertical column of the group's heads (see
+    _mid_key_blocks), so rows_of(query blocks j + g) are all their readers;
+    rows_of maps global query blocks to the global rows this call holds (all
+    rows, or a striped worker's).  dk / dv [keys, d] are the GPU's gradients of
+    the global key positions key_pos (ascending) of group grp."""
+    cu = prob.cu_seqlens
+    n_seg = len(cu) - 1
+    G = prob.h_q // prob.h_kv
+    heads = list(range(grp * G, (grp + 1) * G))
+    kblocks = _mid_key_blocks(oidx, cu, heads, rng, per_seg)
+    qblocks = sorted(set().union(*[_query_blocks_reading(oidx, cu, heads, s, kb)
+                                   for s, kb in enumerate(kblocks)]))
+    rows = rows_of(qblocks)
+    keys = np.concatenate([np.arange(64 * b, 64 * b + 64) for kb in kblocks for b in kb])
+    log(f"  {name}: dK / dV of key blocks {kblocks} (group {grp}), from {len(rows)} rows")
+    gidx = _group_index(oidx, heads, n_seg)
+    k64 = np64(prob.k[0, :, grp:grp + 1])
+    v64 = np64(prob.v[0, :, grp:grp + 1])
+    cols = np.arange(prob.n)
+    q_r, do_r = np64(prob.q[0, rows][:, heads]), np64(prob.do[0, rows][:, heads])
+    O, L = oracle.attn_fwd_support(q_r, k64, v64, rows, cols, cu, gidx)
+    D = oracle.bwd_delta(O, do_r)
+    _, dk_o, dv_o = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, cols, cu, gidx)
+    _, bk, bv = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, gidx, support=True)
+    sel = np.searchsorted(key_pos, keys)
+    assert np.array_equal(key_pos[sel], keys)
+    return [check_close(f"{name} dK (mid keys, group {grp})", dk_o[keys, 0], dk[sel], "bf16", "grad", bk[keys, 0]),
+            check_close(f"{name} dV (mid keys, group {grp})", dv_o[keys, 0], dv[sel], "bf16", "grad", bv[keys, 0])]
+
+
+def _kernel_split_checks(prob, oidx, gq, gk, gv, gdo, dev, rng, verticals=True):
+    """The two dK / dV kernels at full size, each on an index of its own part.
+
+    Slash-only index (the estimated block-diagonals, no verticals): every key
+    is read only through block-diagonals, so mid-sequence key blocks of each
+    segment are compared element by element from the rows j + g that read
+    them; with 8 heads x k_g diagonals a key block's tile list is emptied and
+    refilled several times.  Two such blocks with one document, one per
+    document with several.  Verticals-only index (every 8th estimated column,
+    no block-diagonals; when `verticals`): dK / dV of every key of KV group 0,
+    from the oracle over all rows of the group's heads."""
+    cu = prob.cu_seqlens
+    n_seg = len(cu) - 1
+    errs = []
+    empty = np.zeros(0, np.int64)
+    sl = {key: (empty, val[1]) for key, val in oidx.items()}
+    idx = vs.index_from_lists(lists_for_gpu(sl, prob.h_q, n_seg), dev)
+    log("  GPU forward + backward on the slash-only index")
+    o, lse = vs.sparse_attn_fwd(gq, gk, gv, idx, cu)
+    _, dk, dv = vs.sparse_attn_bwd(gq, gk, gv, o, gdo, lse, idx, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    errs += _check_mid_key_blocks("slash-only", prob, sl, _rows_of_blocks, np64(dk[0, :, 0]),
+                                  np64(dv[0, :, 0]), np.arange(prob.n), 0, rng, 2 if n_seg == 1 else 1)
+    del o, lse, dk, dv
+    if not verticals:
+        return errs
+    vt = {key: (val[0][::8], empty) for key, val in oidx.items()}
+    idx = vs.index_from_lists(lists_for_gpu(vt, prob.h_q, n_seg), dev)
+    log("  GPU forward + backward on the verticals-only index")
+    o, lse = vs.sparse_attn_fwd(gq, gk, gv, idx, cu)
+    _, dk, dv = vs.sparse_attn_bwd(gq, gk, gv, o, gdo, lse, idx, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    G = prob.h_q // prob.h_kv
+    heads = list(range(G))
+    log(f"  oracle on all {prob.n} rows of group 0 (verticals-only index)")
+    rows = np.arange(prob.n)
+    q_r, do_r = np64(prob.q[0][:, heads]), np64(prob.do[0][:, heads])
+    k64, v64 = np64(prob.k[0, :, 0:1]), np64(prob.v[0, :, 0:1])
+    gidx = _group_index(vt, heads, n_seg)
+    O, L = oracle.attn_fwd_support(q_r, k64, v64, rows, rows, cu, gidx)
+    D = oracle.bwd_delta(O, do_r)
+    _, dk_o, dv_o = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, rows, cu, gidx)
+    _, bk, bv = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, rows, cu, gidx, support=True)
+    errs += [check_close("verticals-only dK (all keys, group 0)", dk_o[:, 0], np64(dk[0, :, 0]), "bf16", "grad", bk[:, 0]),
+             check_close("verticals-only dV (all keys, group 0)", dv_o[:, 0], np64(dv[0, :, 0]), "bf16", "grad", bv[:, 0])]
+    return errs
+
+
+def _dv_identity(name, dv, v, o, do, h_q, h_kv):
+    """sum_{h in group} sum_n delta_h[n] == <dV_g, V_g> per KV group, with
+    delta = rowsum(dO * O) from the GPU's own O (fp64 sums of GPU tensors).
+
+    dV = A^T dO gives <dV, V> = sum_n <dO_n, sum_m A[n, m] V_m> = sum_n <dO_n, O_n>
+    (MTraining §3.2 Eq. 1: rowsum(dA * A) = rowsum(dO * O)); both sides use
+    bf16-rounded probabilities, so they agree to a small fraction of
+    sum |dO| |O|."""
+    errs = []
+    for g in range(h_kv):
+        hs = [h for h in range(h_q) if h * h_kv // h_q == g]
+        rhs = sum(float((do[:, h].double() * o[:, h].double()).sum()) for h in hs)
+        mag = sum(float((do[:, h].double() * o[:, h].double()).abs().sum()) for h in hs)
+        lhs = float((dv[:, g].double() * v[:, g].double()).sum())
+        rel = abs(lhs - rhs) / max(mag, 1e-30)
+        log(f"  {name} group {g}: <dV,V>={lhs:.6e} sum delta={rhs:.6e} |diff|/sum|dO*O|={rel:.2e}")
+        if rel > 1e-4:
+            errs.append(f"{name} group {g}: dV identity off by {rel:.2e}")
+    return errs
+
+
 def _group_identity(name, dq, q, dk, k, h_q, h_kv):
     """sum_{h in group} <dQ_h, Q_h> == <dK_g, K_g> per KV group (fp64 sums of the GPU tensors).
 
@@ -127,7 +268,7 @@ def test_fullsize_contiguous(wid):
     dq_o, _, _ = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, cols, cu, oidx)
     bq, _, _ = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, oidx, support=True)
     rt = torch.from_numpy(rows).to(dev)
-    errs += [check_close("O (sampled)", O, np64(o[0, rt]), prob.dtype),
+    errs += [check_close("O (sampled)", O, np64(o[0, rt]), prob.dtype, "o"),
              check_close("LSE (sampled)", L, np64(lse[0][:, rt]), prob.dtype),
              check_close("dQ (sampled)", dq_o, np64(dq[0, rt]), prob.dtype, "grad", bq)]
 
@@ -149,6 +290,9 @@ def test_fullsize_contiguous(wid):
              check_close("dV (tail keys)", dv_o[rows], np64(dv[0, rt]), prob.dtype, "grad", bv[rows])]
 
     errs += _group_identity(prob.name, dq[0], gq[0], dk[0], gk[0], prob.h_q, prob.h_kv)
+    errs += _dv_identity(prob.name, dv[0], gv[0], o[0], gdo[0], prob.h_q, prob.h_kv)
+    del o, lse, dq, dk, dv
+    errs += _kernel_split_checks(prob, oidx, gq, gk, gv, gdo, dev, rng, verticals=(wid == 3))
     errs = [e for e in errs if e]
     assert not errs, errs
 
@@ -205,7 +349,14 @@ def test_fullsize_striped_worker():
     tail_local = [nqb - 2, nqb - 1]
     first_key_blk = rows_all[64 * (nqb - 3)] // 64 + 1
     dk_tail, dv_tail, key_tail = [], [], []
+    # mid-sequence key blocks checked below: no vertical of group 0 in them
+    G = prob.h_q // prob.h_kv
+    rng_mid = np.random.default_rng(prob.seed + 1)
+    mid_blocks = _mid_key_blocks(oidx, cu, list(range(G)), rng_mid)[0]
+    mid_keys = np.concatenate([np.arange(64 * b, 64 * b + 64) for b in mid_blocks])
+    dk_mid, dv_mid, key_mid = [], [], []
     lhs_k = np.zeros(prob.h_kv)
+    lhs_v = np.zeros(prob.h_kv)
     for u, gk, gv in chunks:
         _, dk, dv = vs.sparse_attn_bwd(gq, gk, gv, None, gdo, acc_l, idx, delta=delta, dq=dq,
                                        stripe=(W, w, u), accumulate=True)
@@ -215,8 +366,15 @@ def test_fullsize_striped_worker():
         dk_tail.append(np64(dk[0, st]))
         dv_tail.append(np64(dv[0, st]))
         key_tail.append(kpos[sel])
+        msel = np.nonzero(np.isin(kpos, mid_keys))[0]
+        if msel.size:
+            mt = torch.from_numpy(msel).to(dev)
+            dk_mid.append(np64(dk[0, mt, 0]))
+            dv_mid.append(np64(dv[0, mt, 0]))
+            key_mid.append(kpos[msel])
         for g in range(prob.h_kv):
             lhs_k[g] += float((dk[0, :, g].double() * gk[0, :, g].double()).sum())
+            lhs_v[g] += float((dv[0, :, g].double() * gv[0, :, g].double()).sum())
     torch.cuda.synchronize()
     dk_tail, dv_tail, key_tail = np.concatenate(dk_tail), np.concatenate(dv_tail), np.concatenate(key_tail)
 
@@ -233,7 +391,7 @@ def test_fullsize_striped_worker():
     bq, _, _ = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, oidx,
                                           u_o=2.0 ** -24, support=True)
     lt = torch.from_numpy(lrows).to(dev)
-    errs += [check_close("merged O (sampled)", O, np64(acc_o[0, lt]), "bf16"),
+    errs += [check_close("merged O (sampled)", O, np64(acc_o[0, lt]), "bf16", "o"),
              check_close("merged LSE (sampled)", L, np64(acc_l[0][:, lt]), "bf16"),
              check_close("accumulated dQ (sampled)", dq_o, np64(dq[0, lt]), "bf16", "grad", bq)]
 
@@ -249,6 +407,18 @@ def test_fullsize_striped_worker():
     errs += [check_close("dK share (tail keys)", dk_o[key_tail], dk_tail, "bf16", "grad", bk[key_tail]),
              check_close("dV share (tail keys)", dv_o[key_tail], dv_tail, "bf16", "grad", bv[key_tail])]
 
+    # mid-sequence key blocks: every worker row that reads them (the worker's
+    # rows among the query blocks j + g)
+    dk_mid, dv_mid, key_mid = np.concatenate(dk_mid), np.concatenate(dv_mid), np.concatenate(key_mid)
+    order = np.argsort(key_mid)
+    worker_blocks = set((rows_all[::64] // 64).tolist())
+
+    def worker_rows(qblocks):
+        mine = [b for b in qblocks if b in worker_blocks]
+        return _rows_of_blocks(mine) if mine else np.zeros(0, np.int64)
+
+    errs += _check_mid_key_blocks("ring worker", prob, oidx, worker_rows, dk_mid[order], dv_mid[order],
+                                  key_mid[order], 0, np.random.default_rng(prob.seed + 1))
     for g in range(prob.h_kv):
         hs = [h for h in range(prob.h_q) if h * prob.h_kv // prob.h_q == g]
         lhs = sum(float((dq[0, :, h].double() * gq[0, :, h].double()).sum()) for h in hs)
@@ -257,5 +427,11 @@ def test_fullsize_striped_worker():
         log(f"  ring group {g}: <dQ,Q>={lhs:.6e} sum_u <dK_u,K_u>={lhs_k[g]:.6e} rel={rel:.2e}")
         if rel > 1e-4:
             errs.append(f"ring group {g}: identity off by {rel:.2e}")
+        rhs = sum(float((gdo[0, :, h].double() * acc_o[0, :, h].double()).sum()) for h in hs)
+        magv = sum(float((gdo[0, :, h].double() * acc_o[0, :, h].double()).abs().sum()) for h in hs)
+        relv = abs(lhs_v[g] - rhs) / max(magv, 1e-30)
+        log(f"  ring group {g}: sum_u <dV_u,V_u>={lhs_v[g]:.6e} sum delta={rhs:.6e} rel={relv:.2e}")
+        if relv > 1e-4:
+            errs.append(f"ring group {g}: dV identity off by {relv:.2e}")
     errs = [e for e in errs if e]
     assert not errs, errs

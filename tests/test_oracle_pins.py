@@ -428,6 +428,22 @@ def test_estimator_window_matches_plain_softmax():
 
 
 # ---------------------------------------------------------------- P9 layout identities
+def test_p8_golden_segment_capacities():
+    """Per-document budget shares of packed documents (reading of the pages'
+    budgets for several documents; values worked out by hand in the fixture):
+    a document of L out of N tokens gets ceil(k*L/N) columns and
+    ceil(ceil(k*L/N)/64) block-diagonals, clipped to its candidates.  A floor in
+    place of a ceiling, L/N inverted or the clip dropped fails a case."""
+    with open(os.path.join(GOLDEN, "segment_capacities.json")) as f:
+        fx = json.load(f)
+    cu, n, B = fx["cu_seqlens"], fx["n_total"], fx["block"]
+    assert cu[-1] == n
+    for case in fx["cases"]:
+        got = [list(oracle.capacities(case["v_budget"], case["s_budget"], cu[s + 1] - cu[s], n, B))
+               for s in range(len(cu) - 1)]
+        assert got == case["expected"], (case, got)
+
+
 def test_p9_striped_chunks_merge_to_global_rows():
     rng = np.random.default_rng(15)
     W, B, nbw = 4, 16, 3

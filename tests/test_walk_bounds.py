@@ -1,0 +1,277 @@
+"""Host-side bounds check of the attention kernels' address arithmetic (no GPU).
+
+The bf16 kernels expand the Vertical-Slash index on the device into tiles of
+key rows (query-major forward / dQ) or query rows (key-major dK / dV) and load
+them with direct global -> LDS loads.  This test repeats that arithmetic on
+the host, with the same integer formulas as the device code (local / global
+block relabelling of a striped call, the prepared vertical lists, the
+covered-column test, the tile-list capacities, the direct-load byte offsets
+and LDS destinations), over every work item of a launch, and asserts that
+every address stays inside its tensor or LDS array.  It runs on the shapes of
+a 32-rank striped worker at N = 524288 (each rank's chunk, and all chunks in
+one call) and of packed documents, with seeded random indices that include
+the extreme entries (block-diagonals 0 and nb - 1, the first and last key of
+a segment).
+"""
+import numpy as np
+import pytest
+
+BLOCK = 64
+
+
+class Call:
+    """The relabelling of one call (mirrors the device helpers)."""
+
+    def __init__(self, n_global, cu, W=1, q_rank=0, k_rank=0, k_all=False):
+        self.n_global, self.cu, self.W = n_global, list(cu), W
+        self.q_rank, self.k_rank, self.k_all = q_rank, k_rank, k_all
+        self.n_q = n_global if W == 1 else n_global // W
+        self.n_k = n_global if (W == 1 or k_all) else n_global // W
+        self.nqb, self.nkb = self.n_q // BLOCK, self.n_k // BLOCK
+
+    def local_key_block(self, kb):
+        kb = np.asarray(kb, np.int64)
+        if self.W == 1:
+            return np.where((kb >= 0) & (kb < self.nkb), kb, -1)
+        if self.k_all:
+            nc = self.nkb // self.W
+            j = kb // self.W
+            return np.where((kb >= 0) & (j < nc), (kb % self.W) * nc + j, -1)
+        d = kb - self.k_rank
+        j = d // self.W
+        return np.where((kb >= 0) & (d >= 0) & (d % self.W == 0) & (j < self.nkb), j, -1)
+
+    def global_key_block(self, j):
+        j = np.asarray(j, np.int64)
+        if self.W == 1:
+            return j
+        if self.k_all:
+            nc = self.nkb // self.W
+            return j // nc + self.W * (j % nc)
+        return self.k_rank + self.W * j
+
+    def local_query_block(self, qb):
+        qb = np.asarray(qb, np.int64)
+        if self.W == 1:
+            return np.where((qb >= 0) & (qb < self.nqb), qb, -1)
+        d = qb - self.q_rank
+        i = d // self.W
+        return np.where((d >= 0) & (d % self.W == 0) & (i < self.nqb), i, -1)
+
+    def local_key_pos(self, m):
+        m = np.asarray(m, np.int64)
+        if self.W == 1:
+            return m
+        return self.local_key_block(m // BLOCK) * BLOCK + m % BLOCK
+
+    def row_block(self, i):
+        """(global query block, segment, segment start block, beta, blocks in segment)."""
+        if self.W == 1:
+            starts = np.asarray(self.cu) // BLOCK
+            s = int(np.searchsorted(starts, i, side="right") - 1)
+            return i, s, starts[s], i - starts[s], starts[s + 1] - starts[s]
+        qb = self.q_rank + self.W * i
+        return qb, 0, 0, qb, self.n_global // BLOCK
+
+
+def random_index(rng, cu, k_v, k_g):
+    """Sorted lists per segment with the extreme entries included."""
+    out = []
+    for a, e in zip(cu[:-1], cu[1:]):
+        L, nb = e - a, (e - a) // BLOCK
+        v = set(rng.choice(L, size=min(k_v, L), replace=False).tolist()) | {0, L - 1}
+        g = set(rng.choice(nb, size=min(k_g, nb), replace=False).tolist()) | {0, nb - 1}
+        out.append((np.array(sorted(v), np.int64) + a, np.array(sorted(g), np.int64)))
+    return out
+
+
+def prep_vertical(call, v_idx, seg):
+    """vs_prep_vertical_kernel: the list's columns this call holds, ascending."""
+    a, e = (call.cu[seg], call.cu[seg + 1]) if call.W == 1 else (0, call.n_global)
+    m = np.asarray(v_idx)
+    keep = (m >= a) & (m < e) & (call.local_key_block(m // BLOCK) >= 0)
+    return m[keep]
+
+
+def rows_tile_geometry(D):
+    """RowsTiles<D> constants: (rows per direct load, loads per 32-row tile,
+    padded group bytes, tile bytes)."""
+    cpr = D // 8
+    rpi = 64 // cpr
+    nvl = 32 // rpi
+    group = 1024 + 16
+    return rpi, nvl, group, nvl * group
+
+
+def check_dma_part(D, NP, row_bytes, n_rows, key_rows):
+    """dma_part: every lane's byte offset row * rb + chunk byte stays inside the
+    K / V rows of one (batch, head) and is representable in 32 bits, and the
+    LDS destinations of all loads of a half-tile stay inside its tile."""
+    rpi, nvl, group, tb = rows_tile_geometry(D)
+    cpr = D // 8
+    lanes = np.arange(64)
+    rr, cb = lanes // cpr, ((lanes % cpr) ^ np.array([4 * (b & 3) if D == 128 else
+                                                       4 * ((b >> 1) & 1) + 2 * ((b >> 2) & 1)
+                                                       for b in lanes // cpr])) * 16
+    assert cb.max() + 16 <= D * 2
+    rows = np.asarray(key_rows, np.int64)
+    assert rows.min() >= 0 and rows.max() < n_rows
+    off = rows.max() * row_bytes + cb.max() + 16
+    assert off < 2 ** 32 and off <= (n_rows - 1) * row_bytes + D * 2
+    nu = nvl // NP
+    for part in range(NP):
+        for u0 in range(nu):
+            dst = (part * nu + u0) * group
+            assert dst + 64 * 16 <= tb
+    assert rr.max() < rpi
+
+
+def query_major_walk(call, lists, h_q, n_seg, D, row_bytes):
+    """Tiles of the forward / dQ walk (qmajor_drive with one key stream of
+    two waves: 128 threads, column batches of 256), for every (Q head, local
+    query block): slash key blocks and gathered vertical columns."""
+    nt, ncols = 128, 256
+    R = ncols // nt - 1
+    key_rows = []
+    words_max = (max((e - a) // BLOCK for a, e in zip(call.cu[:-1], call.cu[1:]))
+                 if call.W == 1 else call.n_global // BLOCK) + 31 >> 5
+    for h in range(h_q):
+        for i in range(call.nqb):
+            qb, seg, a_blk, beta, nb_seg = call.row_block(i)
+            iv, is_ = lists[h * n_seg + seg]
+            assert (nb_seg + 31) >> 5 <= words_max
+            g = is_[(is_ >= 0) & (is_ <= beta)]
+            assert g.size == 0 or g.max() < nb_seg
+            j = call.local_key_block(a_blk + beta - g)
+            j = j[j >= 0]
+            assert j.size == 0 or (j.min() >= 0 and j.max() < call.nkb)
+            key_rows.append(j * BLOCK)
+            key_rows.append(j * BLOCK + BLOCK - 1)
+            vsel = prep_vertical(call, iv, seg)
+            lim = (qb + 1) * BLOCK
+            m = vsel[vsel < lim]
+            bm = m // BLOCK - a_blk
+            off = beta - bm
+            assert off.size == 0 or (off.min() >= 0 and off.max() < nb_seg)
+            covered = np.isin(off, is_)
+            cols = call.local_key_pos(m[~covered])
+            assert cols.size == 0 or (cols.min() >= 0 and cols.max() < call.n_k)
+            key_rows.append(cols)
+            # the column buffer never holds more than one batch plus a partial tile
+            assert R * nt + 63 <= ncols
+    key_rows = np.concatenate([np.atleast_1d(x) for x in key_rows if np.size(x)])
+    check_dma_part(D, 2, row_bytes, call.n_k, key_rows)
+
+
+def key_major_slash(call, lists, h_q, h_kv, n_seg):
+    """Tiles of the slash dK/dV kernel for every (KV head, local key block):
+    query blocks kb + g of the group's heads, the tile encoding and the list
+    capacity (512 entries, appended 128 at a time, emptied above 384)."""
+    G = h_q // h_kv
+    starts = np.asarray(call.cu) // BLOCK
+    j = np.arange(call.nkb)
+    kb = call.global_key_block(j)
+    assert np.array_equal(call.local_key_block(kb), j)
+    if call.W == 1:
+        seg = np.searchsorted(starts, j, side="right") - 1
+        a_blk, nb_seg = starts[seg], starts[seg + 1] - starts[seg]
+    else:
+        seg = np.zeros_like(j)
+        a_blk, nb_seg = np.zeros_like(j), np.full_like(j, call.n_global // BLOCK)
+    beta_k = kb - a_blk
+    assert beta_k.min() >= 0 and np.all(beta_k < nb_seg)
+    i0 = call.local_query_block(kb)  # the diagonal tile (g = 0)
+    assert np.all((i0 == -1) | ((i0 >= 0) & (i0 < call.nqb)))
+    for kvh in range(h_kv):
+        count = np.zeros(call.nkb, np.int64)
+        for hh in range(G):
+            assert hh < 32  # the head index sits in the tile word's top bits
+            for s in range(n_seg):
+                mine = seg == s
+                _, is_ = lists[(kvh * G + hh) * n_seg + s]
+                for base in range(0, is_.size, 128):
+                    g = is_[base:base + 128]
+                    ok = (g[None, :] > 0) & (beta_k[mine, None] + g[None, :] < nb_seg[mine, None])
+                    i = call.local_query_block(kb[mine, None] + g[None, :])
+                    i = np.where(ok, i, -1)
+                    assert i.max(initial=-1) < min(call.nqb, 2 ** 25)
+                    count[mine] += (i >= 0).sum(axis=1)
+                    assert count.max(initial=0) <= 512
+                    count[count > 512 - 128] = 0
+
+
+def column_units(call, lists, h_q, n_seg, v_cap):
+    """Column dK/dV units: columns of the prepared list, their local key
+    positions and the query-block range."""
+    col_tiles = (v_cap + 63) // 64
+    qrange_len = 48
+    qranges = (call.nqb + qrange_len - 1) // qrange_len
+    while qranges > 1 and qranges % 2 == 0:
+        qrange_len += 1
+        qranges = (call.nqb + qrange_len - 1) // qrange_len
+    for h in range(h_q):
+        for seg in range(n_seg):
+            vsel = prep_vertical(call, lists[h * n_seg + seg][0], seg)
+            assert vsel.size <= max(v_cap, 1)
+            for ct in range(col_tiles):
+                if 64 * ct >= vsel.size:
+                    continue
+                cols = vsel[64 * ct: 64 * ct + 64]
+                kpos = call.local_key_pos(cols)
+                assert kpos.min() >= 0 and kpos.max() < call.n_k
+                first_blk = int(cols[0] // BLOCK)
+                if call.W == 1:
+                    i_first = first_blk
+                    i_lo, i_hi = call.cu[seg] // BLOCK, call.cu[seg + 1] // BLOCK
+                else:
+                    i_first = 0 if first_blk <= call.q_rank else (first_blk - call.q_rank + call.W - 1) // call.W
+                    i_lo, i_hi = 0, call.nqb
+                for qr in range(qranges):
+                    r_lo = max(i_lo, qr * qrange_len, i_first)
+                    r_hi = min(i_hi, (qr + 1) * qrange_len)
+                    if r_lo < r_hi:
+                        assert 0 <= r_lo and r_hi <= call.nqb
+
+
+@pytest.mark.parametrize("mode", ["rank-chunks", "all-chunks"])
+def test_striped_worker_shape_in_bounds(mode):
+    """32 ranks, 64-token stripes, N = 524288, 16 Q / 2 KV heads, d = 128;
+    worker 0 and a middle worker, against several chunks or all of them."""
+    rng = np.random.default_rng(40)
+    n, W, h_q, h_kv = 524288, 32, 16, 2
+    cu = [0, n]
+    lists = [random_index(rng, cu, 4096, 320)[0] for _ in range(h_q)]
+    v_cap = max(l[0].size for l in lists)
+    for w in (0, 17):
+        calls = ([Call(n, cu, W, w, u) for u in (w, (w - 1) % W, (w + 16) % W)] if mode == "rank-chunks"
+                 else [Call(n, cu, W, w, 0, k_all=True)])
+        for call in calls:
+            query_major_walk(call, lists, h_q, 1, 128, h_kv * 128 * 2)
+            key_major_slash(call, lists, h_q, h_kv, 1)
+            column_units(call, lists, h_q, 1, v_cap)
+
+
+def test_all_chunks_relabelling_is_a_bijection():
+    """Local key block u * (nkb / W) + j <-> global block u + W * j."""
+    call = Call(8192 * 64, [0, 8192 * 64], 32, 5, 0, k_all=True)
+    j = np.arange(call.nkb)
+    g = call.global_key_block(j)
+    assert np.array_equal(np.sort(g), np.arange(call.nkb))
+    assert np.array_equal(call.local_key_block(g), j)
+    # chunk u holds the blocks of rank u, in order
+    nc = call.nkb // call.W
+    assert np.array_equal(g[3 * nc: 4 * nc] % call.W, np.full(nc, 3))
+
+
+def test_packed_documents_in_bounds():
+    rng = np.random.default_rng(41)
+    n, h_q, h_kv = 262144, 16, 2
+    cuts = np.sort(rng.choice(np.arange(1, n // BLOCK), size=7, replace=False)) * BLOCK
+    cu = [0] + cuts.tolist() + [n]
+    per = [random_index(rng, cu, 512 + 400 * h, 40 + 20 * h) for h in range(h_q)]
+    lists = [per[h][s] for h in range(h_q) for s in range(len(cu) - 1)]
+    v_cap = max(l[0].size for l in lists)
+    call = Call(n, cu)
+    query_major_walk(call, lists, h_q, len(cu) - 1, 128, h_kv * 128 * 2)
+    key_major_slash(call, lists, h_q, h_kv, len(cu) - 1)
+    column_units(call, lists, h_q, len(cu) - 1, v_cap)

@@ -45,13 +45,25 @@ def bf16_tol(ref: np.ndarray, got: np.ndarray):
     return float(err.max(initial=0.0)), float(rel)
 
 
+def _bf16_half_ulp(x):
+    """Half the spacing of bfloat16 numbers at |x| (the largest output rounding error)."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 8), 0.0)
+
+
 def check_close(name, ref, got, dtype, kind="out", bound=None):
     """Compare got with ref; returns an error string or None.
 
-    fp32: max-abs <= 1e-4.  bf16 outputs (O, LSE): max-abs <= 2e-2.
-    bf16 gradients: relative L2 <= 1e-2 and, element by element,
-    |err| <= 2 * bound, the first-order bf16 rounding bound of the backward
-    (oracle.bwd_rounding_bounds); the literal max-abs is printed.
+    fp32: max-abs <= 1e-4.  bf16 outputs (O, LSE): max-abs <= 2e-2; for O
+    (kind "o") the log splits the error into the output's own bf16 rounding
+    and the rest.  bf16 gradients: relative L2 <= 1e-2 and, element by
+    element, within twice the first-order bf16 rounding bound of the backward
+    (oracle.bwd_rounding_bounds).  The log also gives rms(ref) and the ratio of
+    the max-abs error to 2e-2 * max(1, rms(ref)): a backward that rounds P and
+    dS to bf16 before its products has errors of the size |dS| |K| u, far
+    above that bar where a row's probability sits on large-norm keys (the
+    bound's maximum is printed beside it).
     """
     ref = np.asarray(ref, np.float64)
     got = np.asarray(got, np.float64)
@@ -65,15 +77,24 @@ def check_close(name, ref, got, dtype, kind="out", bound=None):
         return f"{name}: infinities differ"
     r, g = ref[fin_r], got[fin_g]
     mx, rel = bf16_tol(r, g)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     extra = ""
     if bound is not None:
         b = np.asarray(bound, np.float64)[fin_r]
         ratio = float((np.abs(g - r) / (b + 1e-30)).max(initial=0.0))
-        extra = f" err/bound {ratio:.3f}"
+        extra = f" err/bound {ratio:.3f} (bound max {float(b.max(initial=0.0)):.3e})"
+    if dtype == "bf16" and kind == "grad":
+        q19 = mx / (2e-2 * max(1.0, rms))
+        extra += f" rms(ref) {rms:.3e} max-abs/(2e-2*max(1,rms)) {q19:.2f}"
+    if dtype == "bf16" and kind == "o" and r.size:
+        # the output is stored in bf16: its own rounding is up to half a bf16 spacing
+        rb = torch.tensor(r).to(torch.bfloat16).to(torch.float64).numpy()
+        extra += (f" (vs bf16-rounded ref {float(np.abs(g - rb).max()):.3e},"
+                  f" half-ulp at the worst element {float(_bf16_half_ulp(r)[np.argmax(np.abs(g - r))]):.3e})")
     log(f"  {name}: max-abs {mx:.3e} rel-L2 {rel:.3e}{extra} (n={r.size})")
     if dtype == "f32":
         return None if mx <= 1e-4 else f"{name}: max-abs {mx}"
-    if kind == "out":
+    if kind in ("out", "o"):
         return None if mx <= 2e-2 else f"{name}: max-abs {mx}"
     if rel > 1e-2:
         return f"{name}: rel-L2 {rel}"
@@ -89,7 +110,7 @@ def assert_close(name, ref, got, dtype, kind="out", bound=None):
     assert err is None, err
 
 
-def index_parity(name, o_index, o_scores, g_lists, g_vscore, g_sscore, prob, rel_tie=1e-4):
+def index_parity(name, o_index, o_scores, g_lists, g_vscore, g_sscore, prob, rel_tie=1e-5):
     """Estimator parity.
 
     1. scores: GPU fp32 vertical / slash scores against the oracle's fp64 ones;
