@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
   * ``estimate_index_topp`` — the same with top-p budgets (Algorithm 1 topp);
   * ``sparse_attn_fwd``  — sparse attention forward with LSE;
   * ``sparse_attn_bwd``  — dQ, dK, dV over the same support;
+  * ``sparse_attn_bwd_noalloc`` — the same with the library's fixed per-GPU
+    workspace (for callers that cannot allocate);
   * ``lse_merge``        — merge_out_and_lse of Algorithm 2;
   * ``attn_bwd_delta``   — the row term rowsum(dO * O) of Eq. 1.
 """
@@ -27,7 +29,7 @@ from ._abi import VsError
 
 BLOCK = 64
 __all__ = ["VsIndexT", "index_capacity", "estimate_index", "estimate_index_topp", "sparse_attn_fwd",
-           "sparse_attn_bwd",
+           "sparse_attn_bwd", "sparse_attn_bwd_noalloc",
            "attn_bwd_delta", "lse_merge", "VsError", "BLOCK"]
 
 
@@ -280,9 +282,19 @@ def attn_bwd_delta(o: torch.Tensor, do: torch.Tensor, out: Optional[torch.Tensor
     return delta
 
 
+def sparse_attn_bwd_noalloc(q, k, v, o, do, lse, index: VsIndexT, delta=None, dq=None,
+                            cu_seqlens=None, stripe=None, scale=None, dk=None, dv=None,
+                            accumulate: bool = False):
+    """sparse_attn_bwd through vs_sparse_attn_bwd_noalloc: the library's own
+    per-GPU scratch array serves as the workspace (nothing is allocated for
+    it; calls that overlap on one GPU race on it)."""
+    return sparse_attn_bwd(q, k, v, o, do, lse, index, delta, dq, cu_seqlens, stripe, scale, dk, dv,
+                           accumulate, _noalloc=True)
+
+
 def sparse_attn_bwd(q, k, v, o, do, lse, index: VsIndexT, delta=None, dq=None,
                     cu_seqlens=None, stripe=None, scale=None, dk=None, dv=None,
-                    accumulate: bool = False):
+                    accumulate: bool = False, _noalloc: bool = False):
     """Sparse attention backward.  Returns (dq, dk, dv), fp32.
 
     lse (and delta, if given) are the rows' final values.  dq / dk / dv are
@@ -313,6 +325,11 @@ def sparse_attn_bwd(q, k, v, o, do, lse, index: VsIndexT, delta=None, dq=None,
         _need(delta, "delta", torch.float32, dev)
     ix = index.struct()
     L = _abi.lib()
+    if _noalloc:
+        _abi.check(L.vs_sparse_attn_bwd_noalloc(P.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(o), o_f32, _ptr(do),
+                                                _ptr(lse), _ptr(delta), ctypes.byref(ix), _ptr(dq), int(acc),
+                                                _ptr(dk), _ptr(dv), _stream(dev)))
+        return dq, dk, dv
     nb = ctypes.c_size_t()
     _abi.check(L.vs_workspace_size(P.ref, 2, ctypes.byref(ix), ctypes.byref(nb)))
     ws = _workspace(dev, nb.value)

@@ -52,6 +52,7 @@ SIGNATURES = {
     "vs_sparse_attn_fwd": (i32, [PP, vp, vp, vp, IP, vp, i32, vp, vp, sz, vp]),
     "vs_attn_bwd_delta": (i32, [PP, vp, i32, vp, vp, vp]),
     "vs_sparse_attn_bwd": (i32, [PP, vp, vp, vp, vp, i32, vp, vp, vp, IP, vp, i32, vp, vp, vp, sz, vp]),
+    "vs_sparse_attn_bwd_noalloc": (i32, [PP, vp, vp, vp, vp, i32, vp, vp, vp, IP, vp, i32, vp, vp, vp]),
     "lse_merge": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp]),
     "vs_trace_enable": (i32, [i32]),
     "vs_trace_collect": (i32, [ctypes.c_char_p, sz]),

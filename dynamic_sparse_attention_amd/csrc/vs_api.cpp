@@ -468,11 +468,54 @@ vs_status vs_attn_bwd_delta(const vs_problem* p, const void* o, int32_t o_f32, c
                     "vs_attn_bwd_delta");
 }
 
-vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, const void* v,
-                             const void* o, int32_t o_f32, const void* dout, const float* lse,
-                             const float* delta, const vs_index* idx, float* dq,
-                             int32_t dq_accumulate, float* dk, float* dv, void* ws,
-                             size_t ws_bytes, vs_stream_t stream) {
+}  // extern "C"
+
+// Workspace of vs_sparse_attn_bwd_noalloc: a file-scope device array, one
+// copy per GPU (placed there when the library's code object is loaded on the
+// device, and held until the process ends).  Host code never passes the
+// array's name to a kernel: it is a host-side stand-in, so its device address
+// is looked up once per device and kept in g_scratch_ptr.
+static __device__ __align__(256) char scratch[VS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device of `stream` (the current
+// device for the null stream), looked up on the first call for that device
+// with the device current.
+vs_status scratch_of(hipStream_t stream, void** out) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(VS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return fail(VS_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(VS_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(VS_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr)
+      return fail(VS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return VS_OK;
+}
+
+// The backward; with ws == NULL and use_scratch, the workspace is the
+// device's scratch array (sizes beyond it are refused before any HIP call).
+vs_status attn_bwd(const char* what, const vs_problem* p, const void* q, const void* k, const void* v,
+                   const void* o, int32_t o_f32, const void* dout, const float* lse, const float* delta,
+                   const vs_index* idx, float* dq, int32_t dq_accumulate, float* dk, float* dv, void* ws,
+                   size_t ws_bytes, bool use_scratch, vs_stream_t stream) {
   Prob c;
   vs_status st = check_problem(p, &c);
   if (st) return st;
@@ -486,6 +529,13 @@ vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, 
     return fail(VS_ERR_UNSUPPORTED, "bf16 backward takes at most 32 Q heads per KV head (got %d)",
                 c.h_q / c.h_kv);
   const AttnWs w = attn_ws(c, idx->v_cap_max, true);
+  if (use_scratch) {
+    if (w.total > VS_NOALLOC_SCRATCH_BYTES)
+      return fail(VS_ERR_WORKSPACE, "%s: the problem needs %zu bytes of workspace, beyond the library's "
+                  "fixed %zu bytes", what, w.total, (size_t)VS_NOALLOC_SCRATCH_BYTES);
+    if ((st = scratch_of((hipStream_t)stream, &ws))) return st;
+    ws_bytes = VS_NOALLOC_SCRATCH_BYTES;
+  }
   if (!ws || ws_bytes < w.total)
     return fail(VS_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
   vs::AttnParams a;
@@ -545,7 +595,27 @@ vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, 
   a.lse2 = l2;
   if (e == hipSuccess) e = vs::launch_prep_vertical(a, c.n_lists(), idx->v_ptr, idx->v_idx, s);
   if (e == hipSuccess) e = vs::launch_bwd(a, c.bf16, c.d, s);
-  return hip_status(e, "vs_sparse_attn_bwd");
+  return hip_status(e, what);
+}
+}  // namespace
+
+extern "C" {
+
+vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k, const void* v,
+                             const void* o, int32_t o_f32, const void* dout, const float* lse,
+                             const float* delta, const vs_index* idx, float* dq,
+                             int32_t dq_accumulate, float* dk, float* dv, void* ws,
+                             size_t ws_bytes, vs_stream_t stream) {
+  return attn_bwd("vs_sparse_attn_bwd", p, q, k, v, o, o_f32, dout, lse, delta, idx, dq, dq_accumulate, dk,
+                  dv, ws, ws_bytes, false, stream);
+}
+
+vs_status vs_sparse_attn_bwd_noalloc(const vs_problem* p, const void* q, const void* k, const void* v,
+                                     const void* o, int32_t o_f32, const void* dout, const float* lse,
+                                     const float* delta, const vs_index* idx, float* dq,
+                                     int32_t dq_accumulate, float* dk, float* dv, vs_stream_t stream) {
+  return attn_bwd("vs_sparse_attn_bwd_noalloc", p, q, k, v, o, o_f32, dout, lse, delta, idx, dq,
+                  dq_accumulate, dk, dv, nullptr, 0, true, stream);
 }
 
 vs_status lse_merge(int32_t batch, int32_t n, int32_t heads, int32_t head_dim, float* o_acc,

@@ -256,6 +256,27 @@ vs_status vs_sparse_attn_bwd(const vs_problem* p, const void* q, const void* k,
                              float* dk, float* dv, void* ws, size_t ws_bytes,
                              vs_stream_t stream);
 
+/* vs_sparse_attn_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid hipMalloc.  The workspace is a fixed
+ * array of VS_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU,
+ * placed there when the library's kernels are loaded on the device and held
+ * until the process ends; the call allocates and frees nothing.  Its device
+ * address is looked up on the first call on each device.  Arguments, results
+ * and errors are those of vs_sparse_attn_bwd; a problem whose backward
+ * workspace (vs_workspace_size, op 2) exceeds the array returns
+ * VS_ERR_WORKSPACE before any HIP call.  Every call on one GPU uses the same
+ * array and leaves it in an unspecified state (each call writes every part it
+ * reads before reading it): calls whose work may overlap on one GPU (on
+ * different streams, or on different host threads) race on it and must be
+ * serialised by the caller. */
+#define VS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+vs_status vs_sparse_attn_bwd_noalloc(const vs_problem* p, const void* q, const void* k,
+                                     const void* v, const void* o, int32_t o_f32,
+                                     const void* dout, const float* lse, const float* delta,
+                                     const vs_index* idx, float* dq, int32_t dq_accumulate,
+                                     float* dk, float* dv, vs_stream_t stream);
+
 /* merge_out_and_lse (MTraining paper note, Algorithm 2): combine a partial
  * result over a disjoint key set into an accumulator, in place:
  * L = max(l1, l2) + log(e^(l1-max) + e^(l2-max)),

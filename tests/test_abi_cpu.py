@@ -163,6 +163,26 @@ def test_stride_validation(abi):
     assert status_of(abi, prob(abi, cu=cu, q_stride=wide)) == abi.VS_OK  # Q rows use 64-bit offsets
 
 
+def test_noalloc_backward_refuses_large_problems(abi):
+    """vs_sparse_attn_bwd_noalloc refuses a problem whose workspace exceeds the
+    library's fixed array, before any HIP call (so also without a GPU)."""
+    L = abi.lib()
+    n = 1 << 20
+    p = prob(abi, cu=[0, n], h_q=32, h_kv=4)   # delta and LSE rows alone: 2 * 32 * 2^20 * 4 B = 256 MiB
+    ix = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 64, 4)
+    nb = ctypes.c_size_t()
+    assert L.vs_workspace_size(ctypes.byref(p), 2, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_OK
+    assert nb.value > 64 << 20
+    st = L.vs_sparse_attn_bwd_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None,
+                                      ctypes.byref(ix), FAKE, 0, FAKE, FAKE, None)
+    assert st == abi.VS_ERR_WORKSPACE
+    assert "fixed" in L.vs_last_error().decode()
+    # argument errors come first, as in vs_sparse_attn_bwd
+    st = L.vs_sparse_attn_bwd_noalloc(ctypes.byref(p), None, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None,
+                                      ctypes.byref(ix), FAKE, 0, FAKE, FAKE, None)
+    assert st == abi.VS_ERR_NULL
+
+
 def test_all_chunks_validation(abi):
     """k_rank = VS_ALL_CHUNKS: K / V hold every rank's chunk, so n_k = n_global."""
     W = 8
