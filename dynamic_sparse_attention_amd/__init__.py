@@ -28,7 +28,8 @@ from . import _abi
 from ._abi import VsError
 
 BLOCK = 64
-__all__ = ["VsIndexT", "index_capacity", "estimate_index", "estimate_index_topp", "sparse_attn_fwd",
+__all__ = ["VsIndexT", "index_capacity", "estimate_index", "estimate_index_topp",
+           "estimate_index_xattn", "sparse_attn_fwd",
            "sparse_attn_bwd", "sparse_attn_bwd_noalloc",
            "attn_bwd_delta", "lse_merge", "VsError", "BLOCK"]
 
@@ -98,17 +99,32 @@ class _Problem:
 
 @dataclass
 class VsIndexT:
-    """The Vertical-Slash index on the device (CSR per (batch, Q head, segment))."""
+    """The Vertical-Slash index on the device (CSR per (batch, Q head, segment)).
+
+    blk_mask (optional): a block selection instead of the lists, one bit per
+    (batch, Q head, query block, key block) of blk_size tokens, rows of
+    ceil(nI / 32) int32 words (the layout estimate_index_xattn writes)."""
     v_ptr: torch.Tensor
     v_idx: torch.Tensor
     s_ptr: torch.Tensor
     s_idx: torch.Tensor
     v_cap_max: int
     s_cap_max: int
+    blk_mask: Optional[torch.Tensor] = None
+    blk_size: int = 0
 
     def struct(self) -> _abi.VsIndex:
         return _abi.VsIndex(self.v_ptr.data_ptr(), self.v_idx.data_ptr(), self.s_ptr.data_ptr(),
-                            self.s_idx.data_ptr(), self.v_cap_max, self.s_cap_max)
+                            self.s_idx.data_ptr(), self.v_cap_max, self.s_cap_max,
+                            None if self.blk_mask is None else self.blk_mask.data_ptr(),
+                            self.blk_size)
+
+    def block_selection(self, n: int):
+        """Host copy of a block selection as bool [B*Hq, nI, nI] (n tokens per row)."""
+        nI = -(-n // self.blk_size)
+        w = self.blk_mask.cpu().view(-1, nI, -(-nI // 32)).to(torch.int64) & 0xFFFFFFFF
+        bits = (w.unsqueeze(-1) >> torch.arange(32)) & 1
+        return bits.flatten(-2)[..., :nI].bool()
 
     def lists(self):
         """Host copy: list number -> (verticals, block-diagonals) as int tensors."""
@@ -214,6 +230,40 @@ def estimate_index_topp(q: torch.Tensor, k: torch.Tensor, v_cap: Sequence[int], 
                                         _stream(dev)))
     idx = VsIndexT(v_ptr, v_idx, s_ptr, s_idx, vm, sm)
     return (idx, counts, v_score, s_score) if return_scores else (idx, counts)
+
+
+def estimate_index_xattn(q: torch.Tensor, k: torch.Tensor, threshold: float = 0.9,
+                         block: int = 128, stride: int = 16, return_scores: bool = False):
+    """XAttention block selection for q [B, N, Hq, d], k [B, N, Hkv, d] bf16
+    (one segment): 16-token cells scored along their anti-diagonals, a softmax
+    over each cell row, block scores summed over cells, and per query block the
+    fewest key blocks holding the share ``threshold`` of the row's score.
+
+    Returns (VsIndexT with the block selection, counts [B, Hq, nI] int32) and,
+    with return_scores, also the block scores [B, Hq, nI, nI] fp32 (entries of
+    key blocks after the query block unspecified).
+    """
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, strided=True)
+    _need(k, "k", torch.bfloat16, dev, strided=True)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    P = _Problem(B, Hq, Hkv, d, N, N, _abi.VS_BF16, None, None, None, q=q, k=k)
+    nI = -(-N // block)
+    mask = torch.empty((B * Hq * nI, -(-nI // 32)), dtype=torch.int32, device=dev)
+    counts = torch.empty((B, Hq, nI), dtype=torch.int32, device=dev)
+    scores = torch.empty((B, Hq, nI, nI), dtype=torch.float32, device=dev) if return_scores else None
+    L = _abi.lib()
+    nb = ctypes.c_size_t()
+    _abi.check(L.vs_workspace_size(P.ref, 3, None, ctypes.byref(nb)))
+    ws = _workspace(dev, nb.value)
+    _abi.check(L.vs_estimate_index_xattn(P.ref, _ptr(q), _ptr(k), int(block), int(stride),
+                                         float(threshold), _ptr(mask), _ptr(counts), _ptr(scores),
+                                         _ptr(ws), ws.numel(), _stream(dev)))
+    zeros = torch.zeros(B * Hq + 1, dtype=torch.int32, device=dev)
+    empty = torch.zeros(1, dtype=torch.int32, device=dev)
+    idx = VsIndexT(zeros, empty, zeros, empty, 0, 0, mask, int(block))
+    return (idx, counts, scores) if return_scores else (idx, counts)
 
 
 def index_from_lists(lists: List[Tuple[Sequence[int], Sequence[int]]], device) -> VsIndexT:

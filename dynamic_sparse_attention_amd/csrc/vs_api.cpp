@@ -33,7 +33,11 @@ hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int
                            float2* partials, float* lse2, int tiles_total, const int* tile_prefix,
                            const float* p_v, const float* p_s, int* kcount, hipStream_t st);
 constexpr int kEstKeyTile = 256;
+struct XaParams;
+hipError_t launch_xattn(const XaParams& p, int d, hipStream_t st);
 }  // namespace vs
+
+#include "vs_xattn_params.h"
 
 namespace {
 
@@ -181,7 +185,25 @@ vs_status check_index(const Prob& c, const vs_index* idx) {
   if (idx->s_cap_max > max_seg / c.block)
     return fail(VS_ERR_INDEX, "s_cap_max %d exceeds the block count %d", idx->s_cap_max,
                 max_seg / c.block);
+  if (idx->blk_mask) {
+    if (!c.bf16 || c.W != 1 || c.n_seg != 1)
+      return fail(VS_ERR_UNSUPPORTED, "a block selection takes bf16 inputs, one segment, no striping");
+    if (idx->blk_size != 2 * c.block)
+      return fail(VS_ERR_UNSUPPORTED, "block selection of %d-token blocks unsupported (%d)", idx->blk_size,
+                  2 * c.block);
+    if (idx->v_cap_max != 0 || idx->s_cap_max != 0)
+      return fail(VS_ERR_INDEX, "a block selection comes with empty Vertical-Slash lists");
+  }
   return VS_OK;
+}
+
+// The block-selection fields of the kernels' argument block.
+void fill_bmask(const Prob& c, const vs_index* idx, vs::AttnParams* a) {
+  a->bmask = idx->blk_mask;
+  if (idx->blk_mask) {
+    a->bm_nI = (c.n_global + idx->blk_size - 1) / idx->blk_size;
+    a->bm_words = (a->bm_nI + 31) / 32;
+  }
 }
 
 void fill_params(const Prob& c, vs::AttnParams* a) {
@@ -257,6 +279,25 @@ EstWs est_ws(const Prob& c) {
   w.kcount = off;  // top-p: entries per (list, kind)
   off += align256((size_t)c.n_lists() * 2 * 4);
   w.tprefix = off;
+  w.total = off;
+  return w;
+}
+
+// XAttention estimate: per (batch, Q head) the log-sum-exp of every (cell
+// row, key block) and of every cell row (fp32, log2 domain).
+struct XaWs {
+  size_t cell, row, total;
+  int nC, nI;
+};
+XaWs xa_ws(const Prob& c) {
+  XaWs w;
+  w.nC = c.n_global / 16;
+  w.nI = (c.n_global + 127) / 128;
+  size_t off = 0;
+  w.cell = off;
+  off += align256((size_t)c.batch * c.h_q * w.nC * w.nI * 4);
+  w.row = off;
+  off += align256((size_t)c.batch * c.h_q * w.nC * 4);
   w.total = off;
   return w;
 }
@@ -367,7 +408,11 @@ vs_status vs_workspace_size(const vs_problem* p, int32_t op, const vs_index* idx
     *bytes = est_ws(c).total;
     return ok();
   }
-  if (op != 1 && op != 2) return fail(VS_ERR_SHAPE, "op %d is not 0, 1 or 2", op);
+  if (op == 3) {
+    *bytes = xa_ws(c).total;
+    return ok();
+  }
+  if (op != 1 && op != 2) return fail(VS_ERR_SHAPE, "op %d is not 0, 1, 2 or 3", op);
   if ((st = check_index(c, idx))) return st;
   *bytes = attn_ws(c, idx->v_cap_max, op == 2).total;
   return ok();
@@ -423,6 +468,47 @@ vs_status vs_estimate_index_topp(const vs_problem* p, const void* q, const void*
                   counts, v_score, s_score, ws, ws_bytes, stream);
 }
 
+vs_status vs_estimate_index_xattn(const vs_problem* p, const void* q, const void* k, int32_t block,
+                                  int32_t stride, float threshold, uint32_t* blk_mask, int32_t* counts,
+                                  float* blk_score, void* ws, size_t ws_bytes, vs_stream_t stream) {
+  Prob c;
+  vs_status st = check_problem(p, &c);
+  if (st) return st;
+  if (!q || !k || !blk_mask) return fail(VS_ERR_NULL, "q, k or blk_mask is NULL");
+  if (!c.bf16 || c.W != 1 || c.n_seg != 1)
+    return fail(VS_ERR_UNSUPPORTED, "XAttention estimation takes bf16 inputs, one segment, no striping");
+  if (block != 128 || stride != 16)
+    return fail(VS_ERR_UNSUPPORTED, "XAttention block %d / stride %d unsupported (128 / 16)", block, stride);
+  if (c.n_global > 131072)
+    return fail(VS_ERR_UNSUPPORTED, "XAttention estimation sorts at most 1024 key blocks (n %d)", c.n_global);
+  if (!std::isfinite(threshold)) return fail(VS_ERR_SHAPE, "threshold is not finite");
+  const XaWs w = xa_ws(c);
+  if (!ws || ws_bytes < w.total)
+    return fail(VS_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  vs::XaParams x;
+  std::memset(&x, 0, sizeof x);
+  x.q = static_cast<const __bf16*>(q);
+  x.k = static_cast<const __bf16*>(k);
+  x.sq = c.sq;
+  x.sk = c.sk;
+  x.batch = c.batch;
+  x.h_q = c.h_q;
+  x.h_kv = c.h_kv;
+  x.n = c.n_global;
+  x.nC = w.nC;
+  x.nI = w.nI;
+  x.words = (w.nI + 31) / 32;
+  x.sl2 = c.scale * vs::kLog2e;
+  char* base = static_cast<char*>(ws);
+  x.cell_lse = reinterpret_cast<float*>(base + w.cell);
+  x.row_lse = reinterpret_cast<float*>(base + w.row);
+  x.threshold = threshold;
+  x.bmask = blk_mask;
+  x.counts = counts;
+  x.scores = blk_score;
+  return hip_status(vs::launch_xattn(x, c.d, (hipStream_t)stream), "vs_estimate_index_xattn");
+}
+
 vs_status vs_sparse_attn_fwd(const vs_problem* p, const void* q, const void* k, const void* v,
                              const vs_index* idx, void* o, int32_t o_f32, float* lse, void* ws,
                              size_t ws_bytes, vs_stream_t stream) {
@@ -441,6 +527,7 @@ vs_status vs_sparse_attn_fwd(const vs_problem* p, const void* q, const void* k, 
   a.v = v;
   a.s_ptr = idx->s_ptr;
   a.s_idx = idx->s_idx;
+  fill_bmask(c, idx, &a);
   char* base = static_cast<char*>(ws);
   a.vsel = reinterpret_cast<int*>(base + w.vsel);
   a.vcnt = reinterpret_cast<int*>(base + w.vcnt);
@@ -546,6 +633,7 @@ vs_status attn_bwd(const char* what, const vs_problem* p, const void* q, const v
   a.dout = dout;
   a.s_ptr = idx->s_ptr;
   a.s_idx = idx->s_idx;
+  fill_bmask(c, idx, &a);
   char* base = static_cast<char*>(ws);
   a.vsel = reinterpret_cast<int*>(base + w.vsel);
   a.vcnt = reinterpret_cast<int*>(base + w.vcnt);

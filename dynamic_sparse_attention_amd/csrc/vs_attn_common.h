@@ -60,6 +60,11 @@ struct AttnParams {
   int k_all;          // striped: K/V hold every rank's chunk (k_rank unused)
   int n_global;
   Stride3 sq, sk, sv, so, sdo;  // element strides of Q, K, V, O (its own type), dO
+  // Block selection in place of the Vertical-Slash lists (one segment, W = 1):
+  // bit J of row (b * h_q + h) * bm_nI + I marks 128-key block J for the
+  // 128-row query block I; each 128-block covers two 64-blocks.
+  const uint32_t* bmask;
+  int bm_nI, bm_words;
   int qranges;        // backward column units: query-block ranges per column tile
   int qrange_len;
   int col_tiles;      // backward column units: column tiles per list
@@ -128,6 +133,13 @@ __device__ __forceinline__ int local_query_block(const AttnParams& p, int qb_glo
   if (d < 0 || d % p.W != 0) return -1;
   const int i = d / p.W;
   return i < p.nqb ? i : -1;
+}
+
+// Whether the block selection marks 128-key block J for 128-row block I of
+// list bh (= b * h_q + h).
+__device__ __forceinline__ bool bmask_bit(const AttnParams& p, int bh, int I, int J) {
+  const uint32_t w = p.bmask[((size_t)bh * p.bm_nI + I) * p.bm_words + (J >> 5)];
+  return (w >> (J & 31)) & 1u;
 }
 
 // Local key position of a global position held by this call.

@@ -286,7 +286,10 @@ __device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D>& L, i
   __syncthreads();
 }
 
-template <int D>
+// BLK: the index is a block selection (p.bmask, one segment) instead of
+// block-diagonal lists; a template flag so that the list walk keeps its
+// registers.
+template <int D, bool BLK>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_kv_slash_bf16_kernel(AttnParams p) {
   typedef KvWorkerB<D> W;
   __shared__ KvLdsB<D> L;
@@ -325,14 +328,19 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     *i = (v >> 1) & ((1 << 25) - 1);
     *fl = v & 1;
   };
-  // Diagonal tiles (g = 0, causal inside the block) first, in a walk of their
-  // own, so that the main walk has no masking at all.
+  // Diagonal tiles (g = 0, or the query block itself in a block selection;
+  // causal inside the block) first, in a walk of their own, so that the main
+  // walk has no masking at all.
   {
     int i = -1;
     if (tid >= p.hh_lo && tid < p.hh_hi) {
       const int list = (b * p.h_q + kvh * G + tid) * p.seg.n_seg + seg;
-      const int sp0 = p.s_ptr[list];
-      if (p.s_ptr[list + 1] > sp0 && p.s_idx[sp0] == 0) i = local_query_block(p, kb_glob);
+      if (BLK) {
+        if (bmask_bit(p, list, beta_k >> 1, beta_k >> 1)) i = local_query_block(p, kb_glob);
+      } else {
+        const int sp0 = p.s_ptr[list];
+        if (p.s_ptr[list + 1] > sp0 && p.s_idx[sp0] == 0) i = local_query_block(p, kb_glob);
+      }
     }
     int tot;
     const int slot = block_compact<kKvThreads>(i >= 0, L.wsum, &tot);
@@ -347,14 +355,22 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   };
   for (int hh = p.hh_lo; hh < p.hh_hi; ++hh) {
     const int list = (b * p.h_q + kvh * G + hh) * p.seg.n_seg + seg;
-    const int sp0 = p.s_ptr[list];
-    const int ns = p.s_ptr[list + 1] - sp0;
+    // Candidates: the head's selected block-diagonals g > 0 (query block
+    // kb + g), or with a block selection (one segment) the query blocks after
+    // this key block, kept when their 128-block selected the key's 128-block.
+    const int sp0 = BLK ? 0 : p.s_ptr[list];
+    const int ns = BLK ? nb_seg - 1 - beta_k : p.s_ptr[list + 1] - sp0;
     for (int base = 0; base < ns; base += kKvThreads) {
       const int e = base + tid;
       int i = -1;
       if (e < ns) {
-        const int g = p.s_idx[sp0 + e];
-        if (g > 0 && beta_k + g < nb_seg) i = local_query_block(p, kb_glob + g);
+        if (BLK) {
+          const int ib = beta_k + 1 + e;  // query block of the segment
+          if (bmask_bit(p, list, ib >> 1, beta_k >> 1)) i = local_query_block(p, a_blk + ib);
+        } else {
+          const int g = p.s_idx[sp0 + e];
+          if (g > 0 && beta_k + g < nb_seg) i = local_query_block(p, kb_glob + g);
+        }
       }
       int tot;
       const int slot = block_compact<kKvThreads>(i >= 0, L.wsum, &tot);
@@ -489,10 +505,12 @@ hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
     nb_max = std::max(nb_max, p.seg.start_blk[sgi + 1] - p.seg.start_blk[sgi]);
   const size_t bits_bytes = (size_t)((nb_max + 31) / 32) * 4 + 4;
   if (d == 128) {
-    if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128>), gs, dim3(kKvThreads), 0, st, p));
+    if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, true>), gs, dim3(kKvThreads), 0, st, p));
+    if (gs.x && !p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, false>), gs, dim3(kKvThreads), 0, st, p));
     if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128>), gc, dim3(kKvThreads), bits_bytes, st, p));
   } else {
-    if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64>), gs, dim3(kKvThreads), 0, st, p));
+    if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, true>), gs, dim3(kKvThreads), 0, st, p));
+    if (gs.x && !p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, false>), gs, dim3(kKvThreads), 0, st, p));
     if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64>), gc, dim3(kKvThreads), bits_bytes, st, p));
   }
   return hipGetLastError();

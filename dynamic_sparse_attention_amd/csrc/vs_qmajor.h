@@ -154,6 +154,25 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
   };
   fetch(0);
 
+  // Block selection (an alternative estimator's index, one segment): the
+  // 64-key blocks kb <= beta whose 128-block the query block's 128-block
+  // selected (the second half of the diagonal 128-block lies past every
+  // row of the first half and is left out by kb <= beta).
+  if (p.bmask) {
+    const int bh = list;  // one segment: list = b * h_q + h
+    for (int base = 0; base <= rb.beta; base += NT) {
+      const int kb = base + tid;
+      int j = -1;
+      if (kb <= rb.beta && bmask_bit(p, bh, rb.beta >> 1, kb >> 1)) j = local_key_block(p, rb.a_blk + kb);
+      int tot;
+      const int slot = block_compact<NT>(j >= 0, L.wsum, &tot);
+      if (j >= 0) L.tiles[slot] = 2 * j + (kb == rb.beta);
+      __syncthreads();
+      wk.run(SlashSetT<NS>{L.tiles, tot, wave});
+      __syncthreads();
+    }
+  }
+
   // Slash tiles: key block beta - g for every selected g <= beta.
   for (int base = 0; base < ns; base += NT) {
     const int e = base + tid;

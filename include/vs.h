@@ -131,6 +131,16 @@ typedef struct vs_problem {
  * written by vs_estimate_index when a capacity exceeds the candidates) are
  * ignored.  v_cap_max / s_cap_max are HOST-known upper bounds of the list
  * lengths (vs_index_capacity returns them) used to size launches.
+ *
+ * Block selection (an alternative estimator's index, vs_estimate_index_xattn):
+ * when blk_mask is not NULL the index is a selection of blk_size x blk_size
+ * blocks instead of Vertical-Slash lists: row n attends key m iff m <= n and
+ * bit J = m / blk_size of word J / 32 of row
+ * (b * h_q + h) * nI + n / blk_size is set, nI = ceil(n_global / blk_size),
+ * ceil(nI / 32) words per row (DEVICE).  It requires bf16 inputs, one
+ * segment, stripe_world 1, blk_size 128 and empty lists (v_cap_max and
+ * s_cap_max 0; v_ptr and s_ptr still point at batch*h_q+1 zero offsets),
+ * else VS_ERR_UNSUPPORTED / VS_ERR_INDEX.
  */
 typedef struct vs_index {
   const int32_t* v_ptr;
@@ -139,6 +149,8 @@ typedef struct vs_index {
   const int32_t* s_idx;
   int32_t v_cap_max;
   int32_t s_cap_max;
+  const uint32_t* blk_mask;  /* NULL: the Vertical-Slash lists above */
+  int32_t blk_size;
 } vs_index;
 
 /* List offsets for budgets (MTraining paper note, Algorithm 1: argtopk with
@@ -157,7 +169,7 @@ vs_status vs_index_capacity(const vs_problem* p, const int32_t* v_budget,
 
 /* Workspace bytes an entry point needs: op 0 = vs_estimate_index (and
  * vs_estimate_index_topp),
- * 1 = vs_sparse_attn_fwd, 2 = vs_sparse_attn_bwd.  idx may be NULL for op 0;
+ * 1 = vs_sparse_attn_fwd, 2 = vs_sparse_attn_bwd, 3 = vs_estimate_index_xattn.  idx may be NULL for op 0;
  * for ops 1 and 2 it supplies the capacity bounds.  The workspace is DEVICE
  * memory, 256-byte aligned, owned by the caller, and may be reused across
  * calls on the same stream. */
@@ -210,6 +222,29 @@ vs_status vs_estimate_index_topp(const vs_problem* p, const void* q, const void*
                                  int32_t* s_idx, int32_t* counts, float* v_score,
                                  float* s_score, void* ws, size_t ws_bytes,
                                  vs_stream_t stream);
+
+/* XAttention block estimation, an alternative index estimator for the same
+ * attention calls (the MTraining paper note, appendix, baseline settings,
+ * item 2: blocks scored by sums along their anti-diagonals sampled at a
+ * stride, the high-scoring ones kept; block 128, stride 16, threshold 0.9).
+ * For every (b, h): cell logits z[A, C] = (1/stride) sum_u scale *
+ * q[stride A + u] . k[stride C + stride - 1 - u] (u < stride) for cells
+ * C <= A; a softmax over each cell row; block scores s[I, J] = the sum of
+ * the probabilities of the block's cells; for each query block I the fewest
+ * key blocks J <= I, highest scores first (ties to the lowest J), whose
+ * integer masses rint(s * 2^50) reach ceil(rint(t * 2^24) * total / 2^24)
+ * (t = threshold clamped to [0, 1]).  Writes blk_mask (DEVICE, the layout of
+ * vs_index.blk_mask) and, when not NULL, counts [b, h_q, nI] int32 (blocks
+ * kept) and blk_score [b, h_q, nI, nI] fp32 (s; entries J > I unspecified).
+ * q [batch, n, h_q, d], k [batch, n, h_kv, d] bf16 (strides from the
+ * problem); one segment, stripe_world 1, block 128, stride 16 and n at most
+ * 131072 (1024 query blocks), else VS_ERR_UNSUPPORTED.  Workspace: op 3.
+ * Errors: VS_ERR_NULL, VS_ERR_SHAPE, VS_ERR_UNSUPPORTED, VS_ERR_WORKSPACE,
+ * VS_ERR_HIP. */
+vs_status vs_estimate_index_xattn(const vs_problem* p, const void* q, const void* k,
+                                  int32_t block, int32_t stride, float threshold,
+                                  uint32_t* blk_mask, int32_t* counts, float* blk_score,
+                                  void* ws, size_t ws_bytes, vs_stream_t stream);
 
 /* Sparse attention forward (MTraining paper note, Algorithm 1 last step and
  * Algorithm 2 block_bar_sparse_attention_forward; online softmax as in

@@ -16,6 +16,8 @@ definitions on the pages:
   — the paper note's Appendix E, Algorithm 2;
 * effective-mask-area accounting — MagiAttention "Dynamic Attention Solver",
   "Computation Cost Estimation";
+* the XAttention block estimator (anti-diagonal block scores, threshold
+  selection) — the paper note's appendix, baseline settings, item 2;
 * the RoPE relative-position property — MTraining Theorem 3.1 and the paper
   note's Appendix B.2, Eq. 14.
 
@@ -24,16 +26,19 @@ steps are listed in the repository's design notes.
 """
 from .index import (capacities, window_probs, window_scores, select_topk, estimate_index,
                     topp_count, estimate_index_topp,
-                    dense_mask)
+                    dense_mask, block_selected)
 from .attention import (attn_fwd_dense, attn_bwd_dense, attn_fwd_support, attn_bwd_support,
                         lse_merge, row_groups, support_candidates, bwd_delta,
                         bwd_rounding_bounds)
 from .accounting import mask_area_bruteforce, mask_area_formula, dense_causal_area
+from . import xattn
+from .xattn import antidiag_logits, xattn_block_scores, estimate_index_xattn
 
 __all__ = [
     "capacities", "window_probs", "window_scores", "select_topk", "estimate_index",
     "topp_count", "estimate_index_topp", "dense_mask", "attn_fwd_dense", "attn_bwd_dense", "attn_fwd_support", "attn_bwd_support",
     "lse_merge", "row_groups", "support_candidates", "bwd_delta", "bwd_rounding_bounds",
     "mask_area_bruteforce",
-    "mask_area_formula", "dense_causal_area",
+    "mask_area_formula", "dense_causal_area", "xattn", "antidiag_logits", "xattn_block_scores",
+    "estimate_index_xattn", "block_selected",
 ]

@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .index import dense_mask, _segment_of
+from .index import block_selected, dense_mask, _segment_of
 
 
 def _f64(x):
@@ -114,13 +114,14 @@ def row_groups(rows_pos, cu_seqlens, block=64):
 def support_candidates(seg, beta, rows_max, cols_pos, cu_seqlens, index_hs, block=64):
     """Column indices (into cols_pos) that may hold an entry for rows of (seg, beta).
 
-    The candidates are the key blocks beta - g for selected g, and the
-    selected vertical columns m <= rows_max, restricted to the call's columns.
-    The caller evaluates the exact mask on them.
+    The candidates are the key blocks beta - g for selected g, the selected
+    vertical columns m <= rows_max, and the keys of the blocks selected for
+    the rows' block in the optional block selection, restricted to the
+    call's columns.  The caller evaluates the exact mask on them.
     """
     cols_pos = np.asarray(cols_pos)
     a, e = int(cu_seqlens[seg]), int(cu_seqlens[seg + 1])
-    iv, is_ = index_hs
+    iv, is_ = index_hs[:2]
     want = []
     for g in is_:
         kb = beta - int(g)
@@ -128,6 +129,13 @@ def support_candidates(seg, beta, rows_max, cols_pos, cu_seqlens, index_hs, bloc
             continue
         lo = a + kb * block
         want.append(np.arange(lo, min(lo + block, e)))
+    if len(index_hs) > 2 and index_hs[2] is not None:
+        bb, sel = index_hs[2]
+        I = (beta * block) // bb
+        if I < len(sel):
+            for J in np.nonzero(np.asarray(sel[I]))[0]:
+                lo = a + int(J) * bb
+                want.append(np.arange(lo, min(lo + bb, e)))
     want.append(np.asarray(iv)[np.asarray(iv) <= rows_max])
     want = np.unique(np.concatenate(want)) if want else np.zeros(0, np.int64)
     idx = np.searchsorted(cols_pos, want)
@@ -139,13 +147,14 @@ def support_candidates(seg, beta, rows_max, cols_pos, cu_seqlens, index_hs, bloc
 
 def _group_mask(rows_pos_g, cand_pos, seg, cu_seqlens, index_hs, block):
     a, e = int(cu_seqlens[seg]), int(cu_seqlens[seg + 1])
-    iv, is_ = index_hs
+    iv, is_ = index_hs[:2]
     n = rows_pos_g[:, None]
     m = cand_pos[None, :]
     inseg = (m >= a) & (m < e)
     vert = np.isin(m, iv)
     slash = np.isin((n - a) // block - (m - a) // block, is_)
-    return inseg & (m <= n) & (vert | slash)
+    blk = block_selected(index_hs, n - a, m - a)
+    return inseg & (m <= n) & (vert | slash | blk)
 
 
 def attn_fwd_support(q, k, v, rows_pos, cols_pos, cu_seqlens, index, block=64, scale=None,

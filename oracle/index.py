@@ -168,12 +168,29 @@ def _segment_of(pos, cu_seqlens):
     return np.searchsorted(np.asarray(cu_seqlens), pos, side="right") - 1
 
 
+def block_selected(index_hs, n_off, m_off):
+    """Entries whose (query block, key block) pair is selected in the optional
+    block selection of an index entry (iv, is_, (bb, sel)): sel[I, J] marks key
+    block J (of bb tokens, in-segment offsets m_off // bb) for query block I
+    (n_off // bb).  An entry without that part selects no block."""
+    n_off, m_off = np.asarray(n_off), np.asarray(m_off)
+    if len(index_hs) < 3 or index_hs[2] is None:
+        return np.zeros(np.broadcast(n_off, m_off).shape, dtype=bool)
+    bb, sel = index_hs[2]
+    sel = np.asarray(sel, dtype=bool)
+    I, J = n_off // bb, m_off // bb
+    ok = (I >= 0) & (J >= 0) & (I < sel.shape[0]) & (J < sel.shape[1])
+    return ok & sel[np.clip(I, 0, sel.shape[0] - 1), np.clip(J, 0, sel.shape[1] - 1)]
+
+
 def dense_mask(rows_pos, cols_pos, cu_seqlens, index, h, block=64):
     """``sparseformat``: boolean mask [len(rows_pos), len(cols_pos)] for Q head h.
 
     M[n, m] holds when n and m lie in the same segment, m <= n (causal), and
     m is a selected vertical or beta(n) - beta(m) is a selected
     block-diagonal.  Vertical and slash entries form a union (Algorithm 1).
+    An index entry may also carry a block selection (see block_selected):
+    its selected blocks join the union.
     rows_pos / cols_pos are global positions, so a striped chunk's mask is the
     global mask restricted to its rows and columns.
     """
@@ -188,10 +205,11 @@ def dense_mask(rows_pos, cols_pos, cu_seqlens, index, h, block=64):
         ci = np.nonzero(sc == s)[0]
         if ri.size == 0 or ci.size == 0:
             continue
-        iv, is_ = index[(h, s)]
+        iv, is_ = index[(h, s)][:2]
         n = rows_pos[ri][:, None]
         m = cols_pos[ci][None, :]
         vert = np.isin(m, iv)
         slash = np.isin((n - a) // block - (m - a) // block, is_)
-        M[np.ix_(ri, ci)] = (m <= n) & (vert | slash)
+        blk = block_selected(index[(h, s)], n - a, m - a)
+        M[np.ix_(ri, ci)] = (m <= n) & (vert | slash | blk)
     return M

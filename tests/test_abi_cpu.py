@@ -208,7 +208,7 @@ def test_entry_points_reject_before_launch(abi):
     fwd_ws = nb.value
     assert L.vs_workspace_size(P, 2, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_OK
     assert nb.value > fwd_ws
-    assert L.vs_workspace_size(P, 3, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_ERR_SHAPE
+    assert L.vs_workspace_size(P, 4, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_ERR_SHAPE
     assert L.vs_workspace_size(P, 1, None, ctypes.byref(nb)) == abi.VS_ERR_NULL
     # estimate
     st = L.vs_estimate_index(P, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None)
@@ -290,3 +290,40 @@ def test_executed_area_matches_oracle():
     ref = [int(oracle.dense_mask(rows, np.arange(n), [0, n], idx, h).sum()) for h in range(2)]
     assert got.tolist() == ref
     assert accounting.dense_causal_area([0, n], rows) == oracle.dense_causal_area(rows, [0, n])
+
+
+def test_xattn_and_block_selection_validation(abi):
+    """The XAttention estimator and a block-selection index: supported forms
+    (bf16, one segment, no striping, 128-token blocks, stride 16, at most
+    1024 query blocks) are checked before any HIP call."""
+    L = abi.lib()
+    p = prob(abi)
+    P = ctypes.byref(p)
+    nb = ctypes.c_size_t()
+    assert L.vs_workspace_size(P, 3, None, ctypes.byref(nb)) == abi.VS_OK
+    nC, nI = 4096 // 16, 4096 // 128
+    assert nb.value >= 16 * nC * nI * 4 + 16 * nC * 4   # cell and row log-sum-exps, fp32
+    big = 1 << 40
+    est = L.vs_estimate_index_xattn
+    assert est(P, None, FAKE, 128, 16, 0.9, FAKE, None, None, FAKE, big, None) == abi.VS_ERR_NULL
+    assert est(P, FAKE, FAKE, 128, 16, 0.9, None, None, None, FAKE, big, None) == abi.VS_ERR_NULL
+    assert est(P, FAKE, FAKE, 64, 16, 0.9, FAKE, None, None, FAKE, big, None) == abi.VS_ERR_UNSUPPORTED
+    assert est(P, FAKE, FAKE, 128, 8, 0.9, FAKE, None, None, FAKE, big, None) == abi.VS_ERR_UNSUPPORTED
+    assert est(P, FAKE, FAKE, 128, 16, float("nan"), FAKE, None, None, FAKE, big, None) == abi.VS_ERR_SHAPE
+    assert est(P, FAKE, FAKE, 128, 16, 0.9, FAKE, None, None, FAKE, 16, None) == abi.VS_ERR_WORKSPACE
+    for bad in (prob(abi, dtype=abi.VS_F32), prob(abi, cu=[0, 2048, 4096]),
+                prob(abi, cu=[0, 8192], n_q=1024, n_k=1024, stripe_world=8),
+                prob(abi, cu=[0, 131072 + 128])):
+        assert est(ctypes.byref(bad), FAKE, FAKE, 128, 16, 0.9, FAKE, None, None, FAKE, big,
+                   None) == abi.VS_ERR_UNSUPPORTED
+    # a block-selection index
+    ix = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0x1000, 128)
+    assert L.vs_workspace_size(P, 1, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_OK
+    for bad_ix in (abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0x1000, 64),
+                   abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0x1000, 256)):
+        assert L.vs_workspace_size(P, 1, ctypes.byref(bad_ix), ctypes.byref(nb)) == abi.VS_ERR_UNSUPPORTED
+    lists = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 64, 4, 0x1000, 128)
+    assert L.vs_workspace_size(P, 2, ctypes.byref(lists), ctypes.byref(nb)) == abi.VS_ERR_INDEX
+    for bad in (prob(abi, dtype=abi.VS_F32), prob(abi, cu=[0, 2048, 4096])):
+        assert L.vs_workspace_size(ctypes.byref(bad), 1, ctypes.byref(ix),
+                                   ctypes.byref(nb)) == abi.VS_ERR_UNSUPPORTED

@@ -601,3 +601,160 @@ def test_bwd_rounding_bound_holds_for_simulated_bf16():
         err = np.abs(sim - ref)
         assert np.all(err <= 1.01 * b + 1e-12)
         assert (err / (b + 1e-30)).max() > 0.05
+
+
+# ---------------------------------------------------------------- XAttention block estimator (f4)
+from fractions import Fraction
+
+from oracle import xattn as oxa
+
+
+def test_x1_antidiagonal_sampling_one_hot():
+    """Only an anti-diagonal pair of a 16 x 16 cell reaches the cell logit:
+    one query row and one key row carry the same unit vector, everything else
+    is zero, so z[A, C] is nonzero exactly when (row, key) is the pair
+    (16A + u, 16C + 15 - u) of that cell, where it is scale / 16."""
+    n, d, S = 64, 8, 16
+    for r0, c0, hit in ((17, 30, True), (17, 17, False), (35, 12, True), (35, 3, False),
+                        (0, 15, True), (15, 0, True), (20, 20, False), (63, 48, True)):
+        q = np.zeros((n, d))
+        k = np.zeros((n, d))
+        q[r0, 3] = 1.0
+        k[c0, 3] = 1.0
+        z = oxa.antidiag_logits(q, k, 0, n, 0.5, S)
+        fin = np.where(np.isfinite(z), z, 0.0)
+        A, C = r0 // S, c0 // S
+        on_anti = (r0 % S) + (c0 % S) == S - 1
+        assert on_anti == hit, (r0, c0)
+        expect = np.zeros_like(fin)
+        if hit and C <= A:
+            expect[A, C] = 0.5 / S
+        assert np.array_equal(fin, expect), (r0, c0)
+
+
+def _uniform_block_scores(nI, cpb=8):
+    """Block scores of all-zero logits, worked out with exact fractions: cell
+    row A spreads 1/(A+1) over its A+1 causal cells."""
+    s = [[Fraction(0)] * nI for _ in range(nI)]
+    for A in range(nI * cpb):
+        I = A // cpb
+        for C in range(A + 1):
+            s[I][C // cpb] += Fraction(1, A + 1)
+    return s
+
+
+def test_x2_uniform_scores_closed_form_and_ties():
+    """Q = 0: every cell logit is 0.  Block scores equal the exact sums, and
+    the selection follows them: with 3 blocks, I = 2 sees J = 0 and J = 1 tie
+    exactly (8 * (H_24 - H_16) each); a threshold that one block meets keeps
+    J = 0 (lowest index)."""
+    n, d = 384, 8
+    rng = np.random.default_rng(50)
+    q = np.zeros((n, 1, d))
+    k = rng.standard_normal((n, 1, d))
+    s = oxa.xattn_block_scores(q[:, 0], k[:, 0], 0, n, 0.125)
+    exact = _uniform_block_scores(3)
+    for I in range(3):
+        for J in range(3):
+            assert abs(s[I, J] - float(exact[I][J])) < 1e-12, (I, J)
+    assert exact[2][0] == exact[2][1]
+    for tau, want in ((0.9, {0: [0], 1: [0, 1], 2: [0, 1, 2]}),
+                      (0.6, {0: [0], 1: [0], 2: [0, 1]}),
+                      (0.3, {0: [0], 1: [0], 2: [0]})):
+        idx, sc, cnt = oxa.estimate_index_xattn(q, k, [0, n], threshold=tau, return_scores=True)
+        sel = idx[(0, 0)][2][1]
+        for I, Js in want.items():
+            assert np.nonzero(sel[I])[0].tolist() == Js, (tau, I)
+            assert cnt[(0, 0)][I] == len(Js)
+
+
+def test_x2_cell_logit_is_the_mean():
+    """Equal scaled scores x on every sampled pair give z = x (the mean of the
+    16 samples, not their sum)."""
+    n, d, S = 64, 4, 16
+    vec = np.array([1.0, 2.0, -1.0, 0.5])
+    q = np.tile(vec, (n, 1))
+    k = np.tile(vec, (n, 1))
+    z = oxa.antidiag_logits(q, k, 0, n, 0.25, S)
+    x = 0.25 * float(vec @ vec)
+    fin = np.isfinite(z)
+    assert np.allclose(z[fin], x, rtol=0, atol=1e-14)
+    assert fin.sum() == (n // S) * (n // S + 1) // 2
+
+
+def test_x4_block_scores_sum_to_cell_rows():
+    """Each cell row's probabilities sum to 1, so a query block's scores sum
+    to its cell rows: 8, or 4 for a segment ending half-way through a block."""
+    rng = np.random.default_rng(51)
+    d = 16
+    for L in (512, 576):
+        q, k = rng.standard_normal((L, d)) * 2, rng.standard_normal((L, d)) * 2
+        s = oxa.xattn_block_scores(q, k, 0, L, 1 / 4)
+        rows = np.full(s.shape[0], 8.0)
+        if L % 128:
+            rows[-1] = (L % 128) / 16
+        assert np.abs(s.sum(axis=1) - rows).max() < 1e-12
+        assert np.all(np.triu(s, 1) == 0)
+
+
+def test_x6_threshold_one_is_block_causal_attention():
+    """Threshold 1 keeps every key block with a positive score, i.e. every
+    J <= I: the mask is plain causal attention, forward and backward equal
+    torch's causal SDPA in fp64."""
+    rng = np.random.default_rng(52)
+    n, hq, hkv, d = 384, 2, 1, 16
+    q, k, v, do = (rng.standard_normal((n, h, d)) for h in (hq, hkv, hkv, hq))
+    idx = oxa.estimate_index_xattn(q, k, [0, n], threshold=1.0)
+    for h in range(hq):
+        sel = idx[(h, 0)][2][1]
+        assert np.array_equal(sel, np.tril(np.ones_like(sel)))
+    pos = np.arange(n)
+    O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], idx)
+    qt = torch.tensor(q).permute(1, 0, 2)[None]
+    kt = torch.tensor(k).permute(1, 0, 2)[None].repeat_interleave(hq // hkv, dim=1)
+    vt = torch.tensor(v).permute(1, 0, 2)[None].repeat_interleave(hq // hkv, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    assert np.abs(O - ref[0].permute(1, 0, 2).numpy()).max() < 1e-12
+
+
+def test_block_selection_mask_and_forms():
+    """A block selection in the index: the mask is causal and the key's block
+    selected for the row's block (brute force), and the dense and support
+    forms of attention agree on it, with and without Vertical-Slash entries."""
+    rng = np.random.default_rng(53)
+    B, bb, hq, hkv, d = 16, 32, 2, 1, 8
+    cu = [0, 96, 192]
+    n = cu[-1]
+    q, do = rng.standard_normal((n, hq, d)), rng.standard_normal((n, hq, d))
+    k, v = rng.standard_normal((n, hkv, d)), rng.standard_normal((n, hkv, d))
+    vs_idx = rand_index(rng, n, hq, B, cu=cu)
+    for with_vs in (False, True):
+        idx = {}
+        for key, (iv, is_) in vs_idx.items():
+            L = cu[key[1] + 1] - cu[key[1]]
+            nI = -(-L // bb)
+            sel = np.tril(rng.random((nI, nI)) < 0.4)
+            e = np.zeros(0, np.int64)
+            idx[key] = (iv, is_, (bb, sel)) if with_vs else (e, e, (bb, sel))
+        pos = np.arange(n)
+        for h in range(hq):
+            M = oracle.dense_mask(pos, pos, cu, idx, h, B)
+            for nn in range(0, n, 7):
+                for mm in range(0, n, 5):
+                    s = np.searchsorted(cu, nn, side="right") - 1
+                    a = cu[s]
+                    iv, is_, (_, sel) = idx[(h, s)]
+                    same = a <= mm < cu[s + 1]
+                    want = same and mm <= nn and (mm in iv or ((nn - a) // B - (mm - a) // B) in is_
+                                                 or sel[(nn - a) // bb, (mm - a) // bb])
+                    assert M[nn, mm] == want, (with_vs, h, nn, mm)
+        O, L = oracle.attn_fwd_dense(q, k, v, pos, pos, cu, idx, B)
+        O2, L2 = oracle.attn_fwd_support(q, k, v, pos, pos, cu, idx, B)
+        fin = np.isfinite(L)
+        assert np.array_equal(fin, np.isfinite(L2)) and np.abs(O - O2).max() < 1e-12
+        assert np.abs(L[fin] - L2[fin]).max() < 1e-12
+        D = (O * do).sum(-1).T
+        g1 = oracle.attn_bwd_dense(q, k, v, do, L, D, pos, pos, cu, idx, B)
+        g2 = oracle.attn_bwd_support(q, k, v, do, L, D, pos, pos, cu, idx, B)
+        for x, y in zip(g1, g2):
+            assert np.abs(x - y).max() < 1e-12

@@ -275,3 +275,89 @@ def test_packed_documents_in_bounds():
     query_major_walk(call, lists, h_q, len(cu) - 1, 128, h_kv * 128 * 2)
     key_major_slash(call, lists, h_q, h_kv, len(cu) - 1)
     column_units(call, lists, h_q, len(cu) - 1, v_cap)
+
+
+def block_selection_walks(n, batch, h_q, h_kv, sel_p, rng):
+    """Block-selection index (one segment, 128-token blocks, 64-token tiles):
+    the bitmap words the query-major block phase and the slash dK/dV walk
+    read, the tiles they form, and the dK/dV list capacity."""
+    nb = n // BLOCK
+    nI = -(-n // 128)
+    words = (nI + 31) >> 5
+    n_words = batch * h_q * nI * words
+    sel = rng.random((batch * h_q, nI, nI)) < sel_p
+    sel &= np.tril(np.ones((nI, nI), bool))[None]
+
+    def bit(bh, I, J):
+        w = (bh * nI + I) * words + (J >> 5)
+        assert np.all((w >= 0) & (w < n_words))
+        return sel[bh, I, J]
+
+    beta = np.arange(nb)
+    for bh in range(batch * h_q):
+        # query-major: key blocks kb <= beta, NT = 128 per compaction round
+        for b in range(nb):
+            kb = np.arange(b + 1)
+            on = bit(bh, b >> 1, kb >> 1)
+            for base in range(0, b + 1, 128):
+                assert on[base:base + 128].sum() <= 128  # the tiles[NT] array
+            assert np.all(kb[on] < nb)
+    G = h_q // h_kv
+    for b in range(batch):
+        for kvh in range(h_kv):
+            count = np.zeros(nb, np.int64)
+            for hh in range(G):
+                bh = b * h_q + kvh * G + hh
+                bit(bh, beta >> 1, beta >> 1)  # the diagonal walk
+                nq = nb - 1 - beta
+                for base in range(0, int(nq.max(initial=0)), 128):
+                    e = base + np.arange(128)
+                    ib = beta[:, None] + 1 + e[None, :]
+                    live = e[None, :] < nq[:, None]
+                    ibc = np.where(live, ib, 0)
+                    on = live & bit(bh, ibc >> 1, (beta[:, None] >> 1) + 0 * ibc)
+                    assert np.all(ib[on] < nb)
+                    count += on.sum(axis=1)
+                    assert count.max(initial=0) <= 512
+                    count[count > 512 - 128] = 0
+
+
+def xattn_estimator_addresses(n, batch, h_q, h_kv, d):
+    """Cell and selection kernels: every Q / K row they load, every workspace
+    entry written and read, every output word (stride 16, block 128)."""
+    nC, nI = n // 16, -(-n // 128)
+    words = (nI + 31) >> 5
+    n_rt = -(-nC // 32)
+    for rt in range(n_rt):
+        A = np.minimum(rt * 32 + np.arange(32), nC - 1)
+        rows = 16 * A[:, None] + np.arange(16)[None, :]
+        assert rows.min() >= 0 and rows.max() < n
+        for ct in range(rt + 1):
+            C = np.minimum(ct * 32 + np.arange(32), nC - 1)
+            krows = 16 * C[:, None] + 15 - np.arange(16)[None, :]
+            assert krows.min() >= 0 and krows.max() < n
+            # reduction: thread t < 128 owns cell row rt*32 + t/4, key block 4*ct + t%4
+            Aw = rt * 32 + np.arange(128) // 4
+            Jw = 4 * ct + np.arange(128) % 4
+            keep = (Aw < nC) & (Jw < nI)
+            assert np.all(Jw[keep] < nI) and np.all(Aw[keep] < nC)
+    # the selection reads (A, J) for A in block I, J <= I: written by tile
+    # ct = J // 4 <= rt = A // 32 of the cell kernel
+    for I in range(nI):
+        A = np.arange(I * 8, min(I * 8 + 8, nC))
+        J = np.arange(I + 1)
+        assert np.all((J[None, :] // 4) <= (A[:, None] // 32))
+        assert I + 1 <= 1024 and words <= 1024 // 32
+    cell = batch * h_q * nC * nI
+    assert ((batch * h_q - 1) * nC + nC - 1) * nI + nI - 1 < cell
+    assert d % 16 == 0 and d >= 64
+    # (mass << 10 | 1023 - J) keys: mass <= 8.001 * 2^50 fits above 10 index bits
+    assert (int(8.001 * 2 ** 50) << 10) < 2 ** 64
+
+
+@pytest.mark.parametrize("n,batch,h_q,h_kv", [(4160, 2, 4, 1), (8192, 1, 16, 2), (131072, 1, 2, 1)])
+def test_block_selection_in_bounds(n, batch, h_q, h_kv):
+    rng = np.random.default_rng(42 + n)
+    if n <= 8192:
+        block_selection_walks(n, batch, h_q, h_kv, 0.6, rng)
+    xattn_estimator_addresses(n, batch, h_q, h_kv, 128)
