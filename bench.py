@@ -257,6 +257,10 @@ def main():
     ap.add_argument("--topp", default=None, metavar="P_V,P_S",
                     help="estimate with top-p budgets (vs_estimate_index_topp) at these mass "
                          "fractions, the workload's budgets as caps")
+    ap.add_argument("--estimator", choices=("vs", "xattn"), default="vs",
+                    help="vs: the Vertical-Slash index (default); xattn: XAttention block "
+                         "selection (vs_estimate_index_xattn, block 128, stride 16)")
+    ap.add_argument("--threshold", type=float, default=0.9, help="XAttention selection threshold")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -275,6 +279,8 @@ def main():
             raise SystemExit("--topp takes P_V,P_S")
     if topp is not None and args.workload == 4:
         raise SystemExit("--topp is for the contiguous workloads")
+    if args.estimator == "xattn" and (topp is not None or args.workload in (4, 5)):
+        raise SystemExit("--estimator xattn takes one contiguous segment (workloads 1-3), no --topp")
 
     pool = None
     if args.copy_probe:
@@ -283,7 +289,7 @@ def main():
         t0 = time.time()
         prob = workloads.make_problem(args.workload)
         log(f"inputs {prob.name}: n={prob.n} in {time.time() - t0:.1f} s")
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and args.estimator == "vs":
             pool = OraclePool(prob, topp, min(CPU_SHARE, os.cpu_count() or 1))
 
     import torch
@@ -313,6 +319,7 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
     Hq, d = prob.h_q, prob.d
     stream = torch.cuda.current_stream(dev)
     worker = args.workload == 4
+    xattn = args.estimator == "xattn"
     if not worker:
         q, k, v, do = (t.to(dev) for t in (prob.q, prob.k, prob.v, prob.do))
         o = torch.empty_like(q)
@@ -322,6 +329,8 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
         dv = torch.empty_like(dk)
 
         def estimate():
+            if xattn:
+                return vs.estimate_index_xattn(q, k, args.threshold)[0]
             if topp is None:
                 return vs.estimate_index(q, k, prob.v_budget, prob.s_budget, cu)
             return vs.estimate_index_topp(q, k, prob.v_budget, prob.s_budget, [topp[0]] * Hq,
@@ -405,10 +414,16 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
                 ev[2].record(stream)
 
     lists = [(a.numpy(), b.numpy()) for a, b in idx.lists()]
-    ent_heads = accounting.executed_area(lists, cu, Hq, row_blocks=row_blocks)
-    ent = int(ent_heads.sum())
-    split = accounting.executed_split(lists, cu, Hq, row_blocks=row_blocks)
-    entries = {"all": ent, "slash": int(split["slash"].sum()), "vertical": int(split["vertical"].sum())}
+    if xattn:
+        # block selection: every entry is walked by the block-tile path of the
+        # query-major kernels and the slash dK/dV kernel
+        ent = int(accounting.block_selection_area(idx.block_selection(prob.n).numpy(), prob.n).sum())
+        entries = {"all": ent, "slash": ent, "vertical": 0}
+    else:
+        ent_heads = accounting.executed_area(lists, cu, Hq, row_blocks=row_blocks)
+        ent = int(ent_heads.sum())
+        split = accounting.executed_split(lists, cu, Hq, row_blocks=row_blocks)
+        entries = {"all": ent, "slash": int(split["slash"].sum()), "vertical": int(split["vertical"].sum())}
     dense = accounting.dense_causal_area(cu, row_positions=row_pos) * Hq
     log(f"index: executed entries {ent} of {dense} causal ({ent / dense:.4f})")
 
@@ -473,6 +488,12 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
             rec.update(own_tflop=round(own / 1e12, 4), own_tflops=round(own / (ms_step * 1e-3) / 1e12, 2),
                        own_frac=round(own / (ms_step * 1e-3) / 1e12 / peak, 4),
                        issued_tflops=round(issued / (ms_step * 1e-3) / 1e12, 2))
+        if name == "vs_xa_cells":
+            # causal cell logits: 16 sampled products of d per cell, nC (nC + 1) / 2 cells per head
+            nC = prob.n // 16
+            own = 2 * 16 * d * (nC * (nC + 1) // 2) * Hq
+            rec.update(own_tflop=round(own / 1e12, 4), own_tflops=round(own / (ms_step * 1e-3) / 1e12, 2),
+                       own_frac=round(own / (ms_step * 1e-3) / 1e12 / peak, 4))
         per_kernel[name] = rec
 
     # Roofline of the dominant kernel (largest time per step): its own share
@@ -508,8 +529,9 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
     wl.update({"h_q": Hq, "h_kv": prob.h_kv, "head_dim": d, "block": 64,
                "v_budget": prob.v_budget[0] if len(set(prob.v_budget)) == 1 else list(prob.v_budget),
                "s_budget": prob.s_budget[0] if len(set(prob.s_budget)) == 1 else list(prob.s_budget),
-               "estimator": "fixed budgets" if topp is None else
-               f"top-p p_v={topp[0]} p_s={topp[1]} (budgets as caps)",
+               "estimator": (f"XAttention block selection, block 128, stride 16, threshold {args.threshold}"
+                             if xattn else "fixed budgets" if topp is None else
+                             f"top-p p_v={topp[0]} p_s={topp[1]} (budgets as caps)"),
                "executed_entries": ent, "slash_entries": entries["slash"],
                "vertical_entries": entries["vertical"], "causal_entries": dense,
                "density": round(ent / dense, 5), "phases_ms": {k_: round(v_, 4) for k_, v_ in phases.items()},

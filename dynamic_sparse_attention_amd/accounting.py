@@ -89,3 +89,17 @@ def dense_causal_area(cu_seqlens: Sequence[int], row_positions: Optional[np.ndar
     rp = np.asarray(row_positions, dtype=np.int64)
     seg = np.searchsorted(np.asarray(cu_seqlens), rp, side="right") - 1
     return int((rp - np.asarray(cu_seqlens, dtype=np.int64)[seg] + 1).sum())
+
+
+def block_selection_area(sel: np.ndarray, n: int, blk: int = 128) -> np.ndarray:
+    """Valid entries per row of a block selection sel [..., nI, nI] (bool) of
+    one n-token segment: a selected block J < I adds rows(I) x blk entries, a
+    selected diagonal block its causal triangle rows(I) (rows(I) + 1) / 2,
+    rows(I) = min(blk, n - blk I).  Returns int64 [...] (e.g. per head)."""
+    sel = np.asarray(sel, dtype=bool)
+    nI = sel.shape[-1]
+    rows = np.minimum(blk, n - blk * np.arange(nI, dtype=np.int64))
+    below = np.tril(np.ones((nI, nI), dtype=bool), -1)
+    off = (sel & below).sum(axis=-1).astype(np.int64)           # [..., nI] blocks J < I
+    diag = np.diagonal(sel, axis1=-2, axis2=-1).astype(np.int64)
+    return (off * rows * blk + diag * rows * (rows + 1) // 2).sum(axis=-1)

@@ -290,6 +290,14 @@ def test_executed_area_matches_oracle():
     ref = [int(oracle.dense_mask(rows, np.arange(n), [0, n], idx, h).sum()) for h in range(2)]
     assert got.tolist() == ref
     assert accounting.dense_causal_area([0, n], rows) == oracle.dense_causal_area(rows, [0, n])
+    # a block selection (128-token blocks, ragged last block): the oracle's mask count
+    n, nI = 128 * 5 + 64, 6
+    sel = (rng.random((2, nI, nI)) < 0.5) & np.tril(np.ones((nI, nI), bool))
+    e = np.zeros(0, np.int64)
+    bidx = {(h, 0): (e, e, (128, sel[h])) for h in range(2)}
+    pos = np.arange(n)
+    ref = [int(oracle.dense_mask(pos, pos, [0, n], bidx, h).sum()) for h in range(2)]
+    assert accounting.block_selection_area(sel, n).tolist() == ref
 
 
 def test_xattn_and_block_selection_validation(abi):

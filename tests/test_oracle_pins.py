@@ -616,7 +616,8 @@ def test_x1_antidiagonal_sampling_one_hot():
     (16A + u, 16C + 15 - u) of that cell, where it is scale / 16."""
     n, d, S = 64, 8, 16
     for r0, c0, hit in ((17, 30, True), (17, 17, False), (35, 12, True), (35, 3, False),
-                        (0, 15, True), (15, 0, True), (20, 20, False), (63, 48, True)):
+                        (0, 15, True), (15, 0, True), (20, 20, False), (63, 48, True),
+                        (3, 28, True)):  # on an anti-diagonal, but of a cell above the diagonal (X3)
         q = np.zeros((n, d))
         k = np.zeros((n, d))
         q[r0, 3] = 1.0
