@@ -49,35 +49,107 @@ ENTRY_KIND = {"vs_fwd": "all", "vs_bwd_dq": "all", "vs_bwd_dkdv_slash": "slash",
 
 # HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE, each scaled by what the same counter reads for a plain copy of
-# known size), keyed by kernel, with a digest of the kernel sources they were
-# taken from: the figure is reported only while the sources are unchanged.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen2.5-3b-layer-n128k.json")
+# known size) are kept per workload in profiles/hbm_traffic_<workload>.json,
+# each kernel's figure with a digest of its sources: it is reported only while
+# they are unchanged.
 
 # Host cores the CPU baseline may use on the GPU machine (its CPU share).
 CPU_SHARE = 16
 
 
-def source_digest():
-    h = hashlib.sha256()
+# The translation unit of each traced kernel (bf16 path); the rest are in
+# vs_estimate.hip (vs_est_*) or vs_misc.hip.
+KERNEL_SOURCE = {"vs_fwd": "vs_fwd.hip", "vs_bwd_dq": "vs_bwd_dq.hip", "vs_bwd_dkdv_slash": "vs_bwd_kv.hip",
+                 "vs_bwd_dkdv_cols": "vs_bwd_kv.hip", "vs_xa_cells": "vs_xattn.hip",
+                 "vs_xa_select": "vs_xattn.hip"}
+
+
+def kernel_digest(kernel):
+    """SHA-256 of a kernel's translation unit and the local headers it
+    includes (recursively), so that a counter figure stays valid exactly as
+    long as the code it was taken from."""
     csrc = os.path.join(ROOT, "dynamic_sparse_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+    tu = KERNEL_SOURCE.get(kernel, "vs_estimate.hip" if kernel.startswith("vs_est_") else "vs_misc.hip")
+    seen, stack = set(), [tu]
+    while stack:
+        f = stack.pop()
+        if f in seen or not os.path.exists(os.path.join(csrc, f)):
+            continue
+        seen.add(f)
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            for line in fh:
+                line = line.strip()
+                if line.startswith("#include \""):
+                    stack.append(line.split("\"")[1])
+    h = hashlib.sha256()
+    for f in sorted(seen):
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
 def measured_traffic(kernel, workload):
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")) as fh:
             data = json.load(fh)
     except (OSError, ValueError):
         return None
-    if data.get("source_sha256") != source_digest() or data.get("workload") != workload:
-        return None
     ent = data.get("kernels", {}).get(kernel)
-    return None if ent is None else int(ent["hbm_bytes_per_launch"])
+    if data.get("workload") != workload or ent is None or ent.get("source_sha256") != kernel_digest(kernel):
+        return None
+    return int(ent["hbm_bytes_per_launch"])
+
+
+# rocprofv3 kernel names -> traced names
+_PROF_NAMES = (("vs_fwd_rows_kernel", "vs_fwd"), ("vs_bwd_dq_rows_kernel", "vs_bwd_dq"),
+               ("vs_bwd_kv_slash_bf16_kernel", "vs_bwd_dkdv_slash"), ("vs_bwd_kv_cols_bf16_kernel", "vs_bwd_dkdv_cols"),
+               ("vs_delta_kernel", "vs_delta"), ("vs_est_pass1", "vs_est_pass1"), ("vs_est_pass2", "vs_est_pass2"),
+               ("vs_est_topk", "vs_est_topk"), ("vs_est_combine", "vs_est_combine"), ("vs_lse_log2", "vs_lse_log2"),
+               ("vs_prep_vertical", "vs_prep_vertical"), ("vs_group_share", "vs_group_share"),
+               ("vs_xa_cells_kernel", "vs_xa_cells"), ("vs_xa_select_kernel", "vs_xa_select"))
+
+
+def write_traffic(run_dir, workload):
+    """profiles/hbm_traffic_<workload>.json from four rocprofv3 counter runs
+    under run_dir (fetch, write: the benchmark; copy_fetch, copy_write: the
+    copy probe): per kernel the mean FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by the bytes the copy moves per KiB the same
+    counter reads for it, and the kernel's source digest."""
+    import collections
+    import csv
+
+    def load(sub):
+        agg = collections.defaultdict(list)
+        with open(os.path.join(run_dir, sub, "run_counter_collection.csv")) as fh:
+            for r in csv.DictReader(fh):
+                agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return agg
+
+    def mean(xs):
+        return sum(xs) / len(xs)
+
+    fetch, write = load("fetch"), load("write")
+    copy = "__amd_rocclr_copyBuffer"
+    cf = [v for k, v in load("copy_fetch").items() if copy in k][0]
+    cw = [v for k, v in load("copy_write").items() if copy in k][0]
+    f_fetch = (1 << 30) / (mean(cf) * 1024)
+    f_write = (1 << 30) / (mean(cw) * 1024)
+    kern = {}
+    for k in fetch:
+        name = next((b for a, b in _PROF_NAMES if a in k), None)
+        if name is None or k not in write:
+            continue
+        fk, wk = mean(fetch[k]), mean(write[k])
+        kern[name] = {"fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+                      "hbm_bytes_per_launch": int(fk * 1024 * f_fetch + wk * 1024 * f_write),
+                      "source_sha256": kernel_digest(name)}
+    out = {"workload": workload, "copy_factor_fetch": round(f_fetch, 4), "copy_factor_write": round(f_write, 4),
+           "kernels": kern}
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def copy_probe(dev):
@@ -263,7 +335,14 @@ def main():
     ap.add_argument("--threshold", type=float, default=0.9, help="XAttention selection threshold")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--write-traffic", metavar="RUN_DIR", default=None,
+                    help="no GPU: write profiles/hbm_traffic_<workload>.json from rocprofv3 counter runs "
+                         "RUN_DIR/{fetch,write,copy_fetch,copy_write}")
     args = ap.parse_args()
+    if args.write_traffic:
+        import workloads
+        write_traffic(args.write_traffic, workloads.WORKLOADS[args.workload]["name"])
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
