@@ -65,12 +65,12 @@ def xattn_block_scores(q_h, k_h, a, e, scale, stride=16, block=128):
     nC = z.shape[0]
     cpb = block // stride                         # cells per block side
     nI = -(-nC // cpb)
-    s = np.zeros((nI, nI))
-    for I in range(nI):
-        rows = p[I * cpb:(I + 1) * cpb]
-        for J in range(I + 1):
-            s[I, J] = rows[:, J * cpb:(J + 1) * cpb].sum()
-    return s
+    # s[I, J] = sum of p over the cells of block (I, J): pad the cell grid to
+    # whole blocks with zero probability and sum each cpb x cpb tile
+    padded = np.zeros((nI * cpb, nI * cpb))
+    padded[:nC, :nC] = p
+    s = padded.reshape(nI, cpb, nI, cpb).sum(axis=(1, 3))
+    return np.tril(s)
 
 
 def estimate_index_xattn(q, k, cu_seqlens, block=128, stride=16, threshold=0.9, scale=None,

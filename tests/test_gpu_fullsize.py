@@ -22,7 +22,8 @@ import torch
 
 import oracle
 import workloads
-from vs_cases import check_close, index_parity, lists_for_gpu, log, np64
+from vs_cases import (check_close, check_xattn_row, index_parity, lists_for_gpu, log, np64,
+                      pack_block_selection)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1200)]
 
@@ -433,5 +434,108 @@ def test_fullsize_striped_worker():
         log(f"  ring group {g}: sum_u <dV_u,V_u>={lhs_v[g]:.6e} sum delta={rhs:.6e} rel={relv:.2e}")
         if relv > 1e-4:
             errs.append(f"ring group {g}: dV identity off by {relv:.2e}")
+    errs = [e for e in errs if e]
+    assert not errs, errs
+
+
+def test_fullsize_xattn():
+    """XAttention (block 128, stride 16, threshold 0.9) at N = 131072 on
+    workload 3's inputs, in bench.py --estimator xattn's launch configuration.
+
+    Estimator: for every Q head and query block, the device's count and
+    bitmap equal the integer decision on its own scores; for one Q head per
+    KV group, every block score against the oracle's and every selection
+    against the oracle's (certified near ties allowed).  Attention on a block
+    selection: those two heads take the oracle's selection, the others seeded
+    random selections of 90 % of the causal blocks (host-drawn); O, LSE and
+    dQ of sampled query blocks of the two heads against the oracle, dK and
+    dV of the last key blocks (read only by the last query blocks) against
+    the oracle over all heads, and the group identities."""
+    dev = _dev()
+    thr = 0.9
+    log("full-size XAttention: drawing inputs (workload 3)")
+    prob = workloads.make_problem(3)
+    n, hq, hkv = prob.n, prob.h_q, prob.h_kv
+    nI = n // 128
+    G = hq // hkv
+    cu = prob.cu_seqlens
+    gq, gk, gv, gdo = (t.to(dev) for t in (prob.q, prob.k, prob.v, prob.do))
+    log("  GPU estimator")
+    gidx, gcnt, gsc = vs.estimate_index_xattn(gq, gk, thr, return_scores=True)
+    torch.cuda.synchronize()
+    gsel = gidx.block_selection(n).numpy()
+    gcnt = gcnt[0].cpu().numpy()
+    gsc = gsc[0].cpu().numpy()
+    del gidx
+    # every head: the device's decision on its own scores (oracle count unknown: pass its own)
+    from vs_cases import xattn_count_int
+    for h in range(hq):
+        for I in range(nI):
+            kk, order = xattn_count_int(gsc[h, I, :I + 1], thr)
+            assert gcnt[h, I] == kk, (h, I, int(gcnt[h, I]), kk)
+            want = np.zeros(nI, bool)
+            want[order[:kk]] = True
+            assert np.array_equal(gsel[h, I], want), (h, I)
+    heads = [grp * G for grp in range(hkv)]
+    q64, k64 = np64(prob.q[0]), np64(prob.k[0])
+    osel = {}
+    for h in heads:
+        log(f"  oracle block scores, head {h}")
+        out, osc, ocnt = oracle.estimate_index_xattn(q64[:, h:h + 1], k64[:, h // G:h // G + 1], cu, 128, 16,
+                                                     thr, return_scores=True)
+        worst, flips, swaps = 0.0, 0, 0
+        for I in range(nI):
+            e, f, w, _ = check_xattn_row((h, I), osc[(0, 0)][I, :I + 1], gsc[h, I, :I + 1], gsel[h, I],
+                                         gcnt[h, I], int(ocnt[(0, 0)][I]), thr)
+            worst, flips, swaps = max(worst, e), flips + f, swaps + w
+        osel[h] = out[(0, 0)][2][1]
+        log(f"  head {h}: score err/(1+s) max {worst:.2e}, flips {flips}, swaps {swaps}; "
+            f"{int(osel[h].sum())} of {nI * (nI + 1) // 2} causal blocks selected")
+    del gsc, gsel
+
+    rng = np.random.default_rng(prob.seed + 77)
+    tril = np.tril(np.ones((nI, nI), bool))
+    sels = [osel[h] if h in osel else (rng.random((nI, nI)) < 0.9) & tril for h in range(hq)]
+    mask = pack_block_selection(sels, nI).to(dev)
+    zeros = torch.zeros(hq + 1, dtype=torch.int32, device=dev)
+    one = torch.zeros(1, dtype=torch.int32, device=dev)
+    idx = vs.VsIndexT(zeros, one, zeros, one, 0, 0, mask, 128)
+    log("  GPU forward + backward on the block selection")
+    o, lse = vs.sparse_attn_fwd(gq, gk, gv, idx)
+    dq, dk, dv = vs.sparse_attn_bwd(gq, gk, gv, o, gdo, lse, idx)
+    torch.cuda.synchronize()
+    empty = np.zeros(0, np.int64)
+    cols = np.arange(n)
+    v64 = np64(prob.v[0])
+    errs = []
+    # O, LSE, dQ of sampled query blocks of the two oracle-selected heads
+    blocks = _sample_blocks(n // 64, np.random.default_rng(prob.seed))
+    rows = _rows_of_blocks(blocks)
+    sub = {(i, 0): (empty, empty, (128, sels[h])) for i, h in enumerate(heads)}
+    log(f"  oracle on {len(blocks)} sampled query blocks of heads {heads}")
+    q_r, do_r = q64[rows][:, heads], np64(prob.do[0, rows][:, heads])
+    O, L = oracle.attn_fwd_support(q_r, k64, v64, rows, cols, cu, sub)
+    D = oracle.bwd_delta(O, do_r)
+    dq_o, _, _ = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, cols, cu, sub)
+    bq, _, _ = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, sub, support=True)
+    rt = torch.from_numpy(rows).to(dev)
+    ht = torch.tensor(heads, device=dev)
+    errs += [check_close("xattn O (sampled)", O, np64(o[0, rt][:, ht]), "bf16", "o"),
+             check_close("xattn LSE (sampled)", L, np64(lse[0][ht][:, rt]), "bf16"),
+             check_close("xattn dQ (sampled)", dq_o, np64(dq[0, rt][:, ht]), "bf16", "grad", bq)]
+    # dK / dV of the last TAIL key blocks from the last TAIL query blocks, all heads
+    rows = _rows_of_blocks(range(n // 64 - TAIL, n // 64))
+    full = {(h, 0): (empty, empty, (128, sels[h])) for h in range(hq)}
+    log(f"  oracle on the last {TAIL} query blocks, all heads")
+    q_r, do_r = q64[rows], np64(prob.do[0, rows])
+    O, L = oracle.attn_fwd_support(q_r, k64, v64, rows, cols, cu, full)
+    D = oracle.bwd_delta(O, do_r)
+    _, dk_o, dv_o = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, cols, cu, full)
+    _, bk, bv = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, full, support=True)
+    rt = torch.from_numpy(rows).to(dev)
+    errs += [check_close("xattn dK (tail keys)", dk_o[rows], np64(dk[0, rt]), "bf16", "grad", bk[rows]),
+             check_close("xattn dV (tail keys)", dv_o[rows], np64(dv[0, rt]), "bf16", "grad", bv[rows])]
+    errs += _group_identity("xattn", dq[0], gq[0], dk[0], gk[0], hq, hkv)
+    errs += _dv_identity("xattn", dv[0], gv[0], o[0], gdo[0], hq, hkv)
     errs = [e for e in errs if e]
     assert not errs, errs

@@ -15,7 +15,8 @@ import torch
 
 import oracle
 import workloads
-from vs_cases import check_close, log, np64
+from vs_cases import (XA_SCORE_RTOL, check_close, check_xattn_row, log, np64, pack_block_selection,
+                      xattn_count_int)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,49 +39,13 @@ XA_CASES = {
     "w2-n8192-gqa8-t0.9": (dict(wid=2, n=8192, h_q=8, h_kv=1), 0.9),
 }
 
-# Device block scores: fp32 sums of at most 64 cell probabilities, each from
-# an exp2 of a difference of fp32 log-sum-exps of dot products accumulated in
-# fp32 over 16 x d terms: relative error a few 2^-20 in practice.  The bar is
-# 1e-4 * (1 + s) (s <= 8, the number of cell rows of a block).
-SCORE_RTOL = 1e-4
-
-
-def _count_int(scores_f32, t):
-    """The selection count in the device's integer arithmetic, recomputed from
-    the device's fp32 scores: masses rint(s * 2^50), target
-    ceil(rint(t * 2^24) * total / 2^24), ties to the lowest key block."""
-    tc = np.float32(t)
-    tc = np.float32(min(tc, np.float32(1.0))) if tc > 0 else np.float32(0.0)
-    tq = int(np.rint(np.float64(tc) * 2.0 ** 24))
-    m = [int(x) for x in np.rint(np.asarray(scores_f32, np.float32).astype(np.float64) * 2.0 ** 50)]
-    total = sum(m)
-    order = sorted(range(len(m)), key=lambda j: (-m[j], j))
-    if tq == 0 or total == 0:
-        return 0, order
-    need = -(-(tq * total) // (1 << 24))
-    run = 0
-    for kk, j in enumerate(order):
-        run += m[j]
-        if run >= need:
-            return kk + 1, order
-    return len(m), order
-
-
 def _oracle_case(prob, threshold):
     q, k = np64(prob.q[0]), np64(prob.k[0])
     return oracle.estimate_index_xattn(q, k, prob.cu_seqlens, 128, 16, threshold, return_scores=True)
 
 
 def pack_selection(sel_by_head, nI, dev):
-    """Host bitmap of selections sel[h] [nI, nI] (batch 1): bit J % 32 of word
-    J // 32 of row h * nI + I."""
-    words = (nI + 31) // 32
-    out = np.zeros((len(sel_by_head) * nI, words), np.uint32)
-    for h, sel in enumerate(sel_by_head):
-        for I in range(nI):
-            for J in np.nonzero(sel[I])[0]:
-                out[h * nI + I, J // 32] |= np.uint32(1) << np.uint32(J % 32)
-    return torch.from_numpy(out.view(np.int32)).to(dev)
+    return pack_block_selection(sel_by_head, nI).to(dev)
 
 
 def block_index(mask, dev, h_q):
@@ -112,38 +77,11 @@ def test_xattn_estimator(name):
         s_o = osc[(h, 0)]
         sel_o = osel[(h, 0)][2][1]
         for I in range(nI):
-            so = s_o[I, :I + 1]
-            sg = gsc[h, I, :I + 1]
-            err = np.abs(sg.astype(np.float64) - so)
-            worst = max(worst, float((err / (1 + so)).max()))
-            assert np.all(err <= SCORE_RTOL * (1 + so)), (name, h, I, float(err.max()))
-            # 1. the device's decision, exactly, from its own scores
-            kk, order = _count_int(sg, thr)
-            assert gcnt[h, I] == kk, (name, h, I, int(gcnt[h, I]), kk)
-            want = np.zeros(nI, bool)
-            want[np.asarray(order[:kk], np.int64)] = True
-            assert np.array_equal(gsel[h, I], want), (name, h, I, "bitmap")
-            # 2. against the fp64 oracle
-            ko = int(ocnt[(h, 0)][I])
-            if kk != ko:
-                srt = np.sort(so)[::-1]
-                cum = np.concatenate(([0.0], np.cumsum(srt)))
-                tot = cum[-1]
-                delta = 2 * err.sum() + 2.0 ** -24 * tot + 1e-12
-                tc = min(max(thr, 0.0), 1.0)
-                assert cum[kk] >= tc * tot - delta, (name, h, I, kk, ko)
-                assert kk == 0 or cum[kk - 1] < tc * tot + delta, (name, h, I, kk, ko)
-                flips += 1
-            ref = np.sort(np.lexsort((np.arange(so.size), -so))[:kk])
-            got = np.nonzero(gsel[h, I])[0]
-            if not np.array_equal(ref, got):
-                kth = np.sort(so)[::-1][kk - 1]
-                diff = np.setxor1d(ref, got)
-                tol = 2 * SCORE_RTOL * (1 + kth)
-                assert np.all(np.abs(so[diff] - kth) <= tol), (name, h, I, "non-tie mismatch")
-                swaps += diff.size // 2
-            if kk == ko and np.array_equal(ref, got):
-                assert np.array_equal(got, np.nonzero(sel_o[I])[0]), (name, h, I)
+            e, f, w, ref = check_xattn_row((name, h, I), s_o[I, :I + 1], gsc[h, I, :I + 1], gsel[h, I],
+                                           gcnt[h, I], int(ocnt[(h, 0)][I]), thr)
+            worst, flips, swaps = max(worst, e), flips + f, swaps + w
+            if not f and not w:
+                assert np.array_equal(ref, np.nonzero(sel_o[I])[0]), (name, h, I)
     log(f"  xattn {name}: score err/(1+s) max {worst:.2e}; counts exact; "
         f"certified boundary flips={flips}, near-tie swaps={swaps}")
 
@@ -241,9 +179,9 @@ def test_xattn_then_attention_batch2():
         osel, osc, _ = _oracle_case(p, 0.9)
         for h in range(4):
             err = np.abs(gsc[b, h].cpu().numpy().astype(np.float64) - osc[(h, 0)])
-            assert np.all(np.tril(err) <= SCORE_RTOL * (1 + osc[(h, 0)])), (b, h)
+            assert np.all(np.tril(err) <= XA_SCORE_RTOL * (1 + osc[(h, 0)])), (b, h)
             for I in range(nI):
-                kk, order = _count_int(gsc[b, h, I, :I + 1].cpu().numpy(), 0.9)
+                kk, order = xattn_count_int(gsc[b, h, I, :I + 1].cpu().numpy(), 0.9)
                 want = np.zeros(nI, bool)
                 want[np.asarray(order[:kk], np.int64)] = True
                 assert np.array_equal(gsel[b, h, I], want), (b, h, I)

@@ -156,3 +156,75 @@ def index_parity(name, o_index, o_scores, g_lists, g_vscore, g_sscore, prob, rel
                     swaps += extra.size
     log(f"  {name}: index sets match oracle, near-tie swaps={swaps}, max rel score err={vmax:.2e}")
     return swaps
+
+
+# XAttention block selection: the device scores are fp32 sums of at most 64
+# cell probabilities, each an exp2 of a difference of fp32 log-sum-exps of
+# dot products accumulated in fp32 over 16 x d terms (relative error a few
+# 2^-20 in practice); the bar is 1e-4 * (1 + s), s <= 8 the block's cell rows.
+XA_SCORE_RTOL = 1e-4
+
+
+def xattn_count_int(scores_f32, t):
+    """The XAttention selection count in the device's integer arithmetic,
+    recomputed from the device's fp32 scores of one query block: masses
+    rint(s * 2^50), target ceil(rint(t * 2^24) * total / 2^24), ties to the
+    lowest key block.  Returns (count, key blocks in selection order)."""
+    tc = np.float32(t)
+    tc = np.float32(min(tc, np.float32(1.0))) if tc > 0 else np.float32(0.0)
+    tq = int(np.rint(np.float64(tc) * 2.0 ** 24))
+    m = np.rint(np.asarray(scores_f32, np.float32).astype(np.float64) * 2.0 ** 50).astype(np.int64)
+    order = np.lexsort((np.arange(m.size), -m))
+    total = int(m.sum())
+    if tq == 0 or total == 0:
+        return 0, order
+    need = -(-(tq * total) // (1 << 24))
+    cum = np.cumsum(m[order])
+    return min(int(np.searchsorted(cum, need, side="left")) + 1, m.size), order
+
+
+def check_xattn_row(tag, so, sg, got_bits, cnt_dev, ko, thr):
+    """One query block I of a head: so = the oracle's fp64 scores of key
+    blocks 0..I, sg = the device's fp32 scores, got_bits = the device's
+    bitmap row (bool, all key blocks), cnt_dev its count, ko the oracle's
+    count.  Asserts the scores within XA_SCORE_RTOL, the device's count and
+    bitmap equal to the integer decision on its own scores, and the selection
+    equal to the oracle's except at a certified boundary flip or near tie.
+    Returns (relative score error, flips, swaps)."""
+    so = np.asarray(so, np.float64)
+    err = np.abs(np.asarray(sg, np.float64) - so)
+    assert np.all(err <= XA_SCORE_RTOL * (1 + so)), (tag, float(err.max()))
+    kk, order = xattn_count_int(sg, thr)
+    assert cnt_dev == kk, (tag, int(cnt_dev), kk)
+    want = np.zeros(got_bits.size, bool)
+    want[order[:kk]] = True
+    assert np.array_equal(got_bits, want), (tag, "bitmap")
+    flips = swaps = 0
+    if kk != ko:
+        srt = np.sort(so)[::-1]
+        cum = np.concatenate(([0.0], np.cumsum(srt)))
+        tot = cum[-1]
+        delta = 2 * err.sum() + 2.0 ** -24 * tot + 1e-12
+        tc = min(max(thr, 0.0), 1.0)
+        assert cum[kk] >= tc * tot - delta, (tag, kk, ko)
+        assert kk == 0 or cum[kk - 1] < tc * tot + delta, (tag, kk, ko)
+        flips = 1
+    ref = np.sort(np.lexsort((np.arange(so.size), -so))[:kk])
+    got = np.nonzero(got_bits)[0]
+    if not np.array_equal(ref, got):
+        kth = np.sort(so)[::-1][kk - 1]
+        diff = np.setxor1d(ref, got)
+        assert np.all(np.abs(so[diff] - kth) <= 2 * XA_SCORE_RTOL * (1 + kth)), (tag, "non-tie mismatch")
+        swaps = diff.size // 2
+    return float((err / (1 + so)).max(initial=0.0)), flips, swaps, ref
+
+
+def pack_block_selection(sels, nI):
+    """Host bitmap rows of block selections sels[r] [nI, nI] (bool), one per
+    (batch, Q head) in order: bit J % 32 of word J // 32 of row r * nI + I."""
+    words = (nI + 31) // 32
+    out = np.zeros((len(sels) * nI, words), np.uint32)
+    for r, sel in enumerate(sels):
+        I, J = np.nonzero(np.asarray(sel, bool))
+        np.bitwise_or.at(out, (r * nI + I, J // 32), (np.uint32(1) << (J % 32).astype(np.uint32)))
+    return torch.from_numpy(out.view(np.int32))
