@@ -283,10 +283,10 @@ EstWs est_ws(const Prob& c) {
   return w;
 }
 
-// XAttention estimate: per (batch, Q head) the log-sum-exp of every (cell
-// row, key block) and of every cell row (fp32, log2 domain).
+// XAttention estimate: per (batch, Q head) the log-sum-exp of every (key
+// block, cell row) (fp32, log2 domain).
 struct XaWs {
-  size_t cell, row, total;
+  size_t cell, total;
   int nC, nI;
 };
 XaWs xa_ws(const Prob& c) {
@@ -296,8 +296,6 @@ XaWs xa_ws(const Prob& c) {
   size_t off = 0;
   w.cell = off;
   off += align256((size_t)c.batch * c.h_q * w.nC * w.nI * 4);
-  w.row = off;
-  off += align256((size_t)c.batch * c.h_q * w.nC * 4);
   w.total = off;
   return w;
 }
@@ -501,7 +499,6 @@ vs_status vs_estimate_index_xattn(const vs_problem* p, const void* q, const void
   x.sl2 = c.scale * vs::kLog2e;
   char* base = static_cast<char*>(ws);
   x.cell_lse = reinterpret_cast<float*>(base + w.cell);
-  x.row_lse = reinterpret_cast<float*>(base + w.row);
   x.threshold = threshold;
   x.bmask = blk_mask;
   x.counts = counts;

@@ -12,8 +12,7 @@ struct XaParams {
   int batch, h_q, h_kv, n;  // n tokens per batch row (one segment)
   int nC, nI, words;        // cells, query blocks, bitmap words per row
   float sl2;                // scale * log2(e)
-  float* cell_lse;          // [batch, h_q, nC, nI] log2-domain LSE of (cell row, key block)
-  float* row_lse;           // [batch, h_q, nC] log2-domain LSE of the cell row
+  float* cell_lse;          // [batch, h_q, nI, nC] log2-domain LSE of (key block, cell row)
   float threshold;
   uint32_t* bmask;          // [batch, h_q, nI, words]
   int* counts;              // [batch, h_q, nI] or null

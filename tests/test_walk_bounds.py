@@ -323,41 +323,75 @@ def block_selection_walks(n, batch, h_q, h_kv, sel_p, rng):
 
 
 def xattn_estimator_addresses(n, batch, h_q, h_kv, d):
-    """Cell and selection kernels: every Q / K row they load, every workspace
-    entry written and read, every output word (stride 16, block 128)."""
+    """Cell and selection kernels: the (row tile, column tile) decode of the
+    triangle index, every Q / K row and channel a direct load fetches, every
+    LDS destination and operand read, every log-sum-exp written and read,
+    every output word (stride 16, block 128, 128 x 128 cell tiles, stages of
+    one sample offset and 64 channels)."""
     nC, nI = n // 16, -(-n // 128)
     words = (nI + 31) >> 5
-    n_rt = -(-nC // 32)
-    for rt in range(n_rt):
-        A = np.minimum(rt * 32 + np.arange(32), nC - 1)
-        rows = 16 * A[:, None] + np.arange(16)[None, :]
-        assert rows.min() >= 0 and rows.max() < n
-        for ct in range(rt + 1):
-            C = np.minimum(ct * 32 + np.arange(32), nC - 1)
-            krows = 16 * C[:, None] + 15 - np.arange(16)[None, :]
-            assert krows.min() >= 0 and krows.max() < n
-            # reduction: thread t < 128 owns cell row rt*32 + t/4, key block 4*ct + t%4
-            Aw = rt * 32 + np.arange(128) // 4
-            Jw = 4 * ct + np.arange(128) % 4
-            keep = (Aw < nC) & (Jw < nI)
-            assert np.all(Jw[keep] < nI) and np.all(Aw[keep] < nC)
-    # the selection reads (A, J) for A in block I, J <= I: written by tile
-    # ct = J // 4 <= rt = A // 32 of the cell kernel
+    nt = -(-nC // 128)
+    per_head = nt * (nt + 1) // 2
+    stage_bytes = 128 * 128          # one operand of a stage: 128 rows x 64 channels bf16
+    seen = set()
+    for t in range(per_head):
+        ta = int((np.sqrt(np.float32(8.0) * np.float32(t) + np.float32(1.0)) - np.float32(1.0)) * np.float32(0.5))
+        while ta * (ta + 1) // 2 > t:
+            ta -= 1
+        while (ta + 1) * (ta + 2) // 2 <= t:
+            ta += 1
+        tc = t - ta * (ta + 1) // 2
+        assert 0 <= tc <= ta < nt
+        seen.add((ta, tc))
+    assert len(seen) == per_head
+    lane = np.arange(64)
+    for A0 in {0, 128 * (nt - 1)}:
+        for st in range(16 * d // 64):
+            u, ch0 = st // (d // 64), 64 * (st % (d // 64))
+            for w in range(4):
+                for t0 in range(8):
+                    tt = w * 8 + t0
+                    row = 8 * (tt & 15) + lane // 8
+                    chunk = (lane & 7) ^ ((row >> 1) & 7)
+                    cell = np.minimum(A0 + row, nC - 1)
+                    tok = 16 * cell + u if tt < 16 else 16 * cell + 15 - u
+                    assert tok.min() >= 0 and tok.max() < n
+                    assert ch0 + 8 * chunk.max() + 8 <= d
+                    dst = 1024 * (tt & 15) + 16 * lane
+                    assert dst.max() + 16 <= stage_bytes
+                    # the LDS slot a lane fills holds the chunk the readers expect
+                    r = dst // 128
+                    slot = (dst % 128) // 16
+                    assert np.array_equal(r, row) and np.array_equal(slot ^ ((r >> 1) & 7), chunk)
+    # operand reads: rows < 128, chunk (2 ks + hl) ^ ((r / 2) % 8) inside a row
+    r = np.arange(128)[:, None]
+    c = np.arange(8)[None, :]
+    off = r * 128 + 16 * (c ^ ((r >> 1) & 7))
+    assert off.max() + 16 <= stage_bytes and len(np.unique(off)) == off.size
+    # conflict-free: each 16-lane pass (16 consecutive rows, one chunk) hits 16 bank groups
+    for r0 in range(0, 128, 16):
+        for cc in range(8):
+            rows = np.arange(r0, r0 + 16)
+            groups = ((rows * 128 + 16 * (cc ^ ((rows >> 1) & 7))) // 16) % 16
+            assert len(set(groups.tolist())) == 16
+    # epilogue writes ((bh nI + J) nC + A) for A < nC, J < nI; the selection
+    # reads (bh nI + J) nC + 8 I + a for J <= I, 8 I + a < nC
+    cell = batch * h_q * nI * nC
+    assert ((batch * h_q - 1) * nI + nI - 1) * nC + nC - 1 < cell
     for I in range(nI):
-        A = np.arange(I * 8, min(I * 8 + 8, nC))
-        J = np.arange(I + 1)
-        assert np.all((J[None, :] // 4) <= (A[:, None] // 32))
         assert I + 1 <= 1024 and words <= 1024 // 32
-    cell = batch * h_q * nC * nI
-    assert ((batch * h_q - 1) * nC + nC - 1) * nI + nI - 1 < cell
-    assert d % 16 == 0 and d >= 64
+        na = min(8, nC - 8 * I)
+        assert na >= 1 and 8 * I + na <= nC
+    assert d % 64 == 0
     # (mass << 10 | 1023 - J) keys: mass <= 8.001 * 2^50 fits above 10 index bits
     assert (int(8.001 * 2 ** 50) << 10) < 2 ** 64
 
 
-@pytest.mark.parametrize("n,batch,h_q,h_kv", [(4160, 2, 4, 1), (8192, 1, 16, 2), (131072, 1, 2, 1)])
+@pytest.mark.parametrize("n,batch,h_q,h_kv", [(1024, 1, 2, 1), (4160, 2, 4, 1), (8192, 1, 16, 2),
+                                              (131072, 1, 2, 1)])
 def test_block_selection_in_bounds(n, batch, h_q, h_kv):
     rng = np.random.default_rng(42 + n)
     if n <= 8192:
         block_selection_walks(n, batch, h_q, h_kv, 0.6, rng)
-    xattn_estimator_addresses(n, batch, h_q, h_kv, 128)
+    for d in (64, 128):
+        xattn_estimator_addresses(n, batch, h_q, h_kv, d)
