@@ -395,3 +395,4 @@ def test_block_selection_in_bounds(n, batch, h_q, h_kv):
         block_selection_walks(n, batch, h_q, h_kv, 0.6, rng)
     for d in (64, 128):
         xattn_estimator_addresses(n, batch, h_q, h_kv, d)
+
