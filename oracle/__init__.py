@@ -18,6 +18,8 @@ definitions on the pages:
   "Computation Cost Estimation";
 * the XAttention block estimator (anti-diagonal block scores, threshold
   selection) — the paper note's appendix, baseline settings, item 2;
+* the MoBA block gate (block means, per-query top-k with the own block) —
+  the same appendix, item 1;
 * the RoPE relative-position property — MTraining Theorem 3.1 and the paper
   note's Appendix B.2, Eq. 14.
 
@@ -26,13 +28,14 @@ steps are listed in the repository's design notes.
 """
 from .index import (capacities, window_probs, window_scores, select_topk, estimate_index,
                     topp_count, estimate_index_topp,
-                    dense_mask, block_selected)
+                    dense_mask, block_selected, row_block_selected)
 from .attention import (attn_fwd_dense, attn_bwd_dense, attn_fwd_support, attn_bwd_support,
                         lse_merge, row_groups, support_candidates, bwd_delta,
                         bwd_rounding_bounds)
 from .accounting import mask_area_bruteforce, mask_area_formula, dense_causal_area
-from . import xattn
+from . import xattn, moba
 from .xattn import antidiag_logits, xattn_block_scores, estimate_index_xattn
+from .moba import block_means, gate_scores, select_blocks, estimate_index_moba
 
 __all__ = [
     "capacities", "window_probs", "window_scores", "select_topk", "estimate_index",
@@ -40,5 +43,6 @@ __all__ = [
     "lse_merge", "row_groups", "support_candidates", "bwd_delta", "bwd_rounding_bounds",
     "mask_area_bruteforce",
     "mask_area_formula", "dense_causal_area", "xattn", "antidiag_logits", "xattn_block_scores",
-    "estimate_index_xattn", "block_selected",
+    "estimate_index_xattn", "block_selected", "row_block_selected", "moba", "block_means",
+    "gate_scores", "select_blocks", "estimate_index_moba",
 ]

@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .index import block_selected, dense_mask, _segment_of
+from .index import block_selected, dense_mask, row_block_selected, _segment_of
 
 
 def _f64(x):
@@ -115,9 +115,10 @@ def support_candidates(seg, beta, rows_max, cols_pos, cu_seqlens, index_hs, bloc
     """Column indices (into cols_pos) that may hold an entry for rows of (seg, beta).
 
     The candidates are the key blocks beta - g for selected g, the selected
-    vertical columns m <= rows_max, and the keys of the blocks selected for
-    the rows' block in the optional block selection, restricted to the
-    call's columns.  The caller evaluates the exact mask on them.
+    vertical columns m <= rows_max, the keys of the blocks selected for the
+    rows' block in the optional block selection, and the keys (<= rows_max)
+    of the blocks any row of the block picked in the optional per-row block
+    selection, restricted to the call's columns.  The caller evaluates the exact mask on them.
     """
     cols_pos = np.asarray(cols_pos)
     a, e = int(cu_seqlens[seg]), int(cu_seqlens[seg + 1])
@@ -136,6 +137,13 @@ def support_candidates(seg, beta, rows_max, cols_pos, cu_seqlens, index_hs, bloc
             for J in np.nonzero(np.asarray(sel[I]))[0]:
                 lo = a + int(J) * bb
                 want.append(np.arange(lo, min(lo + bb, e)))
+    if len(index_hs) > 3 and index_hs[3] is not None:
+        bb, sel = index_hs[3]
+        sel = np.asarray(sel, dtype=bool)
+        rows = sel[beta * block:min((beta + 1) * block, sel.shape[0])]
+        for J in np.nonzero(rows.any(axis=0))[0]:
+            lo = a + int(J) * bb
+            want.append(np.arange(lo, min(lo + bb, e, rows_max + 1)))
     want.append(np.asarray(iv)[np.asarray(iv) <= rows_max])
     want = np.unique(np.concatenate(want)) if want else np.zeros(0, np.int64)
     idx = np.searchsorted(cols_pos, want)
@@ -154,7 +162,8 @@ def _group_mask(rows_pos_g, cand_pos, seg, cu_seqlens, index_hs, block):
     vert = np.isin(m, iv)
     slash = np.isin((n - a) // block - (m - a) // block, is_)
     blk = block_selected(index_hs, n - a, m - a)
-    return inseg & (m <= n) & (vert | slash | blk)
+    rblk = row_block_selected(index_hs, n - a, m - a)
+    return inseg & (m <= n) & (vert | slash | blk | rblk)
 
 
 def attn_fwd_support(q, k, v, rows_pos, cols_pos, cu_seqlens, index, block=64, scale=None,

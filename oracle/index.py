@@ -183,14 +183,31 @@ def block_selected(index_hs, n_off, m_off):
     return ok & sel[np.clip(I, 0, sel.shape[0] - 1), np.clip(J, 0, sel.shape[1] - 1)]
 
 
+def row_block_selected(index_hs, n_off, m_off):
+    """Entries whose key block is picked for their row in the optional per-row
+    block selection of an index entry (iv, is_, blk, (bb, sel)): sel[r, J]
+    marks key block J (of bb tokens, in-segment offsets m_off // bb) for the
+    row at in-segment offset r = n_off.  An entry without that part picks
+    nothing."""
+    n_off, m_off = np.broadcast_arrays(np.asarray(n_off), np.asarray(m_off))
+    if len(index_hs) < 4 or index_hs[3] is None:
+        return np.zeros(n_off.shape, dtype=bool)
+    bb, sel = index_hs[3]
+    sel = np.asarray(sel, dtype=bool)
+    J = m_off // bb
+    ok = (n_off >= 0) & (J >= 0) & (n_off < sel.shape[0]) & (J < sel.shape[1])
+    return ok & sel[np.clip(n_off, 0, sel.shape[0] - 1), np.clip(J, 0, sel.shape[1] - 1)]
+
+
 def dense_mask(rows_pos, cols_pos, cu_seqlens, index, h, block=64):
     """``sparseformat``: boolean mask [len(rows_pos), len(cols_pos)] for Q head h.
 
     M[n, m] holds when n and m lie in the same segment, m <= n (causal), and
     m is a selected vertical or beta(n) - beta(m) is a selected
     block-diagonal.  Vertical and slash entries form a union (Algorithm 1).
-    An index entry may also carry a block selection (see block_selected):
-    its selected blocks join the union.
+    An index entry may also carry a block selection (see block_selected) or
+    a per-row block selection (see row_block_selected): their selected
+    blocks join the union.
     rows_pos / cols_pos are global positions, so a striped chunk's mask is the
     global mask restricted to its rows and columns.
     """
@@ -211,5 +228,6 @@ def dense_mask(rows_pos, cols_pos, cu_seqlens, index, h, block=64):
         vert = np.isin(m, iv)
         slash = np.isin((n - a) // block - (m - a) // block, is_)
         blk = block_selected(index[(h, s)], n - a, m - a)
-        M[np.ix_(ri, ci)] = (m <= n) & (vert | slash | blk)
+        rblk = row_block_selected(index[(h, s)], n - a, m - a)
+        M[np.ix_(ri, ci)] = (m <= n) & (vert | slash | blk | rblk)
     return M

@@ -759,3 +759,101 @@ def test_block_selection_mask_and_forms():
         g2 = oracle.attn_bwd_support(q, k, v, do, L, D, pos, pos, cu, idx, B)
         for x, y in zip(g1, g2):
             assert np.abs(x - y).max() < 1e-12
+
+
+# ---------------------------------------------------------------- MoBA (M1-M5)
+from oracle import moba as omb  # noqa: E402
+
+
+def test_m1_m2_block_means_and_scores_closed_form():
+    """Key blocks constant inside a block: each mean is that constant, the
+    short last block included (M1), and a query that is a unit vector scores
+    each block by that component of its constant (M2)."""
+    B, d = 8, 4
+    L = 3 * B + 5                       # three whole blocks and a short one
+    vals = np.array([[1.0, 0, 0, 0], [0, 2.0, 0, 0], [0, 0, -3.0, 0], [0.5, 0.5, 0.5, 0.5]])
+    k = np.concatenate([np.tile(vals[b], (min(B, L - b * B), 1)) for b in range(4)])
+    kb = omb.block_means(k, 0, L, B)
+    assert np.array_equal(kb, vals)
+    q = np.zeros((L, d))
+    q[:, 1] = 1.0
+    s = omb.gate_scores(q, k, 0, L, B)
+    assert np.array_equal(s, np.tile(vals[:, 1], (L, 1)))
+
+
+def test_m3_m4_selection_property_and_ties():
+    """Every row picks its own block and no later one (M3); the earlier blocks
+    it picks are min(k - 1, own) of them and none it leaves out scores higher,
+    or equal with a lower index (M4); two identical key blocks tie exactly and
+    the lower one wins."""
+    rng = np.random.default_rng(60)
+    B, d, L, topk = 4, 3, 40, 4         # 10 blocks
+    q = rng.standard_normal((L, d))
+    k = rng.standard_normal((L, d))
+    k[12:16] = k[4:8]                   # blocks 1 and 3 identical
+    s = omb.gate_scores(q, k, 0, L, B)
+    assert np.array_equal(s[:, 1], s[:, 3])
+    sel = omb.select_blocks(s, B, topk)
+    for r in range(L):
+        own = r // B
+        assert sel[r, own] and not sel[r, own + 1:].any()
+        picked = np.nonzero(sel[r, :own])[0]
+        left = np.setdiff1d(np.arange(own), picked)
+        assert picked.size == min(topk - 1, own)
+        for i in picked:
+            for j in left:
+                assert s[r, i] > s[r, j] or (s[r, i] == s[r, j] and i < j), (r, i, j)
+    # a row that sees blocks 1 and 3 tied at the boundary keeps block 1
+    tied = [r for r in range(16, L) if sel[r, 1] != sel[r, 3]]
+    assert tied and all(sel[r, 1] and not sel[r, 3] for r in tied)
+
+
+def test_m5_mask_brute_force_and_forms():
+    """The per-row block selection as a mask: m <= n and m's block picked for
+    n (brute force over every pair, two segments); the dense and support
+    forms of attention agree on it, forward and backward."""
+    rng = np.random.default_rng(61)
+    B, hq, hkv, d, topk = 16, 2, 1, 8, 2
+    cu = [0, 80, 176]
+    n = cu[-1]
+    q, k, v, do = (rng.standard_normal((n, h, d)) for h in (hq, hkv, hkv, hq))
+    idx = omb.estimate_index_moba(q, k, cu, block=B, topk=topk)
+    pos = np.arange(n)
+    for h in range(hq):
+        M = oracle.dense_mask(pos, pos, cu, idx, h, 64)
+        ref = np.zeros((n, n), bool)
+        for sg in range(2):
+            a, e = cu[sg], cu[sg + 1]
+            sel = idx[(h, sg)][3][1]
+            for r in range(a, e):
+                for m in range(a, r + 1):
+                    ref[r, m] = sel[r - a, (m - a) // B]
+        assert np.array_equal(M, ref), h
+    O1, L1 = oracle.attn_fwd_dense(q, k, v, pos, pos, cu, idx)
+    O2, L2 = oracle.attn_fwd_support(q, k, v, pos, pos, cu, idx)
+    assert np.abs(O1 - O2).max() < 1e-12 and np.abs(L1 - L2).max() < 1e-12
+    D = oracle.bwd_delta(O1, do)
+    g1 = oracle.attn_bwd_dense(q, k, v, do, L1, D, pos, pos, cu, idx)
+    g2 = oracle.attn_bwd_support(q, k, v, do, L1, D, pos, pos, cu, idx)
+    for a_, b_ in zip(g1, g2):
+        assert np.abs(a_ - b_).max() < 1e-12
+
+
+def test_m4_enough_blocks_is_causal_attention():
+    """top-k at least the number of blocks picks every block up to the own
+    one: plain causal attention, equal to torch's causal SDPA in fp64."""
+    rng = np.random.default_rng(62)
+    n, hq, hkv, d, B = 192, 2, 1, 16, 32
+    q, k, v = (rng.standard_normal((n, h, d)) for h in (hq, hkv, hkv))
+    idx = omb.estimate_index_moba(q, k, [0, n], block=B, topk=n // B)
+    for h in range(hq):
+        sel = idx[(h, 0)][3][1]
+        own = np.arange(n) // B
+        assert np.array_equal(sel, np.arange(n // B)[None, :] <= own[:, None])
+    pos = np.arange(n)
+    O, _ = oracle.attn_fwd_dense(q, k, v, pos, pos, [0, n], idx)
+    qt = torch.tensor(q).permute(1, 0, 2)[None]
+    kt = torch.tensor(k).permute(1, 0, 2)[None].repeat_interleave(hq // hkv, dim=1)
+    vt = torch.tensor(v).permute(1, 0, 2)[None].repeat_interleave(hq // hkv, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    assert np.abs(O - ref[0].permute(1, 0, 2).numpy()).max() < 1e-12
