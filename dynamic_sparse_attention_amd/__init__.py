@@ -29,7 +29,7 @@ from ._abi import VsError
 
 BLOCK = 64
 __all__ = ["VsIndexT", "index_capacity", "estimate_index", "estimate_index_topp",
-           "estimate_index_xattn", "sparse_attn_fwd",
+           "estimate_index_xattn", "estimate_index_moba", "sparse_attn_fwd",
            "sparse_attn_bwd", "sparse_attn_bwd_noalloc",
            "attn_bwd_delta", "lse_merge", "VsError", "BLOCK"]
 
@@ -103,7 +103,10 @@ class VsIndexT:
 
     blk_mask (optional): a block selection instead of the lists, one bit per
     (batch, Q head, query block, key block) of blk_size tokens, rows of
-    ceil(nI / 32) int32 words (the layout estimate_index_xattn writes)."""
+    ceil(nI / 32) int32 words (the layout estimate_index_xattn writes).
+    row_mask (optional): a per-row block selection, one int32 word per
+    (batch, Q head, row) whose bit J marks key block J of row_blk tokens (the
+    layout estimate_index_moba writes)."""
     v_ptr: torch.Tensor
     v_idx: torch.Tensor
     s_ptr: torch.Tensor
@@ -112,12 +115,16 @@ class VsIndexT:
     s_cap_max: int
     blk_mask: Optional[torch.Tensor] = None
     blk_size: int = 0
+    row_mask: Optional[torch.Tensor] = None
+    row_blk: int = 0
 
     def struct(self) -> _abi.VsIndex:
         return _abi.VsIndex(self.v_ptr.data_ptr(), self.v_idx.data_ptr(), self.s_ptr.data_ptr(),
                             self.s_idx.data_ptr(), self.v_cap_max, self.s_cap_max,
                             None if self.blk_mask is None else self.blk_mask.data_ptr(),
-                            self.blk_size)
+                            self.blk_size,
+                            None if self.row_mask is None else self.row_mask.data_ptr(),
+                            self.row_blk)
 
     def block_selection(self, n: int):
         """Host copy of a block selection as bool [B*Hq, nI, nI] (n tokens per row)."""
@@ -264,6 +271,37 @@ def estimate_index_xattn(q: torch.Tensor, k: torch.Tensor, threshold: float = 0.
     empty = torch.zeros(1, dtype=torch.int32, device=dev)
     idx = VsIndexT(zeros, empty, zeros, empty, 0, 0, mask, int(block))
     return (idx, counts, scores) if return_scores else (idx, counts)
+
+
+def estimate_index_moba(q: torch.Tensor, k: torch.Tensor, block: int = 4096, topk: int = 12,
+                        return_scores: bool = False):
+    """MoBA block gate for q [B, N, Hq, d], k [B, N, Hkv, d] bf16 (one
+    segment): every query picks its own key block of `block` tokens and the
+    topk - 1 earlier blocks whose mean key scores highest against it.
+
+    Returns a VsIndexT with the per-row selection (row_mask [B, Hq, N] int32)
+    and, with return_scores, also the gate scores [B, Hq, N, nB] fp32
+    (entries of the own block and later unspecified).
+    """
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, strided=True)
+    _need(k, "k", torch.bfloat16, dev, strided=True)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    P = _Problem(B, Hq, Hkv, d, N, N, _abi.VS_BF16, None, None, None, q=q, k=k)
+    nB = -(-N // block)
+    mask = torch.empty((B, Hq, N), dtype=torch.int32, device=dev)
+    scores = torch.empty((B, Hq, N, nB), dtype=torch.float32, device=dev) if return_scores else None
+    L = _abi.lib()
+    nb = ctypes.c_size_t()
+    _abi.check(L.vs_workspace_size(P.ref, 4, None, ctypes.byref(nb)))
+    ws = _workspace(dev, nb.value)
+    _abi.check(L.vs_estimate_index_moba(P.ref, _ptr(q), _ptr(k), int(block), int(topk), _ptr(mask),
+                                        _ptr(scores), _ptr(ws), ws.numel(), _stream(dev)))
+    zeros = torch.zeros(B * Hq + 1, dtype=torch.int32, device=dev)
+    empty = torch.zeros(1, dtype=torch.int32, device=dev)
+    idx = VsIndexT(zeros, empty, zeros, empty, 0, 0, row_mask=mask, row_blk=int(block))
+    return (idx, scores) if return_scores else idx
 
 
 def index_from_lists(lists: List[Tuple[Sequence[int], Sequence[int]]], device) -> VsIndexT:

@@ -38,7 +38,7 @@ class VsProblem(ctypes.Structure):
 
 class VsIndex(ctypes.Structure):
     _fields_ = [("v_ptr", vp), ("v_idx", vp), ("s_ptr", vp), ("s_idx", vp), ("v_cap_max", i32),
-                ("s_cap_max", i32), ("blk_mask", vp), ("blk_size", i32)]
+                ("s_cap_max", i32), ("blk_mask", vp), ("blk_size", i32), ("row_mask", vp), ("row_blk", i32)]
 
 
 PP = ctypes.POINTER(VsProblem)
@@ -50,6 +50,7 @@ SIGNATURES = {
     "vs_estimate_index": (i32, [PP, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     "vs_estimate_index_topp": (i32, [PP, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     "vs_estimate_index_xattn": (i32, [PP, vp, vp, i32, i32, f32, vp, vp, vp, vp, sz, vp]),
+    "vs_estimate_index_moba": (i32, [PP, vp, vp, i32, i32, vp, vp, vp, sz, vp]),
     "vs_sparse_attn_fwd": (i32, [PP, vp, vp, vp, IP, vp, i32, vp, vp, sz, vp]),
     "vs_attn_bwd_delta": (i32, [PP, vp, i32, vp, vp, vp]),
     "vs_sparse_attn_bwd": (i32, [PP, vp, vp, vp, vp, i32, vp, vp, vp, IP, vp, i32, vp, vp, vp, sz, vp]),

@@ -13,7 +13,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvs.so")
-SOURCES = ["vs_api.cpp", "vs_fwd.hip", "vs_bwd.hip", "vs_bwd_kv.hip", "vs_bwd_dq.hip", "vs_estimate.hip", "vs_misc.hip",
+SOURCES = ["vs_api.cpp", "vs_fwd.hip", "vs_bwd.hip", "vs_bwd_kv.hip", "vs_bwd_dq.hip", "vs_estimate.hip", "vs_misc.hip", "vs_moba.hip",
            "vs_xattn.hip"]
 
 

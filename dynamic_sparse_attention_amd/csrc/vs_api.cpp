@@ -35,9 +35,13 @@ hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int
 constexpr int kEstKeyTile = 256;
 struct XaParams;
 hipError_t launch_xattn(const XaParams& p, int d, hipStream_t st);
+struct MobaParams;
+hipError_t launch_moba(const MobaParams& p, hipStream_t st);
+hipError_t launch_moba_union(const uint32_t* rmask, uint32_t* out, int tiles, hipStream_t st);
 }  // namespace vs
 
 #include "vs_xattn_params.h"
+#include "vs_moba_params.h"
 
 namespace {
 
@@ -185,6 +189,19 @@ vs_status check_index(const Prob& c, const vs_index* idx) {
   if (idx->s_cap_max > max_seg / c.block)
     return fail(VS_ERR_INDEX, "s_cap_max %d exceeds the block count %d", idx->s_cap_max,
                 max_seg / c.block);
+  if (idx->row_mask) {
+    if (!c.bf16 || c.W != 1 || c.n_seg != 1)
+      return fail(VS_ERR_UNSUPPORTED, "a per-row block selection takes bf16 inputs, one segment, no striping");
+    const int rb = idx->row_blk;
+    if (rb < c.block || (rb & (rb - 1)) != 0)
+      return fail(VS_ERR_UNSUPPORTED, "per-row selection blocks of %d tokens (a power of two >= %d)", rb, c.block);
+    if ((int64_t)c.n_global > 32 * (int64_t)rb)
+      return fail(VS_ERR_UNSUPPORTED, "a per-row selection holds 32 blocks per row (n %d, blocks of %d)",
+                  c.n_global, rb);
+    if (idx->blk_mask) return fail(VS_ERR_INDEX, "a block selection and a per-row selection together");
+    if (idx->v_cap_max != 0 || idx->s_cap_max != 0)
+      return fail(VS_ERR_INDEX, "a per-row selection comes with empty Vertical-Slash lists");
+  }
   if (idx->blk_mask) {
     if (!c.bf16 || c.W != 1 || c.n_seg != 1)
       return fail(VS_ERR_UNSUPPORTED, "a block selection takes bf16 inputs, one segment, no striping");
@@ -203,6 +220,12 @@ void fill_bmask(const Prob& c, const vs_index* idx, vs::AttnParams* a) {
   if (idx->blk_mask) {
     a->bm_nI = (c.n_global + idx->blk_size - 1) / idx->blk_size;
     a->bm_words = (a->bm_nI + 31) / 32;
+  }
+  a->rmask = idx->row_mask;
+  if (idx->row_mask) {
+    int sh = 0;
+    while ((c.block << sh) < idx->row_blk) ++sh;
+    a->rm_shift = sh;  // row_blk = 64 << sh (checked a power of two)
   }
 }
 
@@ -233,11 +256,13 @@ void fill_params(const Prob& c, vs::AttnParams* a) {
 
 // Workspace layouts.
 struct AttnWs {
-  size_t vsel, vcnt, share, delta, lse2, total;
+  size_t vsel, vcnt, share, delta, lse2, rm_union, total;
 };
 // Forward: prepared vertical lists.  Backward: also delta (when the caller
-// gives none) and LSE * log2(e), one fp32 per (batch, Q head, row) each.
-AttnWs attn_ws(const Prob& c, int v_cap_max, bool backward) {
+// gives none) and LSE * log2(e), one fp32 per (batch, Q head, row) each, and
+// with a per-row block selection the OR of each query block's rows' words.
+AttnWs attn_ws(const Prob& c, const vs_index* idx, bool backward) {
+  const int v_cap_max = idx->v_cap_max;
   AttnWs w;
   size_t off = 0;
   w.vsel = off;
@@ -251,6 +276,8 @@ AttnWs attn_ws(const Prob& c, int v_cap_max, bool backward) {
   if (backward) off += rows;
   w.lse2 = off;
   if (backward) off += rows;
+  w.rm_union = off;
+  if (backward && idx->row_mask) off += align256((size_t)c.batch * c.h_q * c.nqb * 4);
   w.total = off;
   return w;
 }
@@ -289,6 +316,13 @@ struct XaWs {
   size_t cell, total;
   int nC, nI;
 };
+// MoBA gate: the blocks' mean keys, [batch, h_kv, nB, d] fp32, for blocks of
+// blk tokens (the 32-block maximum when blk is not yet known).
+size_t moba_ws(const Prob& c, int blk) {
+  const int nB = blk > 0 ? (c.n_global + blk - 1) / blk : 32;
+  return align256((size_t)c.batch * c.h_kv * nB * c.d * 4);
+}
+
 XaWs xa_ws(const Prob& c) {
   XaWs w;
   w.nC = c.n_global / 16;
@@ -410,9 +444,13 @@ vs_status vs_workspace_size(const vs_problem* p, int32_t op, const vs_index* idx
     *bytes = xa_ws(c).total;
     return ok();
   }
-  if (op != 1 && op != 2) return fail(VS_ERR_SHAPE, "op %d is not 0, 1, 2 or 3", op);
+  if (op == 4) {
+    *bytes = moba_ws(c, 0);
+    return ok();
+  }
+  if (op != 1 && op != 2) return fail(VS_ERR_SHAPE, "op %d is not 0, 1, 2, 3 or 4", op);
   if ((st = check_index(c, idx))) return st;
-  *bytes = attn_ws(c, idx->v_cap_max, op == 2).total;
+  *bytes = attn_ws(c, idx, op == 2).total;
   return ok();
 }
 
@@ -506,6 +544,43 @@ vs_status vs_estimate_index_xattn(const vs_problem* p, const void* q, const void
   return hip_status(vs::launch_xattn(x, c.d, (hipStream_t)stream), "vs_estimate_index_xattn");
 }
 
+vs_status vs_estimate_index_moba(const vs_problem* p, const void* q, const void* k, int32_t block,
+                                 int32_t topk, uint32_t* row_mask, float* gate_scores, void* ws,
+                                 size_t ws_bytes, vs_stream_t stream) {
+  Prob c;
+  vs_status st = check_problem(p, &c);
+  if (st) return st;
+  if (!q || !k || !row_mask) return fail(VS_ERR_NULL, "q, k or row_mask is NULL");
+  if (!c.bf16 || c.W != 1 || c.n_seg != 1)
+    return fail(VS_ERR_UNSUPPORTED, "MoBA estimation takes bf16 inputs, one segment, no striping");
+  if (block < 256 || (block & (block - 1)) != 0)
+    return fail(VS_ERR_UNSUPPORTED, "MoBA block %d unsupported (a power of two >= 256)", block);
+  if ((int64_t)c.n_global > 32 * (int64_t)block)
+    return fail(VS_ERR_UNSUPPORTED, "MoBA estimation picks among at most 32 blocks (n %d, block %d)", c.n_global,
+                block);
+  if (topk < 1) return fail(VS_ERR_SHAPE, "topk %d < 1", topk);
+  const size_t need = moba_ws(c, block);
+  if (!ws || ws_bytes < need) return fail(VS_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  vs::MobaParams m;
+  std::memset(&m, 0, sizeof m);
+  m.q = static_cast<const __bf16*>(q);
+  m.k = static_cast<const __bf16*>(k);
+  m.sq = c.sq;
+  m.sk = c.sk;
+  m.batch = c.batch;
+  m.h_q = c.h_q;
+  m.h_kv = c.h_kv;
+  m.n = c.n_global;
+  m.d = c.d;
+  m.blk = block;
+  m.nB = (c.n_global + block - 1) / block;
+  m.topk = topk;
+  m.kbar = static_cast<float*>(ws);
+  m.rmask = row_mask;
+  m.scores = gate_scores;
+  return hip_status(vs::launch_moba(m, (hipStream_t)stream), "vs_estimate_index_moba");
+}
+
 vs_status vs_sparse_attn_fwd(const vs_problem* p, const void* q, const void* k, const void* v,
                              const vs_index* idx, void* o, int32_t o_f32, float* lse, void* ws,
                              size_t ws_bytes, vs_stream_t stream) {
@@ -514,7 +589,7 @@ vs_status vs_sparse_attn_fwd(const vs_problem* p, const void* q, const void* k, 
   if (st) return st;
   if ((st = check_index(c, idx))) return st;
   if (!q || !k || !v || !o || !lse) return fail(VS_ERR_NULL, "q, k, v, o or lse is NULL");
-  const AttnWs w = attn_ws(c, idx->v_cap_max, false);
+  const AttnWs w = attn_ws(c, idx, false);
   if (!ws || ws_bytes < w.total)
     return fail(VS_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
   vs::AttnParams a;
@@ -612,7 +687,7 @@ vs_status attn_bwd(const char* what, const vs_problem* p, const void* q, const v
   if (c.bf16 && c.h_q / c.h_kv > 32)
     return fail(VS_ERR_UNSUPPORTED, "bf16 backward takes at most 32 Q heads per KV head (got %d)",
                 c.h_q / c.h_kv);
-  const AttnWs w = attn_ws(c, idx->v_cap_max, true);
+  const AttnWs w = attn_ws(c, idx, true);
   if (use_scratch) {
     if (w.total > VS_NOALLOC_SCRATCH_BYTES)
       return fail(VS_ERR_WORKSPACE, "%s: the problem needs %zu bytes of workspace, beyond the library's "
@@ -679,6 +754,11 @@ vs_status attn_bwd(const char* what, const vs_problem* p, const void* q, const v
   a.delta = delta;
   a.lse2 = l2;
   if (e == hipSuccess) e = vs::launch_prep_vertical(a, c.n_lists(), idx->v_ptr, idx->v_idx, s);
+  if (e == hipSuccess && idx->row_mask) {
+    uint32_t* un = reinterpret_cast<uint32_t*>(base + w.rm_union);
+    a.rm_union = un;
+    e = vs::launch_moba_union(idx->row_mask, un, c.batch * c.h_q * c.nqb, s);
+  }
   if (e == hipSuccess) e = vs::launch_bwd(a, c.bf16, c.d, s);
   return hip_status(e, what);
 }

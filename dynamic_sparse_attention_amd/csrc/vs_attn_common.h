@@ -65,6 +65,13 @@ struct AttnParams {
   // 128-row query block I; each 128-block covers two 64-blocks.
   const uint32_t* bmask;
   int bm_nI, bm_words;
+  // Per-row block selection (MoBA's gate; one segment, batch-major rows):
+  // bit J of rmask[(b * h_q + h) * n_q + n] marks key block J (of
+  // 64 << rm_shift tokens) for row n; rm_union[(b * h_q + h) * nqb + i] is
+  // the OR of the 64 rows' words of query block i (backward only).
+  const uint32_t* rmask;
+  const uint32_t* rm_union;
+  int rm_shift;
   int qranges;        // backward column units: query-block ranges per column tile
   int qrange_len;
   int col_tiles;      // backward column units: column tiles per list

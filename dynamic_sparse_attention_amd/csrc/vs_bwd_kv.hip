@@ -51,6 +51,7 @@ struct __attribute__((aligned(16))) KvBuf {
   char dout[RowTile<D>::BYTES];
   float lse2[kTR];  // LSE * log2(e)
   float del[kTR];
+  uint32_t sel[kTR];  // per-row block selection: the rows' picked blocks
 };
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
@@ -58,8 +59,9 @@ typedef __attribute__((address_space(1))) void* glb_vptr;
 
 // Direct loads of query tile (local block i, rows kTR*half .. +kTR, Q head h)
 // into B; each of the two waves issues half of the rows (NDMA / 2
-// instructions) plus one of LSE / delta.
-template <int D>
+// instructions) plus one of LSE / delta, and with SEL wave 0 also the rows'
+// picked-block words of a per-row selection.
+template <int D, bool SEL = false>
 __device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, int b, int h, int i, int half) {
   typedef RowTile<D> RT;
   const int lane = threadIdx.x & 63;
@@ -80,6 +82,8 @@ __device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, in
   const float* src = w == 0 ? p.lse2 : p.delta;
   if (lane < kTR)
     __builtin_amdgcn_global_load_lds((glb_vptr)(src + li), (lds_vptr)(w == 0 ? B.lse2 : B.del), 4, 0, 0);
+  if (SEL && w == 0 && lane < kTR)
+    __builtin_amdgcn_global_load_lds((glb_vptr)(p.rmask + li), (lds_vptr)B.sel, 4, 0, 0);
 }
 
 template <int D>
@@ -252,24 +256,24 @@ struct KvLdsB {
 // One pipeline step: the next tile's loads go to nxt while body computes on
 // cur.  The two buffers never overlap; saying so (restrict) lets the compiler
 // see that the reads of cur need not wait for the loads into nxt.
-template <int D, class BodyF>
+template <int D, bool SEL, class BodyF>
 __device__ __forceinline__ void kv_step(const AttnParams& p, KvBuf<D>* __restrict__ nxt,
                                         const KvBuf<D>* __restrict__ cur, bool more, int b, int h1,
                                         int i1, int half1, int t, int fl, int half, BodyF& body) {
-  if (more) kv_tile_dma<D>(p, *nxt, b, h1, i1, half1);
+  if (more) kv_tile_dma<D, SEL>(p, *nxt, b, h1, i1, half1);
   body(*cur, t, fl, half);
 }
 
 // Double-buffered walk over the two halves of ntiles query blocks:
 // tile_of(t) -> (h, i, flags), body(B, t, flags, half) computes on the staged
 // half tile.
-template <int D, class TileF, class BodyF>
+template <int D, class TileF, class BodyF, bool SEL = false>
 __device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D>& L, int b, int ntiles,
                                             TileF tile_of, BodyF body) {
   if (ntiles == 0) return;
   int h, i, fl;
   tile_of(0, &h, &i, &fl);
-  kv_tile_dma<D>(p, L.buf[0], b, h, i, 0);
+  kv_tile_dma<D, SEL>(p, L.buf[0], b, h, i, 0);
   const int nu = 2 * ntiles;
   for (int u = 0; u < nu; ++u) {
     // this wave's loads of step u are done; the barrier makes every wave's
@@ -280,17 +284,21 @@ __device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D>& L, i
     const bool more = u + 1 < nu;
     if (more) tile_of((u + 1) >> 1, &h1, &i1, &fl1);
     tile_of(u >> 1, &h, &i, &fl);
-    kv_step<D>(p, &L.buf[(u + 1) & 1], &L.buf[u & 1], more, b, h1, i1, (u + 1) & 1, u >> 1, fl,
-               u & 1, body);
+    kv_step<D, SEL>(p, &L.buf[(u + 1) & 1], &L.buf[u & 1], more, b, h1, i1, (u + 1) & 1, u >> 1, fl,
+                    u & 1, body);
   }
   __syncthreads();
 }
 
-// BLK: the index is a block selection (p.bmask, one segment) instead of
-// block-diagonal lists; a template flag so that the list walk keeps its
-// registers.
-template <int D, bool BLK>
+// MODE: 0 the block-diagonal lists; 1 a block selection (p.bmask, one
+// segment); 2 a per-row block selection (p.rmask, one segment).  A template
+// parameter so that the list walk keeps its registers.
+constexpr int kModeLists = 0, kModeBlocks = 1, kModeRows = 2;
+
+template <int D, int MODE>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_kv_slash_bf16_kernel(AttnParams p) {
+  constexpr bool BLK = MODE == kModeBlocks;
+  constexpr bool ROWS = MODE == kModeRows;
   typedef KvWorkerB<D> W;
   __shared__ KvLdsB<D> L;
   const int tid = threadIdx.x;
@@ -328,15 +336,20 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     *i = (v >> 1) & ((1 << 25) - 1);
     *fl = v & 1;
   };
-  // Diagonal tiles (g = 0, or the query block itself in a block selection;
-  // causal inside the block) first, in a walk of their own, so that the main
-  // walk has no masking at all.
+  // per-row selections: the key block's picked-block index
+  const int pick = ROWS ? (beta_k >> p.rm_shift) : 0;
+  // Diagonal tiles (g = 0, or the query block itself in a block or per-row
+  // selection; causal inside the block, and with a per-row selection only the
+  // rows that picked the block) first, in a walk of their own, so that the
+  // main walk of the lists has no masking at all.
   {
     int i = -1;
     if (tid >= p.hh_lo && tid < p.hh_hi) {
       const int list = (b * p.h_q + kvh * G + tid) * p.seg.n_seg + seg;
       if (BLK) {
         if (bmask_bit(p, list, beta_k >> 1, beta_k >> 1)) i = local_query_block(p, kb_glob);
+      } else if (ROWS) {
+        if ((p.rm_union[(size_t)list * p.nqb + kb_glob] >> pick) & 1u) i = local_query_block(p, kb_glob);
       } else {
         const int sp0 = p.s_ptr[list];
         if (p.s_ptr[list + 1] > sp0 && p.s_idx[sp0] == 0) i = local_query_block(p, kb_glob);
@@ -346,20 +359,34 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const int slot = block_compact<kKvThreads>(i >= 0, L.wsum, &tot);
     if (i >= 0) L.tiles[slot] = (tid << 26) | (i << 1) | 1;
     __syncthreads();
-    kv_pipeline<D>(p, L, b, tot, tile_of, [&](const KvBuf<D>& B, int, int, int half) {
-      wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) { return kin <= r; });
-    });
+    auto diag_body = [&](const KvBuf<D>& B, int, int, int half) {
+      if constexpr (ROWS)
+        wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) {
+          return kin <= r && ((B.sel[r - kTR * half] >> pick) & 1u) != 0u;
+        });
+      else
+        wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) { return kin <= r; });
+    };
+    kv_pipeline<D, decltype(tile_of), decltype(diag_body), ROWS>(p, L, b, tot, tile_of, diag_body);
   }
+  // main walk: with a per-row selection every tile is masked by its rows'
+  // picks (one tile variant, so that the walk keeps its registers)
   auto body = [&](const KvBuf<D>& B, int, int, int half) {
-    wk.template tile<false>(B, p.sl2, kTR * half, [](int) { return true; });
+    if constexpr (ROWS)
+      wk.template tile<true>(B, p.sl2, kTR * half,
+                             [&](int r) { return ((B.sel[r - kTR * half] >> pick) & 1u) != 0u; });
+    else
+      wk.template tile<false>(B, p.sl2, kTR * half, [](int) { return true; });
   };
   for (int hh = p.hh_lo; hh < p.hh_hi; ++hh) {
     const int list = (b * p.h_q + kvh * G + hh) * p.seg.n_seg + seg;
     // Candidates: the head's selected block-diagonals g > 0 (query block
     // kb + g), or with a block selection (one segment) the query blocks after
-    // this key block, kept when their 128-block selected the key's 128-block.
-    const int sp0 = BLK ? 0 : p.s_ptr[list];
-    const int ns = BLK ? nb_seg - 1 - beta_k : p.s_ptr[list + 1] - sp0;
+    // this key block, kept when their 128-block selected the key's 128-block,
+    // or with a per-row selection the query blocks after it, kept when one of
+    // their rows picked its block.
+    const int sp0 = (BLK || ROWS) ? 0 : p.s_ptr[list];
+    const int ns = (BLK || ROWS) ? nb_seg - 1 - beta_k : p.s_ptr[list + 1] - sp0;
     for (int base = 0; base < ns; base += kKvThreads) {
       const int e = base + tid;
       int i = -1;
@@ -367,6 +394,10 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
         if (BLK) {
           const int ib = beta_k + 1 + e;  // query block of the segment
           if (bmask_bit(p, list, ib >> 1, beta_k >> 1)) i = local_query_block(p, a_blk + ib);
+        } else if (ROWS) {
+          // query block ib: kept when some row picked this key block
+          const int ib = beta_k + 1 + e;
+          if ((p.rm_union[(size_t)list * p.nqb + a_blk + ib] >> pick) & 1u) i = local_query_block(p, a_blk + ib);
         } else {
           const int g = p.s_idx[sp0 + e];
           if (g > 0 && beta_k + g < nb_seg) i = local_query_block(p, kb_glob + g);
@@ -378,12 +409,12 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
       count += tot;
       __syncthreads();
       if (count > kKvTiles - kKvThreads) {
-        kv_pipeline<D>(p, L, b, count, tile_of, body);
+        kv_pipeline<D, decltype(tile_of), decltype(body), ROWS>(p, L, b, count, tile_of, body);
         count = 0;
       }
     }
   }
-  kv_pipeline<D>(p, L, b, count, tile_of, body);
+  kv_pipeline<D, decltype(tile_of), decltype(body), ROWS>(p, L, b, count, tile_of, body);
   wk.store(p, b, kvh, kpos, p.kv_accumulate ? 1 : 0);
 }
 
@@ -505,12 +536,14 @@ hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
     nb_max = std::max(nb_max, p.seg.start_blk[sgi + 1] - p.seg.start_blk[sgi]);
   const size_t bits_bytes = (size_t)((nb_max + 31) / 32) * 4 + 4;
   if (d == 128) {
-    if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, true>), gs, dim3(kKvThreads), 0, st, p));
-    if (gs.x && !p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, false>), gs, dim3(kKvThreads), 0, st, p));
+    if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, kModeBlocks>), gs, dim3(kKvThreads), 0, st, p));
+    else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, kModeRows>), gs, dim3(kKvThreads), 0, st, p));
+    else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, kModeLists>), gs, dim3(kKvThreads), 0, st, p));
     if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128>), gc, dim3(kKvThreads), bits_bytes, st, p));
   } else {
-    if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, true>), gs, dim3(kKvThreads), 0, st, p));
-    if (gs.x && !p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, false>), gs, dim3(kKvThreads), 0, st, p));
+    if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, kModeBlocks>), gs, dim3(kKvThreads), 0, st, p));
+    else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, kModeRows>), gs, dim3(kKvThreads), 0, st, p));
+    else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, kModeLists>), gs, dim3(kKvThreads), 0, st, p));
     if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64>), gc, dim3(kKvThreads), bits_bytes, st, p));
   }
   return hipGetLastError();

@@ -43,6 +43,35 @@ struct SlashSetT {
   }
 };
 
+// Key-block tiles of a per-row block selection: the rows of the query block
+// that did not pick a tile's block see none of it.
+template <int NS>
+struct MobaSetT {
+  static constexpr bool kContiguous = true;
+  const int* tiles;      // 4 * local key block + 2 * (some row did not pick its block) + (diagonal)
+  int tot;
+  int wave;              // key stream
+  const uint32_t* rsel;  // the 64 rows' picked blocks (one word per row)
+  int shift;             // log2 of the 64-key blocks per picked block
+  __device__ __forceinline__ int n_halves() const { return tot > wave ? 2 * ((tot - wave + NS - 1) / NS) : 0; }
+  __device__ __forceinline__ int n_halves_max() const { return tot > 0 ? 2 * ((tot + NS - 1) / NS) : 0; }
+  __device__ __forceinline__ int tv(int n) const { return tiles[wave + NS * (n >> 1)]; }
+  __device__ __forceinline__ int key_pos(int n, int r) const { return (tv(n) >> 2) * kBlock + 32 * (n & 1) + r; }
+  __device__ __forceinline__ bool full(int n) const { return (tv(n) & 3) == 0; }
+  __device__ __forceinline__ bool picked(int n, int r) const { return (rsel[r] >> ((tv(n) >> 2) >> shift)) & 1u; }
+  __device__ __forceinline__ bool valid(int n, int e, int r) const {
+    return picked(n, r) && (!(tv(n) & 1) || 32 * (n & 1) + e <= r);
+  }
+  template <int KPL>
+  __device__ __forceinline__ void mask(int n, int hl, int r, f32x16& s) const {
+    const bool row_ok = picked(n, r);
+    const bool diag = tv(n) & 1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!row_ok || (diag && 32 * (n & 1) + reg_row<KPL>(i, hl) > r)) s[i] = -INFINITY;
+  }
+};
+
 template <int NS>
 struct ColSetT {
   static constexpr bool kContiguous = false;
@@ -169,6 +198,35 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
       if (j >= 0) L.tiles[slot] = 2 * j + (kb == rb.beta);
       __syncthreads();
       wk.run(SlashSetT<NS>{L.tiles, tot, wave});
+      __syncthreads();
+    }
+  }
+
+  // Per-row block selection (another estimator's index, one segment): the
+  // 64-key blocks kb <= beta of the blocks any row of the query block
+  // picked; a tile is flagged when some row did not pick its block.  The
+  // rows' words sit in the column buffer, which this index leaves unused.
+  if (p.rmask) {
+    static_assert(NCOL >= kBlock, "row words fit the column buffer");
+    uint32_t* rsel = reinterpret_cast<uint32_t*>(L.cols);
+    if (tid < kBlock) rsel[tid] = p.rmask[(size_t)list * p.n_q + (size_t)rb.i_local * kBlock + tid];
+    __syncthreads();
+    uint32_t uni = 0u, all = ~0u;
+    for (int r = 0; r < kBlock; ++r) {
+      const uint32_t w = rsel[r];
+      uni |= w;
+      all &= w;
+    }
+    for (int base = 0; base <= rb.beta; base += NT) {
+      const int kb = base + tid;
+      const int bb = kb >> p.rm_shift;
+      int j = -1;
+      if (kb <= rb.beta && ((uni >> bb) & 1u)) j = local_key_block(p, rb.a_blk + kb);
+      int tot;
+      const int slot = block_compact<NT>(j >= 0, L.wsum, &tot);
+      if (j >= 0) L.tiles[slot] = 4 * j + 2 * (((all >> bb) & 1u) == 0u) + (kb == rb.beta);
+      __syncthreads();
+      wk.run(MobaSetT<NS>{L.tiles, tot, wave, rsel, p.rm_shift});
       __syncthreads();
     }
   }

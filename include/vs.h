@@ -141,6 +141,14 @@ typedef struct vs_problem {
  * segment, stripe_world 1, blk_size 128 and empty lists (v_cap_max and
  * s_cap_max 0; v_ptr and s_ptr still point at batch*h_q+1 zero offsets),
  * else VS_ERR_UNSUPPORTED / VS_ERR_INDEX.
+ *
+ * Per-row block selection (another estimator's index, vs_estimate_index_moba):
+ * when row_mask is not NULL, row n of (b, h) attends key m iff m <= n and bit
+ * J = m / row_blk of the word row_mask[(b * h_q + h) * n_global + n] is set
+ * (DEVICE, one 32-bit word per row).  It requires bf16 inputs, one segment,
+ * stripe_world 1, row_blk a power of two >= 64 with n_global <= 32 * row_blk,
+ * empty lists as for blk_mask, and blk_mask NULL, else VS_ERR_UNSUPPORTED /
+ * VS_ERR_INDEX.
  */
 typedef struct vs_index {
   const int32_t* v_ptr;
@@ -151,6 +159,8 @@ typedef struct vs_index {
   int32_t s_cap_max;
   const uint32_t* blk_mask;  /* NULL: the Vertical-Slash lists above */
   int32_t blk_size;
+  const uint32_t* row_mask;  /* NULL: no per-row block selection */
+  int32_t row_blk;
 } vs_index;
 
 /* List offsets for budgets (MTraining paper note, Algorithm 1: argtopk with
@@ -169,7 +179,8 @@ vs_status vs_index_capacity(const vs_problem* p, const int32_t* v_budget,
 
 /* Workspace bytes an entry point needs: op 0 = vs_estimate_index (and
  * vs_estimate_index_topp),
- * 1 = vs_sparse_attn_fwd, 2 = vs_sparse_attn_bwd, 3 = vs_estimate_index_xattn.  idx may be NULL for op 0;
+ * 1 = vs_sparse_attn_fwd, 2 = vs_sparse_attn_bwd, 3 = vs_estimate_index_xattn,
+ * 4 = vs_estimate_index_moba.  idx may be NULL for op 0;
  * for ops 1 and 2 it supplies the capacity bounds.  The workspace is DEVICE
  * memory, 256-byte aligned, owned by the caller, and may be reused across
  * calls on the same stream. */
@@ -245,6 +256,26 @@ vs_status vs_estimate_index_xattn(const vs_problem* p, const void* q, const void
                                   int32_t block, int32_t stride, float threshold,
                                   uint32_t* blk_mask, int32_t* counts, float* blk_score,
                                   void* ws, size_t ws_bytes, vs_stream_t stream);
+
+/* MoBA block gate, a second alternative estimator for the same attention
+ * calls (the MTraining paper note, appendix, baseline settings, item 1: key
+ * blocks of fixed size, a per-query MoE-style gate picking the top-k blocks,
+ * the query's own block always among them; block 4096, top-12).  For every
+ * (b, h): the mean kbar_J of each key block J of `block` tokens (the last may
+ * be short); for every row n the gate scores q_n . kbar_J (fp32) of the
+ * blocks J before its own block n / block; the picked set is the own block
+ * and the topk - 1 highest-scoring earlier blocks, ties to the lowest J (all
+ * earlier blocks when there are fewer).  Writes row_mask (DEVICE, the layout
+ * of vs_index.row_mask) and, when not NULL, gate_scores [b, h_q, n, nB] fp32
+ * (nB = ceil(n / block); entries of the own block and later unspecified).
+ * q [batch, n, h_q, d], k [batch, n, h_kv, d] bf16 (strides from the
+ * problem); one segment, stripe_world 1, block a power of two >= 256 with
+ * n <= 32 * block, topk >= 1, else VS_ERR_UNSUPPORTED / VS_ERR_SHAPE.
+ * Workspace: op 4.  Errors: VS_ERR_NULL, VS_ERR_SHAPE, VS_ERR_UNSUPPORTED,
+ * VS_ERR_WORKSPACE, VS_ERR_HIP. */
+vs_status vs_estimate_index_moba(const vs_problem* p, const void* q, const void* k, int32_t block,
+                                 int32_t topk, uint32_t* row_mask, float* gate_scores, void* ws,
+                                 size_t ws_bytes, vs_stream_t stream);
 
 /* Sparse attention forward (MTraining paper note, Algorithm 1 last step and
  * Algorithm 2 block_bar_sparse_attention_forward; online softmax as in

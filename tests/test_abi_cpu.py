@@ -208,7 +208,7 @@ def test_entry_points_reject_before_launch(abi):
     fwd_ws = nb.value
     assert L.vs_workspace_size(P, 2, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_OK
     assert nb.value > fwd_ws
-    assert L.vs_workspace_size(P, 4, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_ERR_SHAPE
+    assert L.vs_workspace_size(P, 5, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_ERR_SHAPE
     assert L.vs_workspace_size(P, 1, None, ctypes.byref(nb)) == abi.VS_ERR_NULL
     # estimate
     st = L.vs_estimate_index(P, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None)
@@ -333,5 +333,44 @@ def test_xattn_and_block_selection_validation(abi):
     lists = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 64, 4, 0x1000, 128)
     assert L.vs_workspace_size(P, 2, ctypes.byref(lists), ctypes.byref(nb)) == abi.VS_ERR_INDEX
     for bad in (prob(abi, dtype=abi.VS_F32), prob(abi, cu=[0, 2048, 4096])):
+        assert L.vs_workspace_size(ctypes.byref(bad), 1, ctypes.byref(ix),
+                                   ctypes.byref(nb)) == abi.VS_ERR_UNSUPPORTED
+
+
+def test_moba_and_row_selection_validation(abi):
+    """The MoBA gate and a per-row block selection: supported forms (bf16,
+    one segment, no striping, a power-of-two block of at least 256 tokens
+    for the gate and 64 for the index, at most 32 blocks) are checked before
+    any HIP call."""
+    L = abi.lib()
+    p = prob(abi, cu=[0, 8192])
+    P = ctypes.byref(p)
+    nb = ctypes.c_size_t()
+    assert L.vs_workspace_size(P, 4, None, ctypes.byref(nb)) == abi.VS_OK
+    assert nb.value >= 2 * 32 * 128 * 4        # the blocks' mean keys, fp32, room for 32 blocks
+    big = 1 << 40
+    est = L.vs_estimate_index_moba
+    assert est(P, None, FAKE, 512, 4, FAKE, None, FAKE, big, None) == abi.VS_ERR_NULL
+    assert est(P, FAKE, FAKE, 512, 4, None, None, FAKE, big, None) == abi.VS_ERR_NULL
+    assert est(P, FAKE, FAKE, 128, 4, FAKE, None, FAKE, big, None) == abi.VS_ERR_UNSUPPORTED   # block < 256
+    assert est(P, FAKE, FAKE, 768, 4, FAKE, None, FAKE, big, None) == abi.VS_ERR_UNSUPPORTED   # not a power of 2
+    p64 = prob(abi, cu=[0, 16384])              # 64 blocks of 256: beyond the 32 a row's word holds
+    assert est(ctypes.byref(p64), FAKE, FAKE, 256, 4, FAKE, None, FAKE, big, None) == abi.VS_ERR_UNSUPPORTED
+    assert est(P, FAKE, FAKE, 512, 0, FAKE, None, FAKE, big, None) == abi.VS_ERR_SHAPE
+    assert est(P, FAKE, FAKE, 512, 4, FAKE, None, FAKE, 16, None) == abi.VS_ERR_WORKSPACE
+    for bad in (prob(abi, dtype=abi.VS_F32, cu=[0, 8192]), prob(abi, cu=[0, 4096, 8192]),
+                prob(abi, cu=[0, 8192], n_q=1024, n_k=1024, stripe_world=8)):
+        assert est(ctypes.byref(bad), FAKE, FAKE, 512, 4, FAKE, None, FAKE, big, None) == abi.VS_ERR_UNSUPPORTED
+    # a per-row selection in the index
+    ix = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 0, 0, None, 0, 0x1000, 512)
+    assert L.vs_workspace_size(P, 2, ctypes.byref(ix), ctypes.byref(nb)) == abi.VS_OK
+    for rb in (32, 96, 128):                    # below 64, not a power of 2, 64 blocks at n = 8192
+        bad_ix = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 0, 0, None, 0, 0x1000, rb)
+        assert L.vs_workspace_size(P, 1, ctypes.byref(bad_ix), ctypes.byref(nb)) == abi.VS_ERR_UNSUPPORTED
+    both = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0x1000, 128, 0x1000, 512)
+    assert L.vs_workspace_size(P, 1, ctypes.byref(both), ctypes.byref(nb)) == abi.VS_ERR_INDEX
+    lists = abi.VsIndex(0x1000, 0x1000, 0x1000, 0x1000, 64, 4, None, 0, 0x1000, 512)
+    assert L.vs_workspace_size(P, 2, ctypes.byref(lists), ctypes.byref(nb)) == abi.VS_ERR_INDEX
+    for bad in (prob(abi, dtype=abi.VS_F32, cu=[0, 8192]), prob(abi, cu=[0, 4096, 8192])):
         assert L.vs_workspace_size(ctypes.byref(bad), 1, ctypes.byref(ix),
                                    ctypes.byref(nb)) == abi.VS_ERR_UNSUPPORTED

@@ -396,3 +396,45 @@ def test_block_selection_in_bounds(n, batch, h_q, h_kv):
     for d in (64, 128):
         xattn_estimator_addresses(n, batch, h_q, h_kv, d)
 
+
+
+@pytest.mark.parametrize("n,batch,h_q,h_kv,blk", [(4096, 2, 4, 1, 256), (4160, 1, 2, 1, 512),
+                                                 (131072, 1, 16, 2, 4096)])
+def test_per_row_selection_in_bounds(n, batch, h_q, h_kv, blk):
+    """MoBA gate and per-row selection walks: the gate's workgroups (256 rows
+    inside one key block), the mean and score indices, the query-major walk's
+    row words and tiles, the key-major walk's union words, staged row words
+    and picked-block bit."""
+    assert blk >= 256 and blk & (blk - 1) == 0 and n <= 32 * blk
+    nB = -(-n // blk)
+    rows_words = batch * h_q * n
+    # gate: workgroup of rows r0 .. r0 + 255 shares its own block
+    for r0 in range(0, n, 256):
+        rows = np.arange(r0, min(r0 + 256, n))
+        assert np.all(rows // blk == r0 // blk)
+        own = r0 // blk
+        assert own < nB <= 32 and own * 128 <= 32 * 128      # the LDS block means
+    for J in range(nB):
+        r0, r1 = J * blk, min((J + 1) * blk, n)
+        assert 0 <= r0 < r1 <= n
+    assert (batch * h_q * n - 1) * nB + nB - 1 < batch * h_q * n * nB   # gate scores
+    # query-major: 64 row words of query block i, tiles kb <= beta
+    nqb = n // BLOCK
+    shift = int(np.log2(blk // BLOCK))
+    for bh in (0, batch * h_q - 1):
+        for i in (0, nqb // 2, nqb - 1):
+            idx = bh * n + i * BLOCK + np.arange(BLOCK)
+            assert idx.max() < rows_words
+            kb = np.arange(i + 1)
+            assert np.all((kb >> shift) < 32) and np.all(4 * kb + 3 < 2 ** 31)
+    # key-major: union word of (bh, query block), staged words of 32-row halves
+    for bh in (0, batch * h_q - 1):
+        for j in (0, nqb // 2, nqb - 1):
+            ib = np.arange(j + 1, nqb)
+            assert np.all(bh * nqb + ib < batch * h_q * nqb)
+            pick = j >> shift
+            assert pick < 32
+            for i in ib[:3]:
+                for half in (0, 1):
+                    li = bh * n + i * BLOCK + 32 * half + np.arange(32)
+                    assert li.max() < rows_words
