@@ -329,10 +329,13 @@ def main():
     ap.add_argument("--topp", default=None, metavar="P_V,P_S",
                     help="estimate with top-p budgets (vs_estimate_index_topp) at these mass "
                          "fractions, the workload's budgets as caps")
-    ap.add_argument("--estimator", choices=("vs", "xattn"), default="vs",
+    ap.add_argument("--estimator", choices=("vs", "xattn", "moba"), default="vs",
                     help="vs: the Vertical-Slash index (default); xattn: XAttention block "
-                         "selection (vs_estimate_index_xattn, block 128, stride 16)")
+                         "selection (vs_estimate_index_xattn, block 128, stride 16); moba: the MoBA "
+                         "block gate (vs_estimate_index_moba)")
     ap.add_argument("--threshold", type=float, default=0.9, help="XAttention selection threshold")
+    ap.add_argument("--moba-block", type=int, default=4096, help="MoBA key block (tokens)")
+    ap.add_argument("--moba-topk", type=int, default=12, help="MoBA blocks per query")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--write-traffic", metavar="RUN_DIR", default=None,
@@ -358,8 +361,8 @@ def main():
             raise SystemExit("--topp takes P_V,P_S")
     if topp is not None and args.workload == 4:
         raise SystemExit("--topp is for the contiguous workloads")
-    if args.estimator == "xattn" and (topp is not None or args.workload in (4, 5)):
-        raise SystemExit("--estimator xattn takes one contiguous segment (workloads 1-3), no --topp")
+    if args.estimator != "vs" and (topp is not None or args.workload in (4, 5)):
+        raise SystemExit("--estimator xattn / moba take one contiguous segment (workloads 1-3), no --topp")
 
     pool = None
     if args.copy_probe:
@@ -399,6 +402,7 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
     stream = torch.cuda.current_stream(dev)
     worker = args.workload == 4
     xattn = args.estimator == "xattn"
+    moba = args.estimator == "moba"
     if not worker:
         q, k, v, do = (t.to(dev) for t in (prob.q, prob.k, prob.v, prob.do))
         o = torch.empty_like(q)
@@ -410,6 +414,8 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
         def estimate():
             if xattn:
                 return vs.estimate_index_xattn(q, k, args.threshold)[0]
+            if moba:
+                return vs.estimate_index_moba(q, k, args.moba_block, args.moba_topk)
             if topp is None:
                 return vs.estimate_index(q, k, prob.v_budget, prob.s_budget, cu)
             return vs.estimate_index_topp(q, k, prob.v_budget, prob.s_budget, [topp[0]] * Hq,
@@ -497,6 +503,10 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
         # block selection: every entry is walked by the block-tile path of the
         # query-major kernels and the slash dK/dV kernel
         ent = int(accounting.block_selection_area(idx.block_selection(prob.n).numpy(), prob.n).sum())
+        entries = {"all": ent, "slash": ent, "vertical": 0}
+    elif moba:
+        # per-row selection: the same tile paths, masked per row
+        ent = int(accounting.row_selection_area(idx.row_mask.cpu().numpy(), prob.n, args.moba_block).sum())
         entries = {"all": ent, "slash": ent, "vertical": 0}
     else:
         ent_heads = accounting.executed_area(lists, cu, Hq, row_blocks=row_blocks)
@@ -609,7 +619,9 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
                "v_budget": prob.v_budget[0] if len(set(prob.v_budget)) == 1 else list(prob.v_budget),
                "s_budget": prob.s_budget[0] if len(set(prob.s_budget)) == 1 else list(prob.s_budget),
                "estimator": (f"XAttention block selection, block 128, stride 16, threshold {args.threshold}"
-                             if xattn else "fixed budgets" if topp is None else
+                             if xattn else
+                             f"MoBA gate, block {args.moba_block}, top-{args.moba_topk}" if moba else
+                             "fixed budgets" if topp is None else
                              f"top-p p_v={topp[0]} p_s={topp[1]} (budgets as caps)"),
                "executed_entries": ent, "slash_entries": entries["slash"],
                "vertical_entries": entries["vertical"], "causal_entries": dense,

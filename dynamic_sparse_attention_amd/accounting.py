@@ -103,3 +103,21 @@ def block_selection_area(sel: np.ndarray, n: int, blk: int = 128) -> np.ndarray:
     off = (sel & below).sum(axis=-1).astype(np.int64)           # [..., nI] blocks J < I
     diag = np.diagonal(sel, axis1=-2, axis2=-1).astype(np.int64)
     return (off * rows * blk + diag * rows * (rows + 1) // 2).sum(axis=-1)
+
+
+def row_selection_area(words: np.ndarray, n: int, blk: int) -> np.ndarray:
+    """Valid entries per leading index of per-row block selections
+    words [..., n] (bit J of a row's word picks key block J of blk tokens):
+    row r counts, for each picked block J, its keys m <= r.  Returns int64 [...]."""
+    w = np.asarray(words).astype(np.int64) & 0xFFFFFFFF
+    lead = w.shape[:-1]
+    w = w.reshape(-1, n)
+    nB = -(-n // blk)
+    r = np.arange(n, dtype=np.int64)[:, None]
+    J = np.arange(nB, dtype=np.int64)[None, :]
+    keys = np.clip(np.minimum(r + 1, (J + 1) * blk) - J * blk, 0, None)   # [n, nB]
+    out = np.empty(w.shape[0], dtype=np.int64)
+    for i in range(w.shape[0]):
+        bits = (w[i][:, None] >> J) & 1
+        out[i] = int((bits * keys).sum())
+    return out.reshape(lead)

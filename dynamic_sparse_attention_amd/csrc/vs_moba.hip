@@ -20,27 +20,37 @@
 namespace vs {
 
 
-// One workgroup per (batch, KV head, key block): the mean of its keys, one
-// channel per thread group of 256 / d threads summing every (256 / d)-th row.
+// One workgroup per (batch, KV head, key block): the mean of its keys.
+// Thread t reads 8 channels (c8 = t % (D / 8), one 16-byte load per row) of
+// every RG-th row starting at t / (D / 8); the RG partial sums of a channel
+// are then added in a fixed order, so the means (and the picks) are the same
+// in every run.
 template <int D>
-__global__ __launch_bounds__(256) void vs_moba_means_kernel(MobaParams p) {
-  constexpr int TPC = 256 / D;  // threads per channel
-  __shared__ float part[TPC][D];
+__global__ __launch_bounds__(512) void vs_moba_means_kernel(MobaParams p) {
+  constexpr int CH = D / 8;        // 16-byte chunks per row
+  constexpr int RG = 512 / CH;     // row groups
+  __shared__ float part[RG][D];
   const int J = blockIdx.x % p.nB;
   const int bk = blockIdx.x / p.nB;  // b * h_kv + kvh
   const int b = bk / p.h_kv, kvh = bk % p.h_kv;
-  const int c = threadIdx.x % D, t = threadIdx.x / D;
+  const int c8 = threadIdx.x % CH, g = threadIdx.x / CH;
   const int r0 = J * p.blk, r1 = min(r0 + p.blk, p.n);
-  const __bf16* kb = p.k + p.sk.at(b, 0, kvh);
-  float acc = 0.f;
-  for (int r = r0 + t; r < r1; r += TPC) acc += (float)kb[(size_t)r * p.sk.t + c];
-  part[t][c] = acc;
-  __syncthreads();
-  if (t == 0) {
-    float s = 0.f;
+  const __bf16* kb = p.k + p.sk.at(b, 0, kvh) + 8 * c8;
+  float acc[8];
 #pragma unroll
-    for (int u = 0; u < TPC; ++u) s += part[u][c];
-    p.kbar[((size_t)bk * p.nB + J) * D + c] = s / (float)(r1 - r0);
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int r = r0 + g; r < r1; r += RG) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(kb + (size_t)r * p.sk.t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[g][8 * c8 + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float s = 0.f;
+    for (int u = 0; u < RG; ++u) s += part[u][threadIdx.x];
+    p.kbar[((size_t)bk * p.nB + J) * D + threadIdx.x] = s / (float)(r1 - r0);
   }
 }
 
@@ -105,10 +115,10 @@ hipError_t launch_moba(const MobaParams& p, hipStream_t st) {
   const dim3 gs((unsigned)(p.batch * p.h_q * ((p.n + 255) / 256)));
   if (gs.x == 0) return hipSuccess;
   if (p.d == 128) {
-    VS_TRACED(st, "vs_moba_means", hipLaunchKernelGGL((vs_moba_means_kernel<128>), gm, dim3(256), 0, st, p));
+    VS_TRACED(st, "vs_moba_means", hipLaunchKernelGGL((vs_moba_means_kernel<128>), gm, dim3(512), 0, st, p));
     VS_TRACED(st, "vs_moba_select", hipLaunchKernelGGL((vs_moba_select_kernel<128>), gs, dim3(256), 0, st, p));
   } else {
-    VS_TRACED(st, "vs_moba_means", hipLaunchKernelGGL((vs_moba_means_kernel<64>), gm, dim3(256), 0, st, p));
+    VS_TRACED(st, "vs_moba_means", hipLaunchKernelGGL((vs_moba_means_kernel<64>), gm, dim3(512), 0, st, p));
     VS_TRACED(st, "vs_moba_select", hipLaunchKernelGGL((vs_moba_select_kernel<64>), gs, dim3(256), 0, st, p));
   }
   return hipGetLastError();

@@ -298,6 +298,16 @@ def test_executed_area_matches_oracle():
     pos = np.arange(n)
     ref = [int(oracle.dense_mask(pos, pos, [0, n], bidx, h).sum()) for h in range(2)]
     assert accounting.block_selection_area(sel, n).tolist() == ref
+    # a per-row selection (blocks of 32 tokens, a short last block): the oracle's mask count
+    n, blk = 32 * 5 + 16, 32
+    nB = 6
+    own = np.arange(n) // blk
+    rsel = (rng.random((2, n, nB)) < 0.5) & (np.arange(nB)[None, None, :] <= own[None, :, None])
+    ridx = {(h, 0): (e, e, None, (blk, rsel[h])) for h in range(2)}
+    pos = np.arange(n)
+    ref = [int(oracle.dense_mask(pos, pos, [0, n], ridx, h).sum()) for h in range(2)]
+    words = (rsel * (1 << np.arange(nB))[None, None, :]).sum(axis=-1)
+    assert accounting.row_selection_area(words, n, blk).tolist() == ref
 
 
 def test_xattn_and_block_selection_validation(abi):

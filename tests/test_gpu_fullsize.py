@@ -539,3 +539,110 @@ def test_fullsize_xattn():
     errs += _dv_identity("xattn", dv[0], gv[0], o[0], gdo[0], hq, hkv)
     errs = [e for e in errs if e]
     assert not errs, errs
+
+
+def test_fullsize_moba():
+    """MoBA (block 4096, top-12) at N = 131072 on workload 3's inputs, in
+    bench.py --estimator moba's launch configuration.
+
+    Gate: for every Q head and row, the device's word equals the selection
+    recomputed from its own fp32 scores; for one Q head per KV group, the
+    scores and words against the oracle (certified near ties allowed).
+    Attention on the per-row selection: those two heads take the oracle's
+    selection, the others seeded ones (the own block and 11 random earlier
+    blocks); O, LSE and dQ of sampled query blocks of the two heads, dK and dV
+    of the last key blocks from all heads, and the group identities."""
+    from test_gpu_moba import SCORE_REL, check_gate, words_of
+    dev = _dev()
+    block, topk = 4096, 12
+    log("full-size MoBA: drawing inputs (workload 3)")
+    prob = workloads.make_problem(3)
+    n, hq, hkv = prob.n, prob.h_q, prob.h_kv
+    G = hq // hkv
+    nB = n // block
+    cu = prob.cu_seqlens
+    gq, gk, gv, gdo = (t.to(dev) for t in (prob.q, prob.k, prob.v, prob.do))
+    log("  GPU gate")
+    gidx, gsc = vs.estimate_index_moba(gq, gk, block, topk, return_scores=True)
+    torch.cuda.synchronize()
+    words = gidx.row_mask[0].cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    gsc = gsc[0].cpu().numpy()
+    del gidx
+    own = np.arange(n) // block
+    J = np.arange(nB)
+    earlier = J[None, :] < own[:, None]
+    for h in range(hq):
+        s = gsc[h]
+        # rank of J among the row's earlier blocks (higher first, ties to the lower index)
+        beats = (s[:, :, None] > s[:, None, :]) | ((s[:, :, None] == s[:, None, :]) & (J[:, None] < J[None, :]))
+        rank = (beats & earlier[:, :, None]).sum(axis=1)
+        pick = (earlier & (rank < topk - 1)) | (J[None, :] == own[:, None])
+        assert np.array_equal(words[h], words_of(pick)), h
+    heads = [grp * G for grp in range(hkv)]
+    q64, k64 = np64(prob.q[0]), np64(prob.k[0])
+    sels = {}
+    for h in heads:
+        log(f"  oracle gate, head {h}")
+        out, osc = oracle.estimate_index_moba(q64[:, h:h + 1], k64[:, h // G:h // G + 1], cu, block, topk,
+                                              return_scores=True)
+        sels[h] = out[(0, 0)][3][1]
+        worst, flips = check_gate(("moba", h), q64[:, h], k64[:, h // G], n, block, topk, gsc[h], words[h],
+                                  sels[h], osc[(0, 0)])
+        log(f"  head {h}: score err/bound max {worst:.2e}, certified near-tie rows {flips}; "
+            f"{int(sels[h].sum())} row-blocks picked")
+    del gsc
+    rng = np.random.default_rng(prob.seed + 91)
+    allsel = []
+    for h in range(hq):
+        if h in sels:
+            allsel.append(sels[h])
+            continue
+        s = np.zeros((n, nB), bool)
+        s[np.arange(n), own] = True
+        for b_ in range(1, nB):
+            rows = np.arange(b_ * block, (b_ + 1) * block)
+            r = rng.random((rows.size, b_)).argsort(axis=1)[:, :topk - 1]
+            s[rows[:, None], r] = True
+        allsel.append(s)
+    w = np.stack([words_of(s) for s in allsel]).astype(np.uint32).view(np.int32)
+    zeros = torch.zeros(hq + 1, dtype=torch.int32, device=dev)
+    one = torch.zeros(1, dtype=torch.int32, device=dev)
+    idx = vs.VsIndexT(zeros, one, zeros, one, 0, 0,
+                      row_mask=torch.from_numpy(w).reshape(1, hq, n).to(dev), row_blk=block)
+    log("  GPU forward + backward on the per-row selection")
+    o, lse = vs.sparse_attn_fwd(gq, gk, gv, idx)
+    dq, dk, dv = vs.sparse_attn_bwd(gq, gk, gv, o, gdo, lse, idx)
+    torch.cuda.synchronize()
+    empty = np.zeros(0, np.int64)
+    cols = np.arange(n)
+    v64 = np64(prob.v[0])
+    errs = []
+    blocks = _sample_blocks(n // 64, np.random.default_rng(prob.seed))
+    rows = _rows_of_blocks(blocks)
+    sub = {(i, 0): (empty, empty, None, (block, allsel[h])) for i, h in enumerate(heads)}
+    log(f"  oracle on {len(blocks)} sampled query blocks of heads {heads}")
+    q_r, do_r = q64[rows][:, heads], np64(prob.do[0, rows][:, heads])
+    O, L = oracle.attn_fwd_support(q_r, k64, v64, rows, cols, cu, sub)
+    D = oracle.bwd_delta(O, do_r)
+    dq_o, _, _ = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, cols, cu, sub)
+    bq, _, _ = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, sub, support=True)
+    rt = torch.from_numpy(rows).to(dev)
+    ht = torch.tensor(heads, device=dev)
+    errs += [check_close("moba O (sampled)", O, np64(o[0, rt][:, ht]), "bf16", "o"),
+             check_close("moba LSE (sampled)", L, np64(lse[0][ht][:, rt]), "bf16"),
+             check_close("moba dQ (sampled)", dq_o, np64(dq[0, rt][:, ht]), "bf16", "grad", bq)]
+    rows = _rows_of_blocks(range(n // 64 - TAIL, n // 64))
+    full = {(h, 0): (empty, empty, None, (block, allsel[h])) for h in range(hq)}
+    log(f"  oracle on the last {TAIL} query blocks, all heads")
+    q_r, do_r = q64[rows], np64(prob.do[0, rows])
+    O, L = oracle.attn_fwd_support(q_r, k64, v64, rows, cols, cu, full)
+    D = oracle.bwd_delta(O, do_r)
+    _, dk_o, dv_o = oracle.attn_bwd_support(q_r, k64, v64, do_r, L, D, rows, cols, cu, full)
+    _, bk, bv = oracle.bwd_rounding_bounds(q_r, k64, v64, do_r, O, L, rows, cols, cu, full, support=True)
+    rt = torch.from_numpy(rows).to(dev)
+    errs += [check_close("moba dK (tail keys)", dk_o[rows], np64(dk[0, rt]), "bf16", "grad", bk[rows]),
+             check_close("moba dV (tail keys)", dv_o[rows], np64(dv[0, rt]), "bf16", "grad", bv[rows])]
+    errs += _group_identity("moba", dq[0], gq[0], dk[0], gk[0], hq, hkv)
+    errs += _dv_identity("moba", dv[0], gv[0], o[0], gdo[0], hq, hkv)
+    errs = [e for e in errs if e]
+    assert not errs, errs
