@@ -182,3 +182,71 @@ def test_row_selection_attention(name):
     log(f"case row selection {name}: n={n} hq={hq} hkv={prob.h_kv} d={prob.d} block={block} "
         f"picked {int(sum(s.sum() for s in sels))} row-blocks")
     _attn_case(name, prob, sels, block, dev)
+
+
+def test_moba_batch2_and_strided_estimators():
+    """Batch 2 (two seeded rows) for the MoBA gate and attention on its
+    picks, and both alternative estimators on Q / K sliced from a fused
+    [B, N, Hq + 2 Hkv, d] projection: their outputs equal those of the same
+    values in contiguous tensors bit for bit."""
+    dev = _dev()
+    block, topk = 256, 3
+    p1 = workloads.make_problem(2, n=2048, h_q=4, h_kv=1, seed=21)
+    p2 = workloads.make_problem(2, n=2048, h_q=4, h_kv=1, seed=22)
+    q = torch.cat([p1.q, p2.q])
+    k = torch.cat([p1.k, p2.k])
+    v = torch.cat([p1.v, p2.v])
+    do = torch.cat([p1.do, p2.do])
+    gq, gk, gv, gdo = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    gidx, gsc = vs.estimate_index_moba(gq, gk, block, topk, return_scores=True)
+    torch.cuda.synchronize()
+    words = gidx.row_mask.cpu().numpy()
+    osels = []
+    for b, p in enumerate((p1, p2)):
+        q64, k64 = np64(p.q[0]), np64(p.k[0])
+        osel, osc = oracle.estimate_index_moba(q64, k64, p.cu_seqlens, block, topk, return_scores=True)
+        osels.append(osel)
+        for h in range(4):
+            check_gate(("b", b, h), q64[:, h], k64[:, 0], 2048, block, topk, gsc[b, h].cpu().numpy(), words[b, h],
+                       osel[(h, 0)][3][1], osc[(h, 0)])
+    # attention, batch 2, on the oracle's picks packed into row words
+    ow = np.stack([[words_of(o[(h, 0)][3][1]) for h in range(4)] for o in osels]).astype(np.uint32)
+    zeros = torch.zeros(2 * 4 + 1, dtype=torch.int32, device=dev)
+    one = torch.zeros(1, dtype=torch.int32, device=dev)
+    idx = vs.VsIndexT(zeros, one, zeros, one, 0, 0, row_mask=torch.from_numpy(ow.view(np.int32)).to(dev),
+                      row_blk=block)
+    o, lse = vs.sparse_attn_fwd(gq, gk, gv, idx)
+    gdq, gdk, gdv = vs.sparse_attn_bwd(gq, gk, gv, o, gdo, lse, idx)
+    torch.cuda.synchronize()
+    pos = np.arange(2048)
+    errs = []
+    for b, p in enumerate((p1, p2)):
+        osel = osels[b]
+        q64, k64 = np64(p.q[0]), np64(p.k[0])
+        v64, do64 = np64(p.v[0]), np64(p.do[0])
+        O, L = oracle.attn_fwd_dense(q64, k64, v64, pos, pos, p.cu_seqlens, osel)
+        D = oracle.bwd_delta(O, do64)
+        dq, dk, dv = oracle.attn_bwd_dense(q64, k64, v64, do64, L, D, pos, pos, p.cu_seqlens, osel)
+        bq, bk, bv = oracle.bwd_rounding_bounds(q64, k64, v64, do64, O, L, pos, pos, p.cu_seqlens, osel)
+        errs += [check_close(f"b{b} O", O, np64(o[b]), "bf16", "o"),
+                 check_close(f"b{b} LSE", L, lse[b].cpu().numpy().astype(np.float64), "bf16"),
+                 check_close(f"b{b} dQ", dq, np64(gdq[b]), "bf16", "grad", bq),
+                 check_close(f"b{b} dK", dk, np64(gdk[b]), "bf16", "grad", bk),
+                 check_close(f"b{b} dV", dv, np64(gdv[b]), "bf16", "grad", bv)]
+    errs = [e for e in errs if e]
+    assert not errs, errs
+    # fused projection: [B, N, Hq + 2 Hkv, d], Q / K / V as head slices
+    fused = torch.cat([q, k, v], dim=2).to(dev)
+    fq, fk = fused[:, :, :4], fused[:, :, 4:5]
+    assert fq.stride(1) == 6 * 128 and not fq.is_contiguous()
+    sidx, ssc = vs.estimate_index_moba(fq, fk, block, topk, return_scores=True)
+    xidx, xcnt, xsc = vs.estimate_index_xattn(gq, gk, 0.9, return_scores=True)
+    fxidx, fxcnt, fxsc = vs.estimate_index_xattn(fq, fk, 0.9, return_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sidx.row_mask, gidx.row_mask)
+    own = torch.arange(2048, device=dev) // block
+    early = torch.arange(2048 // block, device=dev)[None, :] < own[:, None]
+    assert torch.equal(ssc[:, :, early], gsc[:, :, early])
+    assert torch.equal(fxidx.blk_mask, xidx.blk_mask) and torch.equal(fxcnt, xcnt)
+    tril = torch.tril(torch.ones(16, 16, dtype=torch.bool, device=dev))
+    assert torch.equal(fxsc[:, :, tril], xsc[:, :, tril])
