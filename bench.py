@@ -47,6 +47,34 @@ ISSUED_PER_ENTRY = {"vs_fwd": 4, "vs_bwd_dq": 6, "vs_bwd_dkdv_slash": 8, "vs_bwd
 ENTRY_KIND = {"vs_fwd": "all", "vs_bwd_dq": "all", "vs_bwd_dkdv_slash": "slash",
               "vs_bwd_dkdv_cols": "vertical"}
 
+# HBM peak of MI355X (published), for the bandwidth-bound kernels.
+HBM_PEAK_GBS = 8000.0
+
+
+def hbm_alg_bytes(name, c):
+    """Algorithmic bytes per launch of the bandwidth-bound kernels: what each
+    must read and write once.  c: batch, n, h_q, h_kv, d, el (input element
+    bytes), n_lists, tiles (256-key estimator tiles), nb (64-blocks), v_ent /
+    s_ent (vertical / block-diagonal list entries, padding included)."""
+    K = c["batch"] * c["n"] * c["h_kv"] * c["d"] * c["el"]
+    Qw = c["n_lists"] * 64 * c["d"] * c["el"]                 # the window rows of every list
+    part = c["batch"] * c["h_q"] * c["tiles"] * 64 * 8         # (max, sum) per window row and key tile
+    lse = c["n_lists"] * 64 * 4
+    vsc = c["batch"] * c["h_q"] * c["n"] * 4                   # column scores v[m]
+    ssc = c["batch"] * c["h_q"] * c["nb"] * 4                  # block-diagonal scores
+    lists = 4 * (c["v_ent"] + c["s_ent"])
+    table = {
+        "vs_est_pass1": K + Qw + part,
+        "vs_est_combine": part + lse,
+        "vs_est_pass2": K + Qw + lse + vsc + ssc,
+        "vs_est_topk": vsc + ssc + lists,
+        "vs_prep_vertical": 2 * 4 * c["v_ent"],
+        "vs_moba_means": K,
+        "vs_moba_select": c["batch"] * c["n"] * c["h_q"] * (c["d"] * c["el"] + 4),
+    }
+    return table.get(name)
+
+
 # HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE, each scaled by what the same counter reads for a plain copy of
 # known size) are kept per workload in profiles/hbm_traffic_<workload>.json,
@@ -539,7 +567,7 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
     exec_tf = 14 * d * ent / (ms * 1e-3) / 1e12
     dense_tf = 14 * d * dense / (ms * 1e-3) / 1e12
     log(f"step {ms:.3f} ms; phases {phases}")
-    one_call = None
+    one_call = merge_rec = None
     if worker:
         for _ in range(args.warmup):
             step_one()
@@ -559,10 +587,32 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
                                   "bwd": round(float(np.mean([e[1].elapsed_time(e[2]) for e in ev1])), 4)},
                     "kernels_avg_ms": {n_: round(t_ / c_, 4) for n_, (c_, t_) in kern1.items()}}
         log(f"one call over all chunks: {ms1:.3f} ms per step; {one_call}")
+        # the boundary's lse_merge on the worker's share (fp32 O [1, rows,
+        # H_q, d] and LSE), a standalone call: read both results, write one
+        o_part, l_part = acc_o.clone(), acc_l.clone()
+        for _ in range(2):
+            vs.lse_merge(acc_o, acc_l, o_part, l_part)
+        torch.cuda.synchronize()
+        lib.vs_trace_enable(1)
+        for _ in range(10):
+            vs.lse_merge(acc_o, acc_l, o_part, l_part)
+        torch.cuda.synchronize()
+        lib.vs_trace_enable(0)
+        cnt_m, tot_m = trace_read(vs)["vs_lse_merge"]
+        mb = 3 * acc_o.numel() * 4 + 3 * acc_l.numel() * 4
+        avg_m = tot_m / cnt_m * 1e-3
+        merge_rec = {"avg_ms": round(tot_m / cnt_m, 4), "alg_bytes": int(mb),
+                     "alg_gbs": round(mb / avg_m / 1e9, 1), "alg_hbm_frac": round(mb / avg_m / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"lse_merge on the worker's share: {merge_rec}")
     for name, (cnt, tot) in sorted(kern.items(), key=lambda x: -x[1][1]):
         log(f"  kernel {name}: {cnt} launches, avg {tot / cnt:.4f} ms, {tot / args.steps:.4f} ms per step")
 
     peak = PEAK_TFLOPS[prob.dtype]
+    seg_len = np.diff(np.asarray(cu))
+    shape = {"batch": 1, "n": prob.n, "h_q": Hq, "h_kv": prob.h_kv, "d": d,
+             "el": 2 if prob.dtype == "bf16" else 4, "n_lists": Hq * len(seg_len),
+             "tiles": int(sum(-(-int(L) // 256) for L in seg_len)), "nb": prob.n // 64,
+             "v_ent": int(sum(a_.size for a_, _ in lists)), "s_ent": int(sum(b_.size for _, b_ in lists))}
     # Per attention kernel: its own share of the method's work and the work it
     # issues, per step, and the rates over its time per step.
     per_kernel = {}
@@ -583,6 +633,16 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
             own = 2 * 16 * d * (nC * (nC + 1) // 2) * Hq
             rec.update(own_tflop=round(own / 1e12, 4), own_tflops=round(own / (ms_step * 1e-3) / 1e12, 2),
                        own_frac=round(own / (ms_step * 1e-3) / 1e12 / peak, 4))
+        ab = hbm_alg_bytes(name, shape)
+        if ab is not None:
+            # bandwidth-bound kernels: algorithmic bytes (and the counters'
+            # HBM bytes, when current) over the average launch
+            avg = tot / cnt * 1e-3
+            rec.update(alg_bytes=int(ab), alg_gbs=round(ab / avg / 1e9, 1),
+                       alg_hbm_frac=round(ab / avg / 1e9 / HBM_PEAK_GBS, 4))
+            hb = measured_traffic(name, prob.name)
+            if hb is not None:
+                rec.update(hbm_bytes=hb, hbm_gbs=round(hb / avg / 1e9, 1))
         per_kernel[name] = rec
 
     # Roofline of the dominant kernel (largest time per step): its own share
@@ -612,7 +672,7 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
         wl = {"workload": prob.name, "batch": 1, "seq_len": prob.n, "stripe_world": prob.stripe_world,
               "worker": prob.stripe_rank, "worker_rows": int(row_pos.size), "kv_chunks": prob.stripe_world,
               "ring": "fwd per chunk with the merge fused (o_f32=2), delta, bwd per chunk accumulating dQ",
-              "one_call": one_call}
+              "one_call": one_call, "lse_merge": merge_rec}
     else:
         wl = {"workload": prob.name, "batch": 1, "seq_len": prob.n, "segments": len(cu) - 1}
     wl.update({"h_q": Hq, "h_kv": prob.h_kv, "head_dim": d, "block": 64,
