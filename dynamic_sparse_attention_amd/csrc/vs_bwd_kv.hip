@@ -58,12 +58,13 @@ typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef __attribute__((address_space(1))) void* glb_vptr;
 
 // Direct loads of query tile (local block i, rows kTR*half .. +kTR, Q head h)
-// into B; each of the two waves issues half of the rows (NDMA / 2
-// instructions) plus one of LSE / delta, and with SEL wave 0 also the rows'
-// picked-block words of a per-row selection.
-template <int D, bool SEL = false>
+// into B; each of the NW waves issues its share of the rows (NDMA / NW
+// instructions), waves 0 and 1 one of LSE / delta, and with SEL one wave
+// (0, or 2 of four) also the rows' picked-block words of a per-row selection.
+template <int D, bool SEL = false, int NW = 2>
 __device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, int b, int h, int i, int half) {
   typedef RowTile<D> RT;
+  static_assert(RT::NDMA % NW == 0, "direct loads per tile must split evenly over the waves");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int row0 = i * kBlock + kTR * half;  // first row of the tile in this batch row
@@ -71,8 +72,8 @@ __device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, in
   const __bf16* db = reinterpret_cast<const __bf16*>(p.dout) + p.sdo.at(b, row0, h);
   const int rsub = lane / RT::CPR;
 #pragma unroll
-  for (int u0 = 0; u0 < RT::NDMA / 2; ++u0) {
-    const int u = w * (RT::NDMA / 2) + u0;
+  for (int u0 = 0; u0 < RT::NDMA / NW; ++u0) {
+    const int u = w * (RT::NDMA / NW) + u0;
     const int chunk = (lane % RT::CPR) ^ RT::swz(u * RT::RPI + rsub);
     const int rr = u * RT::RPI + rsub;  // row of the tile, < kTR
     __builtin_amdgcn_global_load_lds((glb_vptr)(qb + rr * p.sq.t + chunk * 8), (lds_vptr)(B.q + u * 1024), 16, 0, 0);
@@ -80,9 +81,9 @@ __device__ __forceinline__ void kv_tile_dma(const AttnParams& p, KvBuf<D>& B, in
   }
   const size_t li = ((size_t)b * p.h_q + h) * p.n_q + row0 + lane;
   const float* src = w == 0 ? p.lse2 : p.delta;
-  if (lane < kTR)
+  if ((NW == 2 || w < 2) && lane < kTR)
     __builtin_amdgcn_global_load_lds((glb_vptr)(src + li), (lds_vptr)(w == 0 ? B.lse2 : B.del), 4, 0, 0);
-  if (SEL && w == 0 && lane < kTR)
+  if (SEL && w == (NW == 2 ? 0 : 2) && lane < kTR)
     __builtin_amdgcn_global_load_lds((glb_vptr)(p.rmask + li), (lds_vptr)B.sel, 4, 0, 0);
 }
 
@@ -244,11 +245,11 @@ struct KvWorkerB {
   }
 };
 
-template <int D>
+template <int D, int NW = 2>
 struct KvLdsB {
   KvBuf<D> buf[2];
   int tiles[kKvTiles];
-  int wsum[2];
+  int wsum[NW];
 };
 
 // Double-buffered walk over ntiles query tiles: tile_of(t) -> (h, i, flags),
@@ -256,24 +257,24 @@ struct KvLdsB {
 // One pipeline step: the next tile's loads go to nxt while body computes on
 // cur.  The two buffers never overlap; saying so (restrict) lets the compiler
 // see that the reads of cur need not wait for the loads into nxt.
-template <int D, bool SEL, class BodyF>
+template <int D, bool SEL, int NW, class BodyF>
 __device__ __forceinline__ void kv_step(const AttnParams& p, KvBuf<D>* __restrict__ nxt,
                                         const KvBuf<D>* __restrict__ cur, bool more, int b, int h1,
                                         int i1, int half1, int t, int fl, int half, BodyF& body) {
-  if (more) kv_tile_dma<D, SEL>(p, *nxt, b, h1, i1, half1);
+  if (more) kv_tile_dma<D, SEL, NW>(p, *nxt, b, h1, i1, half1);
   body(*cur, t, fl, half);
 }
 
 // Double-buffered walk over the two halves of ntiles query blocks:
 // tile_of(t) -> (h, i, flags), body(B, t, flags, half) computes on the staged
 // half tile.
-template <int D, class TileF, class BodyF, bool SEL = false>
-__device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D>& L, int b, int ntiles,
+template <int D, class TileF, class BodyF, bool SEL = false, int NW = 2>
+__device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D, NW>& L, int b, int ntiles,
                                             TileF tile_of, BodyF body) {
   if (ntiles == 0) return;
   int h, i, fl;
   tile_of(0, &h, &i, &fl);
-  kv_tile_dma<D, SEL>(p, L.buf[0], b, h, i, 0);
+  kv_tile_dma<D, SEL, NW>(p, L.buf[0], b, h, i, 0);
   const int nu = 2 * ntiles;
   for (int u = 0; u < nu; ++u) {
     // this wave's loads of step u are done; the barrier makes every wave's
@@ -284,8 +285,8 @@ __device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D>& L, i
     const bool more = u + 1 < nu;
     if (more) tile_of((u + 1) >> 1, &h1, &i1, &fl1);
     tile_of(u >> 1, &h, &i, &fl);
-    kv_step<D, SEL>(p, &L.buf[(u + 1) & 1], &L.buf[u & 1], more, b, h1, i1, (u + 1) & 1, u >> 1, fl,
-                    u & 1, body);
+    kv_step<D, SEL, NW>(p, &L.buf[(u + 1) & 1], &L.buf[u & 1], more, b, h1, i1, (u + 1) & 1, u >> 1, fl,
+                        u & 1, body);
   }
   __syncthreads();
 }
@@ -418,6 +419,123 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   wk.store(p, b, kvh, kpos, p.kv_accumulate ? 1 : 0);
 }
 
+// Block and per-row selections (one segment): a workgroup of four waves owns
+// the key blocks kb0 = 2 jp and kb0 + 1 (waves 2 kp + kh hold keys
+// 32 kh .. +31 of block kb0 + kp).  Where both blocks lie in one selection
+// block (always for 128-token block selections, and for per-row selections
+// of 128 tokens or more, as the MoBA gate's), a later query block is
+// selected for both or for neither and every staged Q / dO tile serves all
+// four waves: half the tile loads of one block per workgroup.  (A per-row
+// selection of 64-token blocks stages the query blocks either block picked,
+// each wave masking the rows by its own block's bit.)  The diagonal
+// walk stages query blocks kb0 and kb0 + 1 (causal inside their own key
+// block, fully visible to kb0 from kb0 + 1, invisible to kb0 + 1 from kb0);
+// the main walk the query blocks after kb0 + 1.  With an odd block count the
+// second block of the last pair is absent: its waves take part in the loads
+// and barriers only.
+constexpr int kKvPairThreads = 256;
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kKvPairThreads) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_kv_pair_bf16_kernel(AttnParams p) {
+  static_assert(MODE == kModeBlocks || MODE == kModeRows, "pairs serve block and per-row selections");
+  constexpr bool ROWS = MODE == kModeRows;
+  constexpr int NW = kKvPairThreads / 64;
+  typedef KvWorkerB<D> W;
+  __shared__ KvLdsB<D, NW> L;
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wv & 1;
+  const int kp = wv >> 1;
+  const int l32 = tid & 31;
+  const int BH = p.batch * p.h_kv;
+  const int bh = blockIdx.x % BH;
+  const int jp = blockIdx.x / BH;
+  const int b = bh / p.h_kv;
+  const int kvh = bh % p.h_kv;
+  const int G = p.h_q / p.h_kv;
+  const int nb = p.nkb;  // one segment: local = global blocks
+  const int kb0 = 2 * jp;
+  const int kbw = kb0 + kp;  // this wave's key block
+  const bool live = kbw < nb;
+  const int kin = 32 * kh + l32;
+  const int kpos = (live ? kbw : kb0) * kBlock + kin;  // an absent block reads kb0's keys, unused
+  // per-row selections: this wave's picked-block bit, and both blocks' bits
+  const int pick = ROWS ? (kbw >> p.rm_shift) : 0;
+  const uint32_t picks = ROWS ? ((1u << (kb0 >> p.rm_shift)) | (1u << ((kb0 + 1) >> p.rm_shift))) : 0u;
+
+  W wk;
+  wk.init_offsets();
+  wk.load_keys(p, b, kvh, kpos);
+  auto tile_of = [&](int t, int* h, int* i, int* fl) {
+    const int v = L.tiles[t];
+    *h = kvh * G + (v >> 26);
+    *i = (v >> 1) & ((1 << 25) - 1);
+    *fl = v & 1;
+  };
+  auto selected = [&](int list, int ib) -> bool {
+    if (ROWS) return (p.rm_union[(size_t)list * p.nqb + ib] & picks) != 0u;
+    return bmask_bit(p, list, ib >> 1, jp);
+  };
+  // diagonal walk: query blocks kb0 and kb0 + 1 of every head of the group
+  {
+    const int nd = p.hh_hi - p.hh_lo;
+    int i = -1, hh = 0;
+    if (tid < 2 * nd) {
+      hh = p.hh_lo + (tid >> 1);
+      const int ib = kb0 + (tid & 1);
+      const int list = b * p.h_q + kvh * G + hh;
+      if (ib < nb && selected(list, ib)) i = ib;
+    }
+    int tot;
+    const int slot = block_compact<kKvPairThreads>(i >= 0, L.wsum, &tot);
+    if (i >= 0) L.tiles[slot] = (hh << 26) | (i << 1) | 1;
+    __syncthreads();
+    auto diag_body = [&](const KvBuf<D>& B, int t, int, int half) {
+      const int ib = (L.tiles[t] >> 1) & ((1 << 25) - 1);
+      const int off = kin + kBlock * (kbw - ib);  // key position relative to the tile's rows
+      if (!live || kbw > ib) return;              // no row of this tile sees the wave's keys
+      if constexpr (ROWS)
+        wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) {
+          return off <= r && ((B.sel[r - kTR * half] >> pick) & 1u) != 0u;
+        });
+      else
+        wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) { return off <= r; });
+    };
+    kv_pipeline<D, decltype(tile_of), decltype(diag_body), ROWS, NW>(p, L, b, tot, tile_of, diag_body);
+  }
+  // main walk: the selected query blocks after kb0 + 1, fully visible to both
+  // blocks (with a per-row selection masked by the rows' picks)
+  auto body = [&](const KvBuf<D>& B, int, int, int half) {
+    if (!live) return;
+    if constexpr (ROWS)
+      wk.template tile<true>(B, p.sl2, kTR * half,
+                             [&](int r) { return ((B.sel[r - kTR * half] >> pick) & 1u) != 0u; });
+    else
+      wk.template tile<false>(B, p.sl2, kTR * half, [](int) { return true; });
+  };
+  int count = 0;
+  const int ns = nb - kb0 - 2;
+  for (int hh = p.hh_lo; hh < p.hh_hi; ++hh) {
+    const int list = b * p.h_q + kvh * G + hh;
+    for (int base = 0; base < ns; base += kKvPairThreads) {
+      const int e = base + tid;
+      int i = -1;
+      if (e < ns && selected(list, kb0 + 2 + e)) i = kb0 + 2 + e;
+      int tot;
+      const int slot = block_compact<kKvPairThreads>(i >= 0, L.wsum, &tot);
+      if (i >= 0) L.tiles[count + slot] = (hh << 26) | (i << 1);
+      count += tot;
+      __syncthreads();
+      if (count > kKvTiles - kKvPairThreads) {
+        kv_pipeline<D, decltype(tile_of), decltype(body), ROWS, NW>(p, L, b, count, tile_of, body);
+        count = 0;
+      }
+    }
+  }
+  kv_pipeline<D, decltype(tile_of), decltype(body), ROWS, NW>(p, L, b, count, tile_of, body);
+  if (live) wk.store(p, b, kvh, kpos, p.kv_accumulate ? 1 : 0);
+}
+
 template <int D>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_kv_cols_bf16_kernel(AttnParams p) {
   typedef KvWorkerB<D> W;
@@ -535,14 +653,16 @@ hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
   for (int sgi = 0; p.W == 1 && sgi < p.seg.n_seg; ++sgi)
     nb_max = std::max(nb_max, p.seg.start_blk[sgi + 1] - p.seg.start_blk[sgi]);
   const size_t bits_bytes = (size_t)((nb_max + 31) / 32) * 4 + 4;
+  // block and per-row selections: pairs of key blocks per workgroup
+  const dim3 gp((unsigned)(p.batch * p.h_kv * ((p.nkb + 1) / 2)));
   if (d == 128) {
-    if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, kModeBlocks>), gs, dim3(kKvThreads), 0, st, p));
-    else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, kModeRows>), gs, dim3(kKvThreads), 0, st, p));
+    if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<128, kModeBlocks>), gp, dim3(kKvPairThreads), 0, st, p));
+    else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<128, kModeRows>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, kModeLists>), gs, dim3(kKvThreads), 0, st, p));
     if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128>), gc, dim3(kKvThreads), bits_bytes, st, p));
   } else {
-    if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, kModeBlocks>), gs, dim3(kKvThreads), 0, st, p));
-    else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, kModeRows>), gs, dim3(kKvThreads), 0, st, p));
+    if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<64, kModeBlocks>), gp, dim3(kKvPairThreads), 0, st, p));
+    else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<64, kModeRows>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, kModeLists>), gs, dim3(kKvThreads), 0, st, p));
     if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64>), gc, dim3(kKvThreads), bits_bytes, st, p));
   }

@@ -157,6 +157,10 @@ ROW_CASES = {
     # (empty rows), 16 Q heads on one KV head so the dK/dV tile list flushes
     "random-gqa16-n4096-b256": (dict(wid=2, n=4096, h_q=16, h_kv=1), 256, ("random", None)),
     "own-only-n2048-b256": (dict(wid=2, n=2048, h_q=2, h_kv=1), 256, ("gate", 1)),
+    # 64-token row blocks: the two key blocks of a dK/dV pair carry different
+    # picks; 128-token row blocks with an odd key-block count (63)
+    "random-n2048-b64": (dict(wid=2, n=2048, h_q=4, h_kv=1), 64, ("random", None)),
+    "random-n4032-b128-odd": (dict(wid=2, n=4032, h_q=4, h_kv=2), 128, ("random", None)),
 }
 
 

@@ -322,6 +322,55 @@ def block_selection_walks(n, batch, h_q, h_kv, sel_p, rng):
                     count[count > 512 - 128] = 0
 
 
+def key_major_pairs(n, batch, h_q, h_kv, selected, word_index, rm_shift=None):
+    """The paired dK/dV walk of block and per-row selections (workgroups of
+    four waves owning key blocks 2 jp and 2 jp + 1): its grid, the key rows
+    each wave loads, the selection words it reads (word_index(bh, ib, jp) ->
+    flat index, checked by the caller's closure), the tiles of its diagonal
+    and main walks (tile word bits, query rows staged) and the tile list
+    capacity (512 entries, appended 256 at a time, emptied above 256)."""
+    nb = n // BLOCK
+    G = h_q // h_kv
+    assert G <= 32 and (31 << 26) < 2 ** 31
+    npair = (nb + 1) // 2
+    for b in range(batch):
+        for kvh in range(h_kv):
+            for jp in range(npair):
+                kb0 = 2 * jp
+                for kp in (0, 1):
+                    kbw = kb0 + kp
+                    live = kbw < nb
+                    kpos = (kbw if live else kb0) * BLOCK + np.arange(64)
+                    assert kpos.max() < n
+                    if rm_shift is not None and live:
+                        assert (kbw >> rm_shift) < 32
+                if rm_shift is not None:
+                    assert ((kb0 + 1) >> rm_shift) < 32   # the picks mask, also for an absent block
+                diag = 0
+                for hh in range(G):
+                    bh = b * h_q + kvh * G + hh
+                    for ib in (kb0, kb0 + 1):
+                        if ib < nb:
+                            word_index(bh, ib, jp)
+                            diag += bool(selected(bh, ib, jp))
+                assert diag <= 2 * G <= 512
+                count = 0
+                ns = nb - kb0 - 2
+                for hh in range(G):
+                    bh = b * h_q + kvh * G + hh
+                    for base in range(0, max(ns, 0), 256):
+                        ib = kb0 + 2 + base + np.arange(min(256, ns - base))
+                        for x in ib:
+                            word_index(bh, int(x), jp)
+                        on = np.array([bool(selected(bh, int(x), jp)) for x in ib])
+                        assert np.all(ib[on] < nb) and np.all(ib[on] < 2 ** 25)
+                        assert np.all(ib[on] * BLOCK + 63 < n)   # both 32-row halves staged
+                        count += int(on.sum())
+                        assert count <= 512
+                        if count > 512 - 256:
+                            count = 0
+
+
 def xattn_estimator_addresses(n, batch, h_q, h_kv, d):
     """Cell and selection kernels: the (row tile, column tile) decode of the
     triangle index, every Q / K row and channel a direct load fetches, every
@@ -393,20 +442,49 @@ def test_block_selection_in_bounds(n, batch, h_q, h_kv):
     rng = np.random.default_rng(42 + n)
     if n <= 8192:
         block_selection_walks(n, batch, h_q, h_kv, 0.6, rng)
+        nI = -(-n // 128)
+        words = (nI + 31) >> 5
+        sel = rng.random((batch * h_q, nI, nI)) < 0.6
+
+        def word_index(bh, ib, jp):
+            w = (bh * nI + (ib >> 1)) * words + (jp >> 5)
+            assert 0 <= w < batch * h_q * nI * words
+            return w
+
+        key_major_pairs(n, batch, h_q, h_kv, lambda bh, ib, jp: sel[bh, ib >> 1, jp], word_index)
     for d in (64, 128):
         xattn_estimator_addresses(n, batch, h_q, h_kv, d)
 
 
 
 @pytest.mark.parametrize("n,batch,h_q,h_kv,blk", [(4096, 2, 4, 1, 256), (4160, 1, 2, 1, 512),
-                                                 (131072, 1, 16, 2, 4096)])
+                                                 (131072, 1, 16, 2, 4096), (2048, 1, 4, 1, 64),
+                                                 (4032, 1, 4, 2, 128)])
 def test_per_row_selection_in_bounds(n, batch, h_q, h_kv, blk):
     """MoBA gate and per-row selection walks: the gate's workgroups (256 rows
     inside one key block), the mean and score indices, the query-major walk's
     row words and tiles, the key-major walk's union words, staged row words
     and picked-block bit."""
-    assert blk >= 256 and blk & (blk - 1) == 0 and n <= 32 * blk
+    assert blk >= 64 and blk & (blk - 1) == 0 and n <= 32 * blk
     nB = -(-n // blk)
+    nqb = n // BLOCK
+    shift = int(np.log2(blk // BLOCK))
+    if n <= 8192:
+        rng = np.random.default_rng(7 + n)
+        uni = rng.integers(0, 2 ** 32, size=(batch * h_q, nqb), dtype=np.uint64)
+
+        def union_index(bh, ib, jp):
+            u = bh * nqb + ib
+            assert 0 <= u < batch * h_q * nqb
+            return u
+
+        def picked(bh, ib, jp):
+            picks = (1 << ((2 * jp) >> shift)) | (1 << ((2 * jp + 1) >> shift))
+            return int(uni[bh, ib]) & picks
+
+        key_major_pairs(n, batch, h_q, h_kv, picked, union_index, rm_shift=shift)
+    if blk < 256:
+        return  # the gate needs blocks of 256 or more; the per-row index does not
     rows_words = batch * h_q * n
     # gate: workgroup of rows r0 .. r0 + 255 shares its own block
     for r0 in range(0, n, 256):
