@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kQThreads) void vs_bwd_dq_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char buf[BUF];
 
   int hb, i_local;
-  qmajor_item(p, blockIdx.x, &hb, &i_local);
+  qmajor_item(p, blockIdx.x, p.nqb, &hb, &i_local);
   const int b = hb / p.h_q;
   const int h = hb % p.h_q;
   const int kvh = h * p.h_kv / p.h_q;

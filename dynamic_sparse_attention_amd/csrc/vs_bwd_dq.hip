@@ -19,7 +19,7 @@ namespace vs {
 // transposed for dQ^T += K^T dS^T).  Each wave holds Q^T, dO^T and dQ^T of
 // its 32 rows (about 235 registers), so with NS = 1 (the launched form: two
 // waves, under 40 KB of LDS) four independent workgroups share a CU.
-template <int D>
+template <int D, int NP = 2>
 struct DqRowsWorker : RowsTiles<D> {
   typedef RowsTiles<D> T;
   typedef typename T::MF MF;
@@ -28,13 +28,12 @@ struct DqRowsWorker : RowsTiles<D> {
   using T::NCD;
   using T::NCT;
   using T::NCK;
-  using T::NVH;
   using T::kb;
   using T::vb;
   using T::rh;
   using T::k_frag;
   using T::t_frag;
-  using T::dma_half;
+  static constexpr int NVW = T::NVL / NP;  // direct loads per half-tile issued by each wave
 
   frag qf[NCD];     // Q^T of this wave's 32 rows
   frag dof[NCD];    // dO^T
@@ -94,8 +93,8 @@ struct DqRowsWorker : RowsTiles<D> {
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & lgkmcnt_wait0());
     __syncthreads();
     if (n + 2 < N) {
-      dma_half(S, n + 2, kb, this->krb, kta[P]);
-      dma_half(S, n + 2, vb, this->vrb, vta[P]);
+      this->template dma_share<NP>(S, n + 2, kb, this->krb, kta[P]);
+      this->template dma_share<NP>(S, n + 2, vb, this->vrb, vta[P]);
     }
     if (n + 1 < N) scores(kt[P ^ 1], vt[P ^ 1]);
   }
@@ -108,13 +107,13 @@ struct DqRowsWorker : RowsTiles<D> {
     if (NA == 0) return;
     const int N = S.n_halves();
     if (N > 0) {
-      dma_half(S, 0, kb, this->krb, kta[0]);
-      dma_half(S, 0, vb, this->vrb, vta[0]);
-      dma_half(S, 1, kb, this->krb, kta[1]);
-      dma_half(S, 1, vb, this->vrb, vta[1]);
+      this->template dma_share<NP>(S, 0, kb, this->krb, kta[0]);
+      this->template dma_share<NP>(S, 0, vb, this->vrb, vta[0]);
+      this->template dma_share<NP>(S, 1, kb, this->krb, kta[1]);
+      this->template dma_share<NP>(S, 1, vb, this->vrb, vta[1]);
     }
     // this wave's loads of K(0), V(0) have landed (K(1), V(1) may not have)
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * NVH));
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * NVW));
     __syncthreads();
     if (N > 0) scores(kt[0], vt[0]);
     // sets have an even number of halves (two per 64-key tile)
@@ -126,10 +125,16 @@ struct DqRowsWorker : RowsTiles<D> {
   }
 };
 
-template <int D, int NS>
-__global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_dq_rows_kernel(AttnParams p) {
-  typedef DqRowsWorker<D> W;
-  constexpr int NT = 128 * NS;
+// PM = kPairBlocks (block selections): the two query blocks of a 128-row
+// block in one workgroup, four waves on one stream (half the K / V loads);
+// an absent second block's waves compute on the first block's rows and
+// store nothing.
+template <int D, int NS, int PM = 0>
+__global__ __launch_bounds__(128 * NS * (PM ? 2 : 1)) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_dq_rows_kernel(AttnParams p) {
+  constexpr int QB = PM ? 2 : 1;  // query blocks per workgroup
+  static_assert(QB == 1 || NS == 1, "pairs of query blocks run one stream");
+  typedef DqRowsWorker<D, 2 * QB> W;
+  constexpr int NT = 128 * NS * QB;
   constexpr int OB_PITCH = D + 4;
   constexpr int OB_BYTES = 64 * OB_PITCH * 4;
   // [ring slot][K, V][stream] tiles
@@ -138,7 +143,8 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ __attribute__((aligned(16))) char tiles[TILES > OB_BYTES ? TILES : OB_BYTES];
 
   int hb, i_local;
-  qmajor_item(p, blockIdx.x, &hb, &i_local);
+  qmajor_item(p, blockIdx.x, (p.nqb + QB - 1) / QB, &hb, &i_local);
+  i_local *= QB;
   const int b = hb / p.h_q;
   const int h = hb % p.h_q;
   const int kvh = h * p.h_kv / p.h_q;
@@ -153,20 +159,23 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
 
   W wk;
   wk.rh = __builtin_amdgcn_readfirstlane(wave / NS);
-  const int r = 32 * wk.rh + l32;  // this lane's row of the block
+  const int r = 32 * wk.rh + l32;  // this lane's row of the block (pair)
+  const int qh = wk.rh >> 1;       // the query block of this wave's rows
+  const bool live = QB == 1 || i_local + qh < p.nqb;
+  const int rl = live ? r : r - kBlock;  // the row it reads (an absent block's waves read the first block's)
   const __bf16* q = reinterpret_cast<const __bf16*>(p.q);
   const __bf16* dout = reinterpret_cast<const __bf16*>(p.dout);
-  const int row0 = i_local * kBlock;  // first row of the block in this batch row
+  const int row0 = i_local * kBlock;  // first row of the block (pair) in this batch row
   {
-    const size_t qoff = p.sq.at(b, row0 + r, h) + hl * W::KPL;
-    const size_t doff = p.sdo.at(b, row0 + r, h) + hl * W::KPL;
-    const size_t roff = p.so.at(b, row0 + r, h) + hl * W::KPL;  // O, for delta
+    const size_t qoff = p.sq.at(b, row0 + rl, h) + hl * W::KPL;
+    const size_t doff = p.sdo.at(b, row0 + rl, h) + hl * W::KPL;
+    const size_t roff = p.so.at(b, row0 + rl, h) + hl * W::KPL;  // O, for delta
 #pragma unroll
     for (int c = 0; c < W::NCD; ++c) {
       wk.qf[c] = load_frag<__bf16>(q + qoff + c * W::KC);
       wk.dof[c] = load_frag<__bf16>(dout + doff + c * W::KC);
     }
-    const size_t li = ((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + r;
+    const size_t li = ((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + rl;
     const float lse = p.lse[li];
     wk.lse2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
     if (p.delta_out) {
@@ -197,11 +206,11 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
       }
       acc += __shfl_xor(acc, 32, 64);
       wk.dl = acc;
-      if (hl == 0) p.delta_out[li] = acc;
+      if (hl == 0 && live) p.delta_out[li] = acc;
     } else {
       wk.dl = p.delta[li];
     }
-    if (p.lse2_out && hl == 0) p.lse2_out[li] = wk.lse2;
+    if (p.lse2_out && hl == 0 && live) p.lse2_out[li] = wk.lse2;
   }
 #pragma unroll
   for (int ct = 0; ct < W::NCT; ++ct) wk.dq[ct] = f32x16{0};
@@ -219,33 +228,41 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   wk.sl2 = p.sl2;
   wk.init_offsets();
 
-  qmajor_drive<NS>(p, rb, list, L, qm_bits, wk);
+  qmajor_drive<NS, PM>(p, rb, list, L, qm_bits, wk);
 
-  // Sum the streams' dQ^T of every row, then scale and store (or add).
+  // One round per query block of the workgroup: sum the streams' dQ^T of
+  // every row, then scale and store (or add).
   float* ob = reinterpret_cast<float*>(tiles);
-  for (int w = 0; w < NS; ++w) {
-    if (ks == w) {
+  for (int u = 0; u < QB; ++u) {
+    if (i_local + u >= p.nqb) break;  // uniform: an absent second block
+    const bool mine = QB == 1 || qh == u;
+    const int rr = r - kBlock * u;
+    for (int w = 0; w < NS; ++w) {
+      if (mine && ks == w) {
 #pragma unroll
-      for (int ct = 0; ct < W::NCT; ++ct)
+        for (int ct = 0; ct < W::NCT; ++ct)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          float* dst = ob + r * OB_PITCH + 32 * ct + 8 * i4 + 4 * hl;
-          f32x4 v;
+          for (int i4 = 0; i4 < 4; ++i4) {
+            float* dst = ob + rr * OB_PITCH + 32 * ct + 8 * i4 + 4 * hl;
+            f32x4 v;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = wk.dq[ct][4 * i4 + u];
-          if (w == 0) *reinterpret_cast<f32x4*>(dst) = v;
-          else *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
-        }
+            for (int x = 0; x < 4; ++x) v[x] = wk.dq[ct][4 * i4 + x];
+            if (w == 0) *reinterpret_cast<f32x4*>(dst) = v;
+            else *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
+          }
+      }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  for (int x = tid; x < 64 * D / 4; x += NT) {
-    const int rr = x / (D / 4);
-    const int c4 = (x % (D / 4)) * 4;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(ob + rr * OB_PITCH + c4) * p.scale;
-    float* dst = p.dq + (((size_t)b * p.n_q + row0 + rr) * p.h_q + h) * D + c4;
-    if (p.dq_accumulate) *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
-    else *reinterpret_cast<f32x4*>(dst) = v;
+    const int qrow0 = row0 + kBlock * u;
+    for (int x = tid; x < 64 * D / 4; x += NT) {
+      const int orow = x / (D / 4);
+      const int c4 = (x % (D / 4)) * 4;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ob + orow * OB_PITCH + c4) * p.scale;
+      float* dst = p.dq + (((size_t)b * p.n_q + qrow0 + orow) * p.h_q + h) * D + c4;
+      if (p.dq_accumulate) *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
+      else *reinterpret_cast<f32x4*>(dst) = v;
+    }
+    if (QB > 1) __syncthreads();  // the next round reuses the staging buffer
   }
 }
 
@@ -253,7 +270,12 @@ hipError_t launch_bwd_dq_bf16(const AttnParams& p, int d, hipStream_t st) {
   const dim3 gq((unsigned)(p.batch * p.h_q * p.nqb));
   if (gq.x == 0) return hipSuccess;
   const size_t dyn = qmajor_bits_bytes(p);
-  if (d == 128) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_rows_kernel<128, 1>), gq, dim3(128), dyn, st, p));
+  if (p.bmask) {
+    // block selections: pairs of query blocks
+    const dim3 gp((unsigned)(p.batch * p.h_q * ((p.nqb + 1) / 2)));
+    if (d == 128) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_rows_kernel<128, 1, kPairBlocks>), gp, dim3(256), dyn, st, p));
+    else VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_rows_kernel<64, 1, kPairBlocks>), gp, dim3(256), dyn, st, p));
+  } else if (d == 128) VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_rows_kernel<128, 1>), gq, dim3(128), dyn, st, p));
   else VS_TRACED(st, "vs_bwd_dq", hipLaunchKernelGGL((vs_bwd_dq_rows_kernel<64, 1>), gq, dim3(128), dyn, st, p));
   return hipGetLastError();
 }

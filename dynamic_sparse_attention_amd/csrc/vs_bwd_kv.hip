@@ -291,15 +291,9 @@ __device__ __forceinline__ void kv_pipeline(const AttnParams& p, KvLdsB<D, NW>& 
   __syncthreads();
 }
 
-// MODE: 0 the block-diagonal lists; 1 a block selection (p.bmask, one
-// segment); 2 a per-row block selection (p.rmask, one segment).  A template
-// parameter so that the list walk keeps its registers.
-constexpr int kModeLists = 0, kModeBlocks = 1, kModeRows = 2;
-
-template <int D, int MODE>
+// The Vertical-Slash lists: one key block per workgroup.
+template <int D>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_kv_slash_bf16_kernel(AttnParams p) {
-  constexpr bool BLK = MODE == kModeBlocks;
-  constexpr bool ROWS = MODE == kModeRows;
   typedef KvWorkerB<D> W;
   __shared__ KvLdsB<D> L;
   const int tid = threadIdx.x;
@@ -337,72 +331,38 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     *i = (v >> 1) & ((1 << 25) - 1);
     *fl = v & 1;
   };
-  // per-row selections: the key block's picked-block index
-  const int pick = ROWS ? (beta_k >> p.rm_shift) : 0;
-  // Diagonal tiles (g = 0, or the query block itself in a block or per-row
-  // selection; causal inside the block, and with a per-row selection only the
-  // rows that picked the block) first, in a walk of their own, so that the
-  // main walk of the lists has no masking at all.
+  // Diagonal tiles (g = 0: causal inside the block) first, in a walk of their
+  // own, so that the main walk has no masking at all.
   {
     int i = -1;
     if (tid >= p.hh_lo && tid < p.hh_hi) {
       const int list = (b * p.h_q + kvh * G + tid) * p.seg.n_seg + seg;
-      if (BLK) {
-        if (bmask_bit(p, list, beta_k >> 1, beta_k >> 1)) i = local_query_block(p, kb_glob);
-      } else if (ROWS) {
-        if ((p.rm_union[(size_t)list * p.nqb + kb_glob] >> pick) & 1u) i = local_query_block(p, kb_glob);
-      } else {
-        const int sp0 = p.s_ptr[list];
-        if (p.s_ptr[list + 1] > sp0 && p.s_idx[sp0] == 0) i = local_query_block(p, kb_glob);
-      }
+      const int sp0 = p.s_ptr[list];
+      if (p.s_ptr[list + 1] > sp0 && p.s_idx[sp0] == 0) i = local_query_block(p, kb_glob);
     }
     int tot;
     const int slot = block_compact<kKvThreads>(i >= 0, L.wsum, &tot);
     if (i >= 0) L.tiles[slot] = (tid << 26) | (i << 1) | 1;
     __syncthreads();
     auto diag_body = [&](const KvBuf<D>& B, int, int, int half) {
-      if constexpr (ROWS)
-        wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) {
-          return kin <= r && ((B.sel[r - kTR * half] >> pick) & 1u) != 0u;
-        });
-      else
-        wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) { return kin <= r; });
+      wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) { return kin <= r; });
     };
-    kv_pipeline<D, decltype(tile_of), decltype(diag_body), ROWS>(p, L, b, tot, tile_of, diag_body);
+    kv_pipeline<D>(p, L, b, tot, tile_of, diag_body);
   }
-  // main walk: with a per-row selection every tile is masked by its rows'
-  // picks (one tile variant, so that the walk keeps its registers)
   auto body = [&](const KvBuf<D>& B, int, int, int half) {
-    if constexpr (ROWS)
-      wk.template tile<true>(B, p.sl2, kTR * half,
-                             [&](int r) { return ((B.sel[r - kTR * half] >> pick) & 1u) != 0u; });
-    else
-      wk.template tile<false>(B, p.sl2, kTR * half, [](int) { return true; });
+    wk.template tile<false>(B, p.sl2, kTR * half, [](int) { return true; });
   };
   for (int hh = p.hh_lo; hh < p.hh_hi; ++hh) {
     const int list = (b * p.h_q + kvh * G + hh) * p.seg.n_seg + seg;
-    // Candidates: the head's selected block-diagonals g > 0 (query block
-    // kb + g), or with a block selection (one segment) the query blocks after
-    // this key block, kept when their 128-block selected the key's 128-block,
-    // or with a per-row selection the query blocks after it, kept when one of
-    // their rows picked its block.
-    const int sp0 = (BLK || ROWS) ? 0 : p.s_ptr[list];
-    const int ns = (BLK || ROWS) ? nb_seg - 1 - beta_k : p.s_ptr[list + 1] - sp0;
+    // candidates: the head's selected block-diagonals g > 0 (query block kb + g)
+    const int sp0 = p.s_ptr[list];
+    const int ns = p.s_ptr[list + 1] - sp0;
     for (int base = 0; base < ns; base += kKvThreads) {
       const int e = base + tid;
       int i = -1;
       if (e < ns) {
-        if (BLK) {
-          const int ib = beta_k + 1 + e;  // query block of the segment
-          if (bmask_bit(p, list, ib >> 1, beta_k >> 1)) i = local_query_block(p, a_blk + ib);
-        } else if (ROWS) {
-          // query block ib: kept when some row picked this key block
-          const int ib = beta_k + 1 + e;
-          if ((p.rm_union[(size_t)list * p.nqb + a_blk + ib] >> pick) & 1u) i = local_query_block(p, a_blk + ib);
-        } else {
-          const int g = p.s_idx[sp0 + e];
-          if (g > 0 && beta_k + g < nb_seg) i = local_query_block(p, kb_glob + g);
-        }
+        const int g = p.s_idx[sp0 + e];
+        if (g > 0 && beta_k + g < nb_seg) i = local_query_block(p, kb_glob + g);
       }
       int tot;
       const int slot = block_compact<kKvThreads>(i >= 0, L.wsum, &tot);
@@ -410,14 +370,18 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
       count += tot;
       __syncthreads();
       if (count > kKvTiles - kKvThreads) {
-        kv_pipeline<D, decltype(tile_of), decltype(body), ROWS>(p, L, b, count, tile_of, body);
+        kv_pipeline<D>(p, L, b, count, tile_of, body);
         count = 0;
       }
     }
   }
-  kv_pipeline<D, decltype(tile_of), decltype(body), ROWS>(p, L, b, count, tile_of, body);
+  kv_pipeline<D>(p, L, b, count, tile_of, body);
   wk.store(p, b, kvh, kpos, p.kv_accumulate ? 1 : 0);
 }
+
+// MODE of the paired kernel below: a block selection (p.bmask) or a per-row
+// block selection (p.rmask), both of one segment.
+constexpr int kModeBlocks = 1, kModeRows = 2;
 
 // Block and per-row selections (one segment): a workgroup of four waves owns
 // the key blocks kb0 = 2 jp and kb0 + 1 (waves 2 kp + kh hold keys
@@ -658,12 +622,12 @@ hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
   if (d == 128) {
     if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<128, kModeBlocks>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<128, kModeRows>), gp, dim3(kKvPairThreads), 0, st, p));
-    else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128, kModeLists>), gs, dim3(kKvThreads), 0, st, p));
+    else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128>), gs, dim3(kKvThreads), 0, st, p));
     if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128>), gc, dim3(kKvThreads), bits_bytes, st, p));
   } else {
     if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<64, kModeBlocks>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<64, kModeRows>), gp, dim3(kKvPairThreads), 0, st, p));
-    else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64, kModeLists>), gs, dim3(kKvThreads), 0, st, p));
+    else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64>), gs, dim3(kKvThreads), 0, st, p));
     if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64>), gc, dim3(kKvThreads), bits_bytes, st, p));
   }
   return hipGetLastError();

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_f32_kernel(AttnParams p) {
   __shared__ float s_l[4][64];
 
   int hb, i_local;
-  qmajor_item(p, blockIdx.x, &hb, &i_local);
+  qmajor_item(p, blockIdx.x, p.nqb, &hb, &i_local);
   const int b = hb / p.h_q;
   const int h = hb % p.h_q;
   const int kvh = h * p.h_kv / p.h_q;
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kQThreads) void vs_fwd_f32_kernel(AttnParams p) {
 // independent workgroups share a CU: one's index expansion, waits and output
 // merge overlap the others' products.
 
-template <int D>
+template <int D, int NP = 2>
 struct FwdRowsWorker : RowsTiles<D> {
   typedef RowsTiles<D> T;
   typedef typename T::MF MF;
@@ -403,12 +403,11 @@ struct FwdRowsWorker : RowsTiles<D> {
   using T::NCD;
   using T::NCT;
   using T::NCK;
-  using T::NVH;
   using T::kb;
   using T::vb;
   using T::rh;
   using T::k_frag;
-  using T::dma_half;
+  static constexpr int NVW = T::NVL / NP;  // direct loads per half-tile issued by each wave
   static constexpr float kRescale = 8.f;
 
   frag qf[NCD];   // Q^T of this wave's 32 rows
@@ -505,8 +504,8 @@ struct FwdRowsWorker : RowsTiles<D> {
     // have returned before the other waves may overwrite those tiles
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & lgkmcnt_wait0());
     __syncthreads();
-    if (n + 2 < N) dma_half(S, n + 2, kb, this->krb, kta[P]);
-    if (n + 1 < N) dma_half(S, n + 1, vb, this->vrb, vta[P ^ 1]);
+    if (n + 2 < N) this->template dma_share<NP>(S, n + 2, kb, this->krb, kta[P]);
+    if (n + 1 < N) this->template dma_share<NP>(S, n + 1, vb, this->vrb, vta[P ^ 1]);
     if (n < N) compute(S, n, s[P], s[P ^ 1], kt[P ^ 1], vt[P]);
   }
 
@@ -520,11 +519,11 @@ struct FwdRowsWorker : RowsTiles<D> {
     const int N = S.n_halves();
     f32x16 s[2];
     if (N > 0) {
-      dma_half(S, 0, kb, this->krb, kta[0]);
-      dma_half(S, 0, vb, this->vrb, vta[0]);
-      dma_half(S, 1, kb, this->krb, kta[1]);
+      this->template dma_share<NP>(S, 0, kb, this->krb, kta[0]);
+      this->template dma_share<NP>(S, 0, vb, this->vrb, vta[0]);
+      this->template dma_share<NP>(S, 1, kb, this->krb, kta[1]);
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(NVH));
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(NVW));
     __syncthreads();
     if (N > 0) scores(kt[0], s[0]);
     // sets have an even number of halves (two per 64-key tile)
@@ -536,10 +535,17 @@ struct FwdRowsWorker : RowsTiles<D> {
   }
 };
 
-template <int D, int NS>
-__global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) void vs_fwd_rows_kernel(AttnParams p) {
-  typedef FwdRowsWorker<D> W;
-  constexpr int NT = 128 * NS;
+// PM = kPairBlocks (block selections): the workgroup owns the two query
+// blocks of a 128-row block, its four waves rows 0-31 .. 96-127 of the pair
+// on one stream, so every K / V tile serves 128 rows (half the loads); past
+// an odd block count the second block is absent (its waves compute on the
+// first block's rows and store nothing).
+template <int D, int NS, int PM = 0>
+__global__ __launch_bounds__(128 * NS * (PM ? 2 : 1)) __attribute__((amdgpu_waves_per_eu(2))) void vs_fwd_rows_kernel(AttnParams p) {
+  constexpr int QB = PM ? 2 : 1;  // query blocks per workgroup
+  static_assert(QB == 1 || NS == 1, "pairs of query blocks run one stream");
+  typedef FwdRowsWorker<D, 2 * QB> W;
+  constexpr int NT = 128 * NS * QB;
   constexpr int OB_PITCH = D + 4;
   constexpr int OB_BYTES = 64 * OB_PITCH * 4;
   // [ring slot][K, V][stream] tiles
@@ -552,7 +558,8 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ float s_acc[64];
 
   int hb, i_local;
-  qmajor_item(p, blockIdx.x, &hb, &i_local);
+  qmajor_item(p, blockIdx.x, (p.nqb + QB - 1) / QB, &hb, &i_local);
+  i_local *= QB;
   const int b = hb / p.h_q;
   const int h = hb % p.h_q;
   const int kvh = h * p.h_kv / p.h_q;
@@ -569,10 +576,13 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   W wk;
   wk.rh = __builtin_amdgcn_readfirstlane(wave / NS);
   const __bf16* q = reinterpret_cast<const __bf16*>(p.q);
-  const int row0 = i_local * kBlock;  // first row of the block in this batch row
-  const int r = 32 * wk.rh + l32;     // this lane's row of the block
+  const int row0 = i_local * kBlock;  // first row of the block (pair) in this batch row
+  const int r = 32 * wk.rh + l32;     // this lane's row of the block (pair)
+  // the query block of this wave's rows, and whether it exists
+  const int qh = wk.rh >> 1;
+  const bool live = QB == 1 || i_local + qh < p.nqb;
   {
-    const __bf16* qr = q + p.sq.at(b, row0 + r, h);
+    const __bf16* qr = q + p.sq.at(b, row0 + (live ? r : r - kBlock), h);
 #pragma unroll
     for (int c = 0; c < W::NCD; ++c) wk.qf[c] = load_frag<__bf16>(qr + c * W::KC + hl * W::KPL);
   }
@@ -594,72 +604,82 @@ __global__ __launch_bounds__(128 * NS) __attribute__((amdgpu_waves_per_eu(2))) v
   wk.sl2 = p.sl2;
   wk.init_offsets();
 
-  qmajor_drive<NS>(p, rb, list, L, qm_bits, wk);
+  qmajor_drive<NS, PM>(p, rb, list, L, qm_bits, wk);
 
-  // Combine the streams' states of every row.
-  if (hl == 0) {
-    s_m[ks][r] = wk.m;
-    s_l[ks][r] = wk.l;
-  }
-  __syncthreads();
-  float mg = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < NS; ++w) mg = fmaxf(mg, s_m[w][r]);
-  const float f = fast_exp2(wk.m - ((mg == -INFINITY) ? 0.f : mg));
-  float* ob = reinterpret_cast<float*>(tiles);
-  for (int w = 0; w < NS; ++w) {
-    if (ks == w) {
-#pragma unroll
-      for (int ct = 0; ct < W::NCT; ++ct)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          float* dst = ob + r * OB_PITCH + 32 * ct + 8 * i4 + 4 * hl;
-          f32x4 v;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = wk.o[ct][4 * i4 + u] * f;
-          if (w == 0) *reinterpret_cast<f32x4*>(dst) = v;
-          else *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
-        }
+  // One round per query block of the workgroup: combine the streams' states
+  // of every row, normalise, write O and LSE (or merge them into the running
+  // result).
+  for (int u = 0; u < QB; ++u) {
+    if (i_local + u >= p.nqb) break;  // uniform: an absent second block
+    const bool mine = QB == 1 || qh == u;
+    const int rr = r - kBlock * u;    // this lane's row in the round, when mine
+    if (mine && hl == 0) {
+      s_m[ks][rr] = wk.m;
+      s_l[ks][rr] = wk.l;
     }
     __syncthreads();
-  }
-  // Normalise and write O (row-major, coalesced) and LSE (natural log), or
-  // merge them into the running result.
-  if (tid < 64) {
-    float mt = -INFINITY;
-    for (int w = 0; w < NS; ++w) mt = fmaxf(mt, s_m[w][tid]);
-    const float mu = (mt == -INFINITY) ? 0.f : mt;
-    float lg = 0.f;
-    for (int w = 0; w < NS; ++w) lg += s_l[w][tid] * fast_exp2(s_m[w][tid] - mu);
-    const float inv = lg > 0.f ? 1.f / lg : 0.f;
-    const float lse = lg > 0.f ? (mt + __log2f(lg)) * kLn2 : -INFINITY;
-    float* lp = p.lse + ((size_t)b * p.h_q + h) * p.n_q + (size_t)i_local * kBlock + tid;
-    if (p.o_merge) {
-      float a, bo;
-      *lp = merge_row(*lp, lse, inv, &a, &bo);
-      s_acc[tid] = a;
-      s_inv[tid] = bo;
-    } else {
-      *lp = lse;
-      s_inv[tid] = inv;
-    }
-  }
-  __syncthreads();
-  for (int x = tid; x < 64 * D / 4; x += NT) {
-    const int rr = x / (D / 4);
-    const int c4 = (x % (D / 4)) * 4;
-    f32x4 v = *reinterpret_cast<const f32x4*>(ob + rr * OB_PITCH + c4) * s_inv[rr];
-    const size_t off = p.so.at(b, row0 + rr, h) + c4;
-    if (p.o_f32) {
-      float* dst = reinterpret_cast<float*>(p.o_out) + off;
-      if (p.o_merge) v += *reinterpret_cast<const f32x4*>(dst) * s_acc[rr];
-      *reinterpret_cast<f32x4*>(dst) = v;
-    } else {
-      bf16x4 w4;
+    float f = 0.f;
+    if (mine) {
+      float mg = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) w4[u] = (__bf16)v[u];
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.o_out) + off) = w4;
+      for (int w = 0; w < NS; ++w) mg = fmaxf(mg, s_m[w][rr]);
+      f = fast_exp2(wk.m - ((mg == -INFINITY) ? 0.f : mg));
     }
+    float* ob = reinterpret_cast<float*>(tiles);
+    for (int w = 0; w < NS; ++w) {
+      if (mine && ks == w) {
+#pragma unroll
+        for (int ct = 0; ct < W::NCT; ++ct)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            float* dst = ob + rr * OB_PITCH + 32 * ct + 8 * i4 + 4 * hl;
+            f32x4 v;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) v[x] = wk.o[ct][4 * i4 + x] * f;
+            if (w == 0) *reinterpret_cast<f32x4*>(dst) = v;
+            else *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<f32x4*>(dst) + v;
+          }
+      }
+      __syncthreads();
+    }
+    const int qrow0 = row0 + kBlock * u;  // first row of the round's query block
+    if (tid < 64) {
+      float mt = -INFINITY;
+      for (int w = 0; w < NS; ++w) mt = fmaxf(mt, s_m[w][tid]);
+      const float mu = (mt == -INFINITY) ? 0.f : mt;
+      float lg = 0.f;
+      for (int w = 0; w < NS; ++w) lg += s_l[w][tid] * fast_exp2(s_m[w][tid] - mu);
+      const float inv = lg > 0.f ? 1.f / lg : 0.f;
+      const float lse = lg > 0.f ? (mt + __log2f(lg)) * kLn2 : -INFINITY;
+      float* lp = p.lse + ((size_t)b * p.h_q + h) * p.n_q + (size_t)qrow0 + tid;
+      if (p.o_merge) {
+        float a, bo;
+        *lp = merge_row(*lp, lse, inv, &a, &bo);
+        s_acc[tid] = a;
+        s_inv[tid] = bo;
+      } else {
+        *lp = lse;
+        s_inv[tid] = inv;
+      }
+    }
+    __syncthreads();
+    for (int x = tid; x < 64 * D / 4; x += NT) {
+      const int orow = x / (D / 4);
+      const int c4 = (x % (D / 4)) * 4;
+      f32x4 v = *reinterpret_cast<const f32x4*>(ob + orow * OB_PITCH + c4) * s_inv[orow];
+      const size_t off = p.so.at(b, qrow0 + orow, h) + c4;
+      if (p.o_f32) {
+        float* dst = reinterpret_cast<float*>(p.o_out) + off;
+        if (p.o_merge) v += *reinterpret_cast<const f32x4*>(dst) * s_acc[orow];
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else {
+        bf16x4 w4;
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) w4[x4] = (__bf16)v[x4];
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.o_out) + off) = w4;
+      }
+    }
+    if (QB > 1) __syncthreads();  // the next round reuses the staging buffers
   }
 }
 
@@ -668,7 +688,12 @@ hipError_t launch_fwd(const AttnParams& p, int dtype_bf16, int d, hipStream_t st
   const dim3 grid((unsigned)(p.batch * p.h_q * p.nqb));
   if (grid.x == 0) return hipSuccess;
   const size_t dyn = qmajor_bits_bytes(p);
-  if (dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<128, 1>), grid, dim3(128), dyn, st, p));
+  if (dtype_bf16 && p.bmask) {
+    // block selections: pairs of query blocks
+    const dim3 gp((unsigned)(p.batch * p.h_q * ((p.nqb + 1) / 2)));
+    if (d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<128, 1, kPairBlocks>), gp, dim3(256), dyn, st, p));
+    else VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<64, 1, kPairBlocks>), gp, dim3(256), dyn, st, p));
+  } else if (dtype_bf16 && d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<128, 1>), grid, dim3(128), dyn, st, p));
   else if (dtype_bf16) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_rows_kernel<64, 1>), grid, dim3(128), dyn, st, p));
   else if (d == 128) VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_f32_kernel<128>), grid, dim3(kQThreads), dyn, st, p));
   else VS_TRACED(st, "vs_fwd", hipLaunchKernelGGL((vs_fwd_f32_kernel<64>), grid, dim3(kQThreads), dyn, st, p));

@@ -72,6 +72,32 @@ struct MobaSetT {
   }
 };
 
+// Key-block tiles of a pair of query blocks 2I and 2I + 1 of one 128-row
+// block (block selections, whose selection the two share): the
+// pair's rows r = 0..127; key block 2I + d (d = 0, 1) is causal for row r
+// (key offset 64 d + e visible iff <= r), earlier blocks are fully visible.
+template <int NS>
+struct PairSetT {
+  static constexpr bool kContiguous = true;
+  const int* tiles;  // 4 * local key block + 2 * (block 2I + 1) + (block 2I or 2I + 1)
+  int tot;
+  int wave;          // key stream
+  __device__ __forceinline__ int n_halves() const { return tot > wave ? 2 * ((tot - wave + NS - 1) / NS) : 0; }
+  __device__ __forceinline__ int n_halves_max() const { return tot > 0 ? 2 * ((tot + NS - 1) / NS) : 0; }
+  __device__ __forceinline__ int tv(int n) const { return tiles[wave + NS * (n >> 1)]; }
+  __device__ __forceinline__ int key_pos(int n, int r) const { return (tv(n) >> 2) * kBlock + 32 * (n & 1) + r; }
+  __device__ __forceinline__ bool full(int n) const { return (tv(n) & 1) == 0; }
+  __device__ __forceinline__ int koff(int n) const { return 64 * ((tv(n) >> 1) & 1) + 32 * (n & 1); }
+  __device__ __forceinline__ bool valid(int n, int e, int r) const { return koff(n) + e <= r; }
+  template <int KPL>
+  __device__ __forceinline__ void mask(int n, int hl, int r, f32x16& s) const {
+    const int k0 = koff(n);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (k0 + reg_row<KPL>(i, hl) > r) s[i] = -INFINITY;
+  }
+};
+
 template <int NS>
 struct ColSetT {
   static constexpr bool kContiguous = false;
@@ -123,13 +149,49 @@ struct QMajorLds {
   int wsum[NT / 64];
 };
 
+// Block selections over a pair of query blocks rb.beta (even) and
+// rb.beta + 1 (absent past the segment's end): the key blocks up to the
+// pair's last block that its 128-row block selected.
+template <int NS, int NT, int NCOL, class Worker>
+__device__ __forceinline__ void qmajor_drive_pair(const AttnParams& p, const RowBlock& rb, int list,
+                                                  QMajorLds<NT, NCOL>& L, Worker& wk) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) % NS);
+  const int last = min(rb.beta + 1, rb.nb_seg - 1);  // the pair's last query block
+  {
+    const int bh = list;  // one segment: list = b * h_q + h
+    for (int base = 0; base <= last; base += NT) {
+      const int kb = base + tid;
+      int j = -1;
+      if (kb <= last && bmask_bit(p, bh, rb.beta >> 1, kb >> 1)) j = local_key_block(p, rb.a_blk + kb);
+      int tot;
+      const int slot = block_compact<NT>(j >= 0, L.wsum, &tot);
+      if (j >= 0) L.tiles[slot] = 4 * j + 2 * (kb == rb.beta + 1) + (kb >= rb.beta);
+      __syncthreads();
+      wk.run(PairSetT<NS>{L.tiles, tot, wave});
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+}
+
 // NT threads; wave w consumes the tiles of key stream w % NS (with more
 // waves than streams, the waves of a stream split its rows).
 // bits: the block-diagonal bitmap, (longest segment's blocks + 31) / 32 words
 // of dynamic LDS (qmajor_bits_bytes).
-template <int NS = 4, int NT, int NCOL, class Worker>
+// PM = 0: one query block, any index.  PM = kPairBlocks: the workgroup owns
+// query blocks rb (even) and rb + 1 of a block selection (one segment, no
+// lists), walked as a pair.  (Per-row selections keep one query block per
+// workgroup: on the MoBA gate's selection at N = 131072 pairs made the
+// forward 173.6 ms against 90.0 and dQ 124 against 110.)
+constexpr int kPairBlocks = 1;
+
+template <int NS = 4, int PM = 0, int NT, int NCOL, class Worker>
 __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock& rb, int list,
                                              QMajorLds<NT, NCOL>& L, uint32_t* bits, Worker& wk) {
+  if constexpr (PM == kPairBlocks) {
+    qmajor_drive_pair<NS>(p, rb, list, L, wk);
+  } else {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) % NS);
   const int sp0 = p.s_ptr[list];
@@ -299,6 +361,7 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
     __syncthreads();
   }
   __syncthreads();
+  }
 }
 
 // Work-item mapping of a query-major grid of batch*h_q*nqb workgroups.  The
@@ -318,12 +381,13 @@ __device__ __forceinline__ void qmajor_drive(const AttnParams& p, const RowBlock
 //     XCD takes whole groups.
 // upg work units per group (its Q heads, or pairs of them); *unit = group *
 // upg + unit in the group.
-__device__ __forceinline__ void qmajor_item_units(const AttnParams& p, int wg, int upg, int* unit, int* i_local) {
+__device__ __forceinline__ void qmajor_item_units(const AttnParams& p, int wg, int upg, int nq, int* unit,
+                                                  int* i_local) {
   const int NG = p.batch * p.h_kv;
   const int xcd = wg & 7;
   const int slot = wg >> 3;
   int ir;
-  if (8 % NG == 0 && p.nqb % (8 / NG) == 0) {
+  if (8 % NG == 0 && nq % (8 / NG) == 0) {
     const int xpg = 8 / NG;            // XCDs per group
     *unit = (xcd / xpg) * upg + slot % upg;
     ir = (slot / upg) * xpg + xcd % xpg;
@@ -337,13 +401,14 @@ __device__ __forceinline__ void qmajor_item_units(const AttnParams& p, int wg, i
     *unit = wg % HB;
     ir = wg / HB;
   }
-  *i_local = p.nqb - 1 - ir;
+  *i_local = nq - 1 - ir;
 }
 
-// One Q head per workgroup: *hb = b * h_q + h.
-__device__ __forceinline__ void qmajor_item(const AttnParams& p, int wg, int* hb, int* i_local) {
+// One Q head per workgroup: *hb = b * h_q + h, *i_local one of nq row items
+// (the query blocks, or pairs of them).
+__device__ __forceinline__ void qmajor_item(const AttnParams& p, int wg, int nq, int* hb, int* i_local) {
   if (p.map_group && *p.map_group) {
-    qmajor_item_units(p, wg, p.h_q / p.h_kv, hb, i_local);
+    qmajor_item_units(p, wg, p.h_q / p.h_kv, nq, hb, i_local);
     return;
   }
   const int HB = p.batch * p.h_q;
@@ -358,7 +423,7 @@ __device__ __forceinline__ void qmajor_item(const AttnParams& p, int wg, int* hb
     *hb = wg % HB;
     ir = wg / HB;
   }
-  *i_local = p.nqb - 1 - ir;
+  *i_local = nq - 1 - ir;
 }
 
 // Longest segment of a call, in blocks (the whole index grid when striped).

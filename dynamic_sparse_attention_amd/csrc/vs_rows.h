@@ -42,7 +42,6 @@ struct RowsTiles {
   static constexpr int CPR = D / 8;    // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR; // rows per 1 KiB direct load
   static constexpr int NVL = 32 / RPI; // direct loads per 32-row tile
-  static constexpr int NVH = NVL / 2;  // ... issued by each wave of a stream
   static constexpr int GROUP = 1024 + 16;      // bytes per direct-load group, padded
   static constexpr int TB = NVL * GROUP;       // bytes per 32-row tile
   // chunk index XOR of row b (0 .. RPI-1) of a group
@@ -55,7 +54,7 @@ struct RowsTiles {
   const __bf16* kb;   // K of (batch, kv head): key row pos at byte pos * krb
   const __bf16* vb;   // V of (batch, kv head): key row pos at byte pos * vrb
   uint32_t krb, vrb;  // row strides in bytes
-  int rh;             // row half of this wave
+  int rh;             // 32-row slice of this wave: 0-1 of one query block, 0-3 of a pair
 
   __device__ __forceinline__ void init_offsets() {
     const int lane = threadIdx.x & 63;
@@ -121,10 +120,11 @@ struct RowsTiles {
     }
   }
 
-  // This wave's half of the loads when the two waves of a row pair share them.
-  template <class Set>
-  __device__ __forceinline__ void dma_half(const Set& S, int n, const __bf16* src, uint32_t rb, uint32_t dst) const {
-    dma_part<2>(S, n, src, rb, dst, rh);
+  // This wave's share of the loads when the NP waves of a stream (the row
+  // halves of one query block, or the row quarters of two) share them.
+  template <int NP, class Set>
+  __device__ __forceinline__ void dma_share(const Set& S, int n, const __bf16* src, uint32_t rb, uint32_t dst) const {
+    dma_part<NP>(S, n, src, rb, dst, rh);
   }
 
   // Row operand: tile row slot_perm(L % 32), channels of k chunk c.

@@ -322,6 +322,35 @@ def block_selection_walks(n, batch, h_q, h_kv, sel_p, rng):
                     count[count > 512 - 128] = 0
 
 
+def query_major_pairs(n, batch, h_q, selected, word_index):
+    """The paired query-major walk of block selections (four waves over query
+    blocks 2I and 2I + 1): the grid of pairs, the rows each wave reads (an
+    absent second block's waves read the first block's), the selection words
+    read, the tiles of each compaction round (at most 256) and their word
+    bits."""
+    nqb = n // BLOCK
+    npair = (nqb + 1) // 2
+    for bh in range(batch * h_q):
+        for ip in range(npair):
+            i0 = 2 * ip
+            last = min(i0 + 1, nqb - 1)
+            for w in range(4):
+                qh = w >> 1
+                live = i0 + qh < nqb
+                r = 32 * w + np.arange(32)
+                rl = r if live else r - 64
+                rows = i0 * BLOCK + rl
+                assert rows.min() >= 0 and rows.max() < n
+            for base in range(0, last + 1, 256):
+                kb = base + np.arange(min(256, last + 1 - base))
+                for x in kb:
+                    word_index(bh, i0, int(x))
+                on = np.array([bool(selected(bh, i0, int(x))) for x in kb])
+                assert on.sum() <= 256
+                tv = 4 * kb[on] + 3
+                assert tv.max(initial=0) < 2 ** 31 and np.all(kb[on] * BLOCK + 63 < n)
+
+
 def key_major_pairs(n, batch, h_q, h_kv, selected, word_index, rm_shift=None):
     """The paired dK/dV walk of block and per-row selections (workgroups of
     four waves owning key blocks 2 jp and 2 jp + 1): its grid, the key rows
@@ -452,6 +481,8 @@ def test_block_selection_in_bounds(n, batch, h_q, h_kv):
             return w
 
         key_major_pairs(n, batch, h_q, h_kv, lambda bh, ib, jp: sel[bh, ib >> 1, jp], word_index)
+        query_major_pairs(n, batch, h_q, lambda bh, i0, kb: sel[bh, i0 >> 1, kb >> 1],
+                          lambda bh, i0, kb: word_index(bh, i0, kb >> 1))
     for d in (64, 128):
         xattn_estimator_addresses(n, batch, h_q, h_kv, d)
 
