@@ -257,17 +257,19 @@ __device__ __forceinline__ void wave_hist_add(int* hist, int bin, bool active) {
 }
 
 // Run by the 64 lanes of one wave: the digit d of the kr-th largest active
-// entry (counting from the top bin down, hist[d] the count of digit d) and
-// the rank kr - (entries in bins above d) inside that bin, into sel[0..1].
-// Lane l sums bins 255-4l .. 252-4l; a prefix over the lanes finds the lane
-// whose bins reach kr, which then walks its four.  (d = -1 if the bins hold
-// fewer than kr entries.)
+// entry (counting from the top bin down, hist[d] the count of digit d, NB
+// bins) and the rank kr - (entries in bins above d) inside that bin, into
+// sel[0..1].  Lane l sums bins NB-1-PL*l .. NB-PL*(l+1) (PL = NB/64); a
+// prefix over the lanes finds the lane whose bins reach kr, which then
+// walks its PL.  (d = -1 if the bins hold fewer than kr entries.)
+template <int NB = 256>
 __device__ __forceinline__ void select_digit(const int* hist, int kr, int* sel) {
+  constexpr int PL = NB / 64;
   const int lane = threadIdx.x & 63;
-  int c[4], own = 0;
+  int c[PL], own = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    c[q] = hist[255 - 4 * lane - q];
+  for (int q = 0; q < PL; ++q) {
+    c[q] = hist[NB - 1 - PL * lane - q];
     own += c[q];
   }
   int incl = own;
@@ -286,14 +288,19 @@ __device__ __forceinline__ void select_digit(const int* hist, int kr, int* sel) 
   }
   if (lane == __ffsll((unsigned long long)hit) - 1) {
     int cum = incl - own, q = 0;
-    for (; q < 3; ++q) {
+    for (; q < PL - 1; ++q) {
       if (cum + c[q] >= kr) break;
       cum += c[q];
     }
-    sel[0] = 255 - 4 * lane - q;
+    sel[0] = NB - 1 - PL * lane - q;
     sel[1] = kr - cum;
   }
 }
+
+// Entries of the leading 11-bit bin of the k-th largest score that the
+// top-k select gathers in LDS (a list whose bin holds more takes the radix
+// passes over the whole list instead).
+constexpr int kTopkCand = 8192;
 
 // kcount (optional): the number of entries to select per (list, kind), at
 // most the list's capacity; the rest of the list is padded with -1.
@@ -302,8 +309,13 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
                                                                    int* v_idx, const int* s_ptr,
                                                                    int* s_idx, const int* kcount) {
   __shared__ int hist[256];
+  __shared__ int h1[2048];
+  __shared__ uint32_t cv[kTopkCand];
+  __shared__ int ci[kTopkCand];
   __shared__ int wsum[2][kTopkThreads / 64];
+  __shared__ int wcnt[2][kTopkThreads / 64];
   __shared__ int sel[2];
+  __shared__ int ncand;
   const int kind = blockIdx.x & 1;
   const int list = blockIdx.x >> 1;
   const int s = list % p.seg.n_seg;
@@ -342,45 +354,42 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
   }
   for (int x = k + tid; x < cap; x += kTopkThreads) out[x] = -1;
   const uint32_t* u = reinterpret_cast<const uint32_t*>(sc);
-  uint32_t prefix = 0, pmask = 0;
-  int kr = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    // eight candidates per thread in flight at a time; uniform trip count
-    for (int base = 0; base < L; base += kTopkUnroll * kTopkThreads) {
-      uint32_t v[kTopkUnroll];
-#pragma unroll
-      for (int j = 0; j < kTopkUnroll; ++j) {
-        const int x = base + j * kTopkThreads + tid;
-        v[j] = x < L ? u[x] : 0u;
-      }
-#pragma unroll
-      for (int j = 0; j < kTopkUnroll; ++j) {
-        const int x = base + j * kTopkThreads + tid;
-        wave_hist_add(hist, (int)((v[j] >> shift) & 255), x < L && (v[j] & pmask) == prefix);
-      }
-    }
-    __syncthreads();
-    if (tid < 64) select_digit(hist, kr, sel);
-    __syncthreads();
-    prefix |= (uint32_t)sel[0] << shift;
-    pmask |= 255u << shift;
-    kr = sel[1];
-    __syncthreads();
-  }
-  // prefix is the k-th largest value; take everything above it and the kr
-  // lowest-index entries equal to it, in index order.  Wave w owns the
-  // contiguous range [w C, (w + 1) C) of the candidates: it counts them,
-  // one workgroup scan gives every wave its output offset and its number of
-  // equal entries before it, and a second walk writes the chosen indices
-  // (ballot prefixes order the lanes of each 64-entry step).
-  const int C = ((L + kTopkThreads / 64 - 1) / (kTopkThreads / 64) + 63) & ~63;
+  // Scores are non-negative floats, so their bit patterns order as they do.
+  // The k-th largest value is found digit by digit (radix select), then the
+  // entries above it and the lowest-index entries equal to it are written
+  // in index order.  Wave w owns the contiguous range [w C, (w + 1) C) of
+  // the list for the counting and the writing.
+  constexpr int NW = kTopkThreads / 64;
+  const int C = ((L + NW - 1) / NW + 63) & ~63;
   const int x0 = wave * C;
   const int x1 = min(x0 + C, L);
-  int n_gt = 0, n_eq = 0;
-  for (int xb = x0; xb < x1; xb += kTopkUnroll * 64) {
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  // 1. the leading 11 bits of every score: 2048 bins
+  for (int x = tid; x < 2048; x += kTopkThreads) h1[x] = 0;
+  if (tid < NW) {
+    wcnt[0][tid] = 0;
+    wcnt[1][tid] = 0;
+  }
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  for (int base = 0; base < L; base += kTopkUnroll * kTopkThreads) {
+    uint32_t v[kTopkUnroll];
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int x = base + j * kTopkThreads + tid;
+      v[j] = x < L ? u[x] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) wave_hist_add(h1, (int)(v[j] >> 21), base + j * kTopkThreads + tid < L);
+  }
+  __syncthreads();
+  if (tid < 64) select_digit<2048>(h1, k, sel);
+  __syncthreads();
+  const uint32_t d1 = (uint32_t)sel[0];
+  int kr = sel[1];
+  // 2. per wave, the entries above that bin; the bin's entries into LDS
+  int n_above = 0;
+  for (int xb = x0; xb < x1; xb += kTopkUnroll * 64) {  // wave-uniform trip count
     uint32_t v[kTopkUnroll];
 #pragma unroll
     for (int j = 0; j < kTopkUnroll; ++j) {
@@ -390,16 +399,108 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
 #pragma unroll
     for (int j = 0; j < kTopkUnroll; ++j) {
       const int x = xb + 64 * j + lane;
-      n_gt += x < x1 && v[j] > prefix;
-      n_eq += x < x1 && v[j] == prefix;
+      const uint32_t dg = v[j] >> 21;
+      n_above += x < x1 && dg > d1;
+      const bool in = x < x1 && dg == d1;
+      const uint64_t m = __ballot(in);
+      if (m) {  // uniform
+        int b0 = 0;
+        if (lane == 0) b0 = atomicAdd(&ncand, __popcll(m));
+        b0 = __shfl(b0, 0, 64);
+        const int slot = b0 + __popcll(m & below);
+        if (in && slot < kTopkCand) {
+          cv[slot] = v[j];
+          ci[slot] = x;
+        }
+      }
     }
   }
-  // wave totals
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    n_gt += __shfl_xor(n_gt, o, 64);
-    n_eq += __shfl_xor(n_eq, o, 64);
+  for (int o = 32; o > 0; o >>= 1) n_above += __shfl_xor(n_above, o, 64);
+  __syncthreads();
+  const int nc = ncand;
+  uint32_t prefix = d1 << 21, pmask = 0x7FFu << 21;
+  int n_gt = 0, n_eq = 0;  // this wave's entries above / equal to the k-th largest
+  if (nc <= kTopkCand) {
+    // 3. the remaining 21 bits, over the gathered entries only
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 13 : (pass == 1 ? 5 : 0);
+      const uint32_t wm = pass == 2 ? 31u : 255u;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int base = 0; base < nc; base += kTopkThreads) {  // uniform trip count
+        const int i = base + tid;
+        const uint32_t v = i < nc ? cv[i] : 0u;
+        wave_hist_add(hist, (int)((v >> shift) & wm), i < nc && (v & pmask) == prefix);
+      }
+      __syncthreads();
+      if (tid < 64) select_digit(hist, kr, sel);
+      __syncthreads();
+      prefix |= (uint32_t)sel[0] << shift;
+      pmask |= wm << shift;
+      kr = sel[1];
+      __syncthreads();
+    }
+    // per wave: the gathered entries above / equal to it
+    for (int i = tid; i < nc; i += kTopkThreads) {
+      const uint32_t v = cv[i];
+      if (v > prefix) atomicAdd(&wcnt[0][ci[i] / C], 1);
+      else if (v == prefix) atomicAdd(&wcnt[1][ci[i] / C], 1);
+    }
+    __syncthreads();
+    n_gt = n_above + wcnt[0][wave];
+    n_eq = wcnt[1][wave];
+  } else {
+    // the leading bin is too full to gather: radix passes over the whole list
+    kr = k;
+    prefix = 0;
+    pmask = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int base = 0; base < L; base += kTopkUnroll * kTopkThreads) {
+        uint32_t v[kTopkUnroll];
+#pragma unroll
+        for (int j = 0; j < kTopkUnroll; ++j) {
+          const int x = base + j * kTopkThreads + tid;
+          v[j] = x < L ? u[x] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kTopkUnroll; ++j) {
+          const int x = base + j * kTopkThreads + tid;
+          wave_hist_add(hist, (int)((v[j] >> shift) & 255), x < L && (v[j] & pmask) == prefix);
+        }
+      }
+      __syncthreads();
+      if (tid < 64) select_digit(hist, kr, sel);
+      __syncthreads();
+      prefix |= (uint32_t)sel[0] << shift;
+      pmask |= 255u << shift;
+      kr = sel[1];
+      __syncthreads();
+    }
+    for (int xb = x0; xb < x1; xb += kTopkUnroll * 64) {
+      uint32_t v[kTopkUnroll];
+#pragma unroll
+      for (int j = 0; j < kTopkUnroll; ++j) {
+        const int x = xb + 64 * j + lane;
+        v[j] = x < x1 ? u[x] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kTopkUnroll; ++j) {
+        const int x = xb + 64 * j + lane;
+        n_gt += x < x1 && v[j] > prefix;
+        n_eq += x < x1 && v[j] == prefix;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      n_gt += __shfl_xor(n_gt, o, 64);
+      n_eq += __shfl_xor(n_eq, o, 64);
+    }
   }
+  // 4. every wave's output offset and its number of equal entries before it
   if (lane == 0) {
     wsum[0][wave] = n_gt;
     wsum[1][wave] = n_eq;
@@ -412,7 +513,6 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
   }
   int pos = gt_before + min(eq_before, kr);  // taken entries before this wave's range
   int eq_seen = eq_before;
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   for (int xb0 = x0; xb0 < x1; xb0 += kTopkUnroll * 64) {  // wave-uniform trip count
     uint32_t vv[kTopkUnroll];
 #pragma unroll

@@ -493,6 +493,34 @@ def test_tie_index():
     assert not errs, errs
 
 
+def test_topk_ties_beyond_gathered_bin():
+    """The top-k select gathers the entries of the k-th score's leading 11-bit
+    bin in LDS (up to 8192); here the observation-window rows of Q are zero,
+    so the 16320 columns before the window share one vertical score: the
+    select takes its radix passes over the whole list instead, and the lists
+    still equal the oracle's (the lowest indices among the ties)."""
+    dev = _dev()
+    prob = workloads.make_problem(2, n=16384, h_q=2, h_kv=1, v_budget=[100, 100], s_budget=[640, 640],
+                                  out_frac=0.0)
+    n = prob.n
+    q = prob.q.to(torch.float32)
+    q[0, n - 64:] = 0
+    prob.q = q.to(prob.q.dtype)
+    oidx, _ = oracle_index(prob)
+    for h in range(2):
+        assert np.array_equal(oidx[(h, 0)][0], np.arange(100)), h
+    gidx, vsc, _ = vs.estimate_index(prob.q.to(dev), prob.k.to(dev), prob.v_budget, prob.s_budget,
+                                     return_scores=True)
+    torch.cuda.synchronize()
+    vsc = vsc[0].cpu().numpy()
+    glists = [(a.numpy(), b.numpy()) for a, b in gidx.lists()]
+    for h in range(2):
+        assert np.ptp(vsc[h, :n - 64]) == 0, (h, "tied vertical scores differ")
+        assert np.array_equal(glists[h][0], oidx[(h, 0)][0]), (h, glists[h][0][:20])
+        assert np.array_equal(glists[h][1], oidx[(h, 0)][1]), (h, glists[h][1])
+    log("  top-k with 16320 tied scores: lists equal the oracle's")
+
+
 @pytest.mark.parametrize("dtype,d,h_q,h_kv", [("bf16", 128, 4, 2), ("f32", 64, 2, 1)])
 def test_fused_qkv_strides(dtype, d, h_q, h_kv):
     """Q, K, V as slices of one fused [batch, token, h_q + 2 h_kv, d] projection
