@@ -4,6 +4,7 @@
 // HIP call, so a rejected call enqueues nothing (and needs no GPU).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -31,8 +32,10 @@ struct EstParams;
 hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int* v_ptr, int* v_idx,
                            const int* s_ptr, int* s_idx, float* v_score, float* s_score,
                            float2* partials, float* lse2, int tiles_total, const int* tile_prefix,
-                           const float* p_v, const float* p_s, int* kcount, hipStream_t st);
+                           const float* p_v, const float* p_s, int* kcount, uint2* cand, int* ccount,
+                           hipStream_t st);
 constexpr int kEstKeyTile = 256;
+constexpr int kTopkChunk = 16384;  // entries per first-stage workgroup of a long vertical list
 struct XaParams;
 hipError_t launch_xattn(const XaParams& p, int d, hipStream_t st);
 struct MobaParams;
@@ -283,8 +286,9 @@ AttnWs attn_ws(const Prob& c, const vs_index* idx, bool backward) {
 }
 
 struct EstWs {
-  size_t part, lse2, vscore, sscore, kcount, tprefix, total;
+  size_t part, lse2, vscore, sscore, kcount, cand, ccount, tprefix, total;
   int tiles_total;
+  int nchunk;  // top-k first-stage chunks per vertical list (< 2: none)
   std::vector<int> tile_prefix;
 };
 EstWs est_ws(const Prob& c) {
@@ -305,6 +309,16 @@ EstWs est_ws(const Prob& c) {
   off += align256((size_t)c.batch * c.h_q * (c.n_global / c.block) * 4);
   w.kcount = off;  // top-p: entries per (list, kind)
   off += align256((size_t)c.n_lists() * 2 * 4);
+  // top-k of long vertical lists: each 16384-entry chunk's candidates
+  // (score bits, index) and their number
+  int max_len = 0;
+  for (int s = 0; s < c.n_seg; ++s) max_len = std::max(max_len, c.cu[s + 1] - c.cu[s]);
+  w.nchunk = (max_len + vs::kTopkChunk - 1) / vs::kTopkChunk;
+  const size_t nc = w.nchunk >= 2 ? (size_t)c.n_lists() * w.nchunk : 0;
+  w.cand = off;
+  off += align256(nc * vs::kTopkChunk * 8);
+  w.ccount = off;
+  off += align256(nc * 4);
   w.tprefix = off;
   w.total = off;
   return w;
@@ -481,7 +495,10 @@ vs_status estimate(const char* what, const vs_problem* p, const void* q, const v
   return hip_status(vs::launch_estimate(a, c.bf16, c.d, v_ptr, v_idx, s_ptr, s_idx, vsc, ssc,
                                         reinterpret_cast<float2*>(base + w.part),
                                         reinterpret_cast<float*>(base + w.lse2), w.tiles_total,
-                                        w.tile_prefix.data(), p_v, p_s, kc, (hipStream_t)stream),
+                                        w.tile_prefix.data(), p_v, p_s, kc,
+                                        w.nchunk >= 2 ? reinterpret_cast<uint2*>(base + w.cand) : nullptr,
+                                        w.nchunk >= 2 ? reinterpret_cast<int*>(base + w.ccount) : nullptr,
+                                        (hipStream_t)stream),
                     what);
 }
 }  // namespace

@@ -22,6 +22,8 @@
 //           compaction over contiguous per-wave ranges that writes the chosen
 //           indices ascending, taking the lowest indices among scores equal
 //           to the threshold.
+#include <algorithm>
+
 #include "vs_attn_common.h"
 #include "vs_trace.h"
 
@@ -297,80 +299,158 @@ __device__ __forceinline__ void select_digit(const int* hist, int kr, int* sel) 
   }
 }
 
-// Entries of the leading 11-bit bin of the k-th largest score that the
-// top-k select gathers in LDS (a list whose bin holds more takes the radix
-// passes over the whole list instead).
-constexpr int kTopkCand = 8192;
+// Top-k selection (Algorithm 1, argtopk; ties to the lowest index): of the
+// non-negative fp32 scores src[0..L) (whose bit patterns order as the
+// values do) the k largest, emitted in index order as emit(pos, x, bits).
+// The k-th largest value is found digit by digit (radix select); then the
+// entries above it and the lowest-index entries equal to it are written:
+// wave w owns the contiguous range [w C, (w + 1) C) of the list, counts
+// its entries above / equal to it, and one workgroup scan gives every wave
+// its output offset and its number of equal entries before it (ballot
+// prefixes order the lanes of each 64-entry step).
+constexpr int kTopkCand = 16384;   // LDS entries: a gathered bin, or merged candidates
+constexpr int kTopkNW = kTopkThreads / 64;
+constexpr int kTopkChunk = 16384;  // entries per first-stage workgroup of a long vertical list
 
-// kcount (optional): the number of entries to select per (list, kind), at
-// most the list's capacity; the rest of the list is padded with -1.
-__global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p, const float* v_score,
-                                                                   const float* s_score, const int* v_ptr,
-                                                                   int* v_idx, const int* s_ptr,
-                                                                   int* s_idx, const int* kcount) {
-  __shared__ int hist[256];
-  __shared__ int h1[2048];
-  __shared__ uint32_t cv[kTopkCand];
-  __shared__ int ci[kTopkCand];
-  __shared__ int wsum[2][kTopkThreads / 64];
-  __shared__ int wcnt[2][kTopkThreads / 64];
-  __shared__ int sel[2];
-  __shared__ int ncand;
-  const int kind = blockIdx.x & 1;
-  const int list = blockIdx.x >> 1;
-  const int s = list % p.seg.n_seg;
-  const int bh = list / p.seg.n_seg;
-  const int a_blk = p.seg.start_blk[s];
-  const int nb_s = p.seg.start_blk[s + 1] - a_blk;
-  const int nbt = p.n_global / kBlock;
-  const float* sc;
-  int L, k, add;
-  int* out;
-  if (kind == 0) {
-    sc = v_score + (size_t)bh * p.n_global + (size_t)a_blk * kBlock;
-    L = nb_s * kBlock;
-    k = v_ptr[list + 1] - v_ptr[list];
-    out = v_idx + v_ptr[list];
-    add = a_blk * kBlock;
-  } else {
-    sc = s_score + (size_t)bh * nbt + a_blk;
-    L = nb_s;
-    k = s_ptr[list + 1] - s_ptr[list];
-    out = s_idx + s_ptr[list];
-    add = 0;
-  }
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int cap = k;
-  if (kcount) k = min(kcount[blockIdx.x], cap);
-  if (k >= L) {
-    for (int x = tid; x < cap; x += kTopkThreads) out[x] = x < L ? x + add : -1;
-    return;
-  }
-  if (k <= 0) {
-    for (int x = tid; x < cap; x += kTopkThreads) out[x] = -1;
-    return;
-  }
-  for (int x = k + tid; x < cap; x += kTopkThreads) out[x] = -1;
-  const uint32_t* u = reinterpret_cast<const uint32_t*>(sc);
-  // Scores are non-negative floats, so their bit patterns order as they do.
-  // The k-th largest value is found digit by digit (radix select), then the
-  // entries above it and the lowest-index entries equal to it are written
-  // in index order.  Wave w owns the contiguous range [w C, (w + 1) C) of
-  // the list for the counting and the writing.
-  constexpr int NW = kTopkThreads / 64;
-  const int C = ((L + NW - 1) / NW + 63) & ~63;
+struct TopkLds {
+  int hist[256];
+  int h1[2048];
+  uint32_t cv[kTopkCand];
+  int ci[kTopkCand];
+  int wsum[2][kTopkNW];
+  int wcnt[2][kTopkNW];
+  int sel[2];
+  int ncand;
+};
+
+// The write pass, once the k-th largest bit pattern `prefix`, the number kr
+// of entries equal to it to take, and this wave's counts above / equal to it
+// are known.
+template <class Src, class Emit>
+__device__ __forceinline__ void topk_write(TopkLds& S, Src src, int L, uint32_t prefix, int kr, int n_gt,
+                                           int n_eq, Emit& emit) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int C = ((L + kTopkNW - 1) / kTopkNW + 63) & ~63;
   const int x0 = wave * C;
   const int x1 = min(x0 + C, L);
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  // 1. the leading 11 bits of every score: 2048 bins
-  for (int x = tid; x < 2048; x += kTopkThreads) h1[x] = 0;
-  if (tid < NW) {
-    wcnt[0][tid] = 0;
-    wcnt[1][tid] = 0;
+  if (lane == 0) {
+    S.wsum[0][wave] = n_gt;
+    S.wsum[1][wave] = n_eq;
   }
-  if (tid == 0) ncand = 0;
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += S.wsum[0][w];
+    eq_before += S.wsum[1][w];
+  }
+  int pos = gt_before + min(eq_before, kr);  // taken entries before this wave's range
+  int eq_seen = eq_before;
+  for (int xb0 = x0; xb0 < x1; xb0 += kTopkUnroll * 64) {  // wave-uniform trip count
+    uint32_t vv[kTopkUnroll];
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int x = xb0 + 64 * j + lane;
+      vv[j] = x < x1 ? src(x) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int x = xb0 + 64 * j + lane;
+      const uint32_t v = vv[j];
+      const bool gt = x < x1 && v > prefix;
+      const bool eq = x < x1 && v == prefix;
+      const uint64_t meq = __ballot(eq);
+      const bool take = gt || (eq && eq_seen + __popcll(meq & below) < kr);
+      const uint64_t mt = __ballot(take);
+      if (take) emit(pos + __popcll(mt & below), x, v);
+      pos += __popcll(mt);
+      eq_seen += __popcll(meq);
+    }
+  }
+}
+
+// Four 8-bit radix passes over the whole of src[0..L), then the counting and
+// the write.
+template <class Src, class Emit>
+__device__ __forceinline__ void topk_radix4(TopkLds& S, Src src, int L, int k, Emit& emit) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  uint32_t prefix = 0, pmask = 0;
+  int kr = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) S.hist[tid] = 0;
+    __syncthreads();
+    for (int base = 0; base < L; base += kTopkUnroll * kTopkThreads) {  // uniform trip count
+      uint32_t v[kTopkUnroll];
+#pragma unroll
+      for (int j = 0; j < kTopkUnroll; ++j) {
+        const int x = base + j * kTopkThreads + tid;
+        v[j] = x < L ? src(x) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kTopkUnroll; ++j) {
+        const int x = base + j * kTopkThreads + tid;
+        wave_hist_add(S.hist, (int)((v[j] >> shift) & 255), x < L && (v[j] & pmask) == prefix);
+      }
+    }
+    __syncthreads();
+    if (tid < 64) select_digit(S.hist, kr, S.sel);
+    __syncthreads();
+    prefix |= (uint32_t)S.sel[0] << shift;
+    pmask |= 255u << shift;
+    kr = S.sel[1];
+    __syncthreads();
+  }
+  const int C = ((L + kTopkNW - 1) / kTopkNW + 63) & ~63;
+  const int x0 = wave * C;
+  const int x1 = min(x0 + C, L);
+  int n_gt = 0, n_eq = 0;
+  for (int xb = x0; xb < x1; xb += kTopkUnroll * 64) {
+    uint32_t v[kTopkUnroll];
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int x = xb + 64 * j + lane;
+      v[j] = x < x1 ? src(x) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkUnroll; ++j) {
+      const int x = xb + 64 * j + lane;
+      n_gt += x < x1 && v[j] > prefix;
+      n_eq += x < x1 && v[j] == prefix;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    n_gt += __shfl_xor(n_gt, o, 64);
+    n_eq += __shfl_xor(n_eq, o, 64);
+  }
+  topk_write(S, src, L, prefix, kr, n_gt, n_eq, emit);
+}
+
+// Scores in global memory: one pass over the leading 11 bits (2048 bins),
+// one pass that counts per wave the entries above the k-th score's bin and
+// gathers the bin's entries in LDS, the remaining 21 bits over the gathered
+// entries only, and the write: three passes over the list.  A bin too full
+// to gather takes topk_radix4 over the whole list.
+template <class Emit>
+__device__ __forceinline__ void topk_gather(TopkLds& S, const uint32_t* u, int L, int k, Emit& emit) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int C = ((L + kTopkNW - 1) / kTopkNW + 63) & ~63;
+  const int x0 = wave * C;
+  const int x1 = min(x0 + C, L);
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  auto gsrc = [u](int x) { return u[x]; };
+  for (int x = tid; x < 2048; x += kTopkThreads) S.h1[x] = 0;
+  if (tid < kTopkNW) {
+    S.wcnt[0][tid] = 0;
+    S.wcnt[1][tid] = 0;
+  }
+  if (tid == 0) S.ncand = 0;
   __syncthreads();
   for (int base = 0; base < L; base += kTopkUnroll * kTopkThreads) {
     uint32_t v[kTopkUnroll];
@@ -380,14 +460,13 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
       v[j] = x < L ? u[x] : 0u;
     }
 #pragma unroll
-    for (int j = 0; j < kTopkUnroll; ++j) wave_hist_add(h1, (int)(v[j] >> 21), base + j * kTopkThreads + tid < L);
+    for (int j = 0; j < kTopkUnroll; ++j) wave_hist_add(S.h1, (int)(v[j] >> 21), base + j * kTopkThreads + tid < L);
   }
   __syncthreads();
-  if (tid < 64) select_digit<2048>(h1, k, sel);
+  if (tid < 64) select_digit<2048>(S.h1, k, S.sel);
   __syncthreads();
-  const uint32_t d1 = (uint32_t)sel[0];
-  int kr = sel[1];
-  // 2. per wave, the entries above that bin; the bin's entries into LDS
+  const uint32_t d1 = (uint32_t)S.sel[0];
+  int kr = S.sel[1];
   int n_above = 0;
   for (int xb = x0; xb < x1; xb += kTopkUnroll * 64) {  // wave-uniform trip count
     uint32_t v[kTopkUnroll];
@@ -405,12 +484,12 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
       const uint64_t m = __ballot(in);
       if (m) {  // uniform
         int b0 = 0;
-        if (lane == 0) b0 = atomicAdd(&ncand, __popcll(m));
+        if (lane == 0) b0 = atomicAdd(&S.ncand, __popcll(m));
         b0 = __shfl(b0, 0, 64);
         const int slot = b0 + __popcll(m & below);
         if (in && slot < kTopkCand) {
-          cv[slot] = v[j];
-          ci[slot] = x;
+          S.cv[slot] = v[j];
+          S.ci[slot] = x;
         }
       }
     }
@@ -418,122 +497,163 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p,
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) n_above += __shfl_xor(n_above, o, 64);
   __syncthreads();
-  const int nc = ncand;
+  const int nc = S.ncand;
+  if (nc > kTopkCand) {
+    topk_radix4(S, gsrc, L, k, emit);
+    return;
+  }
   uint32_t prefix = d1 << 21, pmask = 0x7FFu << 21;
-  int n_gt = 0, n_eq = 0;  // this wave's entries above / equal to the k-th largest
-  if (nc <= kTopkCand) {
-    // 3. the remaining 21 bits, over the gathered entries only
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 13 : (pass == 1 ? 5 : 0);
-      const uint32_t wm = pass == 2 ? 31u : 255u;
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      for (int base = 0; base < nc; base += kTopkThreads) {  // uniform trip count
-        const int i = base + tid;
-        const uint32_t v = i < nc ? cv[i] : 0u;
-        wave_hist_add(hist, (int)((v >> shift) & wm), i < nc && (v & pmask) == prefix);
-      }
-      __syncthreads();
-      if (tid < 64) select_digit(hist, kr, sel);
-      __syncthreads();
-      prefix |= (uint32_t)sel[0] << shift;
-      pmask |= wm << shift;
-      kr = sel[1];
-      __syncthreads();
-    }
-    // per wave: the gathered entries above / equal to it
-    for (int i = tid; i < nc; i += kTopkThreads) {
-      const uint32_t v = cv[i];
-      if (v > prefix) atomicAdd(&wcnt[0][ci[i] / C], 1);
-      else if (v == prefix) atomicAdd(&wcnt[1][ci[i] / C], 1);
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 13 : (pass == 1 ? 5 : 0);
+    const uint32_t wm = pass == 2 ? 31u : 255u;
+    if (tid < 256) S.hist[tid] = 0;
+    __syncthreads();
+    for (int base = 0; base < nc; base += kTopkThreads) {  // uniform trip count
+      const int i = base + tid;
+      const uint32_t v = i < nc ? S.cv[i] : 0u;
+      wave_hist_add(S.hist, (int)((v >> shift) & wm), i < nc && (v & pmask) == prefix);
     }
     __syncthreads();
-    n_gt = n_above + wcnt[0][wave];
-    n_eq = wcnt[1][wave];
-  } else {
-    // the leading bin is too full to gather: radix passes over the whole list
-    kr = k;
-    prefix = 0;
-    pmask = 0;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      for (int base = 0; base < L; base += kTopkUnroll * kTopkThreads) {
-        uint32_t v[kTopkUnroll];
-#pragma unroll
-        for (int j = 0; j < kTopkUnroll; ++j) {
-          const int x = base + j * kTopkThreads + tid;
-          v[j] = x < L ? u[x] : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < kTopkUnroll; ++j) {
-          const int x = base + j * kTopkThreads + tid;
-          wave_hist_add(hist, (int)((v[j] >> shift) & 255), x < L && (v[j] & pmask) == prefix);
-        }
-      }
-      __syncthreads();
-      if (tid < 64) select_digit(hist, kr, sel);
-      __syncthreads();
-      prefix |= (uint32_t)sel[0] << shift;
-      pmask |= 255u << shift;
-      kr = sel[1];
-      __syncthreads();
-    }
-    for (int xb = x0; xb < x1; xb += kTopkUnroll * 64) {
-      uint32_t v[kTopkUnroll];
-#pragma unroll
-      for (int j = 0; j < kTopkUnroll; ++j) {
-        const int x = xb + 64 * j + lane;
-        v[j] = x < x1 ? u[x] : 0u;
-      }
-#pragma unroll
-      for (int j = 0; j < kTopkUnroll; ++j) {
-        const int x = xb + 64 * j + lane;
-        n_gt += x < x1 && v[j] > prefix;
-        n_eq += x < x1 && v[j] == prefix;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      n_gt += __shfl_xor(n_gt, o, 64);
-      n_eq += __shfl_xor(n_eq, o, 64);
-    }
+    if (tid < 64) select_digit(S.hist, kr, S.sel);
+    __syncthreads();
+    prefix |= (uint32_t)S.sel[0] << shift;
+    pmask |= wm << shift;
+    kr = S.sel[1];
+    __syncthreads();
   }
-  // 4. every wave's output offset and its number of equal entries before it
-  if (lane == 0) {
-    wsum[0][wave] = n_gt;
-    wsum[1][wave] = n_eq;
+  for (int i = tid; i < nc; i += kTopkThreads) {
+    const uint32_t v = S.cv[i];
+    if (v > prefix) atomicAdd(&S.wcnt[0][S.ci[i] / C], 1);
+    else if (v == prefix) atomicAdd(&S.wcnt[1][S.ci[i] / C], 1);
   }
   __syncthreads();
-  int gt_before = 0, eq_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    gt_before += wsum[0][w];
-    eq_before += wsum[1][w];
+  topk_write(S, gsrc, L, prefix, kr, n_above + S.wcnt[0][wave], S.wcnt[1][wave], emit);
+}
+
+// The list (kind 0: vertical columns of a segment, kind 1: its
+// block-diagonals) of workgroup pair 2 list + kind, its length, selection
+// size and output.
+struct TopkList {
+  const uint32_t* u;
+  int L, k, cap, add;
+  int* out;
+};
+__device__ __forceinline__ TopkList topk_list(const AttnParams& p, const float* v_score, const float* s_score,
+                                             const int* v_ptr, int* v_idx, const int* s_ptr, int* s_idx,
+                                             const int* kcount, int list, int kind) {
+  TopkList t;
+  const int s = list % p.seg.n_seg;
+  const int bh = list / p.seg.n_seg;
+  const int a_blk = p.seg.start_blk[s];
+  const int nb_s = p.seg.start_blk[s + 1] - a_blk;
+  if (kind == 0) {
+    t.u = reinterpret_cast<const uint32_t*>(v_score + (size_t)bh * p.n_global + (size_t)a_blk * kBlock);
+    t.L = nb_s * kBlock;
+    t.cap = v_ptr[list + 1] - v_ptr[list];
+    t.out = v_idx ? v_idx + v_ptr[list] : nullptr;
+    t.add = a_blk * kBlock;
+  } else {
+    t.u = reinterpret_cast<const uint32_t*>(s_score + (size_t)bh * (p.n_global / kBlock) + a_blk);
+    t.L = nb_s;
+    t.cap = s_ptr[list + 1] - s_ptr[list];
+    t.out = s_idx + s_ptr[list];
+    t.add = 0;
   }
-  int pos = gt_before + min(eq_before, kr);  // taken entries before this wave's range
-  int eq_seen = eq_before;
-  for (int xb0 = x0; xb0 < x1; xb0 += kTopkUnroll * 64) {  // wave-uniform trip count
-    uint32_t vv[kTopkUnroll];
-#pragma unroll
-    for (int j = 0; j < kTopkUnroll; ++j) {
-      const int x = xb0 + 64 * j + lane;
-      vv[j] = x < x1 ? u[x] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < kTopkUnroll; ++j) {
-      const int x = xb0 + 64 * j + lane;
-      const uint32_t v = vv[j];
-      const bool gt = x < x1 && v > prefix;
-      const bool eq = x < x1 && v == prefix;
-      const uint64_t meq = __ballot(eq);
-      const bool take = gt || (eq && eq_seen + __popcll(meq & below) < kr);
-      const uint64_t mt = __ballot(take);
-      if (take) out[pos + __popcll(mt & below)] = x + add;
-      pos += __popcll(mt);
-      eq_seen += __popcll(meq);
-    }
+  t.k = kcount ? min(kcount[2 * list + kind], t.cap) : t.cap;
+  return t;
+}
+
+// A long vertical list is selected in two stages: each of nch >= 2 chunks
+// of ch entries picks its own top-k (the global top-k, ties to the lowest
+// index, lies in the union of the chunks' top-k: an entry that k others
+// beat inside its chunk is beaten by them in the list), then the top-k of
+// those candidates, which arrive in index order.  Chunks hold at most
+// kTopkChunk entries, or fewer, longer ones where the nch * k candidates
+// would not fit in LDS.
+__device__ __forceinline__ bool topk_two_stage(const TopkList& t, int* nch, int* ch) {
+  if (t.k <= 0 || t.k >= t.L) return false;
+  int n = (t.L + kTopkChunk - 1) / kTopkChunk;
+  if ((long long)n * t.k > kTopkCand) n = kTopkCand / t.k;
+  *nch = n;
+  *ch = (t.L + n - 1) / max(n, 1);
+  return n >= 2;
+}
+
+// First stage: workgroup (list, chunk c) writes its chunk's top-min(k, len)
+// entries (at most k <= kTopkCand / 2 < kTopkChunk), in index order, to
+// cand[(list * nchunk + c) * kTopkChunk ...] as (score bits, index in the
+// list) and their number to ccount; nchunk (the slots per list) is the
+// longest list's kTopkChunk-entry chunk count, at least any list's nch.
+__global__ __launch_bounds__(kTopkThreads) void vs_est_topk_chunk_kernel(AttnParams p, const float* v_score,
+                                                                         const int* v_ptr, const int* kcount,
+                                                                         int nchunk, uint2* cand, int* ccount) {
+  __shared__ TopkLds S;
+  const int list = blockIdx.x / nchunk;
+  const int c = blockIdx.x % nchunk;
+  const TopkList t = topk_list(p, v_score, nullptr, v_ptr, nullptr, nullptr, nullptr, kcount, list, 0);
+  int nch, ch;
+  if (!topk_two_stage(t, &nch, &ch) || c >= nch) return;
+  const int x0 = c * ch;
+  const int len = max(min(ch, t.L - x0), 0);
+  uint2* dst = cand + ((size_t)list * nchunk + c) * kTopkChunk;
+  if (threadIdx.x == 0) ccount[list * nchunk + c] = min(t.k, len);
+  if (len == 0) return;
+  auto emit = [dst, x0](int pos, int x, uint32_t v) { dst[pos] = make_uint2(v, (uint32_t)(x0 + x)); };
+  if (t.k >= len) {
+    for (int x = threadIdx.x; x < len; x += kTopkThreads) emit(x, x, t.u[x0 + x]);
+    return;
   }
+  topk_gather(S, t.u + x0, len, t.k, emit);
+}
+
+// kcount (optional): the number of entries to select per (list, kind), at
+// most the list's capacity; the rest of the list is padded with -1.  Lists
+// of the two-stage select merge their chunks' candidates (cand, ccount).
+__global__ __launch_bounds__(kTopkThreads) void vs_est_topk_kernel(AttnParams p, const float* v_score,
+                                                                   const float* s_score, const int* v_ptr,
+                                                                   int* v_idx, const int* s_ptr,
+                                                                   int* s_idx, const int* kcount, int nchunk,
+                                                                   const uint2* cand, const int* ccount) {
+  __shared__ TopkLds S;
+  const int kind = blockIdx.x & 1;
+  const int list = blockIdx.x >> 1;
+  const TopkList t = topk_list(p, v_score, s_score, v_ptr, v_idx, s_ptr, s_idx, kcount, list, kind);
+  const int tid = threadIdx.x;
+  const int k = t.k, L = t.L, add = t.add;
+  int* out = t.out;
+  if (k >= L) {
+    for (int x = tid; x < t.cap; x += kTopkThreads) out[x] = x < L ? x + add : -1;
+    return;
+  }
+  if (k <= 0) {
+    for (int x = tid; x < t.cap; x += kTopkThreads) out[x] = -1;
+    return;
+  }
+  for (int x = k + tid; x < t.cap; x += kTopkThreads) out[x] = -1;
+  int nch, ch;
+  if (kind == 0 && cand && topk_two_stage(t, &nch, &ch)) {
+    // the chunks' candidates, in index order, into LDS
+    int nc = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int m = ccount[list * nchunk + c];
+      const uint2* src = cand + ((size_t)list * nchunk + c) * kTopkChunk;
+      for (int i = tid; i < m; i += kTopkThreads) {
+        const uint2 e = src[i];
+        S.cv[nc + i] = e.x;
+        S.ci[nc + i] = (int)e.y;
+      }
+      nc += m;
+    }
+    __syncthreads();
+    const uint32_t* lcv = S.cv;
+    auto lsrc = [lcv](int i) { return lcv[i]; };
+    const int* lci = S.ci;
+    auto emit = [out, add, lci](int pos, int i, uint32_t) { out[pos] = lci[i] + add; };
+    topk_radix4(S, lsrc, nc, k, emit);
+    return;
+  }
+  auto emit = [out, add](int pos, int x, uint32_t) { out[pos] = x + add; };
+  topk_gather(S, t.u, L, k, emit);
 }
 
 // Top-p budgets (Algorithm 1, topp): per (list, kind) the fewest top scores,
@@ -755,7 +875,8 @@ __global__ __launch_bounds__(kTopkThreads) void vs_est_topp_kernel(AttnParams p,
 hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int* v_ptr, int* v_idx,
                            const int* s_ptr, int* s_idx, float* v_score, float* s_score,
                            float2* partials, float* lse2, int tiles_total, const int* tile_prefix,
-                           const float* p_v, const float* p_s, int* kcount, hipStream_t st) {
+                           const float* p_v, const float* p_s, int* kcount, uint2* cand, int* ccount,
+                           hipStream_t st) {
   TilePrefix tp;
   for (int s = 0; s <= p.seg.n_seg; ++s) tp.v[s] = tile_prefix[s];
   const int n_lists = p.batch * p.h_q * p.seg.n_seg;
@@ -778,9 +899,18 @@ hipError_t launch_estimate(const AttnParams& p, int dtype_bf16, int d, const int
     VS_TRACED(st, "vs_est_topp", hipLaunchKernelGGL(vs_est_topp_kernel, dim3(2 * n_lists), dim3(kTopkThreads), 0, st, p,
                        (const float*)v_score, (const float*)s_score, v_ptr, s_ptr, p_v, p_s, kcount));
   }
+  // long vertical lists: a first stage per 16384-entry chunk
+  int max_len = 0;
+  for (int s = 0; s < p.seg.n_seg; ++s)
+    max_len = std::max(max_len, (p.seg.start_blk[s + 1] - p.seg.start_blk[s]) * kBlock);
+  const int nchunk = (max_len + kTopkChunk - 1) / kTopkChunk;
+  const int* kc = p_v ? (const int*)kcount : (const int*)nullptr;
+  if (nchunk >= 2 && cand)
+    VS_TRACED(st, "vs_est_topk_chunk", hipLaunchKernelGGL(vs_est_topk_chunk_kernel, dim3(n_lists * nchunk), dim3(kTopkThreads), 0, st, p,
+                       (const float*)v_score, v_ptr, kc, nchunk, cand, ccount));
   VS_TRACED(st, "vs_est_topk", hipLaunchKernelGGL(vs_est_topk_kernel, dim3(2 * n_lists), dim3(kTopkThreads), 0, st, p,
-                     (const float*)v_score, (const float*)s_score, v_ptr, v_idx, s_ptr, s_idx,
-                     p_v ? (const int*)kcount : (const int*)nullptr));
+                     (const float*)v_score, (const float*)s_score, v_ptr, v_idx, s_ptr, s_idx, kc,
+                     nchunk, (const uint2*)(nchunk >= 2 ? cand : nullptr), (const int*)ccount));
   return hipGetLastError();
 }
 
