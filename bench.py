@@ -67,7 +67,11 @@ def hbm_alg_bytes(name, c):
         "vs_est_pass1": K + Qw + part,
         "vs_est_combine": part + lse,
         "vs_est_pass2": K + Qw + lse + vsc + ssc,
-        "vs_est_topk": vsc + ssc + lists,
+        # the two-stage top-k: the chunks read the column scores, the last
+        # stage the block-diagonal scores (and the chunks' candidates) and
+        # writes the lists
+        "vs_est_topk_chunk": vsc,
+        "vs_est_topk": ssc + lists,
         "vs_prep_vertical": 2 * 4 * c["v_ent"],
         "vs_moba_means": K,
         "vs_moba_select": c["batch"] * c["n"] * c["h_q"] * (c["d"] * c["el"] + 4),
