@@ -93,7 +93,8 @@ CPU_SHARE = 16
 # vs_estimate.hip (vs_est_*) or vs_misc.hip.
 KERNEL_SOURCE = {"vs_fwd": "vs_fwd.hip", "vs_bwd_dq": "vs_bwd_dq.hip", "vs_bwd_dkdv_slash": "vs_bwd_kv.hip",
                  "vs_bwd_dkdv_cols": "vs_bwd_kv.hip", "vs_xa_cells": "vs_xattn.hip",
-                 "vs_xa_select": "vs_xattn.hip"}
+                 "vs_xa_select": "vs_xattn.hip", "vs_moba_means": "vs_moba.hip", "vs_moba_select": "vs_moba.hip",
+                 "vs_moba_union": "vs_moba.hip"}
 
 
 def kernel_digest(kernel):
@@ -135,11 +136,15 @@ def measured_traffic(kernel, workload):
 
 # rocprofv3 kernel names -> traced names
 _PROF_NAMES = (("vs_fwd_rows_kernel", "vs_fwd"), ("vs_bwd_dq_rows_kernel", "vs_bwd_dq"),
-               ("vs_bwd_kv_slash_bf16_kernel", "vs_bwd_dkdv_slash"), ("vs_bwd_kv_cols_bf16_kernel", "vs_bwd_dkdv_cols"),
+               ("vs_bwd_kv_slash_bf16_kernel", "vs_bwd_dkdv_slash"), ("vs_bwd_kv_pair_bf16_kernel", "vs_bwd_dkdv_slash"),
+               ("vs_bwd_kv_cols_bf16_kernel", "vs_bwd_dkdv_cols"),
                ("vs_delta_kernel", "vs_delta"), ("vs_est_pass1", "vs_est_pass1"), ("vs_est_pass2", "vs_est_pass2"),
-               ("vs_est_topk", "vs_est_topk"), ("vs_est_combine", "vs_est_combine"), ("vs_lse_log2", "vs_lse_log2"),
+               ("vs_est_topk_chunk_kernel", "vs_est_topk_chunk"), ("vs_est_topk_kernel", "vs_est_topk"),
+               ("vs_est_combine", "vs_est_combine"), ("vs_lse_log2", "vs_lse_log2"),
                ("vs_prep_vertical", "vs_prep_vertical"), ("vs_group_share", "vs_group_share"),
-               ("vs_xa_cells_kernel", "vs_xa_cells"), ("vs_xa_select_kernel", "vs_xa_select"))
+               ("vs_xa_cells_kernel", "vs_xa_cells"), ("vs_xa_select_kernel", "vs_xa_select"),
+               ("vs_moba_means_kernel", "vs_moba_means"), ("vs_moba_select_kernel", "vs_moba_select"),
+               ("vs_moba_union_kernel", "vs_moba_union"))
 
 
 def write_traffic(run_dir, workload):
