@@ -547,3 +547,50 @@ def test_per_row_selection_in_bounds(n, batch, h_q, h_kv, blk):
                 for half in (0, 1):
                     li = bh * n + i * BLOCK + 32 * half + np.arange(32)
                     assert li.max() < rows_words
+
+
+def topk_two_stage(L, k, chunk=16384, cand=16384):
+    """The top-k's choice for a list of L scores and k picks (mirrors the
+    device): (chunks, chunk length) of the two-stage select, or None."""
+    if k <= 0 or k >= L:
+        return None
+    n = -(-L // chunk)
+    if n * k > cand:
+        n = cand // k
+    if n < 2:
+        return None
+    return n, -(-L // n)
+
+
+@pytest.mark.parametrize("n,cu_frac", [(131072, None), (262144, "docs"), (524288, None), (40960, None)])
+def test_topk_chunks_in_bounds(n, cu_frac):
+    """The two-stage top-k: every list's chunks cover it exactly, fit the
+    workspace's slots (the longest list's 16384-entry chunk count per list,
+    16384 candidate pairs per slot) and their candidates fit the merge's LDS
+    (16384); the workspace bytes match the host's sizing."""
+    rng = np.random.default_rng(5 + n)
+    if cu_frac == "docs":
+        cuts = np.sort(rng.choice(np.arange(1, n // BLOCK), 7, replace=False)) * BLOCK
+        cu = [0] + cuts.tolist() + [n]
+    else:
+        cu = [0, n]
+    lens = np.diff(cu)
+    nslots = -(-int(lens.max()) // 16384)
+    h_q, batch = 16, 1
+    n_lists = batch * h_q * len(lens)
+    ws_pairs = n_lists * nslots * 16384 if nslots >= 2 else 0
+    for L in lens:
+        for k in (1, 2, 63, 64, 100, 1024, 2048, 2078, 4096, 8191, 8192, 8193, L - 1, L, L + 5):
+            r = topk_two_stage(int(L), int(k))
+            if r is None:
+                continue
+            nch, ch = r
+            assert 2 <= nch <= nslots and nch * k <= 16384
+            assert k < 16384                                  # a chunk's candidates fit its slot
+            lens_c = [max(min(ch, L - c * ch), 0) for c in range(nch)]
+            assert sum(lens_c) == L and min(lens_c) >= 0
+            assert sum(min(k, x) for x in lens_c) <= 16384    # the merge's LDS
+            for list_ in (0, n_lists - 1):
+                for c in range(nch):
+                    slot = (list_ * nslots + c) * 16384
+                    assert slot + min(k, lens_c[c]) <= ws_pairs
