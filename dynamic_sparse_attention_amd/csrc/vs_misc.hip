@@ -1,5 +1,7 @@
 // vs_misc.hip — memory-bound helper kernels: vertical-list preparation,
 // the backward row term delta, and the LSE merge of chunk partials.
+#include <algorithm>
+
 #include "vs_attn_common.h"
 #include "vs_trace.h"
 
@@ -8,10 +10,13 @@ namespace vs {
 // convert_index for verticals (MTraining paper note, Algorithm 2): keep the
 // selected columns of list l that this call holds (inside the list's segment;
 // for a block-striped call, in a key block of rank k_rank), in ascending
-// order, as global positions.  One workgroup per list, ordered compaction.
-__global__ __launch_bounds__(256) void vs_prep_vertical_kernel(AttnParams p, const int* v_ptr,
-                                                               const int* v_idx) {
-  __shared__ int wsum[4];
+// order, as global positions.  One workgroup per list, ordered compaction
+// in rounds of kPrepThreads entries.
+constexpr int kPrepThreads = 1024;
+
+__global__ __launch_bounds__(kPrepThreads) void vs_prep_vertical_kernel(AttnParams p, const int* v_ptr,
+                                                                        const int* v_idx) {
+  __shared__ int wsum[kPrepThreads / 64];
   const int l = blockIdx.x;
   const int s = l % p.seg.n_seg;
   int a, e;
@@ -22,11 +27,13 @@ __global__ __launch_bounds__(256) void vs_prep_vertical_kernel(AttnParams p, con
     a = 0;
     e = p.n_global;
   }
+  // the group-share accumulators (vs_group_share_kernel, which runs next)
+  if (p.map_group && l == 0 && threadIdx.x < 5) p.map_group[2 + threadIdx.x] = 0;
   const int v0 = v_ptr[l];
   const int nv = v_ptr[l + 1] - v0;
   int* out = const_cast<int*>(p.vsel) + (size_t)l * p.vsel_stride;
   int count = 0;
-  for (int base = 0; base < nv; base += 256) {
+  for (int base = 0; base < nv; base += kPrepThreads) {
     const int i = base + threadIdx.x;
     int m = -1;
     bool keep = false;
@@ -35,7 +42,7 @@ __global__ __launch_bounds__(256) void vs_prep_vertical_kernel(AttnParams p, con
       keep = m >= a && m < e && local_key_block(p, m / kBlock) >= 0;
     }
     int tot;
-    const int slot = block_compact<256>(keep, wsum, &tot);
+    const int slot = block_compact<kPrepThreads>(keep, wsum, &tot);
     if (keep && count + slot < p.vsel_stride) out[count + slot] = m;
     count += tot;
     __syncthreads();
@@ -47,51 +54,56 @@ __global__ __launch_bounds__(256) void vs_prep_vertical_kernel(AttnParams p, con
 // block-diagonals: over up to 1024 evenly spread lists of non-leading heads,
 // the fraction of their entries that the group's first head (same batch and
 // segment) also selected (the first kShareCap entries of each list, a
-// sample for longer ones).  *share = 1 when it is at least one half; this
-// picks the work mapping of the query-major kernels (qmajor_item).  One
-// workgroup: each wave stages the leading head's list in LDS and its lanes
-// binary-search their own entries in it.  Lists are ascending, with -1
-// padding at the end (ordered as +inf).
+// sample for longer ones).  share[0] = 1 when it is at least one half; this
+// picks the work mapping of the query-major kernels (qmajor_item).  Each
+// wave takes one sampled list: it stages the leading head's list in LDS and
+// its lanes binary-search their own entries in it.  Lists are ascending,
+// with -1 padding at the end (ordered as +inf).  The workgroups add their
+// counts into share[2..5] (two 64-bit sums, zeroed by vs_prep_vertical_kernel
+// just before) and take a ticket in share[6]; the last one decides.
 constexpr int kShareCap = 2048;
+constexpr int kShareSample = 1024;
 
 __global__ __launch_bounds__(256) void vs_group_share_kernel(AttnParams p, int* share) {
   __shared__ int lead[4][kShareCap];
   __shared__ long long red[2][4];
+  __shared__ bool last;
   const int GS = p.h_q / p.h_kv;
   const int n_lists = p.batch * p.h_q * p.seg.n_seg;
-  const int stride = n_lists > 1024 ? n_lists / 1024 : 1;
+  const int stride = n_lists > kShareSample ? n_lists / kShareSample : 1;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   long long common = 0, total = 0;
-  for (int t = wave; t * stride < n_lists && t < 1024; t += 4) {  // wave-uniform
+  const int t = 4 * blockIdx.x + wave;  // sampled list t * stride
+  if (t * stride < n_lists && t < kShareSample) {  // wave-uniform
     const int l = t * stride;
     const int seg = l % p.seg.n_seg;
     const int bh = l / p.seg.n_seg;
     const int h = bh % p.h_q;
     const int b = bh / p.h_q;
     const int h0 = (h / GS) * GS;
-    if (h == h0) continue;
-    const int l0 = (b * p.h_q + h0) * p.seg.n_seg + seg;
-    const int* A = p.s_idx + p.s_ptr[l];
-    const int* B = p.s_idx + p.s_ptr[l0];
-    const int na = min(p.s_ptr[l + 1] - p.s_ptr[l], kShareCap);
-    const int nb = min(p.s_ptr[l0 + 1] - p.s_ptr[l0], kShareCap);
-    for (int i = lane; i < nb; i += 64) lead[wave][i] = B[i];
-    wave_sync();
-    for (int i = lane; i < na; i += 64) {
-      const int x = A[i];
-      if (x < 0) continue;
-      ++total;
-      int lo = 0, hi = nb;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        const int v = lead[wave][mid];
-        if (v >= 0 && v < x) lo = mid + 1;
-        else hi = mid;
+    if (h != h0) {
+      const int l0 = (b * p.h_q + h0) * p.seg.n_seg + seg;
+      const int* A = p.s_idx + p.s_ptr[l];
+      const int* B = p.s_idx + p.s_ptr[l0];
+      const int na = min(p.s_ptr[l + 1] - p.s_ptr[l], kShareCap);
+      const int nb = min(p.s_ptr[l0 + 1] - p.s_ptr[l0], kShareCap);
+      for (int i = lane; i < nb; i += 64) lead[wave][i] = B[i];
+      wave_sync();
+      for (int i = lane; i < na; i += 64) {
+        const int x = A[i];
+        if (x < 0) continue;
+        ++total;
+        int lo = 0, hi = nb;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          const int v = lead[wave][mid];
+          if (v >= 0 && v < x) lo = mid + 1;
+          else hi = mid;
+        }
+        common += lo < nb && lead[wave][lo] == x;
       }
-      common += lo < nb && lead[wave][lo] == x;
     }
-    wave_sync();  // every lane is done with lead[wave] before the next list
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -103,19 +115,31 @@ __global__ __launch_bounds__(256) void vs_group_share_kernel(AttnParams p, int* 
     red[1][wave] = total;
   }
   __syncthreads();
+  unsigned long long* acc = reinterpret_cast<unsigned long long*>(share + 2);
+  unsigned int* ticket = reinterpret_cast<unsigned int*>(share + 6);
   if (threadIdx.x == 0) {
-    const long long c = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    const long long n = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-    *share = (n > 0 && 2 * c >= n) ? 1 : 0;
+    atomicAdd(&acc[0], (unsigned long long)(red[0][0] + red[0][1] + red[0][2] + red[0][3]));
+    atomicAdd(&acc[1], (unsigned long long)(red[1][0] + red[1][1] + red[1][2] + red[1][3]));
+    __threadfence();  // the sums are visible before the ticket is taken
+    last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (last && threadIdx.x == 0) {
+    __threadfence();
+    const unsigned long long c = atomicAdd(&acc[0], 0ull);
+    const unsigned long long n = atomicAdd(&acc[1], 0ull);
+    share[0] = (n > 0 && 2 * c >= n) ? 1 : 0;
   }
 }
 
 hipError_t launch_prep_vertical(const AttnParams& p, int n_lists, const int* v_ptr, const int* v_idx,
                                 hipStream_t st) {
   if (n_lists == 0) return hipSuccess;
-  VS_TRACED(st, "vs_prep_vertical", hipLaunchKernelGGL(vs_prep_vertical_kernel, dim3(n_lists), dim3(256), 0, st, p, v_ptr, v_idx));
-  if (p.map_group)
-    VS_TRACED(st, "vs_group_share", hipLaunchKernelGGL(vs_group_share_kernel, dim3(1), dim3(256), 0, st, p, p.map_group));
+  VS_TRACED(st, "vs_prep_vertical", hipLaunchKernelGGL(vs_prep_vertical_kernel, dim3(n_lists), dim3(kPrepThreads), 0, st, p, v_ptr, v_idx));
+  if (p.map_group) {
+    const int n_sample = std::min(n_lists, kShareSample);
+    VS_TRACED(st, "vs_group_share", hipLaunchKernelGGL(vs_group_share_kernel, dim3((unsigned)((n_sample + 3) / 4)), dim3(256), 0, st, p, p.map_group));
+  }
   return hipGetLastError();
 }
 
