@@ -739,8 +739,11 @@ vs_status attn_bwd(const char* what, const vs_problem* p, const void* q, const v
   // range count that is a multiple of 8 every XCD would always get the same
   // ranges, and the early ranges carry little work (few columns start that
   // early), which left one XCD with over twice the work of another.  An odd
-  // count spreads every column tile's ranges over all XCDs.
-  a.qrange_len = 48;
+  // count spreads every column tile's ranges over all XCDs.  A striped call
+  // over one rank's key chunk holds about 1/W of each list's columns, so few
+  // column tiles have work: there units of about 16 query blocks keep more
+  // of them in flight (their partial dK, dV go out with fp32 atomics).
+  a.qrange_len = (c.W > 1 && !c.k_all) ? 16 : 48;
   a.qranges = (c.nqb + a.qrange_len - 1) / a.qrange_len;
   while (a.qranges > 1 && a.qranges % 2 == 0) {
     ++a.qrange_len;

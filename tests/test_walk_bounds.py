@@ -204,7 +204,7 @@ def column_units(call, lists, h_q, n_seg, v_cap):
     """Column dK/dV units: columns of the prepared list, their local key
     positions and the query-block range."""
     col_tiles = (v_cap + 63) // 64
-    qrange_len = 48
+    qrange_len = 16 if (call.W > 1 and not call.k_all) else 48
     qranges = (call.nqb + qrange_len - 1) // qrange_len
     while qranges > 1 and qranges % 2 == 0:
         qrange_len += 1
