@@ -50,6 +50,45 @@ __device__ __forceinline__ void est_load_k(const T* kb, int kvs, int key_l, int 
   for (int c = 0; c < NCD; ++c) kf[c] = load_frag<T>(kr + c * KC + hl * KPL);
 }
 
+// bf16: the workgroup's kEstKeyTile K rows staged in LDS once by direct
+// loads and read by every wave for each of its heads (instead of each wave
+// fetching them from memory per head).  Row r's 16-byte chunk c sits at
+// chunk index c ^ swz(r), so the 16 lanes of a fragment read (16 rows, one
+// chunk) touch 16 distinct bank groups; rows past the tile's end repeat its
+// last row (masked, as the memory path's clamped loads are).
+template <int D>
+struct EstKTile {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;       // rows per 1 KiB direct load
+  static constexpr int NI = kEstKeyTile / RPI;
+  static constexpr int BYTES = kEstKeyTile * D * 2;
+  __device__ static __forceinline__ int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static __forceinline__ int off(int r, int c) { return r * CPR * 16 + 16 * (c ^ swz(r)); }
+
+  // rows k0 .. k0 + kEstKeyTile - 1 of K (clamped to k1 - 1); every wave of
+  // the workgroup issues NI / 4 loads, then waits and meets the others
+  __device__ static __forceinline__ void stage(char* tile, const __bf16* kb, int kvs, int k0, int k1) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rsub = lane / CPR;
+#pragma unroll
+    for (int u0 = 0; u0 < NI / 4; ++u0) {
+      const int u = w * (NI / 4) + u0;
+      const int r = u * RPI + rsub;
+      const int key = min(k0 + r, k1 - 1);
+      const int lc = (lane % CPR) ^ swz(r);
+      dma_lds16(kb + (size_t)key * kvs + lc * 8, tile + u * 1024);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+    __syncthreads();
+  }
+
+  // this lane's K operand of k chunk cc (channels 16 cc + 8 hl ..) for tile row r
+  __device__ static __forceinline__ Mfma<__bf16>::frag frag(const char* tile, int r, int cc, int hl) {
+    return *reinterpret_cast<const Mfma<__bf16>::frag*>(tile + off(r, 2 * cc + hl));
+  }
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void vs_est_pass1_kernel(AttnParams p, TilePrefix tp, int tiles_total,
                                                            float2* part) {
@@ -68,6 +107,9 @@ __global__ __launch_bounds__(256) void vs_est_pass1_kernel(AttnParams p, TilePre
   const int kvs = (int)p.sk.t;
   const T* kb = reinterpret_cast<const T*>(p.k) + p.sk.at(b, 0, kvh);
   const T* q = reinterpret_cast<const T*>(p.q);
+  constexpr bool kLds = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) char ktile[kLds ? EstKTile<D>::BYTES : 16];
+  if constexpr (kLds) EstKTile<D>::stage(ktile, reinterpret_cast<const __bf16*>(kb), kvs, k0, k1);
   for (int hg = wave; hg < G; hg += 4) {
     const int h = kvh * G + hg;
     frag qf[2][NCD];
@@ -103,15 +145,25 @@ __global__ __launch_bounds__(256) void vs_est_pass1_kernel(AttnParams p, TilePre
         m[rg] = mn;
       }
     };
-    // Chunks of 32 keys in pairs (a tile spans whole 64-key blocks), each
-    // chunk's K rows loaded while the previous chunk computes.
-    frag ka[NCD], kn[NCD];
-    est_load_k<T, NCD, KC, KPL>(kb, kvs, min(k0 + l32, k1 - 1), hl, ka);
-    for (int kc = k0; kc < k1; kc += 64) {
-      est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 32 + l32, k1 - 1), hl, kn);
-      chunk(kc, ka);
-      if (kc + 64 < k1) est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 64 + l32, k1 - 1), hl, ka);
-      chunk(kc + 32, kn);
+    if constexpr (kLds) {
+      // chunks of 32 keys from the staged tile
+      for (int kc = k0; kc < k1; kc += 32) {
+        frag kf[NCD];
+#pragma unroll
+        for (int c = 0; c < NCD; ++c) kf[c] = EstKTile<D>::frag(ktile, kc - k0 + l32, c, hl);
+        chunk(kc, kf);
+      }
+    } else {
+      // Chunks of 32 keys in pairs (a tile spans whole 64-key blocks), each
+      // chunk's K rows loaded while the previous chunk computes.
+      frag ka[NCD], kn[NCD];
+      est_load_k<T, NCD, KC, KPL>(kb, kvs, min(k0 + l32, k1 - 1), hl, ka);
+      for (int kc = k0; kc < k1; kc += 64) {
+        est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 32 + l32, k1 - 1), hl, kn);
+        chunk(kc, ka);
+        if (kc + 64 < k1) est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 64 + l32, k1 - 1), hl, ka);
+        chunk(kc + 32, kn);
+      }
     }
     if (hl == 0) {
 #pragma unroll
@@ -180,6 +232,9 @@ __global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePre
   const int nbt = p.n_global / kBlock;
   const T* kb = reinterpret_cast<const T*>(p.k) + p.sk.at(b, 0, kvh);
   const T* q = reinterpret_cast<const T*>(p.q);
+  constexpr bool kLds = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) char ktile[kLds ? EstKTile<D>::BYTES : 16];
+  if constexpr (kLds) EstKTile<D>::stage(ktile, reinterpret_cast<const __bf16*>(kb), kvs, k0, k1);
   for (int hg = wave; hg < G; hg += 4) {
     const int h = kvh * G + hg;
     const int list = (b * p.h_q + h) * p.seg.n_seg + s;
@@ -194,6 +249,12 @@ __global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePre
       for (int c = 0; c < NCD; ++c) qa[rg][c] = load_frag<T>(qr + c * KC + hl * KPL);
     }
     float blk_acc = 0.f;
+    // this lane's rows' LSE (log2 domain), held for the whole tile
+    float lr[2][16];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lr[rg][i] = s_lse[wave][32 * rg + c_row(i, hl)];
     auto chunk = [&](int kc, const frag (&kf)[NCD]) {
       const int key = kc + l32;
       float col = 0.f;
@@ -206,7 +267,7 @@ __global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePre
         for (int i = 0; i < 16; ++i) {
           const int rr = 32 * rg + c_row(i, hl);
           const int row = e - 64 + rr;
-          col += (key < k1 && key <= row) ? fast_exp2(sc[i] * p.sl2 - s_lse[wave][rr]) : 0.f;
+          col += (key < k1 && key <= row) ? fast_exp2(sc[i] * p.sl2 - lr[rg][i]) : 0.f;
         }
       }
       col = half_sum(col);
@@ -223,14 +284,23 @@ __global__ __launch_bounds__(256) void vs_est_pass2_kernel(AttnParams p, TilePre
         blk_acc = 0.f;
       }
     };
-    // as in pass 1: chunk pairs, the next chunk's K rows loaded meanwhile
-    frag ka[NCD], kn[NCD];
-    est_load_k<T, NCD, KC, KPL>(kb, kvs, min(k0 + l32, k1 - 1), hl, ka);
-    for (int kc = k0; kc < k1; kc += 64) {
-      est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 32 + l32, k1 - 1), hl, kn);
-      chunk(kc, ka);
-      if (kc + 64 < k1) est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 64 + l32, k1 - 1), hl, ka);
-      chunk(kc + 32, kn);
+    if constexpr (kLds) {
+      for (int kc = k0; kc < k1; kc += 32) {
+        frag kf[NCD];
+#pragma unroll
+        for (int c = 0; c < NCD; ++c) kf[c] = EstKTile<D>::frag(ktile, kc - k0 + l32, c, hl);
+        chunk(kc, kf);
+      }
+    } else {
+      // as in pass 1: chunk pairs, the next chunk's K rows loaded meanwhile
+      frag ka[NCD], kn[NCD];
+      est_load_k<T, NCD, KC, KPL>(kb, kvs, min(k0 + l32, k1 - 1), hl, ka);
+      for (int kc = k0; kc < k1; kc += 64) {
+        est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 32 + l32, k1 - 1), hl, kn);
+        chunk(kc, ka);
+        if (kc + 64 < k1) est_load_k<T, NCD, KC, KPL>(kb, kvs, min(kc + 64 + l32, k1 - 1), hl, ka);
+        chunk(kc + 32, kn);
+      }
     }
     wave_sync();
   }
