@@ -493,6 +493,40 @@ def test_tie_index():
     assert not errs, errs
 
 
+def test_topp_long_lists_two_stage():
+    """Top-p counts on lists of 32768 columns (N = 32768), where the top-k
+    runs in two stages (per-chunk selections, then their merge) with the
+    device's counts: every count is the integer top-p decision on the
+    device's own scores, and every list is the top-count of those scores
+    (ties to the lowest index), ascending, padded with -1."""
+    dev = _dev()
+    prob = workloads.make_problem(2, n=32768, h_q=8, h_kv=2)
+    hq = prob.h_q
+    grid = [0.05, 0.3, 0.5, 0.7, 0.9, 0.95, 0.99, 1.0]
+    p_v = [grid[h % 8] for h in range(hq)]
+    p_s = [grid[(3 * h + 1) % 8] for h in range(hq)]
+    vcap, scap = [8192] * hq, [32768] * hq
+    gidx, gcnt, vsc, ssc = vs.estimate_index_topp(prob.q.to(dev), prob.k.to(dev), vcap, scap, p_v, p_s,
+                                                  prob.cu_seqlens, return_scores=True)
+    torch.cuda.synchronize()
+    gl = [(a.numpy(), b.numpy()) for a, b in gidx.lists()]
+    gcnt = gcnt.cpu().numpy()
+    vsc, ssc = vsc[0].cpu().numpy(), ssc[0].cpu().numpy()
+    two_stage = 0
+    for h in range(hq):
+        cv, cg = oracle.capacities(vcap[h], scap[h], prob.n, prob.n, prob.block)
+        for kind, pp, cap, gsc in ((0, p_v[h], cv, vsc[h]), (1, p_s[h], cg, ssc[h])):
+            kg = int(gcnt[h, kind])
+            assert kg == min(_topp_count_int(gsc, pp), cap), (h, kind, kg)
+            lst = gl[h][kind]
+            assert lst.size == cap and np.all(lst[kg:] == -1), (h, kind)
+            order = np.lexsort((np.arange(gsc.size), -np.asarray(gsc, np.float64)))
+            assert np.array_equal(lst[:kg], np.sort(order[:kg])), (h, kind)
+            two_stage += kind == 0 and 0 < kg < gsc.size and 2 * kg <= 16384
+    assert two_stage >= 4, two_stage  # the case exercises the two-stage select
+    log(f"  topp on 32768-column lists: counts and lists exact ({two_stage} two-stage lists)")
+
+
 def test_topk_ties_beyond_gathered_bin():
     """The top-k select gathers the entries of the k-th score's leading 11-bit
     bin in LDS (up to 8192); here the observation-window rows of Q are zero,
