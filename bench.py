@@ -617,6 +617,11 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
         log(f"  kernel {name}: {cnt} launches, avg {tot / cnt:.4f} ms, {tot / args.steps:.4f} ms per step")
 
     peak = PEAK_TFLOPS[prob.dtype]
+    # counter figures are kept per workload for its default index (the
+    # Vertical-Slash estimator with fixed budgets); other indices make other
+    # walks, and their traffic is reported only from a file of their own
+    traffic_key = prob.name if (args.estimator == "vs" and topp is None) else f"{prob.name}-{args.estimator}" + (
+        "-topp" if topp is not None else "")
     seg_len = np.diff(np.asarray(cu))
     shape = {"batch": 1, "n": prob.n, "h_q": Hq, "h_kv": prob.h_kv, "d": d,
              "el": 2 if prob.dtype == "bf16" else 4, "n_lists": Hq * len(seg_len),
@@ -649,7 +654,7 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
             avg = tot / cnt * 1e-3
             rec.update(alg_bytes=int(ab), alg_gbs=round(ab / avg / 1e9, 1),
                        alg_hbm_frac=round(ab / avg / 1e9 / HBM_PEAK_GBS, 4))
-            hb = measured_traffic(name, prob.name)
+            hb = measured_traffic(name, traffic_key)
             if hb is not None:
                 rec.update(hbm_bytes=hb, hbm_gbs=round(hb / avg / 1e9, 1))
         per_kernel[name] = rec
@@ -661,7 +666,7 @@ def run(args, prob, topp, dev, torch, vs, accounting, np):
     cnt, tot = kern[dom]
     avg_s = tot / cnt * 1e-3
     launches = cnt / args.steps
-    traffic = measured_traffic(dom, prob.name)
+    traffic = measured_traffic(dom, traffic_key)
     if dom in OWN_PER_ENTRY:
         e = entries[ENTRY_KIND[dom]]
         ach = OWN_PER_ENTRY[dom] * d * e / launches / avg_s / 1e12
