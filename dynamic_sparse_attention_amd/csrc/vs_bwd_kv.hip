@@ -5,7 +5,8 @@
 // them, with P = exp(S - LSE) recomputed from the final LSE and
 // dS = P * (dP - delta), dP = dO V^T.
 //
-// A workgroup is two waves; wave kh owns 32 keys (held as the B operands K^T,
+// A workgroup is two waves (four for pairs of key blocks and for column
+// units); wave kh owns 32 keys (held as the B operands K^T,
 // V^T) and accumulates dK^T, dV^T for them.  The query tiles the unit reads
 // (64 rows of Q and dO of one Q head, plus their LSE * log2(e) and delta)
 // stream through two LDS buffers: while the waves compute on one tile the
@@ -20,7 +21,7 @@
 //   * slash units: (batch, KV head, key block j); the tiles are every
 //     (Q head of the group, selected block-diagonal g) with query block j + g;
 //     dK, dV of the block are complete at the end and are stored.
-//   * column units: (list, 64 gathered vertical columns, range of query
+//   * column units: (list, 128 gathered vertical columns, range of query
 //     blocks); added to dK, dV with fp32 atomics after the slash kernel.
 #include <algorithm>
 
@@ -32,6 +33,7 @@ namespace vs {
 constexpr int kKvThreads = 128;
 constexpr int kKvTiles = 512;  // tile list capacity per pass (query blocks)
 constexpr int kTR = 32;        // query rows per staged tile: half a query block
+constexpr int kKvColWaves = 4;  // waves (32 columns each) per column unit
 
 template <int D>
 struct RowTile {
@@ -500,21 +502,33 @@ __global__ __launch_bounds__(kKvPairThreads) __attribute__((amdgpu_waves_per_eu(
   if (live) wk.store(p, b, kvh, kpos, p.kv_accumulate ? 1 : 0);
 }
 
-template <int D>
-__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_kv_cols_bf16_kernel(AttnParams p) {
+// Column units of NW waves, 32 * NW gathered columns: every staged query
+// tile serves all of them (four waves: the Q / dO tile requests of two
+// waves' units halved).
+template <int NW>
+__host__ __device__ constexpr int kv_col_units(int col_tiles) {
+  return (64 * col_tiles + 32 * NW - 1) / (32 * NW);
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void vs_bwd_kv_cols_bf16_kernel(AttnParams p) {
+  constexpr int NT = 64 * NW;  // threads
+  constexpr int NC = 32 * NW;  // columns per unit
   typedef KvWorkerB<D> W;
-  __shared__ KvLdsB<D> L;
+  __shared__ KvLdsB<D, NW> L;
+  static_assert(sizeof(L.buf) + sizeof(L.tiles) >= NW * 32 * 33 * 4, "epilogue staging must fit in the unit's LDS");
   extern __shared__ uint32_t bits[];  // (nb_seg + 31) / 32 words, sized at launch
   const int tid = threadIdx.x;
   const int kh = tid >> 6;
   const int l32 = tid & 31;
+  const int ctiles = kv_col_units<NW>(p.col_tiles);
   int u = blockIdx.x;
   const int qr = u % p.qranges;
   u /= p.qranges;
-  const int ctile = u % p.col_tiles;
-  const int list = u / p.col_tiles;
+  const int ctile = u % ctiles;
+  const int list = u / ctiles;
   const int vc = p.vcnt[list];
-  if (64 * ctile >= vc) return;
+  if (NC * ctile >= vc) return;
   const int seg = list % p.seg.n_seg;
   const int bh = list / p.seg.n_seg;
   const int b = bh / p.h_q;
@@ -532,8 +546,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     i_lo = 0;
     i_hi = p.nqb;
   }
-  const int* vs = p.vsel + (size_t)list * p.vsel_stride + 64 * ctile;
-  const int ncol = min(64, vc - 64 * ctile);
+  const int* vs = p.vsel + (size_t)list * p.vsel_stride + NC * ctile;
+  const int ncol = min(NC, vc - NC * ctile);
   const int first_blk = vs[0] / kBlock;  // global block of the first column
   // first local query block whose global block is >= first_blk
   int i_first = p.W == 1 ? first_blk : (first_blk <= p.q_rank ? 0 : (first_blk - p.q_rank + p.W - 1) / p.W);
@@ -541,18 +555,18 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int r_hi = min(i_hi, (qr + 1) * p.qrange_len);
   if (r_lo >= r_hi) return;
 
+  // This lane's column, or (past the unit's columns) a position after every
+  // row, which no row sees; the walk keeps only this one value per lane.
   const int col = 32 * kh + l32;
   const bool col_ok = col < ncol;
-  const int m = vs[col_ok ? col : 0];
-  const int bm = m / kBlock - a_blk;
-  const int kpos = local_key_pos(p, m);
+  const int m = col_ok ? vs[col] : 0x3fffffff;
 
   const int sp0 = p.s_ptr[list];
   const int ns = p.s_ptr[list + 1] - sp0;
   const int nwords = (nb_seg + 31) >> 5;
-  for (int w = tid; w < nwords; w += kKvThreads) bits[w] = 0u;
+  for (int w = tid; w < nwords; w += NT) bits[w] = 0u;
   __syncthreads();
-  for (int e = tid; e < ns; e += kKvThreads) {
+  for (int e = tid; e < ns; e += NT) {
     const int g = p.s_idx[sp0 + e];
     if (g >= 0 && g < nb_seg) atomicOr(&bits[g >> 5], 1u << (g & 31));
   }
@@ -560,7 +574,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 
   W wk;
   wk.init_offsets();
-  wk.load_keys(p, b, kvh, kpos);
+  wk.load_keys(p, b, kvh, local_key_pos(p, vs[col_ok ? col : 0]));
   auto qglob = [&](int i) { return p.W == 1 ? i : p.q_rank + p.W * i; };
   auto tile_of = [&](int t, int* hh, int* i, int* fl) {
     *hh = h;
@@ -571,17 +585,18 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   auto body = [&](const KvBuf<D>& B, int t, int, int half) {
     const int qbg = qglob(r_lo + t);
     const int beta_q = qbg - a_blk;
-    const int off = beta_q - bm;
-    const bool lane_ok = col_ok && off >= 0 && ((bits[off >> 5] >> (off & 31)) & 1u) == 0u;
+    const int off = beta_q - ((m >> 6) - a_blk);  // block-diagonal of (query block, column)
+    const bool lane_ok = off >= 0 && ((bits[off >> 5] >> (off & 31)) & 1u) == 0u;
     const int row0 = qbg * kBlock;
     const int mr = lane_ok ? m - row0 : 64;  // first visible row
     wk.template tile<true>(B, p.sl2, kTR * half, [&](int r) { return mr <= r; });
   };
-  kv_pipeline<D>(p, L, b, ntiles, tile_of, body);
+  kv_pipeline<D, decltype(tile_of), decltype(body), false, NW>(p, L, b, ntiles, tile_of, body);
   // Add this wave's dK, dV columns into the gradients, staged through LDS
   // (the tile buffers are free now) one 32-channel slice at a time, so that
   // each atomic instruction covers 32 consecutive channels of two key rows
   // rather than single channels of 32 different rows.
+  const int kpos = local_key_pos(p, vs[col_ok ? col : 0]);
   float* st = reinterpret_cast<float*>(reinterpret_cast<char*>(&L.buf[0]) + kh * 32 * 33 * 4);
   const int nvalid = min(max(ncol - 32 * kh, 0), 32);
   const size_t rstride = (size_t)p.h_kv * D;
@@ -608,7 +623,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
   AttnParams p = p0;
   const dim3 gs((unsigned)(p.batch * p.h_kv * p.nkb));
-  const dim3 gc((unsigned)(p.batch * p.h_q * p.seg.n_seg * p.col_tiles * p.qranges));
+  const dim3 gc((unsigned)(p.batch * p.h_q * p.seg.n_seg * p.qranges * kv_col_units<kKvColWaves>(p.col_tiles)));
   p.hh_lo = 0;
   p.hh_hi = p.h_q / p.h_kv;
   p.kv_accumulate = 0;
@@ -623,12 +638,12 @@ hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
     if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<128, kModeBlocks>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<128, kModeRows>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128>), gs, dim3(kKvThreads), 0, st, p));
-    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128>), gc, dim3(kKvThreads), bits_bytes, st, p));
+    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128, kKvColWaves>), gc, dim3(64 * kKvColWaves), bits_bytes, st, p));
   } else {
     if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<64, kModeBlocks>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<64, kModeRows>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64>), gs, dim3(kKvThreads), 0, st, p));
-    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64>), gc, dim3(kKvThreads), bits_bytes, st, p));
+    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64, kKvColWaves>), gc, dim3(64 * kKvColWaves), bits_bytes, st, p));
   }
   return hipGetLastError();
 }

@@ -200,10 +200,11 @@ def key_major_slash(call, lists, h_q, h_kv, n_seg):
                     count[count > 512 - 128] = 0
 
 
-def column_units(call, lists, h_q, n_seg, v_cap):
-    """Column dK/dV units: columns of the prepared list, their local key
-    positions and the query-block range."""
-    col_tiles = (v_cap + 63) // 64
+def column_units(call, lists, h_q, n_seg, v_cap, cols_per_unit=128):
+    """Column dK/dV units (128 columns each in the bf16 kernel, 64 in the
+    fp32 one): columns of the prepared list, their local key positions and
+    the query-block range."""
+    col_tiles = (64 * ((v_cap + 63) // 64) + cols_per_unit - 1) // cols_per_unit
     qrange_len = 16 if (call.W > 1 and not call.k_all) else 48
     qranges = (call.nqb + qrange_len - 1) // qrange_len
     while qranges > 1 and qranges % 2 == 0:
@@ -214,9 +215,9 @@ def column_units(call, lists, h_q, n_seg, v_cap):
             vsel = prep_vertical(call, lists[h * n_seg + seg][0], seg)
             assert vsel.size <= max(v_cap, 1)
             for ct in range(col_tiles):
-                if 64 * ct >= vsel.size:
+                if cols_per_unit * ct >= vsel.size:
                     continue
-                cols = vsel[64 * ct: 64 * ct + 64]
+                cols = vsel[cols_per_unit * ct: cols_per_unit * (ct + 1)]
                 kpos = call.local_key_pos(cols)
                 assert kpos.min() >= 0 and kpos.max() < call.n_k
                 first_blk = int(cols[0] // BLOCK)
@@ -249,6 +250,7 @@ def test_striped_worker_shape_in_bounds(mode):
             query_major_walk(call, lists, h_q, 1, 128, h_kv * 128 * 2)
             key_major_slash(call, lists, h_q, h_kv, 1)
             column_units(call, lists, h_q, 1, v_cap)
+            column_units(call, lists, h_q, 1, v_cap, cols_per_unit=64)
 
 
 def test_all_chunks_relabelling_is_a_bijection():
