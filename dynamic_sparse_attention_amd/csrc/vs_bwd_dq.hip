@@ -82,13 +82,17 @@ struct DqRowsWorker : RowsTiles<D> {
   // dP^T of n+1 follow.
   template <int P, class Set>
   __device__ __forceinline__ void step(const Set& S, int n, int N) {
+    // Both compute sections run at raised wave priority, the barrier and
+    // the loads at the normal one (8.06 -> 7.97 ms at N = 131072).
     if (n < N) {
       frag dsf[NCK];
+      __builtin_amdgcn_s_setprio(1);
       dscores(S, n, dsf);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int c = 0; c < NCK; ++c) dq[ct] = MF::mma(t_frag(kt[P], ct, c), dsf[c], dq[ct]);
+      __builtin_amdgcn_s_setprio(0);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0) & lgkmcnt_wait0());
     __syncthreads();
@@ -96,7 +100,9 @@ struct DqRowsWorker : RowsTiles<D> {
       this->template dma_share<NP>(S, n + 2, kb, this->krb, kta[P]);
       this->template dma_share<NP>(S, n + 2, vb, this->vrb, vta[P]);
     }
+    __builtin_amdgcn_s_setprio(1);
     if (n + 1 < N) scores(kt[P ^ 1], vt[P ^ 1]);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // All waves take the same number of steps (the longest stream's), so that

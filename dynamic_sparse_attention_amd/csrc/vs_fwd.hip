@@ -468,6 +468,11 @@ struct FwdRowsWorker : RowsTiles<D> {
     float pr[16];
     float rs = 0.f;
     sn = f32x16{0};
+    // The products and exponentials run at raised wave priority, the
+    // barrier and the next tile's loads at the normal one: of the two waves
+    // of a SIMD, the one with work for the matrix cores issues first
+    // (6.50 -> 6.26 ms at N = 131072).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < NCD; ++c) {
       sn = MF::mma(kf[c], qf[c], sn);
@@ -490,6 +495,7 @@ struct FwdRowsWorker : RowsTiles<D> {
       issue(NCD + j + AHEAD);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Step n (P = n % 2).  K(m) and V(m) live in ring slot m % 2.  Entering,
