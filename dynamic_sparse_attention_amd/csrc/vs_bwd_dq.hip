@@ -82,12 +82,14 @@ struct DqRowsWorker : RowsTiles<D> {
   // dP^T of n+1 follow.
   template <int P, class Set>
   __device__ __forceinline__ void step(const Set& S, int n, int N) {
-    // Both compute sections run at raised wave priority, the barrier and
-    // the loads at the normal one (8.06 -> 7.97 ms at N = 131072).
+    // Wave priorities: dS at 1, its dQ products at 2, the barrier and the
+    // loads at 0, the next half's S and dP products at 1 (8.06 -> 7.97 ms
+    // at N = 131072).
     if (n < N) {
       frag dsf[NCK];
       __builtin_amdgcn_s_setprio(1);
       dscores(S, n, dsf);
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll

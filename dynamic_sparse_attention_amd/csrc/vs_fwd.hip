@@ -468,10 +468,11 @@ struct FwdRowsWorker : RowsTiles<D> {
     float pr[16];
     float rs = 0.f;
     sn = f32x16{0};
-    // The products and exponentials run at raised wave priority, the
-    // barrier and the next tile's loads at the normal one: of the two waves
-    // of a SIMD, the one with work for the matrix cores issues first
-    // (6.50 -> 6.26 ms at N = 131072).
+    // Wave priorities: the products of S^T(n+1) with the exponentials at 1,
+    // the P V products at 2, the barrier and the next tile's loads at 0, so
+    // that of the waves of a SIMD the one with matrix-core work issues first
+    // and the one closest to finishing its half goes ahead (6.50 -> 6.26 ms
+    // with 1 / 1 / 0 at N = 131072, 6.14 -> 5.99 ms with 1 / 2 / 0).
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < NCD; ++c) {
@@ -489,6 +490,7 @@ struct FwdRowsWorker : RowsTiles<D> {
     frag pf[NCK];
 #pragma unroll
     for (int c = 0; c < NCK; ++c) pf[c] = MF::pack(&pr[c * KPL]);
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int j = 0; j < NVF; ++j) {
       o[j % NCT] = MF::mma(vf[j], pf[j / NCT], o[j % NCT]);
