@@ -33,7 +33,11 @@ namespace vs {
 constexpr int kKvThreads = 128;
 constexpr int kKvTiles = 512;  // tile list capacity per pass (query blocks)
 constexpr int kTR = 32;        // query rows per staged tile: half a query block
-constexpr int kKvColWaves = 4;  // waves (32 columns each) per column unit
+// Waves (32 columns each) per column unit: four where whole lists are in
+// the call, two for a striped call over one rank's key chunk, which holds
+// about 1/W of each list's columns (there, units of 128 columns would leave
+// half their waves without a column).
+constexpr int kKvColWaves = 4, kKvColWavesChunk = 2;
 
 template <int D>
 struct RowTile {
@@ -623,7 +627,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
   AttnParams p = p0;
   const dim3 gs((unsigned)(p.batch * p.h_kv * p.nkb));
-  const dim3 gc((unsigned)(p.batch * p.h_q * p.seg.n_seg * p.qranges * kv_col_units<kKvColWaves>(p.col_tiles)));
+  const bool chunk = p.W > 1 && !p.k_all;
+  const int ucols = p.batch * p.h_q * p.seg.n_seg * p.qranges;
+  const dim3 gc((unsigned)(ucols * (chunk ? kv_col_units<kKvColWavesChunk>(p.col_tiles)
+                                           : kv_col_units<kKvColWaves>(p.col_tiles))));
   p.hh_lo = 0;
   p.hh_hi = p.h_q / p.h_kv;
   p.kv_accumulate = 0;
@@ -638,12 +645,14 @@ hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
     if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<128, kModeBlocks>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<128, kModeRows>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128>), gs, dim3(kKvThreads), 0, st, p));
-    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128, kKvColWaves>), gc, dim3(64 * kKvColWaves), bits_bytes, st, p));
+    if (gc.x && chunk) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128, kKvColWavesChunk>), gc, dim3(64 * kKvColWavesChunk), bits_bytes, st, p));
+    else if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128, kKvColWaves>), gc, dim3(64 * kKvColWaves), bits_bytes, st, p));
   } else {
     if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<64, kModeBlocks>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<64, kModeRows>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64>), gs, dim3(kKvThreads), 0, st, p));
-    if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64, kKvColWaves>), gc, dim3(64 * kKvColWaves), bits_bytes, st, p));
+    if (gc.x && chunk) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64, kKvColWavesChunk>), gc, dim3(64 * kKvColWavesChunk), bits_bytes, st, p));
+    else if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64, kKvColWaves>), gc, dim3(64 * kKvColWaves), bits_bytes, st, p));
   }
   return hipGetLastError();
 }
