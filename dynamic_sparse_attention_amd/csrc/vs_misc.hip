@@ -52,15 +52,18 @@ __global__ __launch_bounds__(kPrepThreads) void vs_prep_vertical_kernel(AttnPara
 
 // Whether the Q heads of each (batch, KV head) group share their selected
 // block-diagonals: over up to 1024 evenly spread lists of non-leading heads,
-// the fraction of their entries that the group's first head (same batch and
-// segment) also selected (the first kShareCap entries of each list, a
-// sample for longer ones).  share[0] = 1 when it is at least one half; this
-// picks the work mapping of the query-major kernels (qmajor_item).  Each
-// wave takes one sampled list: it stages the leading head's list in LDS and
-// its lanes binary-search their own entries in it.  Lists are ascending,
-// with -1 padding at the end (ordered as +inf).  The workgroups add their
-// counts into share[2..5] (two 64-bit sums, zeroed by vs_prep_vertical_kernel
-// just before) and take a ticket in share[6]; the last one decides.
+// the entries that the group's first head (same batch and segment) also
+// selected, as a fraction of the shorter of the two lists (the first
+// kShareCap entries of each, a sample for longer ones).  Measured against
+// the shorter list, heads whose top-k lists are nested (budgets that differ
+// per head) count as sharing, as their diagonal tiles are shared.
+// share[0] = 1 when the fraction is at least one half; this picks the work
+// mapping of the query-major kernels (qmajor_item).  Each wave takes one
+// sampled list: it stages the leading head's list in LDS and its lanes
+// binary-search their own entries in it.  Lists are ascending, with -1
+// padding at the end (ordered as +inf).  The workgroups add their counts
+// into share[2..5] (two 64-bit sums, zeroed by vs_prep_vertical_kernel just
+// before) and take a ticket in share[6]; the last one decides.
 constexpr int kShareCap = 2048;
 constexpr int kShareSample = 1024;
 
@@ -88,12 +91,16 @@ __global__ __launch_bounds__(256) void vs_group_share_kernel(AttnParams p, int* 
       const int* B = p.s_idx + p.s_ptr[l0];
       const int na = min(p.s_ptr[l + 1] - p.s_ptr[l], kShareCap);
       const int nb = min(p.s_ptr[l0 + 1] - p.s_ptr[l0], kShareCap);
-      for (int i = lane; i < nb; i += 64) lead[wave][i] = B[i];
+      int cb = 0, ca = 0;  // valid entries of the two lists
+      for (int i = lane; i < nb; i += 64) {
+        lead[wave][i] = B[i];
+        cb += B[i] >= 0;
+      }
       wave_sync();
       for (int i = lane; i < na; i += 64) {
         const int x = A[i];
         if (x < 0) continue;
-        ++total;
+        ++ca;
         int lo = 0, hi = nb;
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
@@ -103,6 +110,12 @@ __global__ __launch_bounds__(256) void vs_group_share_kernel(AttnParams p, int* 
         }
         common += lo < nb && lead[wave][lo] == x;
       }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        ca += __shfl_xor(ca, o, 64);
+        cb += __shfl_xor(cb, o, 64);
+      }
+      if (lane == 0) total = min(ca, cb);  // summed over the wave below
     }
   }
 #pragma unroll
