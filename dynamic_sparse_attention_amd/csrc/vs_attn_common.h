@@ -77,6 +77,8 @@ struct AttnParams {
   int col_tiles;      // backward column units: column tiles per list
   int hh_lo, hh_hi;   // backward slash dK/dV: Q heads (within the GQA group) of this launch
   int kv_accumulate;  // backward slash dK/dV: add to dK/dV instead of storing
+  int kv_parts;       // backward slash dK/dV: workgroups per key block, each over
+                      // 1/kv_parts of the heads, adding with fp32 atomics when > 1
   SegTable seg;
 };
 

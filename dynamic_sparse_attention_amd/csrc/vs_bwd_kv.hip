@@ -307,10 +307,17 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int l32 = tid & 31;
   const int BH = p.batch * p.h_kv;
   const int bh = blockIdx.x % BH;
-  const int j = blockIdx.x / BH;
+  // part of the key block's heads (kv_parts workgroups per key block, the
+  // parts of a key block next to each other so that the longest walks start
+  // first)
+  const int part = (blockIdx.x / BH) % p.kv_parts;
+  const int j = blockIdx.x / BH / p.kv_parts;
   const int b = bh / p.h_kv;
   const int kvh = bh % p.h_kv;
   const int G = p.h_q / p.h_kv;
+  const int hpp = (p.hh_hi - p.hh_lo) / p.kv_parts;  // heads per part
+  const int hh_lo = p.hh_lo + part * hpp;
+  const int hh_hi = hh_lo + hpp;
   int kb_glob, seg, a_blk, nb_seg;
   if (p.W == 1) {
     kb_glob = j;
@@ -327,6 +334,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int kpos = j * kBlock + 32 * kh + l32;
   const int kin = 32 * kh + l32;
 
+  static_assert(sizeof(L.buf) >= 2 * 32 * 33 * 4, "epilogue staging must fit in the tile buffers");
   W wk;
   wk.init_offsets();
   wk.load_keys(p, b, kvh, kpos);
@@ -341,7 +349,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // own, so that the main walk has no masking at all.
   {
     int i = -1;
-    if (tid >= p.hh_lo && tid < p.hh_hi) {
+    if (tid >= hh_lo && tid < hh_hi) {
       const int list = (b * p.h_q + kvh * G + tid) * p.seg.n_seg + seg;
       const int sp0 = p.s_ptr[list];
       if (p.s_ptr[list + 1] > sp0 && p.s_idx[sp0] == 0) i = local_query_block(p, kb_glob);
@@ -358,7 +366,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   auto body = [&](const KvBuf<D>& B, int, int, int half) {
     wk.template tile<false>(B, p.sl2, kTR * half, [](int) { return true; });
   };
-  for (int hh = p.hh_lo; hh < p.hh_hi; ++hh) {
+  for (int hh = hh_lo; hh < hh_hi; ++hh) {
     const int list = (b * p.h_q + kvh * G + hh) * p.seg.n_seg + seg;
     // candidates: the head's selected block-diagonals g > 0 (query block kb + g)
     const int sp0 = p.s_ptr[list];
@@ -382,7 +390,31 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
   }
   kv_pipeline<D>(p, L, b, count, tile_of, body);
-  wk.store(p, b, kvh, kpos, p.kv_accumulate ? 1 : 0);
+  if (p.kv_parts == 1) {
+    wk.store(p, b, kvh, kpos, p.kv_accumulate ? 1 : 0);
+    return;
+  }
+  // Several parts add into the same keys: fp32 atomics into the zeroed (or
+  // accumulating) dK, dV, staged through LDS (the tile buffers are free after
+  // the walk's last barrier) one 32-channel slice at a time, so that every
+  // atomic instruction covers 32 consecutive channels of two key rows.
+  float* st = reinterpret_cast<float*>(reinterpret_cast<char*>(&L.buf[0]) + kh * 32 * 33 * 4);
+  const size_t rstride = (size_t)p.h_kv * D;
+  const size_t row0 = (((size_t)b * p.n_k + (size_t)j * kBlock + 32 * kh) * p.h_kv + kvh) * D;
+  float* const gdst[2] = {p.dk + row0, p.dv + row0};
+  const int hl = (tid & 63) >> 5;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ct = 0; ct < W::NCT; ++ct) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        st[l32 * 33 + c_row(i, hl)] = t == 0 ? wk.dk[ct][i] * p.scale : wk.dv[ct][i];
+      wave_sync();
+#pragma unroll 4
+      for (int r = hl; r < 32; r += 2) atomicAdd(gdst[t] + (size_t)r * rstride + 32 * ct + l32, st[r * 33 + l32]);
+      wave_sync();
+    }
 }
 
 // MODE of the paired kernel below: a block selection (p.bmask) or a per-row
@@ -624,6 +656,43 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
 }
 
+// dK = dV = 0 before slash units that add with atomics (a kernel rather than
+// a memset, so that the call can be captured in a graph).
+__global__ __launch_bounds__(256) void vs_zero2_kernel(f32x4* a, f32x4* c, size_t n4) {
+  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n4; x += (size_t)gridDim.x * 256) {
+    a[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    c[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Workgroups per key block of the slash dK/dV kernel.  A unit's walk is
+// proportional to the block-diagonals that still fit after its key block, so
+// the earliest key blocks walk the longest; a grid of fewer than two rounds
+// of resident workgroups (four per CU) finishes with the longest walk, on a
+// chip mostly idle.  There the heads of a key block are split over parts (a
+// power of two dividing the group, at most 4), whose results add with
+// atomics.
+static int slash_parts(const AttnParams& p, unsigned units) {
+  const int G = (p.hh_hi - p.hh_lo);
+  const long rounds2 = 2L * 4 * device_cus();
+  int parts = 1;
+  while (parts < 4 && (long)units * parts < rounds2 && G % (2 * parts) == 0) parts *= 2;
+  return parts;
+}
+
 hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
   AttnParams p = p0;
   const dim3 gs((unsigned)(p.batch * p.h_kv * p.nkb));
@@ -634,6 +703,14 @@ hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
   p.hh_lo = 0;
   p.hh_hi = p.h_q / p.h_kv;
   p.kv_accumulate = 0;
+  p.kv_parts = (p.bmask || p.rmask) ? 1 : slash_parts(p, gs.x);
+  const dim3 gsp(gs.x * p.kv_parts);
+  if (gs.x && p.kv_parts > 1) {
+    const size_t n4 = (size_t)p.batch * p.n_k * p.h_kv * d / 4;
+    const unsigned zb = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
+    VS_TRACED(st, "vs_zero_dkdv", hipLaunchKernelGGL(vs_zero2_kernel, dim3(zb), dim3(256), 0, st,
+                                                      reinterpret_cast<f32x4*>(p.dk), reinterpret_cast<f32x4*>(p.dv), n4));
+  }
   // bitmap of the selected block-diagonals: one bit per block of the longest segment
   int nb_max = p.W == 1 ? 0 : p.n_global / kBlock;
   for (int sgi = 0; p.W == 1 && sgi < p.seg.n_seg; ++sgi)
@@ -644,13 +721,13 @@ hipError_t launch_bwd_kv_bf16(const AttnParams& p0, int d, hipStream_t st) {
   if (d == 128) {
     if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<128, kModeBlocks>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<128, kModeRows>), gp, dim3(kKvPairThreads), 0, st, p));
-    else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128>), gs, dim3(kKvThreads), 0, st, p));
+    else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<128>), gsp, dim3(kKvThreads), 0, st, p));
     if (gc.x && chunk) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128, kKvColWavesChunk>), gc, dim3(64 * kKvColWavesChunk), bits_bytes, st, p));
     else if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<128, kKvColWaves>), gc, dim3(64 * kKvColWaves), bits_bytes, st, p));
   } else {
     if (gs.x && p.bmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<64, kModeBlocks>), gp, dim3(kKvPairThreads), 0, st, p));
     else if (gs.x && p.rmask) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_pair_bf16_kernel<64, kModeRows>), gp, dim3(kKvPairThreads), 0, st, p));
-    else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64>), gs, dim3(kKvThreads), 0, st, p));
+    else if (gs.x) VS_TRACED(st, "vs_bwd_dkdv_slash", hipLaunchKernelGGL((vs_bwd_kv_slash_bf16_kernel<64>), gsp, dim3(kKvThreads), 0, st, p));
     if (gc.x && chunk) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64, kKvColWavesChunk>), gc, dim3(64 * kKvColWavesChunk), bits_bytes, st, p));
     else if (gc.x) VS_TRACED(st, "vs_bwd_dkdv_cols", hipLaunchKernelGGL((vs_bwd_kv_cols_bf16_kernel<64, kKvColWaves>), gc, dim3(64 * kKvColWaves), bits_bytes, st, p));
   }

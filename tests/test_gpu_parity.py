@@ -40,8 +40,11 @@ CASES = {
     "w2-gqa32": dict(wid=2, n=1024, h_q=32, h_kv=1, v_budget=100, s_budget=256),
     # 8 Q heads x 64 block-diagonals: early key blocks are read by up to 512
     # (head, query block) tiles, so the slash dK/dV kernel empties its tile list
-    # and keeps appending (checked below by slash_tile_flushes)
-    "w2-flush-gqa8": dict(wid=2, n=8192, h_q=8, h_kv=1, v_budget=300, s_budget=4096),
+    # and keeps appending (checked below by slash_tile_flushes).  Batch rows 1-15
+    # carry empty lists: with 16 x 128 key blocks the launch has two rounds of
+    # resident workgroups, so every key block's heads stay in one workgroup
+    # (smaller grids split them over several) and its list holds all of them.
+    "w2-flush-gqa8": dict(wid=2, n=8192, h_q=8, h_kv=1, v_budget=300, s_budget=4096, pad_batch=16),
 }
 
 # The slash dK/dV kernel collects the (head, query block) tiles of a key block
@@ -74,6 +77,7 @@ def slash_tile_flushes(index, h_q, h_kv, nb):
 
 def run_case(name, dev, check_index=True):
     kw = dict(CASES[name])
+    pad_batch = kw.pop("pad_batch", 1)
     prob = workloads.make_problem(kw.pop("wid"), **kw)
     log(f"case {name}: n={prob.n} hq={prob.h_q} hkv={prob.h_kv} d={prob.d} dtype={prob.dtype} "
         f"docs={len(prob.cu_seqlens) - 1}")
@@ -103,10 +107,23 @@ def run_case(name, dev, check_index=True):
         torch.cuda.synchronize()
         index_parity(name, oidx, oscores, [(a.numpy(), b.numpy()) for a, b in gidx.lists()],
                      vsc[0].cpu().numpy(), ssc[0].cpu().numpy(), prob)
-    idx = vs.index_from_lists(lists_for_gpu(oidx, prob.h_q, n_seg), dev)
+    lists = lists_for_gpu(oidx, prob.h_q, n_seg)
+    if pad_batch > 1:
+        # batch rows 1.. : other inputs, no selected entries
+        g = torch.Generator().manual_seed(prob.seed + 7)
+        pad = [torch.randn((pad_batch - 1,) + tuple(t.shape[1:]), generator=g).to(t.dtype)
+               for t in (prob.q, prob.k, prob.v, prob.do)]
+        gq, gk, gv, gdo = (torch.cat([t, x]).to(dev) for t, x in zip((prob.q, prob.k, prob.v, prob.do), pad))
+        lists = lists + [([], [])] * (len(lists) * (pad_batch - 1))
+        log(f"  {pad_batch} batch rows, rows 1-{pad_batch - 1} with empty lists")
+    idx = vs.index_from_lists(lists, dev)
     o, lse = vs.sparse_attn_fwd(gq, gk, gv, idx, cu)
     gdq, gdk, gdv = vs.sparse_attn_bwd(gq, gk, gv, o, gdo, lse, idx, cu_seqlens=cu)
     torch.cuda.synchronize()
+    if pad_batch > 1:
+        assert torch.isneginf(lse[1:]).all()
+        for t in (o, gdq, gdk, gdv):
+            assert not t[1:].float().abs().max().item(), "rows without selected entries must stay zero"
     bq = bk = bv = None
     if prob.dtype == "bf16":
         bq, bk, bv = oracle.bwd_rounding_bounds(q, k, v, do, O, L, pos, pos, prob.cu_seqlens, oidx)

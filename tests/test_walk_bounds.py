@@ -200,6 +200,63 @@ def key_major_slash(call, lists, h_q, h_kv, n_seg):
                     count[count > 512 - 128] = 0
 
 
+def slash_parts(units, G, cus=256):
+    """Workgroups per key block of the slash dK/dV kernel (mirrors the
+    launcher): doubled while the grid is under two rounds of four resident
+    workgroups per CU, up to 4, as long as the part count divides the group."""
+    parts = 1
+    while parts < 4 and units * parts < 2 * 4 * cus and G % (2 * parts) == 0:
+        parts *= 2
+    return parts
+
+
+def slash_grid(batch, h_kv, nkb, G, n_k, D):
+    """Decode of every workgroup of the slash dK/dV grid, as the kernel does:
+    (batch, KV head) fastest, then the part, then the key block.  Every
+    (batch, KV head, key block, head) is walked by exactly one workgroup, the
+    head ranges stay inside the group, and the atomic epilogue's rows and
+    channels (part count above one), the zero fill and the LDS staging stay
+    inside dK / dV and the tile buffers."""
+    parts = slash_parts(batch * h_kv * nkb, G)
+    BH = batch * h_kv
+    wg = np.arange(BH * nkb * parts)
+    bh = wg % BH
+    part = (wg // BH) % parts
+    j = wg // BH // parts
+    assert j.max() < nkb
+    hpp = G // parts
+    assert hpp * parts == G
+    seen = np.zeros((BH, nkb, G), np.int64)
+    for hh in range(hpp):
+        np.add.at(seen, (bh, j, part * hpp + hh), 1)
+    assert np.all(seen == 1)
+    if parts > 1:
+        # epilogue: rows j*64 + 32*kh + r (kh < 2, r < 32), channels 32*ct + l32
+        b, kvh = bh // h_kv, bh % h_kv
+        last_row = ((b * n_k + j * BLOCK + 32 + 31) * h_kv + kvh) * D + (D - 32) + 31
+        assert last_row.max() < batch * n_k * h_kv * D
+        assert (batch * n_k * h_kv * D) % 4 == 0  # the zero fill's 16-byte stores
+        q_bytes = 32 * D * 2
+        assert 2 * (2 * q_bytes + 3 * 32 * 4) >= 2 * 32 * 33 * 4
+    return parts
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 512, 8), (1, 2, 256, 8), (1, 2, 2048, 8), (1, 1, 128, 8),
+                                   (16, 1, 128, 8), (2, 2, 64, 8), (1, 1, 48, 3), (1, 1, 16, 32),
+                                   (1, 4, 32, 1), (1, 2, 8192, 8)])
+def test_slash_parts_grid(shape):
+    """The split of a key block's heads over workgroups, at the benchmark
+    shapes (N = 32768 and 131072, a striped chunk call of 16384 keys, the
+    one-call worker) and the small test shapes."""
+    batch, h_kv, nkb, G = shape
+    for D in (64, 128):
+        parts = slash_grid(batch, h_kv, nkb, G, nkb * BLOCK, D)
+    want = {(1, 2, 512, 8): 2, (1, 2, 256, 8): 4, (1, 2, 2048, 8): 1, (16, 1, 128, 8): 1,
+            (1, 2, 8192, 8): 1, (1, 1, 48, 3): 1}
+    if shape in want:
+        assert parts == want[shape]
+
+
 def column_units(call, lists, h_q, n_seg, v_cap, cols_per_unit=128):
     """Column dK/dV units (128 columns each in the bf16 kernel, 64 in the
     fp32 one): columns of the prepared list, their local key positions and
