@@ -50,6 +50,13 @@ def _stream(dev: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _small_to_dev(values, dtype, dev: torch.device) -> torch.Tensor:
+    """A short host list on the device, staged in pinned memory and copied
+    asynchronously on the current stream (a copy from pageable memory would
+    first wait for the stream's earlier work)."""
+    return torch.tensor(values, dtype=dtype).pin_memory().to(dev, non_blocking=True)
+
+
 def _need(t: torch.Tensor, name: str, dtype=None, dev=None, strided=False):
     """Checks a tensor argument.  strided: a [batch, token, head, d] view whose
     last dimension is contiguous is accepted (its strides go to the library);
@@ -180,8 +187,8 @@ def estimate_index(q: torch.Tensor, k: torch.Tensor, v_budget: Sequence[int],
     dc = _dtype_code(q)
     vp, sp, vm, sm = index_capacity(B, Hq, Hkv, d, N, v_budget, s_budget, cu_seqlens, dc)
     P = _Problem(B, Hq, Hkv, d, N, N, dc, cu_seqlens, None, None, q=q, k=k)
-    v_ptr = torch.tensor(vp, dtype=torch.int32, device=dev)
-    s_ptr = torch.tensor(sp, dtype=torch.int32, device=dev)
+    v_ptr = _small_to_dev(vp, torch.int32, dev)
+    s_ptr = _small_to_dev(sp, torch.int32, dev)
     v_idx = torch.empty(max(vp[-1], 1), dtype=torch.int32, device=dev)
     s_idx = torch.empty(max(sp[-1], 1), dtype=torch.int32, device=dev)
     v_score = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if return_scores else None
@@ -218,12 +225,12 @@ def estimate_index_topp(q: torch.Tensor, k: torch.Tensor, v_cap: Sequence[int], 
     dc = _dtype_code(q)
     vp, sp, vm, sm = index_capacity(B, Hq, Hkv, d, N, v_cap, s_cap, cu_seqlens, dc)
     P = _Problem(B, Hq, Hkv, d, N, N, dc, cu_seqlens, None, None, q=q, k=k)
-    v_ptr = torch.tensor(vp, dtype=torch.int32, device=dev)
-    s_ptr = torch.tensor(sp, dtype=torch.int32, device=dev)
+    v_ptr = _small_to_dev(vp, torch.int32, dev)
+    s_ptr = _small_to_dev(sp, torch.int32, dev)
     v_idx = torch.empty(max(vp[-1], 1), dtype=torch.int32, device=dev)
     s_idx = torch.empty(max(sp[-1], 1), dtype=torch.int32, device=dev)
-    pv = torch.tensor([float(x) for x in p_v], dtype=torch.float32, device=dev)
-    ps = torch.tensor([float(x) for x in p_s], dtype=torch.float32, device=dev)
+    pv = _small_to_dev([float(x) for x in p_v], torch.float32, dev)
+    ps = _small_to_dev([float(x) for x in p_s], torch.float32, dev)
     counts = torch.empty((len(vp) - 1, 2), dtype=torch.int32, device=dev)
     v_score = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if return_scores else None
     s_score = torch.empty((B, Hq, N // BLOCK), dtype=torch.float32, device=dev) if return_scores else None
