@@ -20,7 +20,9 @@
 //
 //   * slash units: (batch, KV head, key block j); the tiles are every
 //     (Q head of the group, selected block-diagonal g) with query block j + g;
-//     dK, dV of the block are complete at the end and are stored.
+//     dK, dV of the block are complete at the end and are stored.  A grid too
+//     small for the chip splits each key block's heads over 2 or 4 units,
+//     which add their dK, dV with fp32 atomics into zeroed arrays.
 //   * column units: (list, 128 gathered vertical columns, range of query
 //     blocks); added to dK, dV with fp32 atomics after the slash kernel.
 #include <algorithm>
