@@ -26,6 +26,7 @@
 //   * column units: (list, 128 gathered vertical columns, range of query
 //     blocks); added to dK, dV with fp32 atomics after the slash kernel.
 #include <algorithm>
+#include <atomic>
 
 #include "vs_attn_common.h"
 #include "vs_trace.h"
@@ -667,17 +668,18 @@ __global__ __launch_bounds__(256) void vs_zero2_kernel(f32x4* a, f32x4* c, size_
   }
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; calls from
+// several host threads may both look it up and store the same value).
 static int device_cus() {
-  static int cus[64];
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // Workgroups per key block of the slash dK/dV kernel.  A unit's walk is
